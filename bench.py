@@ -1,0 +1,199 @@
+"""Benchmark of the verify-decode layer step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one whole layer step (input boundary -> attention -> attention boundary ->
+router/routing/pooler -> experts -> unpooler) of b = 8 verify rows at hidden 4096 with an
+8192-token paged context, replayed from a HIP graph.  Inputs are resident in HBM before the
+timed region.  To keep the 256 MB MALL and the L2s from serving repeat reads, steps rotate
+over R independent copies of the weights and KV (R * touched bytes >= 1 GB).  Prints one
+JSON line.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def algorithmic_bytes(wk, counts_per_layer):
+    """Weights + KV bytes one layer step must move (activations excluded; experts counted
+    only if they received a routed row)."""
+    d, w = wk["dims"], wk["workload"]
+    H, Hq, Hkv, D = d["hidden"], d["n_q_heads"], d["n_kv_heads"], d["head_dim"]
+    E, I, b = d["n_experts"], d["inter"], w.b
+    dense = 2 * (2 * Hq + 2 * Hkv) * D * H + 2 * H * Hq * D + 2 * E * H + 4 * 4 * H
+    per_expert = 3 * H * I * (0.5 + 1.0 / 16) + 8
+    total = 0.0
+    for li, counts in enumerate(counts_per_layer):
+        lens = wk["layers"][li]["seq_lens"].numpy().astype(np.int64)
+        kv = lens.sum() * Hkv * D * 2 * 2 + b * Hkv * D * 2 * 2
+        total += dense + int((counts > 0).sum()) * per_expert + kv
+    return total, int((counts_per_layer[0] > 0).sum()) * per_expert
+
+
+def cpu_baseline(wk):
+    """The oracle, as it stands, on one full layer step of the workload."""
+    import threadpoolctl
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import oracle
+    from tests.helpers import np64, oracle_layer_inputs
+    lay, act, d = wk["layers"][0], wk["act"], wk["dims"]
+    inp = oracle_layer_inputs(lay, act)
+    threads = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
+    t0 = time.perf_counter()
+    oracle.layer_step(inp, d, branch_in=np64(act["branch_in"]))
+    dt = time.perf_counter() - t0
+    return {"value": dt * 1e6, "unit": "us per layer-step", "cores": int(threads), "kind": "oracle",
+            "sample": f"one full layer step of {wk['workload'].name} (fp64 NumPy oracle), "
+                      f"{len(os.sched_getaffinity(0))} host cores visible"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="h4096_b8_ctx8k")
+    ap.add_argument("--copies", type=int, default=0, help="rotation copies (0: auto, >= 1 GB)")
+    ap.add_argument("--roofline-iters", type=int, default=100)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported by this build "
+              "(the layer step is measured on one GPU's share; see the sharding notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    from speculative_verify_decode_amd import binding as B
+    from speculative_verify_decode_amd import synth
+    from speculative_verify_decode_amd.runner import StepRunner
+
+    B.lib()                                   # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    wk = synth.make_workload(args.workload)
+    print(f"[bench] generated {args.workload} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    # first copy: one eager step to learn the routing (touched experts) and the byte count
+    r0 = StepRunner(wk, dev)
+    s = r0.act["stream"].clone()
+    r0.layer_step(0, s, r0.act["branch_in"])
+    torch.cuda.synchronize()
+    counts = r0.route_t["expert_counts"].cpu().numpy()
+    step_bytes, expert_bytes = algorithmic_bytes(wk, [counts])
+    R = args.copies or max(2, math.ceil(1.0e9 / step_bytes))
+    runners = [r0] + [StepRunner(wk, dev) for _ in range(R - 1)]
+    print(f"[bench] {R} rotation copies, {step_bytes / 1e6:.1f} MB algorithmic per step",
+          file=sys.stderr, flush=True)
+
+    # one captured graph per copy, on a side stream
+    st = torch.cuda.Stream()
+    graphs, streams = [], []
+    for r in runners:
+        sb = r.act["stream"].clone()
+        streams.append(sb)
+        with torch.cuda.stream(st):
+            r.layer_step(0, sb, r.act["branch_in"], stream=st)      # warm (lazy module load)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=st):
+            r.layer_step(0, sb, r.act["branch_in"], stream=st)
+        graphs.append(g)
+    torch.cuda.synchronize()
+
+    with torch.cuda.stream(st):
+        for i in range(args.warmup):
+            graphs[i % R].replay()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    with torch.cuda.stream(st):
+        ev[0].record(st)
+        for i in range(K):
+            graphs[i % R].replay()
+            ev[i + 1].record(st)
+    torch.cuda.synchronize()
+    total_ms = ev[0].elapsed_time(ev[K])
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(K)]) * 1e3   # us
+    us = total_ms * 1e3 / K
+
+    # hot-cache number (same copy every step), labelled separately
+    with torch.cuda.stream(st):
+        h0 = torch.cuda.Event(enable_timing=True)
+        h1 = torch.cuda.Event(enable_timing=True)
+        for _ in range(10):
+            graphs[0].replay()
+        h0.record(st)
+        for _ in range(50):
+            graphs[0].replay()
+        h1.record(st)
+    torch.cuda.synchronize()
+    hot_us = h0.elapsed_time(h1) * 1e3 / 50
+
+    # dominant kernels: the routed-expert GEMMs (sd_moe_experts), timed live with HIP events
+    # on their launch stream, rotating over the copies like the step
+    d, b = wk["dims"], wk["workload"].b
+    y = torch.empty(b * d["top_k"], d["hidden"], dtype=torch.float32, device=dev)
+    x = [r.act["front_embed"] for r in runners]
+    n_it = args.roofline_iters
+    e0 = [torch.cuda.Event(enable_timing=True) for _ in range(n_it)]
+    e1 = [torch.cuda.Event(enable_timing=True) for _ in range(n_it)]
+    with torch.cuda.stream(st):
+        for i in range(10):
+            r = runners[i % R]
+            B.moe_experts(r.dims, b, x[i % R], r.layers[0].moe_w, r.route, y, None, r.ws, stream=st)
+        for i in range(n_it):
+            r = runners[i % R]
+            e0[i].record(st)
+            B.moe_experts(r.dims, b, x[i % R], r.layers[0].moe_w, r.route, y, None, r.ws, stream=st)
+            e1[i].record(st)
+    torch.cuda.synchronize()
+    exp_us = float(np.mean([e0[i].elapsed_time(e1[i]) for i in range(n_it)])) * 1e3
+    achieved = expert_bytes / (exp_us * 1e-6) / 1e9
+
+    out = {
+        "metric": "µs per decode layer-step (b=8 verify) + achieved HBM GB/s vs peak",
+        "value": round(us, 3),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "b": b, "hidden": d["hidden"],
+                   "n_q_heads": d["n_q_heads"], "n_kv_heads": d["n_kv_heads"],
+                   "head_dim": d["head_dim"], "experts": d["n_experts"], "top_k": d["top_k"],
+                   "inter": d["inter"], "context": int(wk["layers"][0]["seq_lens"].sum()),
+                   "touched_experts": int((counts > 0).sum()), "rotation_copies": R},
+        "step_bytes": int(step_bytes),
+        "step_GBps": round(step_bytes / (us * 1e-6) / 1e9, 1),
+        "step_frac_hbm": round(step_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        "tokens_per_s": round(b * 1e6 / us, 1),
+        "us_p10_p50_p90": [round(float(np.percentile(per, q)), 3) for q in (10, 50, 90)],
+        "hot_cache_us": round(hot_us, 3),
+        "roofline": {"bound": "hbm", "kernel": "routed-expert GEMMs (sd_moe_experts)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "launch_us": round(exp_us, 3), "bytes_per_launch": int(expert_bytes)},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on one layer step", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wk)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

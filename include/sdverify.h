@@ -1,0 +1,208 @@
+/*
+ * sdverify.h -- C ABI of libsdverify.so: one speculative-verification decode layer step of
+ * a Muse-Spark-style MoE decoder layer on one MI355X (gfx950) GPU.
+ *
+ * Sources, cited by page title and section:
+ *   [DEC] "vllm.models.muse_spark.nvidia.specialized_decode.runtime.decode": module
+ *         docstring (the per-layer step list), SpecializedDecode.run / .build / .plan,
+ *         decode_metadata.
+ *   [RT]  "vllm.models.muse_spark.nvidia.specialized_decode.runtime": unsupported
+ *         (BF16 KV cache, block size 16, 7 speculative tokens, BF16 draft logits).
+ *   [DSP] "vllm.models.muse_spark.common.dspark": MuseSparkDSparkDecoderLayer.forward
+ *         (sandwich norms), MuseSparkDSparkForCausalLM (stacked weights, output transform,
+ *         draft_id_to_target_id), MuseSparkDSparkModel.precompute_and_store_context_kv.
+ *
+ * Conventions (all entry points):
+ *   - Every pointer is a DEVICE pointer unless stated otherwise; the caller owns all memory.
+ *     The library never allocates, frees or synchronises; weights are read-only (the
+ *     executor reads the backbone and never modifies it, [DEC] SpecializedDecode).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only enqueues
+ *     kernels on it and may be captured into a HIP graph ([DEC] module docstring and
+ *     SpecializedDecode.plan: the step runs inside a captured graph).
+ *   - bf16 tensors are raw 16-bit bfloat16; fp32 are IEEE float; all row-major, contiguous.
+ *   - b = rows of the step = n_req * q_rows, request-major (row t belongs to request
+ *     t / q_rows).  q_rows = 1 + 7 verify tokens ([RT] unsupported; [DEC] decode_metadata).
+ *   - Return 0 on success, a negative SD_E* code otherwise; nothing is enqueued on an
+ *     error.  sd_last_error() gives the first failing reason in words (thread-local).
+ *   - Validation happens on the host, before any launch: dims, sizes, null pointers,
+ *     16-byte alignment of vector-loaded tensors, workspace size.  Device-side contents
+ *     (block-table entries, slot mapping, positions) are the caller's contract: they must
+ *     address blocks < num_blocks, positions < seq_len, and be consistent with each other.
+ *   - Calls that share a workspace on different streams must not overlap.
+ */
+#ifndef SDVERIFY_H
+#define SDVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SD_ABI_VERSION 1
+
+enum {
+  SD_OK = 0,
+  SD_EINVAL = -1,        /* a null pointer, a bad size or a misaligned tensor            */
+  SD_EUNSUPPORTED = -2,  /* valid request outside what the kernels implement             */
+  SD_EHIP = -3,          /* a HIP runtime call failed (launch error)                     */
+  SD_EWORKSPACE = -4     /* workspace null or smaller than sd_workspace_bytes()          */
+};
+
+/* Layer dimensions.  Supported: hidden % 256 == 0 and <= 8192; head_dim in {64, 128};
+ * n_q_heads % n_kv_heads == 0 with (n_q_heads / n_kv_heads) * q_rows in {16, 32, 64};
+ * q_rows == 8; block_size == 16 ([RT] unsupported: KV block sizes other than 16);
+ * n_experts in [1, 256]; 1 <= top_k <= min(8, n_experts); inter % 128 == 0;
+ * qk_norm in {0, 1}; eps > 0; attn_scale 0 means head_dim ** -0.5. */
+typedef struct sd_dims {
+  int32_t hidden, n_q_heads, n_kv_heads, head_dim, q_rows, block_size;
+  int32_t n_experts, top_k, inter, qk_norm;
+  float eps, rope_theta, attn_scale;
+} sd_dims;
+
+/* Attention weights, bf16.  w_qkv [(2*Hq + 2*Hkv) * D, H]: rows are the stacked q | k | v |
+ * o_gate projections in that order ([DSP] hf_to_vllm_mapper).  w_o [H, Hq * D]. */
+typedef struct sd_attn_weights {
+  const void *w_qkv;
+  const void *w_o;
+} sd_attn_weights;
+
+/* Routed-MoE weights.  w_router bf16 [E, H].  Experts are block-scaled FP4: for matrix
+ * [N, K] of expert e, codes uint8 [E, N, K/2] hold two E2M1 codes per byte (low nibble =
+ * even k), scales uint8 [E, N, K/16] hold one E4M3FN scale per 16 consecutive k, gscale
+ * fp32 [E] one scale per matrix: W[n, k] = e2m1 * e4m3 * gscale.  W13 is [2I, H] with the
+ * gate rows first ([DSP] hf_to_vllm_mapper: gate_proj then up_proj); W2 is [H, I]. */
+typedef struct sd_moe_weights {
+  const void *w_router;
+  const uint8_t *w13_codes, *w13_scales;
+  const float *w13_gscale;
+  const uint8_t *w2_codes, *w2_scales;
+  const float *w2_gscale;
+} sd_moe_weights;
+
+/* One layer.  Gains are fp32 [H]: g_post_prev is the post-norm of the incoming branch (the
+ * previous layer's post-FFN norm), g_pre_attn / g_post_attn / g_pre_ffn the layer's own
+ * sandwich norms ([DSP] MuseSparkDSparkDecoderLayer.forward). */
+typedef struct sd_layer_weights {
+  const float *g_post_prev, *g_pre_attn, *g_post_attn, *g_pre_ffn;
+  sd_attn_weights attn;
+  sd_moe_weights moe;
+} sd_layer_weights;
+
+/* Paged KV cache and the step's metadata ([DEC] plan: block-table decode metadata and
+ * the step's slot mapping).  k_cache bf16 [num_blocks, Hkv, 16, D] (token-major inside
+ * a block); v_cache bf16 [num_blocks, Hkv, D, 16] (dim-major inside a block).
+ * block_table int32 [n_req, max_blocks]; seq_lens int32 [n_req] count every token of the
+ * request including its q_rows verify tokens; positions int32 [b] (row j of request r is
+ * at seq_lens[r] - q_rows + j); slot_mapping int64 [b] = block * 16 + offset where that
+ * row's K/V is written (a negative slot writes nothing).  max_seq_len bounds seq_lens
+ * (host value, sizes the launch; device seq_lens are clamped to max_blocks * 16). */
+typedef struct sd_kv {
+  void *k_cache, *v_cache;
+  int32_t num_blocks;
+  const int32_t *block_table;
+  int32_t max_blocks;
+  const int32_t *seq_lens;
+  const int32_t *positions;
+  const int64_t *slot_mapping;
+  int32_t n_req, max_seq_len;
+} sd_kv;
+
+/* Routing outputs.  topk_ids int32 [b, k] (descending logit, ties to the lower expert
+ * index), topk_w fp32 [b, k] (softmax over the k selected logits), expert_counts int32
+ * [E], expert_offsets int32 [E + 1] (exclusive prefix sum), slot_of int32 [b, k] (pooled
+ * slot of each choice: a stable counting sort by (expert, row)), token_of_slot int32
+ * [b * k] (its inverse), active_experts int32 [E + 1]: the ids of experts with a nonzero
+ * count in ascending order, then at index E their number. */
+typedef struct sd_route {
+  int32_t *topk_ids;
+  float *topk_w;
+  int32_t *expert_counts, *expert_offsets, *slot_of, *token_of_slot, *active_experts;
+} sd_route;
+
+int sd_abi_version(void);
+const char *sd_last_error(void);
+
+/* Bytes of workspace every call below needs for this shape (the largest of them). */
+size_t sd_workspace_bytes(const sd_dims *dims, int32_t b, int32_t n_req, int32_t max_seq_len);
+
+/* Input boundary / front / final boundary ([DEC] module docstring: the first layer's front,
+ * the input boundary's dual norm, the final boundary; order from [DSP]
+ * MuseSparkDSparkDecoderLayer.forward).  stream fp32 [b, H] in/out.
+ *   branch != NULL: stream += RMSNorm(branch; g_post); out = bf16(RMSNorm(stream; g_pre)).
+ *   branch == NULL (front): stream = front_embed; out = bf16(RMSNorm(stream; g_pre)).
+ * branch fp32 [b, H] (the branches between blocks are fp32); front_embed bf16 [b, H];
+ * gains fp32 [H]; out bf16 [b, H] (e.g. the final hidden cast for the draft head). */
+int sd_boundary_dualnorm(const sd_dims *dims, int32_t b, float *stream, const float *branch,
+                         const void *front_embed, const float *g_post, const float *g_pre,
+                         void *out, void *stream_handle);
+
+/* Attention of one layer ([DEC] module docstring: QKV front -> attn2 -> o_proj):
+ * stacked QKV projection of x (bf16 [b, H]); weightless per-head RMSNorm of q and k when
+ * dims->qk_norm; RoPE at each row's position; bf16 K/V written to the cache at
+ * slot_mapping (the cache is modified there and nowhere else); causal GQA attention of each
+ * row over positions 0..p of its request; output gate o * sigmoid(o_gate); o_proj.
+ * out fp32 [b, H] (the attention branch). */
+int sd_attn_verify(const sd_dims *dims, int32_t b, const void *x, const sd_attn_weights *w,
+                   const sd_kv *kv, float *out, void *ws, size_t ws_bytes, void *stream_handle);
+
+/* Router -> routing -> pooler ([DEC] module docstring).  z = x (bf16 [b, H]) * w_router^T
+ * + logit_bias (fp32 [b, E], may be NULL); top-k, weights and pooler maps into *route
+ * (every field required).  logits_out fp32 [b, E] may be NULL. */
+int sd_moe_route(const sd_dims *dims, int32_t b, const void *x, const void *w_router,
+                 const float *logit_bias, const sd_route *route, float *logits_out,
+                 void *ws, size_t ws_bytes, void *stream_handle);
+
+/* Routed experts over pooled slots ([DEC] module docstring: routed experts; [RT] module
+ * list: NVFP4 routed experts): for slot s = (row t, expert e), y[s] = W2_e * h[s] with
+ * h[s] = silu(g) * u and [g | u] = W13_e * x[t], weights dequantised exactly, fp32
+ * accumulation, h kept at near-fp32 precision between the two GEMMs.  x bf16 [b, H];
+ * route as produced by sd_moe_route; y_slots fp32 [b * k, H]; h_slots (may be NULL)
+ * receives bf16(h) [b * k, I]. */
+int sd_moe_experts(const sd_dims *dims, int32_t b, const void *x, const sd_moe_weights *w,
+                   const sd_route *route, void *y_slots, void *h_slots, void *ws,
+                   size_t ws_bytes, void *stream_handle);
+
+/* Unpooler ([DEC] module docstring): out[t] = sum over j < k, in order, of
+ * topk_w[t, j] * y_slots[slot_of[t, j]], in fp32.  y_slots fp32 [b * k, H];
+ * out fp32 [b, H] (the MoE branch). */
+int sd_moe_unpool(const sd_dims *dims, int32_t b, const float *y_slots, const sd_route *route,
+                  float *out, void *stream_handle);
+
+/* One whole layer step in the order of [DEC] SpecializedDecode.run: input boundary (or the
+ * front when branch_in == NULL, taking front_embed) -> attention -> attention boundary ->
+ * router -> routing -> pooler -> experts -> unpooler.  stream fp32 [b, H] in/out;
+ * branch_in fp32 [b, H] (the previous layer's MoE output); front_embed bf16 [b, H];
+ * branch_out fp32 [b, H] receives the unpooled MoE output (the next boundary's branch;
+ * it may alias branch_in, which is read first).  route_out may be NULL (then routing lives
+ * in the workspace); logit_bias may be NULL. */
+int sd_layer_step(const sd_dims *dims, int32_t b, float *stream, const float *branch_in,
+                  const void *front_embed, const sd_layer_weights *w, const sd_kv *kv,
+                  const float *logit_bias, float *branch_out, const sd_route *route_out,
+                  void *ws, size_t ws_bytes, void *stream_handle);
+
+/* Draft head on bf16 hidden rows h [b, hidden] ([DSP] compute_draft_logits,
+ * apply_output_logit_transform, draft_id_to_target_id; [RT] unsupported: BF16 logits):
+ * logits = bf16(h * w_lm^T) with w_lm bf16 [draft_vocab, hidden]; tau = soft_cap *
+ * tanh(logits * multiplier / soft_cap) (soft_cap <= 0: tau = logits * multiplier);
+ * draft_ids int32 [b] = lowest index of the largest logit; target_ids int64 [b] =
+ * d2t[draft_ids] with d2t int64 [draft_vocab].  tau_out fp32 [b, draft_vocab] may be NULL.
+ * multiplier must be > 0 (the transform is then monotone and keeps the argmax). */
+int sd_draft_head(int32_t hidden, int32_t draft_vocab, int32_t b, const void *h,
+                  const void *w_lm, float multiplier, float soft_cap, const int64_t *d2t,
+                  float *tau_out, int32_t *draft_ids, int64_t *target_ids, void *ws,
+                  size_t ws_bytes, void *stream_handle);
+
+/* Bytes of workspace sd_draft_head needs. */
+size_t sd_draft_head_workspace_bytes(int32_t hidden, int32_t draft_vocab, int32_t b);
+
+/* Test entry: dequantise block-scaled FP4 rows [n, k] exactly as the expert kernels do,
+ * into out fp32 [n, k] (codes [n, k/2], scales [n, k/16], one gscale).  k % 32 == 0. */
+int sd_debug_dequant(int32_t n, int32_t k, const uint8_t *codes, const uint8_t *scales,
+                     float gscale, float *out, void *stream_handle);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SDVERIFY_H */

@@ -126,6 +126,8 @@ def kv_write(k_cache, v_cache, k, v, slot_mapping):
     kc = np.array(k_cache, dtype=np.float64, copy=True)
     vc = np.array(v_cache, dtype=np.float64, copy=True)
     for t, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
+        if slot < 0:                   # a negative slot marks a row whose K/V is not stored
+            continue
         blk, off = int(slot) // BLOCK, int(slot) % BLOCK
         kc[blk, :, off, :] = bf16_round(k[t])
         vc[blk, :, :, off] = bf16_round(v[t])
@@ -309,8 +311,9 @@ def layer_step(inp, dims, branch_in=None, front_embed=None, route_override=None)
     ``inp`` holds the layer's weights, caches and step metadata as arrays (fp64 values
     of the bf16/fp32 inputs, raw codes for FP4/E4M3).  ``dims`` is a mapping with
     hidden, n_q_heads, n_kv_heads, head_dim, q_rows, n_experts, top_k, inter, eps,
-    rope_theta, qk_norm.  ``route_override`` (ids) replaces this chain's own top-k,
-    for teacher forcing at near ties.
+    rope_theta, qk_norm.  ``route_override`` (ids, or a function (z, ids) -> ids)
+    replaces this step's own top-k, for teacher forcing at near ties; the weights are
+    then the softmax over the replaced selection.
     Returns a dict with the new stream, the branch output m, the updated caches and
     every intermediate.
     """
@@ -331,7 +334,8 @@ def layer_step(inp, dims, branch_in=None, front_embed=None, route_override=None)
     z = router_logits(x_m, inp["w_router"], inp.get("logit_bias"))
     ids, w = topk_route(z, d["top_k"])
     if route_override is not None:
-        ids = np.asarray(route_override, dtype=np.int32)
+        ids = route_override(z, ids) if callable(route_override) else route_override
+        ids = np.asarray(ids, dtype=np.int32)
         sel = np.take_along_axis(z, ids.astype(np.int64), axis=1)
         ex = np.exp(sel - sel.max(axis=1, keepdims=True))
         w = ex / ex.sum(axis=1, keepdims=True)

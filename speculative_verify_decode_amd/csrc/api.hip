@@ -1,0 +1,491 @@
+// C ABI of libsdverify.so: host-side validation, workspace layout and the launch order of
+// one layer step.  Nothing here allocates, frees or synchronises; every call enqueues its
+// kernels on the caller's stream and returns.
+//
+// The per-layer order is the one of page
+// "vllm.models.muse_spark.nvidia.specialized_decode.runtime.decode", SpecializedDecode.run:
+// input boundary -> attention -> attention boundary -> MoE.  Validation mirrors that page's
+// and page "vllm.models.muse_spark.nvidia.specialized_decode.runtime"'s host-only checks
+// (`unsupported`: the first failing reason, in words), before any launch.
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "sd_common.h"
+
+namespace {
+
+thread_local std::string g_err = "no error";
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err = "no error";
+  return SD_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(SD_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define SD_LAUNCH(expr, what)                          \
+  do {                                                 \
+    hipError_t e_ = (expr);                            \
+    if (e_ != hipSuccess) return hip_fail(e_, what);   \
+  } while (0)
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+constexpr int kMaxRows = 64;
+
+bool norm_width_ok(int H) {
+  if (H <= 0 || H % 256) return false;
+  switch (H / 256) {
+    case 1: case 2: case 4: case 8: case 12: case 16: case 20: case 24: case 32: return true;
+    default: return false;
+  }
+}
+
+int check_dims(const sd_dims* d) {
+  if (d == nullptr) return fail(SD_EINVAL, "dims is null");
+  if (!norm_width_ok(d->hidden))
+    return fail(SD_EUNSUPPORTED, "hidden %d (need 256 * {1,2,4,8,12,16,20,24,32})", d->hidden);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(SD_EUNSUPPORTED, "head_dim %d (need 64 or 128)", d->head_dim);
+  if (d->n_q_heads <= 0 || d->n_kv_heads <= 0 || d->n_q_heads % d->n_kv_heads)
+    return fail(SD_EINVAL, "n_q_heads %d must be a positive multiple of n_kv_heads %d",
+                d->n_q_heads, d->n_kv_heads);
+  if (d->q_rows != 8)
+    return fail(SD_EUNSUPPORTED, "q_rows %d (verify steps are 1 + 7 tokens)", d->q_rows);
+  const int qg = (d->n_q_heads / d->n_kv_heads) * d->q_rows;
+  if (!((d->head_dim == 128 && (qg == 16 || qg == 32)) ||
+        (d->head_dim == 64 && (qg == 16 || qg == 32 || qg == 64))))
+    return fail(SD_EUNSUPPORTED, "query group %d per KV head at head_dim %d", qg, d->head_dim);
+  if ((d->n_q_heads * d->head_dim) % 128)
+    return fail(SD_EUNSUPPORTED, "n_q_heads * head_dim = %d (o_proj needs a multiple of 128)",
+                d->n_q_heads * d->head_dim);
+  if (d->block_size != 16)
+    return fail(SD_EUNSUPPORTED, "KV cache block size %d (only 16)", d->block_size);
+  if (d->n_experts < 1 || d->n_experts > 256)
+    return fail(SD_EUNSUPPORTED, "n_experts %d (1..256)", d->n_experts);
+  if (d->top_k < 1 || d->top_k > 8 || d->top_k > d->n_experts)
+    return fail(SD_EUNSUPPORTED, "top_k %d (1..min(8, n_experts))", d->top_k);
+  if (d->inter <= 0 || d->inter % 128)
+    return fail(SD_EUNSUPPORTED, "inter %d (need a multiple of 128)", d->inter);
+  if (d->qk_norm != 0 && d->qk_norm != 1) return fail(SD_EINVAL, "qk_norm %d", d->qk_norm);
+  if (!(d->eps > 0.f)) return fail(SD_EINVAL, "eps must be > 0");
+  if (!(d->rope_theta > 0.f)) return fail(SD_EINVAL, "rope_theta must be > 0");
+  if (d->attn_scale < 0.f) return fail(SD_EINVAL, "attn_scale must be >= 0");
+  return SD_OK;
+}
+
+int check_rows(const sd_dims* d, int b) {
+  if (b <= 0 || b > kMaxRows || b % d->q_rows)
+    return fail(SD_EUNSUPPORTED, "b = %d rows (need a multiple of q_rows = %d, at most %d)", b,
+                d->q_rows, kMaxRows);
+  return SD_OK;
+}
+
+struct Ws {
+  size_t x_a, x_a_lo, qkv, q, q_lo, part_acc, part_ml, o, o_lo, a, x_m, x_m_lo, x16, x16_lo, z,
+      ids, w, counts, offsets, slot_of, tos, active, h16, h16_lo, y, total;
+};
+
+size_t up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+Ws ws_layout(const sd_dims& d, int b, int n_req, int max_seq_len) {
+  const AttnPlan p = attn_plan(d, n_req, max_seq_len);
+  const size_t H = d.hidden, D = d.head_dim, Hq = d.n_q_heads, Hkv = d.n_kv_heads;
+  const size_t E = d.n_experts, k = d.top_k, I = d.inter, B = b;
+  const size_t N = (2 * Hq + 2 * Hkv) * D;
+  const size_t parts = (size_t)n_req * Hkv * p.n_chunks;
+  Ws w;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o += up(bytes); return at; };
+  w.x_a = take(B * H * 2);
+  w.x_a_lo = take(B * H * 2);
+  w.qkv = take(B * N * 4);
+  w.q = take(B * Hq * D * 2);
+  w.q_lo = take(B * Hq * D * 2);
+  w.part_acc = take(parts * p.qg * D * 4);
+  w.part_ml = take(parts * p.qg * 2 * 4);
+  w.o = take(B * Hq * D * 2);
+  w.o_lo = take(B * Hq * D * 2);
+  w.a = take(B * H * 4);
+  w.x_m = take(B * H * 2);
+  w.x_m_lo = take(B * H * 2);
+  w.x16 = take(B * H * 2);
+  w.x16_lo = take(B * H * 2);
+  w.z = take(B * E * 4);
+  w.ids = take(B * k * 4);
+  w.w = take(B * k * 4);
+  w.counts = take(E * 4);
+  w.offsets = take((E + 1) * 4);
+  w.slot_of = take(B * k * 4);
+  w.tos = take(B * k * 4);
+  w.active = take((E + 1) * 4);
+  w.h16 = take(B * k * I * 2);
+  w.h16_lo = take(B * k * I * 2);
+  w.y = take(B * k * H * 4);
+  w.total = o;
+  return w;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) { return (T*)((char*)ws + off); }
+
+int check_kv(const sd_dims* d, int b, const sd_kv* kv) {
+  if (kv == nullptr) return fail(SD_EINVAL, "kv is null");
+  if (!kv->k_cache || !kv->v_cache || !kv->block_table || !kv->seq_lens || !kv->positions ||
+      !kv->slot_mapping)
+    return fail(SD_EINVAL, "a kv pointer is null");
+  if (!aligned16(kv->k_cache) || !aligned16(kv->v_cache))
+    return fail(SD_EINVAL, "KV caches must be 16-byte aligned");
+  if (kv->n_req * d->q_rows != b)
+    return fail(SD_EUNSUPPORTED,
+                "b = %d but n_req = %d requests of %d verify rows (one step verifies q_rows "
+                "tokens of every request)",
+                b, kv->n_req, d->q_rows);
+  if (kv->max_seq_len < d->q_rows)
+    return fail(SD_EINVAL, "max_seq_len %d shorter than the %d verify tokens", kv->max_seq_len,
+                d->q_rows);
+  if (kv->num_blocks <= 0) return fail(SD_EINVAL, "num_blocks %d", kv->num_blocks);
+  if (kv->max_blocks * 16 < kv->max_seq_len)
+    return fail(SD_EINVAL, "block table of %d blocks per request cannot hold %d tokens",
+                kv->max_blocks, kv->max_seq_len);
+  return SD_OK;
+}
+
+int check_ws(const sd_dims* d, int b, int n_req, int max_seq_len, const void* ws,
+             size_t ws_bytes) {
+  const size_t need = ws_layout(*d, b, n_req, max_seq_len).total;
+  if (ws == nullptr || ws_bytes < need)
+    return fail(SD_EWORKSPACE, "workspace of %zu bytes, need %zu", ws ? ws_bytes : 0, need);
+  if (!aligned16(ws)) return fail(SD_EINVAL, "workspace must be 16-byte aligned");
+  return SD_OK;
+}
+
+float scale_of(const sd_dims* d) {
+  return d->attn_scale > 0.f ? d->attn_scale : 1.0f / sqrtf((float)d->head_dim);
+}
+
+#define SD_CHECK(expr)        \
+  do {                        \
+    int rc_ = (expr);         \
+    if (rc_ != SD_OK) return rc_; \
+  } while (0)
+
+// ---- launch sequences (validated arguments only) ----
+// x (bf16 hi terms) and x_lo (bf16 lo terms, may be null) -> out fp32 [b, H].
+int run_attention(const sd_dims* d, int b, const uint16_t* x, const uint16_t* x_lo,
+                  const sd_attn_weights* w, const sd_kv* kv, float* out, void* ws, const Ws& L,
+                  hipStream_t st) {
+  const int H = d->hidden, D = d->head_dim, Hq = d->n_q_heads, Hkv = d->n_kv_heads;
+  const int N = (2 * Hq + 2 * Hkv) * D;
+  float* qkv = at<float>(ws, L.qkv);
+  GemmArgs g{};
+  g.M = b; g.N = N; g.K = H; g.x = x; g.x_lo = x_lo; g.w = (const uint16_t*)w->w_qkv;
+  g.y = qkv;
+  SD_LAUNCH(launch_gemm(GEMM_F32, g, st), "qkv projection");
+  uint16_t* q = at<uint16_t>(ws, L.q);
+  uint16_t* q_lo = at<uint16_t>(ws, L.q_lo);
+  SD_LAUNCH(launch_qkv_post(qkv, b, Hq, Hkv, D, d->qk_norm, d->eps, d->rope_theta,
+                            kv->positions, kv->slot_mapping, q, q_lo, (uint16_t*)kv->k_cache,
+                            (uint16_t*)kv->v_cache, st),
+            "qkv front epilogue");
+  const AttnPlan p = attn_plan(*d, kv->n_req, kv->max_seq_len);
+  AttnArgs aa{};
+  aa.q = q; aa.q_lo = q_lo;
+  aa.k_cache = (const uint16_t*)kv->k_cache; aa.v_cache = (const uint16_t*)kv->v_cache;
+  aa.block_table = kv->block_table; aa.max_blocks = kv->max_blocks; aa.seq_lens = kv->seq_lens;
+  aa.positions = kv->positions; aa.n_req = kv->n_req; aa.Hq = Hq; aa.Hkv = Hkv; aa.D = D;
+  aa.q_rows = d->q_rows; aa.scale = scale_of(d);
+  aa.part_acc = at<float>(ws, L.part_acc); aa.part_ml = at<float>(ws, L.part_ml);
+  aa.gate = qkv + (size_t)(Hq + 2 * Hkv) * D; aa.gate_stride = N;
+  uint16_t* o = at<uint16_t>(ws, L.o);
+  uint16_t* o_lo = at<uint16_t>(ws, L.o_lo);
+  aa.out = o; aa.out_lo = o_lo;
+  SD_LAUNCH(launch_attention(aa, p, st), "paged attention");
+  GemmArgs go{};
+  go.M = b; go.N = H; go.K = Hq * D; go.x = o; go.x_lo = o_lo; go.w = (const uint16_t*)w->w_o;
+  go.y = out;
+  SD_LAUNCH(launch_gemm(GEMM_F32, go, st), "o_proj");
+  return SD_OK;
+}
+
+int run_route(const sd_dims* d, int b, const uint16_t* x, const uint16_t* x_lo,
+              const void* w_router, const float* bias, const sd_route* r, float* z,
+              hipStream_t st) {
+  GemmArgs g{};
+  g.M = b; g.N = d->n_experts; g.K = d->hidden; g.x = x; g.x_lo = x_lo;
+  g.w = (const uint16_t*)w_router;
+  g.y = z; g.bias = bias;
+  SD_LAUNCH(launch_gemm(GEMM_F32_BIAS, g, st), "router");
+  SD_LAUNCH(launch_route_pool(z, b, d->n_experts, d->top_k, r->topk_ids, r->topk_w,
+                              r->expert_counts, r->expert_offsets, r->slot_of, r->token_of_slot,
+                              r->active_experts, st),
+            "routing and pooler");
+  return SD_OK;
+}
+
+int run_experts(const sd_dims* d, int b, const _Float16* x16, const _Float16* x16_lo,
+                const sd_moe_weights* w, const sd_route* r, float* y, uint16_t* h_bf16,
+                _Float16* h16, _Float16* h16_lo, hipStream_t st) {
+  MoeArgs m{};
+  m.b = b; m.H = d->hidden; m.I = d->inter; m.E = d->n_experts; m.k = d->top_k;
+  m.x16 = x16; m.x16_lo = x16_lo; m.h16_lo = h16_lo;
+  m.w13_codes = w->w13_codes; m.w13_scales = w->w13_scales; m.w13_gscale = w->w13_gscale;
+  m.w2_codes = w->w2_codes; m.w2_scales = w->w2_scales; m.w2_gscale = w->w2_gscale;
+  m.counts = r->expert_counts; m.offsets = r->expert_offsets; m.tos = r->token_of_slot;
+  m.h16 = h16; m.h_bf16 = h_bf16; m.y = y;
+  SD_LAUNCH(launch_moe_experts(m, st), "routed experts");
+  return SD_OK;
+}
+
+int check_attn_weights(const sd_attn_weights* w) {
+  if (w == nullptr || !w->w_qkv || !w->w_o) return fail(SD_EINVAL, "attention weight is null");
+  if (!aligned16(w->w_qkv) || !aligned16(w->w_o))
+    return fail(SD_EINVAL, "attention weights must be 16-byte aligned");
+  return SD_OK;
+}
+
+int check_moe_weights(const sd_moe_weights* w, bool need_router, bool need_experts) {
+  if (w == nullptr) return fail(SD_EINVAL, "moe weights are null");
+  if (need_router && (!w->w_router || !aligned16(w->w_router)))
+    return fail(SD_EINVAL, "router weight null or not 16-byte aligned");
+  if (need_experts) {
+    if (!w->w13_codes || !w->w13_scales || !w->w13_gscale || !w->w2_codes || !w->w2_scales ||
+        !w->w2_gscale)
+      return fail(SD_EINVAL, "an expert weight pointer is null");
+    if (!aligned16(w->w13_codes) || !aligned16(w->w2_codes))
+      return fail(SD_EINVAL, "expert codes must be 16-byte aligned");
+    if (((uintptr_t)w->w13_scales & 1u) || ((uintptr_t)w->w2_scales & 1u))
+      return fail(SD_EINVAL, "expert scales must be 2-byte aligned");
+  }
+  return SD_OK;
+}
+
+int check_route(const sd_route* r) {
+  if (r == nullptr || !r->topk_ids || !r->topk_w || !r->expert_counts || !r->expert_offsets ||
+      !r->slot_of || !r->token_of_slot || !r->active_experts)
+    return fail(SD_EINVAL, "a route pointer is null");
+  return SD_OK;
+}
+
+sd_route ws_route(void* ws, const Ws& L) {
+  sd_route r;
+  r.topk_ids = at<int32_t>(ws, L.ids);
+  r.topk_w = at<float>(ws, L.w);
+  r.expert_counts = at<int32_t>(ws, L.counts);
+  r.expert_offsets = at<int32_t>(ws, L.offsets);
+  r.slot_of = at<int32_t>(ws, L.slot_of);
+  r.token_of_slot = at<int32_t>(ws, L.tos);
+  r.active_experts = at<int32_t>(ws, L.active);
+  return r;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sd_abi_version(void) { return SD_ABI_VERSION; }
+
+const char* sd_last_error(void) { return g_err.c_str(); }
+
+size_t sd_workspace_bytes(const sd_dims* dims, int32_t b, int32_t n_req, int32_t max_seq_len) {
+  if (check_dims(dims) != SD_OK || check_rows(dims, b) != SD_OK || n_req <= 0 ||
+      max_seq_len <= 0)
+    return 0;
+  return ws_layout(*dims, b, n_req, max_seq_len).total;
+}
+
+int sd_boundary_dualnorm(const sd_dims* dims, int32_t b, float* stream, const float* branch,
+                         const void* front_embed, const float* g_post, const float* g_pre,
+                         void* out, void* stream_handle) {
+  SD_CHECK(check_dims(dims));
+  SD_CHECK(check_rows(dims, b));
+  if (!stream || !out || !g_pre) return fail(SD_EINVAL, "stream, out or g_pre is null");
+  if (branch == nullptr && front_embed == nullptr)
+    return fail(SD_EINVAL, "front mode needs front_embed");
+  if (branch != nullptr && g_post == nullptr) return fail(SD_EINVAL, "g_post is null");
+  if (branch != nullptr && !aligned16(branch)) return fail(SD_EINVAL, "branch misaligned");
+  SD_LAUNCH(launch_dualnorm(b, dims->hidden, stream, (const float*)branch,
+                            (const uint16_t*)front_embed, g_post, g_pre, dims->eps,
+                            (uint16_t*)out, nullptr, nullptr, nullptr,
+                            (hipStream_t)stream_handle),
+            "dual norm");
+  return ok();
+}
+
+int sd_attn_verify(const sd_dims* dims, int32_t b, const void* x, const sd_attn_weights* w,
+                   const sd_kv* kv, float* out, void* ws, size_t ws_bytes, void* stream_handle) {
+  SD_CHECK(check_dims(dims));
+  SD_CHECK(check_rows(dims, b));
+  SD_CHECK(check_attn_weights(w));
+  SD_CHECK(check_kv(dims, b, kv));
+  if (!x || !out || !aligned16(x) || !aligned16(out))
+    return fail(SD_EINVAL, "x or out null or misaligned");
+  SD_CHECK(check_ws(dims, b, kv->n_req, kv->max_seq_len, ws, ws_bytes));
+  const Ws L = ws_layout(*dims, b, kv->n_req, kv->max_seq_len);
+  SD_CHECK(run_attention(dims, b, (const uint16_t*)x, nullptr, w, kv, (float*)out, ws, L,
+                         (hipStream_t)stream_handle));
+  return ok();
+}
+
+int sd_moe_route(const sd_dims* dims, int32_t b, const void* x, const void* w_router,
+                 const float* logit_bias, const sd_route* route, float* logits_out, void* ws,
+                 size_t ws_bytes, void* stream_handle) {
+  SD_CHECK(check_dims(dims));
+  SD_CHECK(check_rows(dims, b));
+  SD_CHECK(check_route(route));
+  if (!x || !aligned16(x) || !w_router || !aligned16(w_router))
+    return fail(SD_EINVAL, "x or w_router null or misaligned");
+  if (logits_out && !aligned16(logits_out)) return fail(SD_EINVAL, "logits_out misaligned");
+  SD_CHECK(check_ws(dims, b, b / dims->q_rows, dims->q_rows, ws, ws_bytes));
+  const Ws L = ws_layout(*dims, b, b / dims->q_rows, dims->q_rows);
+  float* z = logits_out ? logits_out : at<float>(ws, L.z);
+  SD_CHECK(run_route(dims, b, (const uint16_t*)x, nullptr, w_router, logit_bias, route, z,
+                     (hipStream_t)stream_handle));
+  return ok();
+}
+
+int sd_moe_experts(const sd_dims* dims, int32_t b, const void* x, const sd_moe_weights* w,
+                   const sd_route* route, void* y_slots, void* h_slots, void* ws,
+                   size_t ws_bytes, void* stream_handle) {
+  SD_CHECK(check_dims(dims));
+  SD_CHECK(check_rows(dims, b));
+  SD_CHECK(check_moe_weights(w, false, true));
+  SD_CHECK(check_route(route));
+  if (!x || !y_slots) return fail(SD_EINVAL, "x or y_slots is null");
+  if (!aligned16(y_slots) || (h_slots && !aligned16(h_slots)))
+    return fail(SD_EINVAL, "y_slots / h_slots must be 16-byte aligned");
+  SD_CHECK(check_ws(dims, b, b / dims->q_rows, dims->q_rows, ws, ws_bytes));
+  const Ws L = ws_layout(*dims, b, b / dims->q_rows, dims->q_rows);
+  hipStream_t st = (hipStream_t)stream_handle;
+  _Float16* x16 = at<_Float16>(ws, L.x16);
+  // a bf16 input is exact as one fp16 term (no lo term)
+  SD_LAUNCH(launch_to_f16(b * dims->hidden, (const uint16_t*)x, x16, st), "expert input");
+  SD_CHECK(run_experts(dims, b, x16, nullptr, w, route, (float*)y_slots, (uint16_t*)h_slots,
+                       at<_Float16>(ws, L.h16), at<_Float16>(ws, L.h16_lo), st));
+  return ok();
+}
+
+int sd_moe_unpool(const sd_dims* dims, int32_t b, const float* y_slots, const sd_route* route,
+                  float* out, void* stream_handle) {
+  SD_CHECK(check_dims(dims));
+  SD_CHECK(check_rows(dims, b));
+  SD_CHECK(check_route(route));
+  if (!y_slots || !out || !aligned16(y_slots) || !aligned16(out))
+    return fail(SD_EINVAL, "y_slots or out null or misaligned");
+  SD_LAUNCH(launch_unpool(b, dims->hidden, dims->top_k, (const float*)y_slots, route->topk_w,
+                          route->slot_of, (float*)out, (hipStream_t)stream_handle),
+            "unpooler");
+  return ok();
+}
+
+int sd_layer_step(const sd_dims* dims, int32_t b, float* stream, const float* branch_in,
+                  const void* front_embed, const sd_layer_weights* w, const sd_kv* kv,
+                  const float* logit_bias, float* branch_out, const sd_route* route_out,
+                  void* ws, size_t ws_bytes, void* stream_handle) {
+  SD_CHECK(check_dims(dims));
+  SD_CHECK(check_rows(dims, b));
+  if (w == nullptr) return fail(SD_EINVAL, "layer weights are null");
+  if (!w->g_pre_attn || !w->g_post_attn || !w->g_pre_ffn)
+    return fail(SD_EINVAL, "a layer gain is null");
+  if (branch_in != nullptr && !w->g_post_prev) return fail(SD_EINVAL, "g_post_prev is null");
+  if (branch_in == nullptr && front_embed == nullptr)
+    return fail(SD_EINVAL, "the first layer's front needs front_embed");
+  SD_CHECK(check_attn_weights(&w->attn));
+  SD_CHECK(check_moe_weights(&w->moe, true, true));
+  SD_CHECK(check_kv(dims, b, kv));
+  if (!stream || !branch_out || !aligned16(branch_out) ||
+      (branch_in != nullptr && !aligned16(branch_in)))
+    return fail(SD_EINVAL, "stream or branch_out null, or a branch misaligned");
+  if (route_out) SD_CHECK(check_route(route_out));
+  SD_CHECK(check_ws(dims, b, kv->n_req, kv->max_seq_len, ws, ws_bytes));
+  const Ws L = ws_layout(*dims, b, kv->n_req, kv->max_seq_len);
+  hipStream_t st = (hipStream_t)stream_handle;
+  const int H = dims->hidden;
+  uint16_t* x_a = at<uint16_t>(ws, L.x_a);
+  uint16_t* x_a_lo = at<uint16_t>(ws, L.x_a_lo);
+  SD_LAUNCH(launch_dualnorm(b, H, stream, (const float*)branch_in,
+                            (const uint16_t*)front_embed, w->g_post_prev, w->g_pre_attn,
+                            dims->eps, x_a, x_a_lo, nullptr, nullptr, st),
+            "input boundary");
+  float* a = at<float>(ws, L.a);
+  SD_CHECK(run_attention(dims, b, x_a, x_a_lo, &w->attn, kv, a, ws, L, st));
+  uint16_t* x_m = at<uint16_t>(ws, L.x_m);
+  uint16_t* x_m_lo = at<uint16_t>(ws, L.x_m_lo);
+  _Float16* x16 = at<_Float16>(ws, L.x16);
+  _Float16* x16_lo = at<_Float16>(ws, L.x16_lo);
+  SD_LAUNCH(launch_dualnorm(b, H, stream, a, nullptr, w->g_post_attn, w->g_pre_ffn, dims->eps,
+                            x_m, x_m_lo, x16, x16_lo, st),
+            "attention boundary");
+  const sd_route r = route_out ? *route_out : ws_route(ws, L);
+  SD_CHECK(run_route(dims, b, x_m, x_m_lo, w->moe.w_router, logit_bias, &r, at<float>(ws, L.z),
+                     st));
+  float* y = at<float>(ws, L.y);
+  SD_CHECK(run_experts(dims, b, x16, x16_lo, &w->moe, &r, y, nullptr, at<_Float16>(ws, L.h16),
+                       at<_Float16>(ws, L.h16_lo), st));
+  SD_LAUNCH(launch_unpool(b, H, dims->top_k, y, r.topk_w, r.slot_of, (float*)branch_out, st),
+            "unpooler");
+  return ok();
+}
+
+size_t sd_draft_head_workspace_bytes(int32_t hidden, int32_t draft_vocab, int32_t b) {
+  if (hidden <= 0 || draft_vocab <= 0 || b <= 0) return 0;
+  const size_t tiles = (size_t)draft_vocab / 16;
+  return up((size_t)b * tiles * 4) * 2;
+}
+
+int sd_draft_head(int32_t hidden, int32_t draft_vocab, int32_t b, const void* h,
+                  const void* w_lm, float multiplier, float soft_cap, const int64_t* d2t,
+                  float* tau_out, int32_t* draft_ids, int64_t* target_ids, void* ws,
+                  size_t ws_bytes, void* stream_handle) {
+  if (hidden <= 0 || hidden % 128)
+    return fail(SD_EUNSUPPORTED, "hidden %d (need a multiple of 128)", hidden);
+  if (draft_vocab <= 0 || draft_vocab % 16)
+    return fail(SD_EUNSUPPORTED, "draft_vocab %d (need a multiple of 16)", draft_vocab);
+  if (b <= 0 || b > kMaxRows) return fail(SD_EUNSUPPORTED, "b = %d rows (1..%d)", b, kMaxRows);
+  if (!(multiplier > 0.f))
+    return fail(SD_EINVAL, "multiplier must be > 0 (the transform must keep the argmax)");
+  if (!h || !w_lm || !d2t || !draft_ids || !target_ids)
+    return fail(SD_EINVAL, "a draft head pointer is null");
+  if (!aligned16(h) || !aligned16(w_lm) || (tau_out && !aligned16(tau_out)))
+    return fail(SD_EINVAL, "h, w_lm and tau_out must be 16-byte aligned");
+  const size_t need = sd_draft_head_workspace_bytes(hidden, draft_vocab, b);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(SD_EWORKSPACE, "workspace of %zu bytes, need %zu", ws ? ws_bytes : 0, need);
+  hipStream_t st = (hipStream_t)stream_handle;
+  const int tiles = draft_vocab / 16;
+  float* val = (float*)ws;
+  int* idx = (int*)((char*)ws + up((size_t)b * tiles * 4));
+  GemmArgs g{};
+  g.M = b; g.N = draft_vocab; g.K = hidden; g.x = (const uint16_t*)h;
+  g.w = (const uint16_t*)w_lm; g.y = tau_out; g.head_val = val; g.head_idx = idx;
+  g.multiplier = multiplier; g.soft_cap = soft_cap;
+  SD_LAUNCH(launch_gemm(GEMM_HEAD, g, st), "lm_head");
+  SD_LAUNCH(launch_head_argmax(b, tiles, val, idx, d2t, draft_ids, target_ids, st),
+            "draft argmax");
+  return ok();
+}
+
+int sd_debug_dequant(int32_t n, int32_t k, const uint8_t* codes, const uint8_t* scales,
+                     float gscale, float* out, void* stream_handle) {
+  if (n <= 0 || k <= 0 || k % 32) return fail(SD_EINVAL, "n %d, k %d (k % 32 == 0)", n, k);
+  if (!codes || !scales || !out || !aligned16(codes) || ((uintptr_t)scales & 1u))
+    return fail(SD_EINVAL, "codes/scales/out null or misaligned");
+  SD_LAUNCH(launch_debug_dequant(n, k, codes, scales, gscale, out, (hipStream_t)stream_handle),
+            "debug dequant");
+  return ok();
+}
+
+}  // extern "C"

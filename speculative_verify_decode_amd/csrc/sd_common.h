@@ -1,0 +1,210 @@
+// Internal declarations shared by the gfx950 kernels and the C-ABI host code.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sdverify.h"
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// Precision.  The stream and the branches between blocks are fp32.  An activation that
+// feeds a matrix-core reduction enters as two 16-bit terms, x ~ hi + lo: bf16 hi/lo
+// (~2^-16 relative) against bf16 weights, and fp16 hi/lo of x * 2^-8 (~2^-22 relative, an
+// absolute floor of 2^-16 below |x| = 2^-6) against the exactly dequantised fp16 expert
+// weights.  With at most 8 rows per MFMA column tile, columns 0-7 carry the hi terms and
+// columns 8-15 the lo terms of the same rows, and the epilogue adds the two columns (lanes
+// l and l ^ 8); attention runs its hi and lo operands as separate MFMAs.  Expert results
+// are multiplied back by 2^8 (exact in fp32).  Only the KV cache and the draft-head logits
+// are rounded to 16 bits, as the format fixes them.
+#define SD_X16_SCALE 0.00390625f
+#define SD_X16_UNSCALE 256.0f
+
+namespace sd {
+
+__device__ __forceinline__ float bf2f(uint16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
+
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+// fp32 -> (hi, lo) fp16 terms of x * 2^-8.
+__device__ __forceinline__ void split_f16(float x, _Float16& hi, _Float16& lo) {
+  const float xs = x * SD_X16_SCALE;
+  hi = (_Float16)xs;
+  lo = (_Float16)(xs - (float)hi);
+}
+
+// fp32 -> (hi, lo) bf16 terms: x ~ hi + lo to ~2^-16 relative.
+__device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
+  hi = f2bf(x);
+  lo = f2bf(x - bf2f(hi));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Sum over a block of NW waves; `red` holds NW floats of LDS.  All threads get the sum.
+template <int NW>
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) s += red[i];
+  __syncthreads();
+  return s;
+}
+
+// E4M3FN byte -> fp32 (gfx950 decodes the OCP E4M3FN encoding).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
+  return __builtin_amdgcn_cvt_f32_fp8(byte, 0);
+}
+
+// Eight E2M1 codes (one dword, low nibble first) -> eight fp16 weights w = e2m1 * scale.
+// The hardware convert applies only the exponent of its scale operand, so it runs at
+// scale 1 (exact E2M1 values) and the E4M3 block scale is a packed fp16 multiply.  The
+// product of an E2M1 value (<= 2 significant bits) and an E4M3 value (<= 4 significant
+// bits, 2^-9 .. 448) is exact in fp16, so each weight is the exact dequantised value.
+__device__ __forceinline__ f16x8_t dequant8(uint32_t codes, f16x2_t scale2) {
+  f16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0);
+  f16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1);
+  f16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2);
+  f16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3);
+  p0 *= scale2;
+  p1 *= scale2;
+  p2 *= scale2;
+  p3 *= scale2;
+  f16x8_t r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+__device__ __forceinline__ f16x2_t scale_pair(uint32_t e4m3_byte) {
+  _Float16 s = (_Float16)e4m3_to_f32(e4m3_byte);
+  f16x2_t r = {s, s};
+  return r;
+}
+
+// A 32-weight unit: 16 bytes of codes + 2 scale bytes -> four MFMA A/B operands of 8 fp16
+// (operand m holds weights 8m .. 8m+7 of the unit).
+__device__ __forceinline__ void dequant_unit(u32x4_t codes, uint32_t scales2, f16x8_t out[4]) {
+  const f16x2_t s0 = scale_pair(scales2 & 0xFF);
+  const f16x2_t s1 = scale_pair((scales2 >> 8) & 0xFF);
+  out[0] = dequant8(codes[0], s0);
+  out[1] = dequant8(codes[1], s0);
+  out[2] = dequant8(codes[2], s1);
+  out[3] = dequant8(codes[3], s1);
+}
+
+}  // namespace sd
+
+// ---------------------------------------------------------------------------- launches
+// Every launcher enqueues on `st` and returns the launch status (hipGetLastError).
+
+// branch: fp32 [b, H] (null: front mode, the stream becomes the bf16 `front` rows).
+// out: bf16 pre-norm output (hi term); out_lo (optional): its bf16 lo term; x16 / x16_lo
+// (optional): fp16 hi / lo terms of the pre-norm output * 2^-8 (the expert input).
+hipError_t launch_dualnorm(int b, int H, float* stream, const float* branch,
+                           const uint16_t* front, const float* g_post, const float* g_pre,
+                           float eps, uint16_t* out, uint16_t* out_lo, _Float16* x16,
+                           _Float16* x16_lo, hipStream_t st);
+
+enum GemmMode { GEMM_F32 = 0, GEMM_BF16 = 1, GEMM_F32_BIAS = 2, GEMM_HEAD = 3 };
+
+struct GemmArgs {
+  int M, N, K;
+  const uint16_t* x;   // bf16 [M, K]
+  const uint16_t* x_lo; // optional bf16 lo terms of x [M, K] (column-split MFMA)
+  const uint16_t* w;   // bf16 [N, K]
+  void* y;             // fp32 or bf16 [M, N] (GEMM_HEAD: optional fp32 tau)
+  const float* bias;   // [M, N] for GEMM_F32_BIAS (may be null)
+  float* head_val;     // GEMM_HEAD: per (m, tile) best logit
+  int* head_idx;       // GEMM_HEAD: per (m, tile) its index
+  float multiplier, soft_cap;
+};
+hipError_t launch_gemm(GemmMode mode, const GemmArgs& a, hipStream_t st);
+
+hipError_t launch_qkv_post(const float* qkv, int b, int Hq, int Hkv, int D, int qk_norm,
+                           float eps, float theta, const int* positions, const int64_t* slots,
+                           uint16_t* q_out, uint16_t* q_lo, uint16_t* k_cache,
+                           uint16_t* v_cache, hipStream_t st);
+
+struct AttnPlan {
+  int chunk_blocks;   // blocks per workgroup (even)
+  int n_chunks;       // chunks per (request, kv head) at max_seq_len
+  int qg;             // queries per (request, kv head) = group * q_rows
+};
+AttnPlan attn_plan(const sd_dims& d, int n_req, int max_seq_len);
+
+struct AttnArgs {
+  const uint16_t* q;          // bf16 hi terms [b, Hq, D]
+  const uint16_t* q_lo;       // bf16 lo terms [b, Hq, D]
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int* block_table;
+  int max_blocks;
+  const int* seq_lens;
+  const int* positions;
+  int n_req, Hq, Hkv, D, q_rows;
+  float scale;
+  float* part_acc;            // [n_req * Hkv * n_chunks, qg, D]
+  float* part_ml;             // [n_req * Hkv * n_chunks, qg, 2]
+  const float* gate;          // row t at gate + t * gate_stride (fp32, Hq * D values)
+  int gate_stride;
+  uint16_t* out;              // bf16 hi terms of the gated output [b, Hq * D]
+  uint16_t* out_lo;           // bf16 lo terms
+};
+hipError_t launch_attention(const AttnArgs& a, const AttnPlan& p, hipStream_t st);
+
+hipError_t launch_route_pool(const float* z, int b, int E, int k, int* ids, float* w,
+                             int* counts, int* offsets, int* slot_of, int* tos, int* active,
+                             hipStream_t st);
+
+struct MoeArgs {
+  int b, H, I, E, k;
+  const _Float16* x16;        // [b, H] hi terms of the expert input * 2^-8
+  const _Float16* x16_lo;     // [b, H] lo terms (may be null: the input is exact in fp16)
+  const uint8_t *w13_codes, *w13_scales;
+  const float* w13_gscale;
+  const uint8_t *w2_codes, *w2_scales;
+  const float* w2_gscale;
+  const int *counts, *offsets, *tos;
+  _Float16* h16;              // [b*k, I] scratch: hi terms of the SwiGLU output * 2^-8
+  _Float16* h16_lo;           // [b*k, I] scratch: lo terms
+  uint16_t* h_bf16;           // [b*k, I] optional bf16 copy of the SwiGLU output
+  float* y;                   // fp32 [b*k, H]
+};
+hipError_t launch_moe_experts(const MoeArgs& a, hipStream_t st);
+
+hipError_t launch_unpool(int b, int H, int k, const float* y, const float* w,
+                         const int* slot_of, float* out, hipStream_t st);
+
+hipError_t launch_to_f16(int n, const uint16_t* x, _Float16* out, hipStream_t st);
+
+hipError_t launch_head_argmax(int b, int n_tiles, const float* val, const int* idx,
+                              const int64_t* d2t, int32_t* ids, int64_t* target,
+                              hipStream_t st);
+
+hipError_t launch_debug_dequant(int n, int k, const uint8_t* codes, const uint8_t* scales,
+                                float gscale, float* out, hipStream_t st);

@@ -1,0 +1,100 @@
+"""Device-side plumbing around the C ABI: upload a generated workload, allocate the
+step's outputs and workspace, and call the entry points.  PyTorch is used here for device
+memory and streams only; every step of the computation is a library call."""
+
+import torch
+
+from . import binding as B
+
+LAYER_TENSORS = ("g_post_prev", "g_pre_attn", "g_post_attn", "g_pre_ffn", "g_post_ffn", "w_qkv",
+                 "w_o", "w_router", "w13_codes", "w13_scales", "w13_gscale", "w2_codes",
+                 "w2_scales", "w2_gscale", "k_cache", "v_cache", "block_table", "seq_lens",
+                 "positions", "slot_mapping")
+
+
+def to_dev(t, device):
+    return None if t is None else t.to(device).contiguous()
+
+
+class DeviceLayer:
+    """One layer's weights, KV pool and step metadata on the device, with its C structs."""
+
+    def __init__(self, lay, device):
+        self.t = {k: to_dev(lay[k], device) for k in LAYER_TENSORS}
+        for k in ("num_blocks", "max_blocks", "max_seq_len"):
+            self.t[k] = lay[k]
+        self.weights = B.make_layer_weights(self.t)
+        self.kv = B.make_kv(self.t)
+        self.attn_w = self.weights.attn
+        self.moe_w = self.weights.moe
+
+
+def alloc_route(b, k, E, device):
+    i32 = dict(dtype=torch.int32, device=device)
+    r = dict(topk_ids=torch.empty(b, k, **i32), topk_w=torch.empty(b, k, dtype=torch.float32, device=device),
+             expert_counts=torch.empty(E, **i32), expert_offsets=torch.empty(E + 1, **i32),
+             slot_of=torch.empty(b, k, **i32), token_of_slot=torch.empty(b * k, **i32),
+             active_experts=torch.empty(E + 1, **i32))
+    return r, B.make_route(r)
+
+
+class StepRunner:
+    """A whole workload (activations, layers, head) resident on one device."""
+
+    def __init__(self, wk, device="cuda:0"):
+        self.device = torch.device(device)
+        self.w = wk["workload"]
+        self.d = wk["dims"]
+        self.dims = B.make_dims(self.d)
+        self.b = self.w.b
+        self.act = {k: to_dev(v, device) for k, v in wk["act"].items()
+                    if isinstance(v, torch.Tensor)}
+        self.act["logit_bias"] = to_dev(wk["act"].get("logit_bias"), device)
+        # the branches between blocks are fp32 at the boundary (values of the bf16 draw)
+        self.act["branch_in"] = self.act["branch_in"].float()
+        self.layers = [DeviceLayer(l, device) for l in wk["layers"]]
+        max_seq = max(l.t["max_seq_len"] for l in self.layers)
+        self.ws_bytes = B.workspace_bytes(self.dims, self.b, self.w.n_req, max_seq)
+        if self.ws_bytes == 0:
+            raise B.SdError(-1, B.lib().sd_last_error().decode())
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        self.route_t, self.route = alloc_route(self.b, self.d["top_k"], self.d["n_experts"], device)
+        H = self.d["hidden"]
+        self.branch_out = torch.empty(self.b, H, dtype=torch.float32, device=device)
+        self.head = None
+        if wk.get("head") is not None:
+            h = wk["head"]
+            self.head = dict(w_lm=to_dev(h["w_lm"], device), g_final=to_dev(h["g_final"], device),
+                             d2t=to_dev(h["d2t"], device), multiplier=h["multiplier"],
+                             soft_cap=h["soft_cap"])
+            V = h["w_lm"].shape[0]
+            self.head_ws = torch.empty(B.draft_head_workspace_bytes(H, V, self.b),
+                                       dtype=torch.uint8, device=device)
+            self.head_h = torch.empty(self.b, H, dtype=torch.bfloat16, device=device)
+            self.draft_ids = torch.empty(self.b, dtype=torch.int32, device=device)
+            self.target_ids = torch.empty(self.b, dtype=torch.int64, device=device)
+            self.tau = torch.empty(self.b, V, dtype=torch.float32, device=device)
+
+    def layer_step(self, i, stream_buf, branch_in, front_embed=None, branch_out=None,
+                   with_route=True, stream=None):
+        L = self.layers[i]
+        out = self.branch_out if branch_out is None else branch_out
+        B.layer_step(self.dims, self.b, stream_buf, branch_in, front_embed, L.weights, L.kv,
+                     self.act["logit_bias"], out, self.route if with_route else None, self.ws,
+                     stream)
+        return out
+
+    def chain(self, stream_buf, branch_in, branch_bufs, with_tau=True, stream=None):
+        """All layers through their input boundaries, the final boundary and the head.
+        branch_bufs: one fp32 [b, H] buffer per layer for the layer outputs."""
+        u = branch_in
+        for i in range(len(self.layers)):
+            u = self.layer_step(i, stream_buf, u, branch_out=branch_bufs[i], stream=stream)
+        hd = self.head
+        B.boundary_dualnorm(self.dims, self.b, stream_buf, u, None,
+                            self.layers[-1].t["g_post_ffn"], hd["g_final"], self.head_h, stream)
+        V = hd["w_lm"].shape[0]
+        B.draft_head(self.d["hidden"], V, self.b, self.head_h, hd["w_lm"], hd["multiplier"],
+                     hd["soft_cap"], hd["d2t"], self.tau if with_tau else None, self.draft_ids,
+                     self.target_ids, self.head_ws, stream)
+        return self.draft_ids, self.target_ids

@@ -1,0 +1,207 @@
+"""Per-call GPU parity (stage A: the oracle takes the same inputs the GPU call took).
+
+Floats: |gpu - ref| <= 2e-2 * (1 + |ref|) elementwise.  Discrete outputs: bit-exact
+(expert ids except near ties, which must still be a valid top-k; pooler maps always).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.formats import dequant_nvfp4
+from speculative_verify_decode_amd import binding as B
+from speculative_verify_decode_amd import synth
+from speculative_verify_decode_amd.runner import alloc_route
+from tests.gpu_util import (DEV, check_route_stage_a, head_flags, require_lib, runner, say,
+                            workload)
+from tests.helpers import assert_close, np64
+
+pytestmark = pytest.mark.gpu
+
+ALL = ["tiny_b8_ctx128", "h4096_b8_ctx8k", "h4096_b64_ragged", "h4096_b8_ctx131k"]
+
+
+# ------------------------------------------------------------------------ dequant
+def test_debug_dequant_is_bit_exact():
+    require_lib()
+    rng = np.random.default_rng(3)
+    n, k = 48, 4096
+    codes = rng.integers(0, 256, (n, k // 2), dtype=np.uint8)
+    valid = [c for c in range(256) if c not in (0x7F, 0xFF)]
+    scales = rng.choice(valid, (n, k // 16)).astype(np.uint8)      # every finite E4M3 code
+    out = torch.empty(n, k, dtype=torch.float32, device=DEV)
+    for gscale in (1.0, 0.5, 4.0):
+        B.debug_dequant(n, k, torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV),
+                        gscale, out)
+        torch.cuda.synchronize()
+        ref = dequant_nvfp4(codes, scales, gscale)
+        assert np.array_equal(out.cpu().numpy().astype(np.float64), ref), gscale
+
+
+# ------------------------------------------------------------------------ dual norm
+@pytest.mark.parametrize("name", ["tiny_b8_ctx128", "h4096_b8_ctx8k"])
+def test_boundary_dualnorm_modes(name):
+    require_lib()
+    wk = workload(name)
+    act, lay, d = wk["act"], wk["layers"][0], wk["dims"]
+    dims, b, H = B.make_dims(d), wk["workload"].b, d["hidden"]
+    s = act["stream"].to(DEV).clone()
+    out = torch.empty(b, H, dtype=torch.bfloat16, device=DEV)
+    gp, gq = lay["g_post_prev"].to(DEV), lay["g_pre_attn"].to(DEV)
+    B.boundary_dualnorm(dims, b, s, act["branch_in"].float().to(DEV), None, gp, gq, out)
+    torch.cuda.synchronize()
+    s_ref, x_ref = oracle.dual_norm(np64(act["stream"]), np64(act["branch_in"]), np64(lay["g_post_prev"]),
+                                    np64(lay["g_pre_attn"]), d["eps"])
+    assert_close(np64(s), s_ref, "stream")
+    assert_close(np64(out), x_ref, "pre-norm output")
+    # front mode: the stream becomes the embedding
+    B.boundary_dualnorm(dims, b, s, None, act["front_embed"].to(DEV), None, gq, out)
+    torch.cuda.synchronize()
+    s_ref, x_ref = oracle.front_norm(np64(act["front_embed"]), np64(lay["g_pre_attn"]), d["eps"])
+    assert np.array_equal(np64(s), s_ref)
+    assert_close(np64(out), x_ref, "front pre-norm output")
+
+
+# ------------------------------------------------------------------------ attention
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ALL)
+def test_attn_verify_matches_oracle(name):
+    wk = workload(name)
+    r = runner(wk)
+    lay, d, b = wk["layers"][0], wk["dims"], r.b
+    say(f"[gpu-test] attn_verify {name}")
+    x = wk["act"]["front_embed"]
+    out = torch.empty(b, d["hidden"], dtype=torch.float32, device=DEV)
+    L = r.layers[0]
+    B.attn_verify(r.dims, b, x.to(DEV), L.attn_w, L.kv, out, r.ws)
+    torch.cuda.synchronize()
+    q, k, v, gate = oracle.qkv_front(np64(x), np64(lay["w_qkv"]), np64(lay["positions"]),
+                                     d["n_q_heads"], d["n_kv_heads"], d["head_dim"], d["eps"],
+                                     d["rope_theta"], bool(d["qk_norm"]))
+    kc, vc = oracle.kv_write(np64(lay["k_cache"]), np64(lay["v_cache"]), k, v, np64(lay["slot_mapping"]))
+    o = oracle.paged_attention(q, kc, vc, np64(lay["block_table"]), np64(lay["positions"]), d["q_rows"])
+    a = oracle.gate_oproj(o, gate, np64(lay["w_o"]))
+    w = assert_close(np64(out), a, "attention output")
+    say(f"[gpu-test] attn {name}: worst scaled err {w:.2e}")
+    # the cache changed exactly at the step's slots, to the bf16 K/V of the oracle
+    slots = np64(lay["slot_mapping"])
+    for key, ref_cache, new in (("k_cache", kc, L.t["k_cache"]), ("v_cache", vc, L.t["v_cache"])):
+        before = lay[key].to(DEV)
+        same = (new == before) | (torch.isnan(new) & torch.isnan(before))
+        changed = (~same).reshape(new.shape[0], -1).any(dim=1).nonzero().flatten().cpu().numpy()
+        assert set(changed.tolist()) <= set((slots // 16).tolist()), key
+        blocks = np.unique(slots // 16)
+        got = np64(new[torch.from_numpy(blocks).to(DEV)])
+        want = ref_cache[blocks]
+        mask = ~np.isnan(want)
+        assert np.array_equal(np.isnan(got), ~mask), key
+        assert_close(got[mask], want[mask], key)
+
+
+# ------------------------------------------------------------------------ routing
+@pytest.mark.parametrize("name", ["tiny_b8_ctx128", "h4096_b8_ctx8k", "h4096_b64_ragged"])
+def test_moe_route_matches_oracle(name):
+    wk = workload(name)
+    r = runner(wk)
+    lay, d, b = wk["layers"][0], wk["dims"], r.b
+    x = wk["act"]["front_embed"]
+    z = torch.empty(b, d["n_experts"], dtype=torch.float32, device=DEV)
+    B.moe_route(r.dims, b, x.to(DEV), r.layers[0].t["w_router"], r.act["logit_bias"], r.route, z, r.ws)
+    torch.cuda.synchronize()
+    z_ref = oracle.router_logits(np64(x), np64(lay["w_router"]), np64(wk["act"].get("logit_bias")))
+    assert_close(np64(z), z_ref, "router logits", tol=1e-3)
+    gid = np64(r.route_t["topk_ids"])
+    flagged = check_route_stage_a(z_ref, gid, d["top_k"])
+    say(f"[gpu-test] route {name}: {len(flagged)} near-tie rows")
+    # weights: softmax over the GPU's own selection of the exact logits
+    sel = np.take_along_axis(z_ref, gid.astype(np.int64), 1)
+    ex = np.exp(sel - sel.max(1, keepdims=True))
+    assert_close(np64(r.route_t["topk_w"]), ex / ex.sum(1, keepdims=True), "route weights", tol=1e-3)
+    counts, offsets, slot_of, tos = oracle.pooler(gid, d["n_experts"])
+    assert np.array_equal(np64(r.route_t["expert_counts"]), counts)
+    assert np.array_equal(np64(r.route_t["expert_offsets"]), offsets)
+    assert np.array_equal(np64(r.route_t["slot_of"]), slot_of)
+    assert np.array_equal(np64(r.route_t["token_of_slot"]), tos)
+    act_list = np64(r.route_t["active_experts"])
+    assert act_list[-1] == (counts > 0).sum()
+    assert np.array_equal(act_list[:act_list[-1]], np.nonzero(counts)[0])
+    if "skew_rows" in wk["act"]:
+        assert np.all(gid[wk["act"]["skew_rows"], 0] == 0)
+
+
+# ------------------------------------------------------------------------ experts + unpool
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["tiny_b8_ctx128", "h4096_b8_ctx8k", "h4096_b64_ragged"])
+def test_moe_experts_and_unpool_match_oracle(name):
+    wk = workload(name)
+    r = runner(wk)
+    lay, d, b = wk["layers"][0], wk["dims"], r.b
+    k, I, H = d["top_k"], d["inter"], d["hidden"]
+    x = wk["act"]["front_embed"]
+    B.moe_route(r.dims, b, x.to(DEV), r.layers[0].t["w_router"], r.act["logit_bias"], r.route, None, r.ws)
+    y = torch.empty(b * k, H, dtype=torch.float32, device=DEV)
+    h = torch.empty(b * k, I, dtype=torch.bfloat16, device=DEV)
+    B.moe_experts(r.dims, b, x.to(DEV), r.layers[0].moe_w, r.route, y, h, r.ws)
+    m = torch.empty(b, H, dtype=torch.float32, device=DEV)
+    B.moe_unpool(r.dims, b, y, r.route, m)
+    torch.cuda.synchronize()
+    rt = {kk: np64(v) for kk, v in r.route_t.items()}
+    counts, offsets, tos = rt["expert_counts"], rt["expert_offsets"], rt["token_of_slot"]
+    touched = np.nonzero(counts)[0]
+    subset = touched if len(touched) <= 24 else np.concatenate([touched[:1], touched[-5:]])
+    say(f"[gpu-test] experts {name}: checking {len(subset)} of {len(touched)} touched experts")
+    h_ref, y_ref = oracle.moe_experts(np64(x), counts, offsets, tos, np64(lay["w13_codes"]),
+                                      np64(lay["w13_scales"]), np64(lay["w13_gscale"]),
+                                      np64(lay["w2_codes"]), np64(lay["w2_scales"]),
+                                      np64(lay["w2_gscale"]), I, experts=set(subset.tolist()))
+    rows = np.concatenate([np.arange(offsets[e], offsets[e + 1]) for e in subset])
+    assert_close(np64(h)[rows], h_ref[rows], "SwiGLU output h")
+    assert_close(np64(y)[rows], y_ref[rows], "expert output y")
+    m_ref = oracle.unpool(np64(y), rt["topk_w"], rt["slot_of"])
+    assert_close(np64(m), m_ref, "unpooled output")
+
+
+# ------------------------------------------------------------------------ draft head
+@pytest.mark.timeout(600)
+def test_draft_head_full_size_matches_oracle():
+    require_lib()
+    w = synth.WORKLOADS["h4096_chain4_head"]
+    hd = synth.make_head(w, 0)
+    H, V, b = w.hidden, w.draft_vocab, w.b
+    h = synth._bf16(synth._normal(0, "head_probe_h", (b, H)))
+    w_lm, d2t = hd["w_lm"].to(DEV), hd["d2t"].to(DEV)
+    ws = torch.empty(B.draft_head_workspace_bytes(H, V, b), dtype=torch.uint8, device=DEV)
+    tau = torch.empty(b, V, dtype=torch.float32, device=DEV)
+    ids = torch.empty(b, dtype=torch.int32, device=DEV)
+    tgt = torch.empty(b, dtype=torch.int64, device=DEV)
+    B.draft_head(H, V, b, h.to(DEV), w_lm, hd["multiplier"], hd["soft_cap"], d2t, tau, ids, tgt, ws)
+    torch.cuda.synchronize()
+    ref = oracle.draft_head(np64(h), np64(hd["w_lm"]), hd["multiplier"], hd["soft_cap"], np64(hd["d2t"]))
+    exact = np64(h) @ np64(hd["w_lm"]).T
+    flagged = head_flags(exact)
+    say(f"[gpu-test] head: {flagged.sum()} near-midpoint rows")
+    gid = np64(ids)
+    for t in range(b):
+        if flagged[t]:
+            assert exact[t, gid[t]] >= exact[t].max() - 2 * 2.0 ** -6
+        else:
+            assert gid[t] == ref["ids"][t], (t, gid[t], ref["ids"][t])
+    assert np.array_equal(np64(tgt), np64(hd["d2t"])[gid])
+    assert_close(np64(tau), ref["tau"], "transformed logits", tol=1e-2)
+
+
+def test_draft_head_ties_take_the_lower_index():
+    require_lib()
+    H, V, b = 128, 64, 8
+    w = torch.zeros(V, H, dtype=torch.bfloat16)
+    w[[5, 17, 40], 0] = 1.0                  # three identical best rows
+    h = torch.zeros(b, H, dtype=torch.bfloat16)
+    h[:, 0] = 2.0
+    d2t = torch.arange(V, dtype=torch.int64) * 7 + 3
+    ws = torch.empty(B.draft_head_workspace_bytes(H, V, b), dtype=torch.uint8, device=DEV)
+    ids = torch.empty(b, dtype=torch.int32, device=DEV)
+    tgt = torch.empty(b, dtype=torch.int64, device=DEV)
+    B.draft_head(H, V, b, h.to(DEV), w.to(DEV), 0.25, 30.0, d2t.to(DEV), None, ids, tgt, ws)
+    torch.cuda.synchronize()
+    assert ids.cpu().tolist() == [5] * b and tgt.cpu().tolist() == [38] * b
