@@ -50,7 +50,7 @@ def draft_head(h, w_lm, multiplier, soft_cap, d2t):
 
 
 def chain_step(layers, dims, stream, branch_in, g_final, w_lm, multiplier, soft_cap, d2t,
-               route_overrides=None):
+               route_overrides=None, on_layer=None):
     """Several layers of [DEC] ``SpecializedDecode.run`` chained through their input
     boundaries, then the final boundary and the draft head.
 
@@ -67,6 +67,8 @@ def chain_step(layers, dims, stream, branch_in, g_final, w_lm, multiplier, soft_
         ro = None if route_overrides is None else route_overrides[i]
         out = layer_step(li, dims, branch_in=u, route_override=ro)
         outs.append(out)
+        if on_layer is not None:          # progress report only
+            on_layer(i)
         s, u = out["stream"], out["m"]
     s, h = final_boundary(s, u, layers[-1]["g_post_ffn"], g_final, dims["eps"])
     return dict(layers=outs, stream=s, h=h,

@@ -172,7 +172,8 @@ def test_chain_of_four_layers_with_draft_head():
     ref = oracle.chain_step(layers, d, np64(act["stream"]), np64(act["branch_in"]),
                             np64(wk["head"]["g_final"]), np64(wk["head"]["w_lm"]),
                             wk["head"]["multiplier"], wk["head"]["soft_cap"], np64(wk["head"]["d2t"]),
-                            route_overrides=[teacher_forcer(g, STAGE_B_GAP, forced) for g in gids])
+                            route_overrides=[teacher_forcer(g, STAGE_B_GAP, forced) for g in gids],
+                            on_layer=lambda i: say(f"[gpu-test] chain oracle: layer {i} done"))
     for i in range(4):
         say(f"[gpu-test] chain layer {i}: teacher-forced rows {forced[i].tolist()}")
         free = np.setdiff1d(np.arange(b), forced[i])
