@@ -80,6 +80,11 @@ int check_dims(const sd_dims* d) {
     return fail(SD_EUNSUPPORTED, "top_k %d (1..min(8, n_experts))", d->top_k);
   if (d->inter <= 0 || d->inter % 128)
     return fail(SD_EUNSUPPORTED, "inter %d (need a multiple of 128)", d->inter);
+  if (!moe_shape_supported(d->hidden, d->inter))
+    return fail(SD_EUNSUPPORTED,
+                "expert GEMM split of hidden %d / inter %d (each must be 128 * n * ks with "
+                "n <= 4, ks in {1, 2, 4, 8})",
+                d->hidden, d->inter);
   if (d->qk_norm != 0 && d->qk_norm != 1) return fail(SD_EINVAL, "qk_norm %d", d->qk_norm);
   if (!(d->eps > 0.f)) return fail(SD_EINVAL, "eps must be > 0");
   if (!(d->rope_theta > 0.f)) return fail(SD_EINVAL, "rope_theta must be > 0");
@@ -245,6 +250,7 @@ int run_experts(const sd_dims* d, int b, const _Float16* x16, const _Float16* x1
   m.w13_codes = w->w13_codes; m.w13_scales = w->w13_scales; m.w13_gscale = w->w13_gscale;
   m.w2_codes = w->w2_codes; m.w2_scales = w->w2_scales; m.w2_gscale = w->w2_gscale;
   m.counts = r->expert_counts; m.offsets = r->expert_offsets; m.tos = r->token_of_slot;
+  m.active = r->active_experts;
   m.h16 = h16; m.h_bf16 = h_bf16; m.y = y;
   SD_LAUNCH(launch_moe_experts(m, st), "routed experts");
   return SD_OK;

@@ -218,17 +218,35 @@ __global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a, int chunk_bloc
   const int L = min(a.seq_lens[r], a.max_blocks * 16);
   const int nc = (((L + 15) >> 4) + chunk_blocks - 1) / chunk_blocks;
   const size_t p0 = ((size_t)r * a.Hkv + g) * n_chunks;
-  float M = -INFINITY;
-  for (int c = 0; c < nc; ++c) M = fmaxf(M, a.part_ml[((p0 + c) * qg + qi) * 2]);
-  float acc = 0.f, l = 0.f;
-  for (int c = 0; c < nc; ++c) {
+  __shared__ float s_w[1024], s_l[1024], s_red[2];
+  // chunk maxima and sums: one load per chunk, spread over the threads
+  float mloc = -INFINITY;
+  for (int c = d; c < nc; c += blockDim.x) {
     const float m = a.part_ml[((p0 + c) * qg + qi) * 2];
-    if (m == -INFINITY) continue;
-    const float f = exp2f(m - M);
-    l += f * a.part_ml[((p0 + c) * qg + qi) * 2 + 1];
-    acc += f * a.part_acc[((p0 + c) * qg + qi) * a.D + d];
+    s_w[c] = m;
+    s_l[c] = a.part_ml[((p0 + c) * qg + qi) * 2 + 1];
+    mloc = fmaxf(mloc, m);
   }
-  const float o = acc / l;
+  mloc = sd::wave_max(mloc);
+  if ((d & 63) == 0) s_red[d >> 6] = mloc;
+  __syncthreads();
+  const float M = blockDim.x > 64 ? fmaxf(s_red[0], s_red[1]) : s_red[0];
+  __syncthreads();
+  for (int c = d; c < nc; c += blockDim.x)
+    s_w[c] = s_w[c] == -INFINITY ? 0.f : exp2f(s_w[c] - M);
+  __syncthreads();
+  // independent loads across chunks: 4 accumulators
+  float acc[4] = {0.f, 0.f, 0.f, 0.f}, l = 0.f;
+  const float* pa = a.part_acc + (p0 * qg + qi) * a.D + d;
+  const size_t cs = (size_t)qg * a.D;  // chunk stride
+  int c = 0;
+  for (; c + 4 <= nc; c += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[u] += s_w[c + u] * pa[(c + u) * cs];
+  }
+  for (; c < nc; ++c) acc[0] += s_w[c] * pa[c * cs];
+  for (int cc = 0; cc < nc; ++cc) l += s_w[cc] * s_l[cc];
+  const float o = (acc[0] + acc[1] + acc[2] + acc[3]) / l;
   const float gate = a.gate[(size_t)t * a.gate_stride + h * a.D + d];
   const float sig = 1.0f / (1.0f + __expf(-gate));
   uint16_t hi, lo;

@@ -14,14 +14,18 @@
 
 namespace {
 
-template <int NCT, int U, int MODE, bool SPLIT>
-__global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
+// NW waves split K; each wave works in passes of S MFMA steps (32 k each) and issues every
+// weight and activation load of a pass before the first MFMA of it.  Loads are
+// unconditional (rows past M or N read a valid clamped row) so nothing serialises them;
+// activation rows past M are zeroed after their loads.
+template <int NCT, int NW, int S, int MODE, bool SPLIT>
+__global__ __launch_bounds__(64 * NW) void k_gemm(GemmArgs a) {
   constexpr int RPC = SPLIT ? 8 : 16;  // activation rows per column tile
-  __shared__ f32x4_t red[3][NCT][64];
+  __shared__ f32x4_t red[NW - 1][NCT][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int i = lane & 15, g = lane >> 4;
   const int n0 = blockIdx.x * 16;
-  const int KW = a.K >> 2;
+  const int KW = a.K / NW;
   const int k0 = wave * KW + 8 * g;
   // rows past N (a ragged last tile) re-read row N-1; their results are never stored
   const uint16_t* wrow = a.w + (size_t)min(n0 + i, a.N - 1) * a.K + k0;
@@ -38,22 +42,24 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
 #pragma unroll
   for (int c = 0; c < NCT; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const bf16x8_t zero8 = {};
-  for (int kk = 0; kk < KW; kk += 32 * U) {
-    bf16x8_t av[U];
-    bf16x8_t bv[U][NCT];
+  const int passes = (KW >> 5) / S;
+  for (int p = 0; p < passes; ++p) {
+    const int s0 = p * S * 32;
+    bf16x8_t av[S];
+    bf16x8_t bv[S][NCT];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      av[u] = __builtin_nontemporal_load((const bf16x8_t*)(wrow + kk + 32 * u));
+    for (int u = 0; u < S; ++u)
+      av[u] = __builtin_nontemporal_load((const bf16x8_t*)(wrow + s0 + 32 * u));
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < S; ++u)
+#pragma unroll
+      for (int c = 0; c < NCT; ++c) bv[u][c] = *(const bf16x8_t*)(xrow[c] + s0 + 32 * u);
+#pragma unroll
+    for (int u = 0; u < S; ++u)
 #pragma unroll
       for (int c = 0; c < NCT; ++c)
-        bv[u][c] = xv[c] ? *(const bf16x8_t*)(xrow[c] + kk + 32 * u) : zero8;
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int c = 0; c < NCT; ++c)
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], bv[u][c], acc[c], 0, 0, 0);
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], xv[c] ? bv[u][c] : zero8, acc[c],
+                                                         0, 0, 0);
   }
   if (wave > 0) {
 #pragma unroll
@@ -63,7 +69,8 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
   if (wave != 0) return;
 #pragma unroll
   for (int c = 0; c < NCT; ++c) {
-    acc[c] += red[0][c][lane] + red[1][c][lane] + red[2][c][lane];
+#pragma unroll
+    for (int w = 0; w < NW - 1; ++w) acc[c] += red[w][c][lane];
     if (SPLIT) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[c][r] += __shfl_xor(acc[c][r], 8, 64);
@@ -128,14 +135,28 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
   }
 }
 
+template <int NCT, int NW, int MODE, bool SPLIT>
+void launch_s(const GemmArgs& a, hipStream_t st) {
+  // steps per wave; the pass size S divides it and keeps the in-flight registers bounded
+  constexpr int SCAP = NCT >= 8 ? 2 : 16 / NCT;
+  const int steps = a.K / NW / 32;
+  const dim3 grid((a.N + 15) / 16), block(64 * NW);
+  if (SCAP >= 16 && steps % 16 == 0)
+    hipLaunchKernelGGL((k_gemm<NCT, NW, (SCAP >= 16 ? 16 : 1), MODE, SPLIT>), grid, block, 0, st, a);
+  else if (SCAP >= 8 && steps % 8 == 0)
+    hipLaunchKernelGGL((k_gemm<NCT, NW, (SCAP >= 8 ? 8 : 1), MODE, SPLIT>), grid, block, 0, st, a);
+  else if (SCAP >= 4 && steps % 4 == 0)
+    hipLaunchKernelGGL((k_gemm<NCT, NW, (SCAP >= 4 ? 4 : 1), MODE, SPLIT>), grid, block, 0, st, a);
+  else if (steps % 2 == 0)
+    hipLaunchKernelGGL((k_gemm<NCT, NW, 2, MODE, SPLIT>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((k_gemm<NCT, NW, 1, MODE, SPLIT>), grid, block, 0, st, a);
+}
+
 template <int NCT, int MODE, bool SPLIT>
 hipError_t launch_u(const GemmArgs& a, hipStream_t st) {
-  const int steps = (a.K / 4) / 32;
-  const dim3 grid((a.N + 15) / 16), block(256);
-  if (steps % 8 == 0) hipLaunchKernelGGL((k_gemm<NCT, 8, MODE, SPLIT>), grid, block, 0, st, a);
-  else if (steps % 4 == 0) hipLaunchKernelGGL((k_gemm<NCT, 4, MODE, SPLIT>), grid, block, 0, st, a);
-  else if (steps % 2 == 0) hipLaunchKernelGGL((k_gemm<NCT, 2, MODE, SPLIT>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((k_gemm<NCT, 1, MODE, SPLIT>), grid, block, 0, st, a);
+  if (a.K % 256 == 0) launch_s<NCT, 8, MODE, SPLIT>(a, st);
+  else launch_s<NCT, 4, MODE, SPLIT>(a, st);
   return hipGetLastError();
 }
 

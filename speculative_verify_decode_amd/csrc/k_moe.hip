@@ -6,11 +6,14 @@
 // routed experts are NVFP4 (page "vllm.models.muse_spark.nvidia.specialized_decode.
 // runtime", module list: expert_tp).
 //
-// Expert GEMMs: workgroup (n-tile of 16 output features, expert e) with KS waves splitting
-// K.  Weights are the A operand of v_mfma_f32_16x16x32_f16, dequantised exactly in
-// registers (dequant_unit); each lane streams a contiguous run of K/(4*KS) codes of its
-// row.  The pooled tokens of expert e are the B operand, 8 per column tile as hi/lo fp16
-// terms (columns 0-7 / 8-15).  Workgroups of experts with no routed token exit at once.
+// Expert GEMMs: workgroup (16-feature tile, active expert) with KS waves splitting K.
+// Weights are the A operand of v_mfma_f32_16x16x32_f16, dequantised exactly in registers.
+// Each load instruction covers 64 contiguous code bytes of each of 16 rows (4 lanes per
+// row, 32 weights per lane) and a wave issues all of its weight loads before it waits on
+// any, so the whole K slice of the tile is in flight at once.  The pooled tokens of the
+// expert are the B operand, 8 per column tile as hi/lo fp16 terms (columns 0-7 / 8-15).
+// Workgroups are indexed by the ascending active-expert list, so the grid's live part is
+// dispatched first and the rest exits at once.
 #include "sd_common.h"
 
 namespace {
@@ -26,12 +29,18 @@ __global__ __launch_bounds__(256) void k_route_pool(const float* __restrict__ z,
                                                     int* __restrict__ slot_of,
                                                     int* __restrict__ tos,
                                                     int* __restrict__ active) {
+  __shared__ float s_z[64 * 256 + 1];
   __shared__ int s_ids[64 * 8];
   __shared__ int s_cnt[256];
   __shared__ int s_off[257];
   const int tid = threadIdx.x;
+  for (int p = tid; p < b * E; p += 256) {
+    const float v = z[p];
+    s_z[p] = v != v ? -INFINITY : v;  // NaN ranks last
+  }
+  __syncthreads();
   if (tid < b) {
-    const float* zr = z + (size_t)tid * E;
+    const float* zr = s_z + tid * E;
     float prev_v = INFINITY;
     int prev_i = -1;
     float sel[8];
@@ -39,7 +48,7 @@ __global__ __launch_bounds__(256) void k_route_pool(const float* __restrict__ z,
       float bv = -INFINITY;
       int bi = -1;
       for (int e = 0; e < E; ++e) {
-        const float v = zr[e] != zr[e] ? -INFINITY : zr[e];  // NaN ranks last
+        const float v = zr[e];
         // eligible: after the previous pick in the order (-z, index)
         const bool after = v < prev_v || (v == prev_v && e > prev_i);
         if (after && (bi < 0 || v > bv)) { bv = v; bi = e; }
@@ -88,67 +97,94 @@ __global__ __launch_bounds__(256) void k_route_pool(const float* __restrict__ z,
 }
 
 // ---------------------------------------------------------------- expert GEMMs
-// Load 16 bytes of codes + 2 scale bytes of one row at k offset kk (a 32-weight unit).
-__device__ __forceinline__ void load_unit(const uint8_t* codes_row, const uint8_t* scale_row,
-                                          int kk, u32x4_t& c, uint32_t& s) {
-  c = __builtin_nontemporal_load((const u32x4_t*)(codes_row + (kk >> 1)));
-  s = *(const uint16_t*)(scale_row + (kk >> 4));
+// One wave's share of a 16-row weight tile: NU groups of 128 weights per row.  Lane (i, G)
+// holds weights kw0 + 128u + 32G + [0, 32) of row i: 16 code bytes and 2 scale bytes per
+// group, so each load instruction covers 64 contiguous code bytes of each of the 16 rows.
+template <int NU>
+struct RowSlice {
+  u32x4_t codes[NU];
+  uint32_t scales[NU];
+};
+
+template <int NU>
+__device__ __forceinline__ void load_slice(RowSlice<NU>& s, const uint8_t* codes_row,
+                                           const uint8_t* scale_row, int kw0, int G) {
+  const uint8_t* c = codes_row + (kw0 >> 1) + 16 * G;
+  const uint8_t* sc = scale_row + (kw0 >> 4) + 2 * G;
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    s.codes[u] = __builtin_nontemporal_load((const u32x4_t*)(c + 64 * u));
+    s.scales[u] = *(const uint16_t*)(sc + 8 * u);
+  }
 }
 
-// Column-tile rows of the B operand: lane column i holds token slot 8c + (i & 7), hi term
-// for i < 8 and lo term for i >= 8.  Returns the row pointer at k offset kl0, or null.
-__device__ __forceinline__ const _Float16* b_row(const _Float16* hi, const _Float16* lo,
-                                                 size_t row, int K, int kl0, int i) {
-  const _Float16* base = (i >> 3) ? lo : hi;
-  return base == nullptr ? nullptr : base + row * K + kl0;
+// B operand of one column tile: lane column i holds a pooled token (hi term for i < 8, lo
+// term for i >= 8); f16x8 m of group u covers k = kw0 + 128u + 32G + 8m.  `row` is always
+// a valid row (invalid lanes read row 0) and `valid` zeroes the operand after the loads.
+template <int NU>
+__device__ __forceinline__ void load_b(f16x8_t (&bx)[NU][4], const _Float16* row, bool valid) {
+#pragma unroll
+  for (int u = 0; u < NU; ++u)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) bx[u][m] = *(const f16x8_t*)(row + 128 * u + 8 * m);
+  if (!valid) {
+    const f16x8_t zero8 = {};
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) bx[u][m] = zero8;
+  }
 }
 
-// W13 (gate rows [0, I), up rows [I, 2I)) + SwiGLU.
-template <int NCT, int KS>
+// W13 (gate rows [0, I), up rows [I, 2I)) + SwiGLU.  KS waves split K = H, NU = H/(128 KS).
+template <int NCT, int NU, int KS>
 __global__ __launch_bounds__(64 * KS) void k_moe_w13(MoeArgs a) {
   __shared__ f32x4_t red[KS > 1 ? KS - 1 : 1][2][NCT][64];
-  const int nt = blockIdx.x, e = blockIdx.y;
-  const int Te = a.counts[e];
-  if (Te == 0) return;
-  const int off = a.offsets[e];
-  const int nct = (Te + 7) >> 3;
+  if ((int)blockIdx.y >= a.active[a.E]) return;
+  const int e = a.active[blockIdx.y];
+  const int nt = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int i = lane & 15, G = lane >> 4;
   const int K = a.H;
-  const int KL = K / (4 * KS);
-  const int kl0 = wave * (K / KS) + G * KL;
+  const int kw0 = wave * (NU * 128);
   const size_t rowg = (size_t)e * 2 * a.I + nt * 16 + i;
   const size_t rowu = rowg + a.I;
-  const uint8_t* cg = a.w13_codes + rowg * (K >> 1);
-  const uint8_t* cu = a.w13_codes + rowu * (K >> 1);
-  const uint8_t* sg = a.w13_scales + rowg * (K >> 4);
-  const uint8_t* su = a.w13_scales + rowu * (K >> 4);
-  const _Float16* xr[NCT];
-#pragma unroll
-  for (int c = 0; c < NCT; ++c) {
-    const int slot = 8 * c + (i & 7);
-    xr[c] = slot < Te ? b_row(a.x16, a.x16_lo, a.tos[off + slot], K, kl0, i) : nullptr;
-  }
+  RowSlice<NU> wg, wu;
+  load_slice<NU>(wg, a.w13_codes + rowg * (K >> 1), a.w13_scales + rowg * (K >> 4), kw0, G);
+  load_slice<NU>(wu, a.w13_codes + rowu * (K >> 1), a.w13_scales + rowu * (K >> 4), kw0, G);
+  const int Te = a.counts[e];
+  const int off = a.offsets[e];
+  const int nct = (Te + 7) >> 3;
   f32x4_t ag[NCT], au[NCT];
 #pragma unroll
   for (int c = 0; c < NCT; ++c) ag[c] = au[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const f16x8_t zero8 = {};
-  for (int kk = 0; kk < KL; kk += 32) {
-    u32x4_t c0, c1;
-    uint32_t s0, s1;
-    load_unit(cg, sg, kl0 + kk, c0, s0);
-    load_unit(cu, su, kl0 + kk, c1, s1);
-    f16x8_t wg[4], wu[4];
-    sd::dequant_unit(c0, s0, wg);
-    sd::dequant_unit(c1, s1, wu);
 #pragma unroll
-    for (int c = 0; c < NCT; ++c) {
-      if (c >= nct) break;
+  for (int c = 0; c < NCT; ++c) {
+    if (c >= nct) break;
+    const int slot = 8 * c + (i & 7);
+    const bool lo = (i >> 3) != 0;
+    const bool valid = slot < Te && (!lo || a.x16_lo != nullptr);
+    const _Float16* base = (lo && a.x16_lo != nullptr) ? a.x16_lo : a.x16;
+    // the tile's 8 token ids through uniform (scalar) loads, which do not queue behind the
+    // weight loads; each lane then selects its own
+    int tok = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int t = (8 * c + j < Te) ? a.tos[off + 8 * c + j] : 0;
+      tok = ((i & 7) == j) ? t : tok;
+    }
+    tok = valid ? tok : 0;
+    f16x8_t bx[NU][4];
+    load_b<NU>(bx, base + (size_t)tok * K + kw0 + 32 * G, valid);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      f16x8_t dg[4], du[4];
+      sd::dequant_unit(wg.codes[u], wg.scales[u], dg);
+      sd::dequant_unit(wu.codes[u], wu.scales[u], du);
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const f16x8_t bx = xr[c] != nullptr ? *(const f16x8_t*)(xr[c] + kk + 8 * m) : zero8;
-        ag[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wg[m], bx, ag[c], 0, 0, 0);
-        au[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wu[m], bx, au[c], 0, 0, 0);
+        ag[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dg[m], bx[u][m], ag[c], 0, 0, 0);
+        au[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(du[m], bx[u][m], au[c], 0, 0, 0);
       }
     }
   }
@@ -205,47 +241,41 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w13(MoeArgs a) {
   }
 }
 
-// W2: y[slot, n] = h[slot] . W2_e[n], fp32.
-template <int NCT, int KS>
+// W2: y[slot, n] = h[slot] . W2_e[n], fp32.  KS waves split K = I, NU = I/(128 KS).
+template <int NCT, int NU, int KS>
 __global__ __launch_bounds__(64 * KS) void k_moe_w2(MoeArgs a) {
   __shared__ f32x4_t red[KS > 1 ? KS - 1 : 1][NCT][64];
-  const int nt = blockIdx.x, e = blockIdx.y;
-  const int Te = a.counts[e];
-  if (Te == 0) return;
-  const int off = a.offsets[e];
-  const int nct = (Te + 7) >> 3;
+  if ((int)blockIdx.y >= a.active[a.E]) return;
+  const int e = a.active[blockIdx.y];
+  const int nt = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int i = lane & 15, G = lane >> 4;
   const int K = a.I;
-  const int KL = K / (4 * KS);
-  const int kl0 = wave * (K / KS) + G * KL;
+  const int kw0 = wave * (NU * 128);
   const size_t row = (size_t)e * a.H + nt * 16 + i;
-  const uint8_t* cw = a.w2_codes + row * (K >> 1);
-  const uint8_t* sw = a.w2_scales + row * (K >> 4);
-  const _Float16* xr[NCT];
-#pragma unroll
-  for (int c = 0; c < NCT; ++c) {
-    const int slot = 8 * c + (i & 7);
-    xr[c] = slot < Te ? b_row(a.h16, a.h16_lo, off + slot, K, kl0, i) : nullptr;
-  }
+  RowSlice<NU> wv;
+  load_slice<NU>(wv, a.w2_codes + row * (K >> 1), a.w2_scales + row * (K >> 4), kw0, G);
+  const int Te = a.counts[e];
+  const int off = a.offsets[e];
+  const int nct = (Te + 7) >> 3;
   f32x4_t acc[NCT];
 #pragma unroll
   for (int c = 0; c < NCT; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const f16x8_t zero8 = {};
-  for (int kk = 0; kk < KL; kk += 32) {
-    u32x4_t c0;
-    uint32_t s0;
-    load_unit(cw, sw, kl0 + kk, c0, s0);
-    f16x8_t wv[4];
-    sd::dequant_unit(c0, s0, wv);
 #pragma unroll
-    for (int c = 0; c < NCT; ++c) {
-      if (c >= nct) break;
+  for (int c = 0; c < NCT; ++c) {
+    if (c >= nct) break;
+    const int slot = 8 * c + (i & 7);
+    const bool valid = slot < Te;
+    const _Float16* base = (i >> 3) ? a.h16_lo : a.h16;
+    f16x8_t bx[NU][4];
+    load_b<NU>(bx, base + (size_t)(off + (valid ? slot : 0)) * K + kw0 + 32 * G, valid);
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const f16x8_t bx = xr[c] != nullptr ? *(const f16x8_t*)(xr[c] + kk + 8 * m) : zero8;
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv[m], bx, acc[c], 0, 0, 0);
-      }
+    for (int u = 0; u < NU; ++u) {
+      f16x8_t dw[4];
+      sd::dequant_unit(wv.codes[u], wv.scales[u], dw);
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dw[m], bx[u][m], acc[c], 0, 0, 0);
     }
   }
   if (KS > 1) {
@@ -301,9 +331,8 @@ __global__ __launch_bounds__(256) void k_debug_dequant(int n, int k, const uint8
   const int u = blockIdx.x * 256 + threadIdx.x;
   if (u >= n * units) return;
   const int row = u / units, kk = (u - row * units) * 32;
-  u32x4_t c;
-  uint32_t s;
-  load_unit(codes + (size_t)row * (k >> 1), scales + (size_t)row * (k >> 4), kk, c, s);
+  const u32x4_t c = *(const u32x4_t*)(codes + (size_t)row * (k >> 1) + (kk >> 1));
+  const uint32_t s = *(const uint16_t*)(scales + (size_t)row * (k >> 4) + (kk >> 4));
   f16x8_t wv[4];
   sd::dequant_unit(c, s, wv);
   float* o = out + (size_t)row * k + kk;
@@ -313,23 +342,48 @@ __global__ __launch_bounds__(256) void k_debug_dequant(int n, int k, const uint8
     for (int e = 0; e < 8; ++e) o[8 * m + e] = (float)wv[m][e] * gscale;
 }
 
+// A K split of an expert GEMM: K = 128 * NU * KS with NU <= 4 groups per wave.
+struct Split { int nu, ks; };
+Split split_for(int K) {
+  const int g = K / 128;
+  for (int ks = 8; ks >= 1; ks >>= 1)
+    if (K % 128 == 0 && g % ks == 0 && g / ks >= 1 && g / ks <= 4) return {g / ks, ks};
+  return {0, 0};
+}
+
+#define SD_SPLITS(X) X(1, 1) X(1, 2) X(1, 4) X(1, 8) X(2, 1) X(2, 2) X(2, 4) X(2, 8) \
+                     X(3, 1) X(3, 2) X(3, 4) X(3, 8) X(4, 1) X(4, 2) X(4, 4) X(4, 8)
+
 template <int NCT>
 hipError_t launch_experts_nct(const MoeArgs& a, hipStream_t st) {
-  auto ks_for = [](int K) { return K % 512 == 0 ? 4 : (K % 256 == 0 ? 2 : 1); };
-  const int ks13 = ks_for(a.H), ks2 = ks_for(a.I);
+  const Split s13 = split_for(a.H), s2 = split_for(a.I);
   const dim3 g13(a.I / 16, a.E), g2(a.H / 16, a.E);
-  if (ks13 == 4) hipLaunchKernelGGL((k_moe_w13<NCT, 4>), g13, dim3(256), 0, st, a);
-  else if (ks13 == 2) hipLaunchKernelGGL((k_moe_w13<NCT, 2>), g13, dim3(128), 0, st, a);
-  else hipLaunchKernelGGL((k_moe_w13<NCT, 1>), g13, dim3(64), 0, st, a);
+  bool done = false;
+#define SD_W13(NU, KS)                                                                     \
+  if (!done && s13.nu == NU && s13.ks == KS) {                                             \
+    hipLaunchKernelGGL((k_moe_w13<NCT, NU, KS>), g13, dim3(64 * KS), 0, st, a);            \
+    done = true;                                                                          \
+  }
+  SD_SPLITS(SD_W13)
+#undef SD_W13
+  if (!done) return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (ks2 == 4) hipLaunchKernelGGL((k_moe_w2<NCT, 4>), g2, dim3(256), 0, st, a);
-  else if (ks2 == 2) hipLaunchKernelGGL((k_moe_w2<NCT, 2>), g2, dim3(128), 0, st, a);
-  else hipLaunchKernelGGL((k_moe_w2<NCT, 1>), g2, dim3(64), 0, st, a);
+  done = false;
+#define SD_W2(NU, KS)                                                                      \
+  if (!done && s2.nu == NU && s2.ks == KS) {                                               \
+    hipLaunchKernelGGL((k_moe_w2<NCT, NU, KS>), g2, dim3(64 * KS), 0, st, a);              \
+    done = true;                                                                          \
+  }
+  SD_SPLITS(SD_W2)
+#undef SD_W2
+  if (!done) return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 }  // namespace
+
+bool moe_shape_supported(int H, int I) { return split_for(H).nu > 0 && split_for(I).nu > 0; }
 
 hipError_t launch_route_pool(const float* z, int b, int E, int k, int* ids, float* w,
                              int* counts, int* offsets, int* slot_of, int* tos, int* active,
@@ -340,10 +394,9 @@ hipError_t launch_route_pool(const float* z, int b, int E, int k, int* ids, floa
 }
 
 hipError_t launch_moe_experts(const MoeArgs& a, hipStream_t st) {
-  // a token chooses an expert at most once, so an expert holds at most b pooled tokens
+  // a token chooses an expert at most once, so an expert holds at most b pooled tokens;
+  // b <= 8 fits one column tile, larger batches take up to 8 tiles (64 tokens)
   if (a.b <= 8) return launch_experts_nct<1>(a, st);
-  if (a.b <= 16) return launch_experts_nct<2>(a, st);
-  if (a.b <= 32) return launch_experts_nct<4>(a, st);
   return launch_experts_nct<8>(a, st);
 }
 

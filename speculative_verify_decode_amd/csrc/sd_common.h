@@ -190,12 +190,14 @@ struct MoeArgs {
   const uint8_t *w2_codes, *w2_scales;
   const float* w2_gscale;
   const int *counts, *offsets, *tos;
+  const int* active;          // [E + 1]: active expert ids ascending, then their number
   _Float16* h16;              // [b*k, I] scratch: hi terms of the SwiGLU output * 2^-8
   _Float16* h16_lo;           // [b*k, I] scratch: lo terms
   uint16_t* h_bf16;           // [b*k, I] optional bf16 copy of the SwiGLU output
   float* y;                   // fp32 [b*k, H]
 };
 hipError_t launch_moe_experts(const MoeArgs& a, hipStream_t st);
+bool moe_shape_supported(int H, int I);  // the expert GEMMs' K splits exist for H and I
 
 hipError_t launch_unpool(int b, int H, int k, const float* y, const float* w,
                          const int* slot_of, float* out, hipStream_t st);
