@@ -19,7 +19,9 @@
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only enqueues
  *     kernels on it and may be captured into a HIP graph ([DEC] module docstring and
  *     SpecializedDecode.plan: the step runs inside a captured graph).
- *   - bf16 tensors are raw 16-bit bfloat16; fp32 are IEEE float; all row-major, contiguous.
+ *   - bf16 tensors are raw 16-bit bfloat16; fp32 are IEEE float; activations, caches and
+ *     metadata are row-major and contiguous.  Weight matrices are in the packed layouts
+ *     below, made once from row-major weights by sd_pack_dense / sd_pack_fp4.
  *   - b = rows of the step = n_req * q_rows, request-major (row t belongs to request
  *     t / q_rows).  q_rows = 1 + 7 verify tokens ([RT] unsupported; [DEC] decode_metadata).
  *   - Return 0 on success, a negative SD_E* code otherwise; nothing is enqueued on an
@@ -40,7 +42,7 @@
 extern "C" {
 #endif
 
-#define SD_ABI_VERSION 1
+#define SD_ABI_VERSION 2
 
 enum {
   SD_OK = 0,
@@ -61,14 +63,33 @@ typedef struct sd_dims {
   float eps, rope_theta, attn_scale;
 } sd_dims;
 
-/* Attention weights, bf16.  w_qkv [(2*Hq + 2*Hkv) * D, H]: rows are the stacked q | k | v |
- * o_gate projections in that order ([DSP] hf_to_vllm_mapper).  w_o [H, Hq * D]. */
+/* Packed weight layouts.  The step streams every weight byte once per step; it reads them
+ * in the order the matrix cores consume them, so that each load instruction of a wave is
+ * one contiguous 1 KB piece.  Packing is a one-time preprocessing of loaded weights.
+ *
+ * Dense bf16 W [N, K] (w_qkv, w_o, w_router, w_lm), K % 32 == 0: ceil(N / 16) tiles of 16
+ * rows by K / 32 tiles of 32 columns.  Tile (nt, kt) is 512 contiguous bf16 starting at
+ * element (nt * (K / 32) + kt) * 512; its element 8 * l + j (l < 64, j < 8) is
+ * W[16 nt + l % 16, 32 kt + 8 (l / 16) + j], and 0 for rows >= N.  Size:
+ * sd_packed_dense_bytes(N, K) = ceil(N / 16) * 16 * K * 2 bytes.
+ *
+ * Block-scaled FP4 weights [E, N, K] (codes [E, N, K/2], scales [E, N, K/16] as described at
+ * sd_moe_weights), N % 16 == 0, K % 128 == 0: tiles of 16 rows by 128 weights, indexed
+ * t = (e * (N / 16) + nt) * (K / 128) + kt.  Codes tile t is 1024 bytes at t * 1024: bytes
+ * 16 l .. 16 l + 15 are the code bytes 64 kt + 16 (l / 16) .. + 15 of row 16 nt + l % 16 of
+ * expert e.  Scales tile t is 128 bytes at t * 128: bytes 2 l, 2 l + 1 are the scale bytes
+ * 8 kt + 2 (l / 16), + 1 of that row.  Packed sizes equal the row-major sizes. */
+
+/* Attention weights, packed bf16 (see above).  w_qkv [(2*Hq + 2*Hkv) * D, H]: rows are the
+ * stacked q | k | v | o_gate projections in that order ([DSP] hf_to_vllm_mapper).
+ * w_o [H, Hq * D]. */
 typedef struct sd_attn_weights {
   const void *w_qkv;
   const void *w_o;
 } sd_attn_weights;
 
-/* Routed-MoE weights.  w_router bf16 [E, H].  Experts are block-scaled FP4: for matrix
+/* Routed-MoE weights, packed (see above).  w_router bf16 [E, H].  Experts are block-scaled
+ * FP4; in row-major terms, for matrix
  * [N, K] of expert e, codes uint8 [E, N, K/2] hold two E2M1 codes per byte (low nibble =
  * even k), scales uint8 [E, N, K/16] hold one E4M3FN scale per 16 consecutive k, gscale
  * fp32 [E] one scale per matrix: W[n, k] = e2m1 * e4m3 * gscale.  W13 is [2I, H] with the
@@ -123,6 +144,19 @@ typedef struct sd_route {
 
 int sd_abi_version(void);
 const char *sd_last_error(void);
+
+/* Bytes of the packed copy of a dense bf16 [n, k] weight (0 if k % 32 != 0 or n, k <= 0). */
+size_t sd_packed_dense_bytes(int32_t n, int32_t k);
+
+/* Pack a row-major bf16 weight src [n, k] into dst (sd_packed_dense_bytes(n, k) bytes).
+ * k % 32 == 0; src and dst 16-byte aligned and not overlapping.  Enqueued on stream. */
+int sd_pack_dense(int32_t n, int32_t k, const void *src, void *dst, void *stream_handle);
+
+/* Pack row-major block-scaled FP4 weights of e matrices [n, k] (codes [e, n, k/2], scales
+ * [e, n, k/16]) into codes_out / scales_out of the same sizes.  n % 16 == 0, k % 128 == 0;
+ * codes 16-byte and scales 2-byte aligned; outputs do not overlap inputs. */
+int sd_pack_fp4(int32_t e, int32_t n, int32_t k, const uint8_t *codes, const uint8_t *scales,
+                uint8_t *codes_out, uint8_t *scales_out, void *stream_handle);
 
 /* Bytes of workspace every call below needs for this shape (the largest of them). */
 size_t sd_workspace_bytes(const sd_dims *dims, int32_t b, int32_t n_req, int32_t max_seq_len);
@@ -184,7 +218,7 @@ int sd_layer_step(const sd_dims *dims, int32_t b, float *stream, const float *br
 
 /* Draft head on bf16 hidden rows h [b, hidden] ([DSP] compute_draft_logits,
  * apply_output_logit_transform, draft_id_to_target_id; [RT] unsupported: BF16 logits):
- * logits = bf16(h * w_lm^T) with w_lm bf16 [draft_vocab, hidden]; tau = soft_cap *
+ * logits = bf16(h * w_lm^T) with w_lm packed bf16 [draft_vocab, hidden]; tau = soft_cap *
  * tanh(logits * multiplier / soft_cap) (soft_cap <= 0: tau = logits * multiplier);
  * draft_ids int32 [b] = lowest index of the largest logit; target_ids int64 [b] =
  * d2t[draft_ids] with d2t int64 [draft_vocab].  tau_out fp32 [b, draft_vocab] may be NULL.
@@ -197,8 +231,9 @@ int sd_draft_head(int32_t hidden, int32_t draft_vocab, int32_t b, const void *h,
 /* Bytes of workspace sd_draft_head needs. */
 size_t sd_draft_head_workspace_bytes(int32_t hidden, int32_t draft_vocab, int32_t b);
 
-/* Test entry: dequantise block-scaled FP4 rows [n, k] exactly as the expert kernels do,
- * into out fp32 [n, k] (codes [n, k/2], scales [n, k/16], one gscale).  k % 32 == 0. */
+/* Test entry: dequantise row-major block-scaled FP4 rows [n, k] exactly as the expert
+ * kernels do, into out fp32 [n, k] (codes [n, k/2], scales [n, k/16], one gscale).
+ * k % 32 == 0. */
 int sd_debug_dequant(int32_t n, int32_t k, const uint8_t *codes, const uint8_t *scales,
                      float gscale, float *out, void *stream_handle);
 

@@ -53,6 +53,10 @@ class SdRoute(ctypes.Structure):
 SYMBOLS = {
     "sd_abi_version": (c_int, []),
     "sd_last_error": (ctypes.c_char_p, []),
+    "sd_packed_dense_bytes": (c_size_t, [c_int, c_int]),
+    "sd_pack_dense": (c_int, [c_int, c_int, c_void_p, c_void_p, c_void_p]),
+    "sd_pack_fp4": (c_int, [c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
+                            c_void_p]),
     "sd_workspace_bytes": (c_size_t, [ctypes.POINTER(SdDims), c_int, c_int, c_int]),
     "sd_boundary_dualnorm": (c_int, [ctypes.POINTER(SdDims), c_int, c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_void_p, c_void_p, c_void_p]),
@@ -162,6 +166,29 @@ def make_route(r):
 # ------------------------------------------------------------------ entry points
 def abi_version():
     return lib().sd_abi_version()
+
+
+def pack_dense(w, stream=None):
+    """Packed copy (sd_pack_dense) of a row-major bf16 device weight [n, k].  The result is
+    shaped [ceil(n / 16) * 16, k] for size bookkeeping only: its elements are in the packed
+    tile order, not row-major."""
+    n, k = w.shape
+    nbytes = lib().sd_packed_dense_bytes(n, k)
+    if nbytes == 0:
+        raise SdError(-1, f"dense weight [{n}, {k}] cannot be packed")
+    out = torch.empty(nbytes // (2 * k), k, dtype=torch.bfloat16, device=w.device)
+    _check(lib().sd_pack_dense(n, k, ptr(w), ptr(out), cur_stream(stream)))
+    return out
+
+
+def pack_fp4(codes, scales, stream=None):
+    """Packed copies (sd_pack_fp4) of block-scaled FP4 device weights: codes uint8 [e, n, k/2],
+    scales uint8 [e, n, k/16]."""
+    e, n, kh = codes.shape
+    co, so = torch.empty_like(codes), torch.empty_like(scales)
+    _check(lib().sd_pack_fp4(e, n, 2 * kh, ptr(codes), ptr(scales), ptr(co), ptr(so),
+                             cur_stream(stream)))
+    return co, so
 
 
 def workspace_bytes(dims, b, n_req, max_seq_len):

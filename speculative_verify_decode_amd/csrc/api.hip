@@ -100,8 +100,8 @@ int check_rows(const sd_dims* d, int b) {
 }
 
 struct Ws {
-  size_t x_a, x_a_lo, qkv, q, q_lo, part_acc, part_ml, o, o_lo, a, x_m, x_m_lo, x16, x16_lo, z,
-      ids, w, counts, offsets, slot_of, tos, active, h16, h16_lo, y, total;
+  size_t x_a, x_a_lo, qkv, q, q_lo, part_acc, part_ml, o, o_lo, a, x_m, x_m_lo, x16, x16_lo,
+      zpart, counter, ids, w, counts, offsets, slot_of, tos, active, h16, h16_lo, y, total;
 };
 
 size_t up(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -129,7 +129,8 @@ Ws ws_layout(const sd_dims& d, int b, int n_req, int max_seq_len) {
   w.x_m_lo = take(B * H * 2);
   w.x16 = take(B * H * 2);
   w.x16_lo = take(B * H * 2);
-  w.z = take(B * E * 4);
+  w.zpart = take((H / 256) * B * E * 4);
+  w.counter = take(4);
   w.ids = take(B * k * 4);
   w.w = take(B * k * 4);
   w.counts = take(E * 4);
@@ -211,6 +212,7 @@ int run_attention(const sd_dims* d, int b, const uint16_t* x, const uint16_t* x_
   aa.q = q; aa.q_lo = q_lo;
   aa.k_cache = (const uint16_t*)kv->k_cache; aa.v_cache = (const uint16_t*)kv->v_cache;
   aa.block_table = kv->block_table; aa.max_blocks = kv->max_blocks; aa.seq_lens = kv->seq_lens;
+  aa.num_blocks = kv->num_blocks;
   aa.positions = kv->positions; aa.n_req = kv->n_req; aa.Hq = Hq; aa.Hkv = Hkv; aa.D = D;
   aa.q_rows = d->q_rows; aa.scale = scale_of(d);
   aa.part_acc = at<float>(ws, L.part_acc); aa.part_ml = at<float>(ws, L.part_ml);
@@ -226,18 +228,19 @@ int run_attention(const sd_dims* d, int b, const uint16_t* x, const uint16_t* x_
   return SD_OK;
 }
 
+// The router kernel's arrival counter must be 0 at launch: in a layer step the attention
+// boundary's norm kernel zeroes it; a standalone call zeroes it first.
 int run_route(const sd_dims* d, int b, const uint16_t* x, const uint16_t* x_lo,
-              const void* w_router, const float* bias, const sd_route* r, float* z,
-              hipStream_t st) {
-  GemmArgs g{};
-  g.M = b; g.N = d->n_experts; g.K = d->hidden; g.x = x; g.x_lo = x_lo;
-  g.w = (const uint16_t*)w_router;
-  g.y = z; g.bias = bias;
-  SD_LAUNCH(launch_gemm(GEMM_F32_BIAS, g, st), "router");
-  SD_LAUNCH(launch_route_pool(z, b, d->n_experts, d->top_k, r->topk_ids, r->topk_w,
-                              r->expert_counts, r->expert_offsets, r->slot_of, r->token_of_slot,
-                              r->active_experts, st),
-            "routing and pooler");
+              const void* w_router, const float* bias, const sd_route* r, float* logits,
+              void* ws, const Ws& L, hipStream_t st) {
+  RouterArgs ra{};
+  ra.b = b; ra.H = d->hidden; ra.E = d->n_experts; ra.k = d->top_k;
+  ra.x = x; ra.x_lo = x_lo; ra.w = (const uint16_t*)w_router; ra.bias = bias;
+  ra.part = at<float>(ws, L.zpart); ra.counter = at<int>(ws, L.counter); ra.logits = logits;
+  ra.ids = r->topk_ids; ra.w_out = r->topk_w; ra.counts = r->expert_counts;
+  ra.offsets = r->expert_offsets; ra.slot_of = r->slot_of; ra.tos = r->token_of_slot;
+  ra.active = r->active_experts;
+  SD_LAUNCH(launch_router(ra, st), "router, routing and pooler");
   return SD_OK;
 }
 
@@ -306,6 +309,40 @@ int sd_abi_version(void) { return SD_ABI_VERSION; }
 
 const char* sd_last_error(void) { return g_err.c_str(); }
 
+size_t sd_packed_dense_bytes(int32_t n, int32_t k) {
+  if (n <= 0 || k <= 0 || k % 32) return 0;
+  return (size_t)((n + 15) / 16) * 16 * (size_t)k * 2;
+}
+
+int sd_pack_dense(int32_t n, int32_t k, const void* src, void* dst, void* stream_handle) {
+  if (sd_packed_dense_bytes(n, k) == 0)
+    return fail(SD_EINVAL, "dense weight [%d, %d] (need n, k > 0 and k %% 32 == 0)", n, k);
+  if (!src || !dst || !aligned16(src) || !aligned16(dst))
+    return fail(SD_EINVAL, "src/dst null or not 16-byte aligned");
+  if (src == dst) return fail(SD_EINVAL, "packing is out of place");
+  SD_LAUNCH(launch_pack_dense(n, k, (const uint16_t*)src, (uint16_t*)dst,
+                              (hipStream_t)stream_handle),
+            "dense weight packing");
+  return ok();
+}
+
+int sd_pack_fp4(int32_t e, int32_t n, int32_t k, const uint8_t* codes, const uint8_t* scales,
+                uint8_t* codes_out, uint8_t* scales_out, void* stream_handle) {
+  if (e <= 0 || n <= 0 || k <= 0 || n % 16 || k % 128)
+    return fail(SD_EINVAL, "fp4 weights [%d, %d, %d] (need n %% 16 == 0, k %% 128 == 0)", e, n,
+                k);
+  if (!codes || !scales || !codes_out || !scales_out)
+    return fail(SD_EINVAL, "a packing pointer is null");
+  if (!aligned16(codes) || !aligned16(codes_out) || ((uintptr_t)scales & 1u) ||
+      ((uintptr_t)scales_out & 1u))
+    return fail(SD_EINVAL, "codes must be 16-byte and scales 2-byte aligned");
+  if (codes == codes_out || scales == scales_out) return fail(SD_EINVAL, "packing is out of place");
+  SD_LAUNCH(launch_pack_fp4(e, n, k, codes, scales, codes_out, scales_out,
+                            (hipStream_t)stream_handle),
+            "fp4 weight packing");
+  return ok();
+}
+
 size_t sd_workspace_bytes(const sd_dims* dims, int32_t b, int32_t n_req, int32_t max_seq_len) {
   if (check_dims(dims) != SD_OK || check_rows(dims, b) != SD_OK || n_req <= 0 ||
       max_seq_len <= 0)
@@ -325,7 +362,7 @@ int sd_boundary_dualnorm(const sd_dims* dims, int32_t b, float* stream, const fl
   if (branch != nullptr && !aligned16(branch)) return fail(SD_EINVAL, "branch misaligned");
   SD_LAUNCH(launch_dualnorm(b, dims->hidden, stream, (const float*)branch,
                             (const uint16_t*)front_embed, g_post, g_pre, dims->eps,
-                            (uint16_t*)out, nullptr, nullptr, nullptr,
+                            (uint16_t*)out, nullptr, nullptr, nullptr, nullptr,
                             (hipStream_t)stream_handle),
             "dual norm");
   return ok();
@@ -357,9 +394,10 @@ int sd_moe_route(const sd_dims* dims, int32_t b, const void* x, const void* w_ro
   if (logits_out && !aligned16(logits_out)) return fail(SD_EINVAL, "logits_out misaligned");
   SD_CHECK(check_ws(dims, b, b / dims->q_rows, dims->q_rows, ws, ws_bytes));
   const Ws L = ws_layout(*dims, b, b / dims->q_rows, dims->q_rows);
-  float* z = logits_out ? logits_out : at<float>(ws, L.z);
-  SD_CHECK(run_route(dims, b, (const uint16_t*)x, nullptr, w_router, logit_bias, route, z,
-                     (hipStream_t)stream_handle));
+  hipStream_t st = (hipStream_t)stream_handle;
+  SD_LAUNCH(launch_zero_i32(at<int>(ws, L.counter), st), "router counter");
+  SD_CHECK(run_route(dims, b, (const uint16_t*)x, nullptr, w_router, logit_bias, route,
+                     logits_out, ws, L, st));
   return ok();
 }
 
@@ -424,7 +462,7 @@ int sd_layer_step(const sd_dims* dims, int32_t b, float* stream, const float* br
   uint16_t* x_a_lo = at<uint16_t>(ws, L.x_a_lo);
   SD_LAUNCH(launch_dualnorm(b, H, stream, (const float*)branch_in,
                             (const uint16_t*)front_embed, w->g_post_prev, w->g_pre_attn,
-                            dims->eps, x_a, x_a_lo, nullptr, nullptr, st),
+                            dims->eps, x_a, x_a_lo, nullptr, nullptr, nullptr, st),
             "input boundary");
   float* a = at<float>(ws, L.a);
   SD_CHECK(run_attention(dims, b, x_a, x_a_lo, &w->attn, kv, a, ws, L, st));
@@ -433,10 +471,10 @@ int sd_layer_step(const sd_dims* dims, int32_t b, float* stream, const float* br
   _Float16* x16 = at<_Float16>(ws, L.x16);
   _Float16* x16_lo = at<_Float16>(ws, L.x16_lo);
   SD_LAUNCH(launch_dualnorm(b, H, stream, a, nullptr, w->g_post_attn, w->g_pre_ffn, dims->eps,
-                            x_m, x_m_lo, x16, x16_lo, st),
+                            x_m, x_m_lo, x16, x16_lo, at<int>(ws, L.counter), st),
             "attention boundary");
   const sd_route r = route_out ? *route_out : ws_route(ws, L);
-  SD_CHECK(run_route(dims, b, x_m, x_m_lo, w->moe.w_router, logit_bias, &r, at<float>(ws, L.z),
+  SD_CHECK(run_route(dims, b, x_m, x_m_lo, w->moe.w_router, logit_bias, &r, nullptr, ws, L,
                      st));
   float* y = at<float>(ws, L.y);
   SD_CHECK(run_experts(dims, b, x16, x16_lo, &w->moe, &r, y, nullptr, at<_Float16>(ws, L.h16),

@@ -23,43 +23,82 @@
 namespace {
 
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr int kMaxChunkBlocks = 2048;
 
+// Workgroup (chunk, kv head g, request r): blocks [chunk * cb, +cb) of the request, one
+// workgroup per CU at most.  The chunk's block ids (clamped to the pool) and the query
+// group (hi/lo) are staged in LDS first; each of the 4 waves then streams 2-block windows
+// w = 2 * wave + 8 j, loading window j + 1 while window j is in the matrix cores.  Loads
+// are unconditional: tokens past the request's end are masked after loading (scores by
+// selection to -inf, V by selection to 0).
 template <int D, int NQT>
-__global__ __launch_bounds__(256) void k_attn_split(AttnArgs a, int chunk_blocks, int n_chunks) {
+__global__ __launch_bounds__(256) void k_attn_split(AttnArgs a, int cb, int n_chunks) {
   constexpr int QG = 16 * NQT;
   constexpr int NC = D / 32;   // MFMA steps over the head dim
   constexpr int NDT = D / 16;  // output dim tiles
   constexpr int DL = D / 4;    // dims per lane group
-  __shared__ float s_acc[4][QG][D];
+  constexpr int QP = D + 8;    // padded LDS row of the query terms
+  constexpr int AP = D + 4;    // padded LDS row of the cross-wave accumulators
+  __shared__ float s_acc[4][QG][AP];
   __shared__ float s_m[4][QG], s_l[4][QG];
+  __shared__ uint16_t s_q[2][QG][QP];
+  __shared__ int s_bt[kMaxChunkBlocks];
 
   const int chunk = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
-  const int L = min(a.seq_lens[r], a.max_blocks * 16);  // never read past the table row
-  const int nblk = (L + 15) >> 4;
-  const int blk_begin = chunk * chunk_blocks;
-  if (blk_begin >= nblk) return;  // past this request's end (uniform per workgroup)
-  const int blk_end = min(blk_begin + chunk_blocks, nblk);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int i = lane & 15, G = lane >> 4;
   const int group = a.Hq / a.Hkv;
-
-  // Q^T B operands (hi and lo terms) and the causal bound of the lane's query column
-  bf16x8_t bq[NQT][NC], bql[NQT][NC];
+  const int blk_begin = chunk * cb;
+  // stage block ids and queries; neither depends on the request length
+  const int* btr = a.block_table + (size_t)r * a.max_blocks;
+  const int ncb = min(cb, a.max_blocks - blk_begin);  // >= 1: the grid covers max_blocks
+  for (int j = tid; j < ncb; j += 256) s_bt[j] = min(max(btr[blk_begin + j], 0), a.num_blocks - 1);
+  constexpr int QCH = QG * D / 8;  // 16-byte pieces of one query term
+  for (int c = tid; c < 2 * QCH; c += 256) {
+    const int term = c / QCH, rem = c - term * QCH;
+    const int qi = rem / (D / 8), d8 = (rem - qi * (D / 8)) * 8;
+    const int hh = qi / a.q_rows, jr = qi - hh * a.q_rows;
+    const size_t qo = ((size_t)(r * a.q_rows + jr) * a.Hq + g * group + hh) * D + d8;
+    *(u32x4_t*)&s_q[term][qi][d8] = *(const u32x4_t*)((term ? a.q_lo : a.q) + qo);
+  }
+  const int L = min(a.seq_lens[r], a.max_blocks * 16);  // never read past the table row
   int qpos[NQT];
 #pragma unroll
   for (int qt = 0; qt < NQT; ++qt) {
     const int qi = 16 * qt + i;
-    const int hh = qi / a.q_rows, jr = qi - hh * a.q_rows;
-    const int row = r * a.q_rows + jr;
-    const size_t qo = ((size_t)row * a.Hq + g * group + hh) * D + G * DL;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      bq[qt][c] = *(const bf16x8_t*)(a.q + qo + 8 * c);
-      bql[qt][c] = *(const bf16x8_t*)(a.q_lo + qo + 8 * c);
-    }
-    qpos[qt] = a.positions[row];
+    qpos[qt] = a.positions[r * a.q_rows + (qi - (qi / a.q_rows) * a.q_rows)];
   }
+  __syncthreads();
+  const int nblk = (L + 15) >> 4;
+  if (blk_begin >= nblk) return;  // past this request's end (uniform per workgroup)
+  const int blk_end = min(blk_begin + cb, nblk);
   const float sl2 = a.scale * LOG2E;
+  const size_t kvh = (size_t)16 * D;  // elements per (block, head)
+
+  struct Win {
+    bf16x8_t k[2][NC];
+    bf16x8_t v[NDT];
+  };
+  // window at block wb (wb + 1 may be past blk_end: then it re-reads block wb, masked)
+  auto load_win = [&](Win& W, int wb) {
+    const int pb0 = s_bt[wb - blk_begin];
+    const int pb1 = wb + 1 < blk_end ? s_bt[wb + 1 - blk_begin] : pb0;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      // K rows: tile t, row i <-> window token 8 * (i / 4) + 4 t + i % 4
+      const int tw = 8 * (i >> 2) + 4 * t + (i & 3);
+      const int pb = (tw >> 4) ? pb1 : pb0;
+      const uint16_t* kp = a.k_cache + ((size_t)pb * a.Hkv + g) * kvh + (size_t)(tw & 15) * D + G * DL;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) W.k[t][c] = __builtin_nontemporal_load((const bf16x8_t*)(kp + 8 * c));
+    }
+    // V^T rows: dim 16 dt + i, window tokens 8G .. 8G+7
+    const int pb = (G >> 1) ? pb1 : pb0;
+    const uint16_t* vp = a.v_cache + ((size_t)pb * a.Hkv + g) * kvh + (size_t)i * 16 + 8 * (G & 1);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) W.v[dt] = __builtin_nontemporal_load((const bf16x8_t*)(vp + (size_t)dt * 256));
+  };
 
   float mrun[NQT], lsum[NQT];
   f32x4_t acc[NDT][NQT];
@@ -70,70 +109,43 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a, int chunk_blocks
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) acc[dt][qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  const bf16x8_t zero8 = {};
-  const int* bt = a.block_table + (size_t)r * a.max_blocks;
-  const size_t kv_head_stride = (size_t)16 * D;  // elements per (block, head)
 
-  for (int wb = blk_begin + 2 * wave; wb < blk_end; wb += 8) {
-    const bool has1 = wb + 1 < blk_end;
-    const int pb0 = bt[wb];
-    const int pb1 = has1 ? bt[wb + 1] : pb0;
+  auto compute = [&](Win& W, int wb) {
     const int tok_base = wb * 16;
-    // K rows: tile t, row i <-> window token 8*(i/4) + 4t + i%4
-    bf16x8_t ka[2][NC];
+    // V of tokens past the request's end is zeroed (the cache there may hold anything)
+    const int nvalid = L - (tok_base + 8 * G);
+    if (nvalid < 8) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int tw = 8 * (i >> 2) + 4 * t + (i & 3);
-      const bool ok = tok_base + tw < L;
-      const int pb = (tw >> 4) ? pb1 : pb0;
-      const uint16_t* kp = a.k_cache + ((size_t)pb * a.Hkv + g) * kv_head_stride +
-                           (size_t)(tw & 15) * D + G * DL;
+      for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int c = 0; c < NC; ++c)
-        ka[t][c] = ok ? __builtin_nontemporal_load((const bf16x8_t*)(kp + 8 * c)) : zero8;
-    }
-    // V^T rows: dim 16dt + i, window tokens 8G .. 8G+7
-    bf16x8_t va[NDT];
-    {
-      const int tok0 = tok_base + 8 * G;
-      const int pb = (G >> 1) ? pb1 : pb0;
-      const uint16_t* vp =
-          a.v_cache + ((size_t)pb * a.Hkv + g) * kv_head_stride + (size_t)i * 16 + 8 * (G & 1);
-      const int nvalid = L - tok0;  // tokens of this lane's 8 that exist
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        bf16x8_t v = nvalid > 0 ? __builtin_nontemporal_load((const bf16x8_t*)(vp + (size_t)dt * 256))
-                                : zero8;
-        if (nvalid < 8) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (e >= nvalid) v[e] = (__bf16)0.0f;
-        }
-        va[dt] = v;
-      }
+        for (int e = 0; e < 8; ++e)
+          if (e >= nvalid) W.v[dt][e] = (__bf16)0.0f;
     }
 #pragma unroll
     for (int qt = 0; qt < NQT; ++qt) {
-      f32x4_t s[2];
+      f32x4_t sh[2], slo[2];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        f32x4_t sh = {0.f, 0.f, 0.f, 0.f}, slo = {0.f, 0.f, 0.f, 0.f};
+      for (int t = 0; t < 2; ++t) sh[t] = slo[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          sh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[t][c], bq[qt][c], sh, 0, 0, 0);
-          slo = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[t][c], bql[qt][c], slo, 0, 0, 0);
+      for (int c = 0; c < NC; ++c) {
+        const bf16x8_t qh = *(const bf16x8_t*)&s_q[0][16 * qt + i][G * DL + 8 * c];
+        const bf16x8_t ql = *(const bf16x8_t*)&s_q[1][16 * qt + i][G * DL + 8 * c];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          sh[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(W.k[t][c], qh, sh[t], 0, 0, 0);
+          slo[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(W.k[t][c], ql, slo[t], 0, 0, 0);
         }
-        s[t] = sh + slo;
       }
       // lane's scores: token tok_base + 8G + 4t + rr for query column 16qt + i
+      float sc[2][4];
       float mx = -INFINITY;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int tok = tok_base + 8 * G + 4 * t + rr;
-          const float v = tok <= qpos[qt] ? s[t][rr] * sl2 : -INFINITY;
-          s[t][rr] = v;
+          const float v = tok <= qpos[qt] ? (sh[t][rr] + slo[t][rr]) * sl2 : -INFINITY;
+          sc[t][rr] = v;
           mx = fmaxf(mx, v);
         }
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
@@ -146,7 +158,7 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a, int chunk_blocks
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          const float p = s[t][rr] == -INFINITY ? 0.f : exp2f(s[t][rr] - mnew);
+          const float p = sc[t][rr] == -INFINITY ? 0.f : exp2f(sc[t][rr] - mnew);
           psum += p;
           const __bf16 ph = (__bf16)p;
           pb[4 * t + rr] = ph;
@@ -157,58 +169,72 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a, int chunk_blocks
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         acc[dt][qt] *= alpha;
-        acc[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], pb, acc[dt][qt], 0, 0, 0);
-        acc[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[dt], pbl, acc[dt][qt], 0, 0, 0);
+        acc[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(W.v[dt], pb, acc[dt][qt], 0, 0, 0);
+        acc[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(W.v[dt], pbl, acc[dt][qt], 0, 0, 0);
       }
     }
+  };
+
+  Win W0, W1;
+  int wb = blk_begin + 2 * wave;
+  if (wb < blk_end) {
+    load_win(W0, wb);
+    while (true) {
+      const int w1 = wb + 8;
+      if (w1 < blk_end) load_win(W1, w1);
+      compute(W0, wb);
+      if (w1 >= blk_end) break;
+      const int w2 = w1 + 8;
+      if (w2 < blk_end) load_win(W0, w2);
+      compute(W1, w1);
+      if (w2 >= blk_end) break;
+      wb = w2;
+    }
   }
-  // per-wave state -> LDS; the lane's column is query 16qt + i, rows are dims 16dt + 4G + rr
+
+  // cross-wave combine: rescale each wave's state to the chunk maximum, then add
 #pragma unroll
   for (int qt = 0; qt < NQT; ++qt) {
     float l = lsum[qt];
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
-    const int qi = 16 * qt + i;
-    if (G == 0) {
-      s_m[wave][qi] = mrun[qt];
-      s_l[wave][qi] = l;
-    }
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) s_acc[wave][qi][16 * dt + 4 * G + rr] = acc[dt][qt][rr];
+    lsum[qt] = l;
+    if (G == 0) s_m[wave][16 * qt + i] = mrun[qt];
   }
   __syncthreads();
-  // combine the 4 waves; write one partial (m, l, acc) per query
+#pragma unroll
+  for (int qt = 0; qt < NQT; ++qt) {
+    const int qi = 16 * qt + i;
+    const float M = fmaxf(fmaxf(s_m[0][qi], s_m[1][qi]), fmaxf(s_m[2][qi], s_m[3][qi]));
+    const float f = mrun[qt] == -INFINITY ? 0.f : exp2f(mrun[qt] - M);
+    if (G == 0) s_l[wave][qi] = lsum[qt] * f;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) *(f32x4_t*)&s_acc[wave][qi][16 * dt + 4 * G] = acc[dt][qt] * f;
+  }
+  __syncthreads();
   const size_t pidx = ((size_t)r * a.Hkv + g) * n_chunks + chunk;
   float* pacc = a.part_acc + pidx * QG * D;
   float* pml = a.part_ml + pidx * QG * 2;
-  for (int e = threadIdx.x; e < QG * D; e += 256) {
+  for (int e = tid * 4; e < QG * D; e += 1024) {
     const int qi = e / D, d = e - qi * D;
-    float M = s_m[0][qi];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, s_m[w][qi]);
-    float v = 0.f, l = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float f = exp2f(s_m[w][qi] - M);
-        v += f * s_acc[w][qi][d];
-        l += f * s_l[w][qi];
-      }
-    }
-    pacc[e] = v;
+    f32x4_t v = *(const f32x4_t*)&s_acc[0][qi][d];
+    v += *(const f32x4_t*)&s_acc[1][qi][d];
+    v += *(const f32x4_t*)&s_acc[2][qi][d];
+    v += *(const f32x4_t*)&s_acc[3][qi][d];
+    *(f32x4_t*)(pacc + e) = v;
     if (d == 0) {
-      pml[2 * qi] = M;
-      pml[2 * qi + 1] = l;
+      pml[2 * qi] = fmaxf(fmaxf(s_m[0][qi], s_m[1][qi]), fmaxf(s_m[2][qi], s_m[3][qi]));
+      pml[2 * qi + 1] = s_l[0][qi] + s_l[1][qi] + s_l[2][qi] + s_l[3][qi];
     }
   }
 }
 
 // One workgroup of D threads per (row, query head): LSE-combine the chunks, normalise,
-// apply the output gate o * sigmoid(o_gate), store bf16 hi/lo terms.
-__global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a, int chunk_blocks, int n_chunks,
-                                                      int qg) {
+// apply the output gate o * sigmoid(o_gate), store bf16 hi/lo terms.  Chunk statistics go
+// to LDS while each thread's chunk values for its dim are already in flight (32 per pass).
+__global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a, int cb, int n_chunks, int qg) {
+  constexpr int PASS = 32;
+  __shared__ float s_m[1024], s_l[1024], s_red[2];
   const int t = blockIdx.x / a.Hq, h = blockIdx.x - t * a.Hq;
   const int d = threadIdx.x;
   const int r = t / a.q_rows, jr = t - r * a.q_rows;
@@ -216,14 +242,17 @@ __global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a, int chunk_bloc
   const int g = h / group, hh = h - g * group;
   const int qi = hh * a.q_rows + jr;
   const int L = min(a.seq_lens[r], a.max_blocks * 16);
-  const int nc = (((L + 15) >> 4) + chunk_blocks - 1) / chunk_blocks;
+  const int nc = min((((L + 15) >> 4) + cb - 1) / cb, n_chunks);
   const size_t p0 = ((size_t)r * a.Hkv + g) * n_chunks;
-  __shared__ float s_w[1024], s_l[1024], s_red[2];
-  // chunk maxima and sums: one load per chunk, spread over the threads
+  const float* pa = a.part_acc + (p0 * qg + qi) * a.D + d;
+  const size_t cs = (size_t)qg * a.D;  // chunk stride
+  float vals[PASS];
+#pragma unroll
+  for (int u = 0; u < PASS; ++u) vals[u] = pa[min(u, nc - 1) * cs];
   float mloc = -INFINITY;
   for (int c = d; c < nc; c += blockDim.x) {
     const float m = a.part_ml[((p0 + c) * qg + qi) * 2];
-    s_w[c] = m;
+    s_m[c] = m;
     s_l[c] = a.part_ml[((p0 + c) * qg + qi) * 2 + 1];
     mloc = fmaxf(mloc, m);
   }
@@ -231,22 +260,24 @@ __global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a, int chunk_bloc
   if ((d & 63) == 0) s_red[d >> 6] = mloc;
   __syncthreads();
   const float M = blockDim.x > 64 ? fmaxf(s_red[0], s_red[1]) : s_red[0];
-  __syncthreads();
-  for (int c = d; c < nc; c += blockDim.x)
-    s_w[c] = s_w[c] == -INFINITY ? 0.f : exp2f(s_w[c] - M);
-  __syncthreads();
-  // independent loads across chunks: 4 accumulators
-  float acc[4] = {0.f, 0.f, 0.f, 0.f}, l = 0.f;
-  const float* pa = a.part_acc + (p0 * qg + qi) * a.D + d;
-  const size_t cs = (size_t)qg * a.D;  // chunk stride
-  int c = 0;
-  for (; c + 4 <= nc; c += 4) {
+  float o = 0.f, l = 0.f;
+  for (int c0 = 0; c0 < nc; c0 += PASS) {
+    if (c0 > 0) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc[u] += s_w[c + u] * pa[(c + u) * cs];
+      for (int u = 0; u < PASS; ++u) vals[u] = pa[min(c0 + u, nc - 1) * cs];
+    }
+#pragma unroll
+    for (int u = 0; u < PASS; ++u) {
+      const int c = c0 + u;
+      if (c < nc) {
+        const float m = s_m[c];
+        const float w = m == -INFINITY ? 0.f : exp2f(m - M);
+        o += w * vals[u];
+        l += w * s_l[c];
+      }
+    }
   }
-  for (; c < nc; ++c) acc[0] += s_w[c] * pa[c * cs];
-  for (int cc = 0; cc < nc; ++cc) l += s_w[cc] * s_l[cc];
-  const float o = (acc[0] + acc[1] + acc[2] + acc[3]) / l;
+  o /= l;
   const float gate = a.gate[(size_t)t * a.gate_stride + h * a.D + d];
   const float sig = 1.0f / (1.0f + __expf(-gate));
   uint16_t hi, lo;
@@ -262,8 +293,9 @@ AttnPlan attn_plan(const sd_dims& d, int n_req, int max_seq_len) {
   AttnPlan p;
   const int max_blocks = (max_seq_len + 15) / 16;
   const long units = (long)n_req * d.n_kv_heads * max_blocks;
-  int cb = 8;                      // 4 waves x one 2-block window
-  while (units / cb > 512 && cb < 4096) cb *= 2;
+  // about one workgroup per CU (4 waves x 2-block windows, so a multiple of 8 blocks)
+  int cb = 8;
+  while (units / cb > 256 && cb < kMaxChunkBlocks) cb *= 2;
   p.chunk_blocks = cb;
   p.n_chunks = (max_blocks + cb - 1) / cb;
   p.qg = (d.n_q_heads / d.n_kv_heads) * d.q_rows;

@@ -1,65 +1,204 @@
 // K-B: skinny bf16 GEMM for the step's dense projections (QKV, o_proj, router, lm_head),
 // y[m, n] = sum_k x[m, k] * W[n, k] with M <= 64 rows, on v_mfma_f32_16x16x32_bf16.
 //
-// A workgroup owns 16 output features (one MFMA row tile) and all M rows; its 4 waves
-// split K and meet in LDS.  Weights are the A operand, streamed once from HBM with
-// 16-byte loads (4 lanes cover 64 contiguous bytes of a row per step); the activation
-// rows are the B operand, read from L2.  Only the weight bytes scale with the layer, so
-// the kernel is HBM-bound at b <= 64.  SPLIT: x carries bf16 hi/lo terms, 8 rows per
-// column tile (columns 0-7 hi, 8-15 lo), summed in the epilogue.
+// Weights are stored packed in the order the matrix cores consume them: the 16 x 32 tile
+// (rows 16nt.., columns 32kt..) is 1 KB of contiguous bf16, lane l's A operand (row l%16,
+// columns 8(l/16) .. +7) at bytes 16l .. 16l+15.  Every weight load instruction of a wave
+// is therefore one contiguous 1 KB piece, which streams at close to the HBM rate.
 //
-// Also here: the QKV front's per-head epilogue (weightless qk RMSNorm, RoPE, bf16 K/V
-// cache write) and the draft head's argmax reduction.
+// M <= 8 with hi/lo terms (or M <= 16 without): one column tile.  A persistent grid of one
+// workgroup per CU walks the 16-row tiles; its NW waves split K and keep their slice of
+// the activations in registers for the whole launch; the next tile's weights are loaded
+// while the current one is reduced, so the weight stream never drains.  Larger M: one
+// workgroup per tile, activations re-read per tile from L2.  Activation rows past M are
+// read through buffer loads whose range check returns zero without a memory access.
+//
+// SPLIT: x carries bf16 hi/lo terms, 8 rows per column tile (columns 0-7 hi, 8-15 lo),
+// summed in the epilogue.
+//
+// Also here: the weight packing, the QKV front's per-head epilogue (weightless qk RMSNorm,
+// RoPE, bf16 K/V cache write) and the draft head's argmax reduction.
 #include "sd_common.h"
 
 namespace {
 
-// NW waves split K; each wave works in passes of S MFMA steps (32 k each) and issues every
-// weight and activation load of a pass before the first MFMA of it.  Loads are
-// unconditional (rows past M or N read a valid clamped row) so nothing serialises them;
-// activation rows past M are zeroed after their loads.
+// Buffer resource over [p, p + bytes): loads past `bytes` return 0 and touch no memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ bf16x8_t buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+constexpr uint32_t kOob = 0x80000000u;  // a byte offset past every activation buffer
+
+// Byte offset of the lane's activation row `m` at column k (kOob when m >= M).
+__device__ __forceinline__ uint32_t x_off(int m, int M, int K, int k) {
+  return m < M ? (uint32_t)(((size_t)m * K + k) * 2) : kOob;
+}
+
+// B operand of column tile c at byte offset `off` (+ du bytes per step): for SPLIT, lanes
+// 8..15 of each 16 read the lo terms, the others the hi terms.
+template <bool SPLIT>
+__device__ __forceinline__ bf16x8_t load_b(__amdgpu_buffer_rsrc_t rh, __amdgpu_buffer_rsrc_t rl,
+                                           uint32_t off_h, uint32_t off_l) {
+  if (!SPLIT) return buf_load8(rh, off_h);
+  const u32x4_t h = __builtin_bit_cast(u32x4_t, buf_load8(rh, off_h));
+  const u32x4_t l = __builtin_bit_cast(u32x4_t, buf_load8(rl, off_l));
+  return __builtin_bit_cast(bf16x8_t, h | l);  // one of the two is zero
+}
+
+// Epilogue of one 16-feature tile: lane (i, g) holds y[m = RPC*c + i][n = 16 t + 4g + r].
+template <int MODE>
+__device__ __forceinline__ void store_tile(const GemmArgs& a, int m, int tile, int ntiles,
+                                           int g, f32x4_t v) {
+  const int nb = tile * 16 + 4 * g;
+  const bool mv = m < a.M;
+  if (MODE == GEMM_F32 || MODE == GEMM_F32_BIAS) {
+    if (!mv) return;
+    if (MODE == GEMM_F32_BIAS && a.bias != nullptr) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (nb + r < a.N) v[r] += a.bias[(size_t)m * a.N + nb + r];
+    }
+    float* y = (float*)a.y + (size_t)m * a.N + nb;
+    if (nb + 3 < a.N) {
+      *(f32x4_t*)y = v;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (nb + r < a.N) y[r] = v[r];
+    }
+  } else {  // GEMM_HEAD: bf16 logits, optional transform, per-tile argmax (ties: low index)
+    float best = -INFINITY;
+    int bidx = nb;  // always a valid index, even if every logit is NaN
+    f32x4_t tau;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float lg = sd::bf2f(sd::f2bf(v[r]));
+      if (lg > best) { best = lg; bidx = nb + r; }
+      const float x = lg * a.multiplier;
+      tau[r] = a.soft_cap > 0.f ? a.soft_cap * tanhf(x / a.soft_cap) : x;
+    }
+    if (mv && a.y != nullptr) *(f32x4_t*)((float*)a.y + (size_t)m * a.N + nb) = tau;
+#pragma unroll
+    for (int o = 16; o <= 32; o <<= 1) {
+      const float ov = __shfl_xor(best, o, 64);
+      const int oi = __shfl_xor(bidx, o, 64);
+      if (ov > best || (ov == best && oi < bidx)) { best = ov; bidx = oi; }
+    }
+    if (mv && g == 0) {
+      a.head_val[(size_t)m * ntiles + tile] = best;
+      a.head_idx[(size_t)m * ntiles + tile] = bidx;
+    }
+  }
+}
+
+// Persistent kernel, one column tile: wave w owns K steps [w S, (w+1) S) of every tile.
+template <int NW, int S, int MODE, bool SPLIT>
+__global__ __launch_bounds__(64 * NW) void k_gemm_res(GemmArgs a, int ntiles) {
+  __shared__ f32x4_t red[2][NW - 1][64];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int i = lane & 15, g = lane >> 4;
+  const int KT = a.K >> 5;
+  const int kt0 = wave * S;
+  const uint32_t xbytes = (uint32_t)(a.M * a.K * 2);
+  const auto rh = rsrc(a.x, xbytes);
+  const auto rl = rsrc(SPLIT ? a.x_lo : a.x, xbytes);
+  const int m = SPLIT ? (i & 7) : i;
+  const bool lo = SPLIT && (i >> 3);
+  const uint32_t ob = x_off(m, a.M, a.K, kt0 * 32 + 8 * g);
+  const uint32_t oh = lo ? kOob : ob, ol = lo ? ob : kOob;
+  bf16x8_t bv[S];
+#pragma unroll
+  for (int u = 0; u < S; ++u) bv[u] = load_b<SPLIT>(rh, rl, oh + 64 * u, ol + 64 * u);
+
+  bf16x8_t A0[S], A1[S];
+  auto load = [&](bf16x8_t (&A)[S], int tile) {
+    const uint16_t* wt = a.w + ((size_t)tile * KT + kt0) * 512 + lane * 8;
+#pragma unroll
+    for (int u = 0; u < S; ++u) A[u] = __builtin_nontemporal_load((const bf16x8_t*)(wt + 512 * u));
+  };
+  auto finish = [&](bf16x8_t (&A)[S], int tile, int buf) {
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < S; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[u], bv[u], acc, 0, 0, 0);
+    if (wave > 0) red[buf][wave - 1][lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int w = 0; w < NW - 1; ++w) acc += red[buf][w][lane];
+      if (SPLIT) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] += __shfl_xor(acc[r], 8, 64);
+      }
+      if (!SPLIT || i < 8) store_tile<MODE>(a, m, tile, ntiles, g, acc);
+    }
+  };
+  int t = blockIdx.x;  // the grid never exceeds ntiles
+  load(A0, t);
+  while (true) {
+    const int t1 = t + gridDim.x;
+    if (t1 < ntiles) load(A1, t1);
+    finish(A0, t, 0);
+    if (t1 >= ntiles) break;
+    const int t2 = t1 + gridDim.x;
+    if (t2 < ntiles) load(A0, t2);
+    finish(A1, t1, 1);
+    if (t2 >= ntiles) break;
+    t = t2;
+  }
+}
+
+// One workgroup per tile, NCT column tiles (M up to 64): NW waves split K, each in passes
+// of S steps whose weight and activation loads are all issued before the first MFMA.
 template <int NCT, int NW, int S, int MODE, bool SPLIT>
-__global__ __launch_bounds__(64 * NW) void k_gemm(GemmArgs a) {
+__global__ __launch_bounds__(64 * NW) void k_gemm_tile(GemmArgs a) {
   constexpr int RPC = SPLIT ? 8 : 16;  // activation rows per column tile
   __shared__ f32x4_t red[NW - 1][NCT][64];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int i = lane & 15, g = lane >> 4;
-  const int n0 = blockIdx.x * 16;
-  const int KW = a.K / NW;
-  const int k0 = wave * KW + 8 * g;
-  // rows past N (a ragged last tile) re-read row N-1; their results are never stored
-  const uint16_t* wrow = a.w + (size_t)min(n0 + i, a.N - 1) * a.K + k0;
-  const uint16_t* xrow[NCT];
-  bool xv[NCT];
+  const int tile = blockIdx.x;
+  const int KT = a.K >> 5;
+  const int KTW = KT / NW;  // steps per wave
+  const int kt0 = wave * KTW;
+  const uint32_t xbytes = (uint32_t)(a.M * a.K * 2);
+  const auto rh = rsrc(a.x, xbytes);
+  const auto rl = rsrc(SPLIT ? a.x_lo : a.x, xbytes);
+  const bool lo = SPLIT && (i >> 3);
+  uint32_t oh[NCT], ol[NCT];
 #pragma unroll
   for (int c = 0; c < NCT; ++c) {
-    const int m = RPC * c + (SPLIT ? (i & 7) : i);
-    const uint16_t* src = (SPLIT && (i >> 3)) ? a.x_lo : a.x;
-    xv[c] = m < a.M;
-    xrow[c] = src + (size_t)(xv[c] ? m : 0) * a.K + k0;
+    const uint32_t ob = x_off(RPC * c + (SPLIT ? (i & 7) : i), a.M, a.K, kt0 * 32 + 8 * g);
+    oh[c] = lo ? kOob : ob;
+    ol[c] = lo ? ob : kOob;
   }
+  const uint16_t* wt = a.w + ((size_t)tile * KT + kt0) * 512 + lane * 8;
   f32x4_t acc[NCT];
 #pragma unroll
   for (int c = 0; c < NCT; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const bf16x8_t zero8 = {};
-  const int passes = (KW >> 5) / S;
+  const int passes = KTW / S;
   for (int p = 0; p < passes; ++p) {
-    const int s0 = p * S * 32;
     bf16x8_t av[S];
     bf16x8_t bv[S][NCT];
 #pragma unroll
     for (int u = 0; u < S; ++u)
-      av[u] = __builtin_nontemporal_load((const bf16x8_t*)(wrow + s0 + 32 * u));
+      av[u] = __builtin_nontemporal_load((const bf16x8_t*)(wt + (size_t)(p * S + u) * 512));
 #pragma unroll
     for (int u = 0; u < S; ++u)
 #pragma unroll
-      for (int c = 0; c < NCT; ++c) bv[u][c] = *(const bf16x8_t*)(xrow[c] + s0 + 32 * u);
+      for (int c = 0; c < NCT; ++c) {
+        const uint32_t d = (uint32_t)(p * S + u) * 64;
+        bv[u][c] = load_b<SPLIT>(rh, rl, oh[c] + d, ol[c] + d);
+      }
 #pragma unroll
     for (int u = 0; u < S; ++u)
 #pragma unroll
       for (int c = 0; c < NCT; ++c)
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], xv[c] ? bv[u][c] : zero8, acc[c],
-                                                         0, 0, 0);
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], bv[u][c], acc[c], 0, 0, 0);
   }
   if (wave > 0) {
 #pragma unroll
@@ -77,101 +216,128 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(GemmArgs a) {
     }
   }
   if (SPLIT && i >= 8) return;
+#pragma unroll
+  for (int c = 0; c < NCT; ++c) store_tile<MODE>(a, RPC * c + i, tile, gridDim.x, g, acc[c]);
+}
 
-  // lane holds y[m = RPC*c + i][n = n0 + 4g + r], r = 0..3
-  const int nb = n0 + 4 * g;
-  const bool full = nb + 3 < a.N;
-#pragma unroll
-  for (int c = 0; c < NCT; ++c) {
-    const int m = RPC * c + i;
-    const bool mv = m < a.M;
-    if (MODE == GEMM_F32 || MODE == GEMM_F32_BIAS) {
-      f32x4_t v = acc[c];
-      if (MODE == GEMM_F32_BIAS && a.bias != nullptr && mv) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (nb + r < a.N) v[r] += a.bias[(size_t)m * a.N + nb + r];
-      }
-      if (mv && full) {
-        *(f32x4_t*)((float*)a.y + (size_t)m * a.N + nb) = v;
-      } else if (mv) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (nb + r < a.N) ((float*)a.y)[(size_t)m * a.N + nb + r] = v[r];
-      }
-    } else if (MODE == GEMM_BF16) {
-      if (mv && full) {
-        uint32_t lo = sd::f2bf(acc[c][0]) | ((uint32_t)sd::f2bf(acc[c][1]) << 16);
-        uint32_t hi = sd::f2bf(acc[c][2]) | ((uint32_t)sd::f2bf(acc[c][3]) << 16);
-        *(u32x2_t*)((uint16_t*)a.y + (size_t)m * a.N + nb) = u32x2_t{lo, hi};
-      } else if (mv) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (nb + r < a.N) ((uint16_t*)a.y)[(size_t)m * a.N + nb + r] = sd::f2bf(acc[c][r]);
-      }
-    } else {  // GEMM_HEAD: bf16 logits, optional transform, per-tile argmax (ties: low index)
-      float best = -INFINITY;
-      int bidx = nb;  // always a valid index, even if every logit is NaN
-      f32x4_t tau;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float lg = sd::bf2f(sd::f2bf(acc[c][r]));
-        if (lg > best) { best = lg; bidx = nb + r; }
-        const float x = lg * a.multiplier;
-        tau[r] = a.soft_cap > 0.f ? a.soft_cap * tanhf(x / a.soft_cap) : x;
-      }
-      if (mv && a.y != nullptr) *(f32x4_t*)((float*)a.y + (size_t)m * a.N + nb) = tau;
-#pragma unroll
-      for (int o = 16; o <= 32; o <<= 1) {
-        const float ov = __shfl_xor(best, o, 64);
-        const int oi = __shfl_xor(bidx, o, 64);
-        if (ov > best || (ov == best && oi < bidx)) { best = ov; bidx = oi; }
-      }
-      if (mv && g == 0) {
-        a.head_val[(size_t)m * gridDim.x + blockIdx.x] = best;
-        a.head_idx[(size_t)m * gridDim.x + blockIdx.x] = bidx;
-      }
-    }
+int cu_count() {
+  static int n[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (n[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        v <= 0)
+      v = 256;
+    n[dev] = v;
+  }
+  return n[dev];
+}
+
+template <int NW, int MODE, bool SPLIT>
+bool try_res(const GemmArgs& a, int ntiles, hipStream_t st) {
+  const int KT = a.K / 32;
+  if (KT % NW) return false;
+  const int grid = min(ntiles, cu_count());
+  const dim3 block(64 * NW);
+  switch (KT / NW) {
+    case 16:
+      if (NW > 8) return false;  // 16 waves x 16 resident steps do not fit the registers
+      hipLaunchKernelGGL((k_gemm_res<NW, 16, MODE, SPLIT>), dim3(grid), block, 0, st, a, ntiles); return true;
+    case 8: hipLaunchKernelGGL((k_gemm_res<NW, 8, MODE, SPLIT>), dim3(grid), block, 0, st, a, ntiles); return true;
+    case 4: hipLaunchKernelGGL((k_gemm_res<NW, 4, MODE, SPLIT>), dim3(grid), block, 0, st, a, ntiles); return true;
+    case 2: hipLaunchKernelGGL((k_gemm_res<NW, 2, MODE, SPLIT>), dim3(grid), block, 0, st, a, ntiles); return true;
+    case 1: hipLaunchKernelGGL((k_gemm_res<NW, 1, MODE, SPLIT>), dim3(grid), block, 0, st, a, ntiles); return true;
+    default: return false;
   }
 }
 
 template <int NCT, int NW, int MODE, bool SPLIT>
-void launch_s(const GemmArgs& a, hipStream_t st) {
-  // steps per wave; the pass size S divides it and keeps the in-flight registers bounded
+void launch_tile_s(const GemmArgs& a, int ntiles, hipStream_t st) {
+  // pass size: divides the steps per wave and bounds the in-flight registers
   constexpr int SCAP = NCT >= 8 ? 2 : 16 / NCT;
   const int steps = a.K / NW / 32;
-  const dim3 grid((a.N + 15) / 16), block(64 * NW);
+  const dim3 grid(ntiles), block(64 * NW);
   if (SCAP >= 16 && steps % 16 == 0)
-    hipLaunchKernelGGL((k_gemm<NCT, NW, (SCAP >= 16 ? 16 : 1), MODE, SPLIT>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((k_gemm_tile<NCT, NW, (SCAP >= 16 ? 16 : 1), MODE, SPLIT>), grid, block, 0, st, a);
   else if (SCAP >= 8 && steps % 8 == 0)
-    hipLaunchKernelGGL((k_gemm<NCT, NW, (SCAP >= 8 ? 8 : 1), MODE, SPLIT>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((k_gemm_tile<NCT, NW, (SCAP >= 8 ? 8 : 1), MODE, SPLIT>), grid, block, 0, st, a);
   else if (SCAP >= 4 && steps % 4 == 0)
-    hipLaunchKernelGGL((k_gemm<NCT, NW, (SCAP >= 4 ? 4 : 1), MODE, SPLIT>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((k_gemm_tile<NCT, NW, (SCAP >= 4 ? 4 : 1), MODE, SPLIT>), grid, block, 0, st, a);
   else if (steps % 2 == 0)
-    hipLaunchKernelGGL((k_gemm<NCT, NW, 2, MODE, SPLIT>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((k_gemm_tile<NCT, NW, 2, MODE, SPLIT>), grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL((k_gemm<NCT, NW, 1, MODE, SPLIT>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((k_gemm_tile<NCT, NW, 1, MODE, SPLIT>), grid, block, 0, st, a);
 }
 
 template <int NCT, int MODE, bool SPLIT>
-hipError_t launch_u(const GemmArgs& a, hipStream_t st) {
-  if (a.K % 256 == 0) launch_s<NCT, 8, MODE, SPLIT>(a, st);
-  else launch_s<NCT, 4, MODE, SPLIT>(a, st);
+hipError_t launch_tile(const GemmArgs& a, int ntiles, hipStream_t st) {
+  if (a.K % 256 == 0) launch_tile_s<NCT, 8, MODE, SPLIT>(a, ntiles, st);
+  else launch_tile_s<NCT, 4, MODE, SPLIT>(a, ntiles, st);
   return hipGetLastError();
 }
 
 template <int MODE>
 hipError_t launch_m(const GemmArgs& a, hipStream_t st) {
+  const int ntiles = (a.N + 15) / 16;
   if (a.x_lo != nullptr) {
     if (MODE == GEMM_HEAD) return hipErrorInvalidValue;
-    if (a.M <= 8) return launch_u<1, MODE, true>(a, st);
-    if (a.M <= 16) return launch_u<2, MODE, true>(a, st);
-    if (a.M <= 32) return launch_u<4, MODE, true>(a, st);
-    return launch_u<8, MODE, true>(a, st);
+    if (a.M <= 8) {
+      if (try_res<8, MODE, true>(a, ntiles, st) || try_res<16, MODE, true>(a, ntiles, st) ||
+          try_res<4, MODE, true>(a, ntiles, st))
+        return hipGetLastError();
+      return launch_tile<1, MODE, true>(a, ntiles, st);
+    }
+    if (a.M <= 16) return launch_tile<2, MODE, true>(a, ntiles, st);
+    if (a.M <= 32) return launch_tile<4, MODE, true>(a, ntiles, st);
+    return launch_tile<8, MODE, true>(a, ntiles, st);
   }
-  if (a.M <= 16) return launch_u<1, MODE, false>(a, st);
-  if (a.M <= 32) return launch_u<2, MODE, false>(a, st);
-  return launch_u<4, MODE, false>(a, st);
+  if (a.M <= 16) {
+    if (try_res<8, MODE, false>(a, ntiles, st) || try_res<16, MODE, false>(a, ntiles, st) ||
+        try_res<4, MODE, false>(a, ntiles, st))
+      return hipGetLastError();
+    return launch_tile<1, MODE, false>(a, ntiles, st);
+  }
+  if (a.M <= 32) return launch_tile<2, MODE, false>(a, ntiles, st);
+  return launch_tile<4, MODE, false>(a, ntiles, st);
+}
+
+// Row-major bf16 [N, K] -> packed tiles (rows past N are zero).  One thread per 16 bytes.
+__global__ __launch_bounds__(256) void k_pack_dense(int N, int K, const uint16_t* __restrict__ src,
+                                                    uint16_t* __restrict__ dst, size_t nchunks) {
+  const int KT = K >> 5;
+  for (size_t c = (size_t)blockIdx.x * 256 + threadIdx.x; c < nchunks;
+       c += (size_t)gridDim.x * 256) {
+    const size_t tile = c >> 6;
+    const int l = (int)(c & 63);
+    const size_t row = (tile / KT) * 16 + (l & 15);
+    const int k = (int)(tile % KT) * 32 + 8 * (l >> 4);
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (row < (size_t)N) v = *(const u32x4_t*)(src + row * K + k);
+    *(u32x4_t*)(dst + c * 8) = v;
+  }
+}
+
+// Row-major block-scaled FP4 [E, N, K] -> packed tiles of 16 rows x 128 weights: 1 KB of
+// codes (lane l: 16 code bytes of row l%16 at weight 32(l/16)) and 128 B of scales (lane l:
+// its 2 scale bytes).  One thread per (tile, lane).
+__global__ __launch_bounds__(256) void k_pack_fp4(int N, int K, const uint8_t* __restrict__ codes,
+                                                  const uint8_t* __restrict__ scales,
+                                                  uint8_t* __restrict__ codes_out,
+                                                  uint8_t* __restrict__ scales_out,
+                                                  size_t nlanes) {
+  const int KT = K >> 7;
+  for (size_t c = (size_t)blockIdx.x * 256 + threadIdx.x; c < nlanes;
+       c += (size_t)gridDim.x * 256) {
+    const size_t tile = c >> 6;
+    const int l = (int)(c & 63);
+    const size_t row = (tile / KT) * 16 + (l & 15);  // rows of all matrices, expert-major
+    const int kt = (int)(tile % KT);
+    *(u32x4_t*)(codes_out + c * 16) =
+        *(const u32x4_t*)(codes + row * (K >> 1) + 64 * kt + 16 * (l >> 4));
+    *(uint16_t*)(scales_out + c * 2) =
+        *(const uint16_t*)(scales + row * (K >> 4) + 8 * kt + 2 * (l >> 4));
+  }
 }
 
 // One wave per (row, head).  Lane d < D/2 owns the rotate-half pair (d, d + D/2).
@@ -267,11 +433,27 @@ __global__ __launch_bounds__(256) void k_head_argmax(int n_tiles, int n_vocab,
 hipError_t launch_gemm(GemmMode mode, const GemmArgs& a, hipStream_t st) {
   switch (mode) {
     case GEMM_F32: return launch_m<GEMM_F32>(a, st);
-    case GEMM_BF16: return launch_m<GEMM_BF16>(a, st);
     case GEMM_F32_BIAS: return launch_m<GEMM_F32_BIAS>(a, st);
     case GEMM_HEAD: return launch_m<GEMM_HEAD>(a, st);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_pack_dense(int N, int K, const uint16_t* src, uint16_t* dst, hipStream_t st) {
+  const size_t nchunks = (size_t)((N + 15) / 16) * 16 * K / 8;
+  const size_t blocks = (nchunks + 255) / 256;
+  hipLaunchKernelGGL(k_pack_dense, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256),
+                     0, st, N, K, src, dst, nchunks);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_fp4(int E, int N, int K, const uint8_t* codes, const uint8_t* scales,
+                           uint8_t* codes_out, uint8_t* scales_out, hipStream_t st) {
+  const size_t nlanes = (size_t)E * N * K / 128 / 16 * 64;
+  const size_t blocks = (nlanes + 255) / 256;
+  hipLaunchKernelGGL(k_pack_fp4, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256),
+                     0, st, N, K, codes, scales, codes_out, scales_out, nlanes);
+  return hipGetLastError();
 }
 
 hipError_t launch_qkv_post(const float* qkv, int b, int Hq, int Hkv, int D, int qk_norm,

@@ -6,302 +6,567 @@
 // routed experts are NVFP4 (page "vllm.models.muse_spark.nvidia.specialized_decode.
 // runtime", module list: expert_tp).
 //
-// Expert GEMMs: workgroup (16-feature tile, active expert) with KS waves splitting K.
-// Weights are the A operand of v_mfma_f32_16x16x32_f16, dequantised exactly in registers.
-// Each load instruction covers 64 contiguous code bytes of each of 16 rows (4 lanes per
-// row, 32 weights per lane) and a wave issues all of its weight loads before it waits on
-// any, so the whole K slice of the tile is in flight at once.  The pooled tokens of the
-// expert are the B operand, 8 per column tile as hi/lo fp16 terms (columns 0-7 / 8-15).
-// Workgroups are indexed by the ascending active-expert list, so the grid's live part is
-// dispatched first and the rest exits at once.
+// Expert GEMMs: the weights are the A operand of v_mfma_f32_16x16x32_f16, dequantised
+// exactly in registers from packed tiles, and the pooled tokens of the expert are the B
+// operand.  Only the experts the router picked are walked: the work list is the ascending
+// active-expert list the pooler writes.
 #include "sd_common.h"
 
 namespace {
 
-// ---------------------------------------------------------------- routing + pooler
-// One workgroup.  Top-k by (-z, index); weights = softmax over the selected logits;
-// pooler = stable counting sort of (row, choice) pairs by expert.
-__global__ __launch_bounds__(256) void k_route_pool(const float* __restrict__ z, int b, int E,
-                                                    int k, int* __restrict__ ids,
-                                                    float* __restrict__ w,
-                                                    int* __restrict__ counts,
-                                                    int* __restrict__ offsets,
-                                                    int* __restrict__ slot_of,
-                                                    int* __restrict__ tos,
-                                                    int* __restrict__ active) {
-  __shared__ float s_z[64 * 256 + 1];
-  __shared__ int s_ids[64 * 8];
-  __shared__ int s_cnt[256];
+// ---------------------------------------------------------------- router + routing + pooler
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
+
+constexpr uint32_t kOob = 0x80000000u;  // a byte offset past every activation buffer
+
+__device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// Phase 1, every workgroup: partial logits of one 16-expert tile over 256 columns of H
+// (4 waves x 2 MFMA steps; rows as bf16 hi/lo terms in columns 0-7 / 8-15 of NCT tiles),
+// written to part[ks, t, e].  Phase 2, the last workgroup to arrive: z = sum over ks in
+// order + bias; top-k per row by (-z, index) with one wave per row; weights = softmax
+// over the selected logits; pooler = stable counting sort of (row, choice) by expert,
+// through per-expert row bitmasks (a row picks an expert at most once, so an entry's
+// rank within its expert is the number of earlier rows in the expert's mask).
+template <int NCT>
+__global__ __launch_bounds__(256) void k_router(RouterArgs a) {
+  __shared__ f32x4_t red[3][NCT][64];
+  __shared__ float s_z[64 * 256];
+  __shared__ int s_last;
+  __shared__ int s_ids[512];
+  __shared__ uint32_t s_mlo[256], s_mhi[256];
   __shared__ int s_off[257];
-  const int tid = threadIdx.x;
-  for (int p = tid; p < b * E; p += 256) {
-    const float v = z[p];
-    s_z[p] = v != v ? -INFINITY : v;  // NaN ranks last
-  }
-  __syncthreads();
-  if (tid < b) {
-    const float* zr = s_z + tid * E;
-    float prev_v = INFINITY;
-    int prev_i = -1;
-    float sel[8];
-    for (int j = 0; j < k; ++j) {
-      float bv = -INFINITY;
-      int bi = -1;
-      for (int e = 0; e < E; ++e) {
-        const float v = zr[e];
-        // eligible: after the previous pick in the order (-z, index)
-        const bool after = v < prev_v || (v == prev_v && e > prev_i);
-        if (after && (bi < 0 || v > bv)) { bv = v; bi = e; }
-      }
-      s_ids[tid * k + j] = bi;
-      ids[tid * k + j] = bi;
-      sel[j] = bv;
-      prev_v = bv;
-      prev_i = bi;
-    }
-    float den = 0.f;
-    for (int j = 0; j < k; ++j) den += __expf(sel[j] - sel[0]);
-    for (int j = 0; j < k; ++j) w[tid * k + j] = __expf(sel[j] - sel[0]) / den;
-  }
-  __syncthreads();
-  const int nk = b * k;
-  if (tid < E) {
-    int c = 0;
-    for (int p = 0; p < nk; ++p) c += s_ids[p] == tid;
-    s_cnt[tid] = c;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int o = 0, na = 0;
-    for (int e = 0; e < E; ++e) {
-      s_off[e] = o;
-      offsets[e] = o;
-      counts[e] = s_cnt[e];
-      if (s_cnt[e] > 0) active[na++] = e;
-      o += s_cnt[e];
-    }
-    s_off[E] = o;
-    offsets[E] = o;
-    active[E] = na;
-  }
-  __syncthreads();
-  if (tid < E) {
-    int slot = s_off[tid];
-    for (int p = 0; p < nk; ++p)
-      if (s_ids[p] == tid) {
-        slot_of[p] = slot;
-        tos[slot] = p / k;
-        ++slot;
-      }
-  }
-}
-
-// ---------------------------------------------------------------- expert GEMMs
-// One wave's share of a 16-row weight tile: NU groups of 128 weights per row.  Lane (i, G)
-// holds weights kw0 + 128u + 32G + [0, 32) of row i: 16 code bytes and 2 scale bytes per
-// group, so each load instruction covers 64 contiguous code bytes of each of the 16 rows.
-template <int NU>
-struct RowSlice {
-  u32x4_t codes[NU];
-  uint32_t scales[NU];
-};
-
-template <int NU>
-__device__ __forceinline__ void load_slice(RowSlice<NU>& s, const uint8_t* codes_row,
-                                           const uint8_t* scale_row, int kw0, int G) {
-  const uint8_t* c = codes_row + (kw0 >> 1) + 16 * G;
-  const uint8_t* sc = scale_row + (kw0 >> 4) + 2 * G;
-#pragma unroll
-  for (int u = 0; u < NU; ++u) {
-    s.codes[u] = __builtin_nontemporal_load((const u32x4_t*)(c + 64 * u));
-    s.scales[u] = *(const uint16_t*)(sc + 8 * u);
-  }
-}
-
-// B operand of one column tile: lane column i holds a pooled token (hi term for i < 8, lo
-// term for i >= 8); f16x8 m of group u covers k = kw0 + 128u + 32G + 8m.  `row` is always
-// a valid row (invalid lanes read row 0) and `valid` zeroes the operand after the loads.
-template <int NU>
-__device__ __forceinline__ void load_b(f16x8_t (&bx)[NU][4], const _Float16* row, bool valid) {
-#pragma unroll
-  for (int u = 0; u < NU; ++u)
-#pragma unroll
-    for (int m = 0; m < 4; ++m) bx[u][m] = *(const f16x8_t*)(row + 128 * u + 8 * m);
-  if (!valid) {
-    const f16x8_t zero8 = {};
-#pragma unroll
-    for (int u = 0; u < NU; ++u)
-#pragma unroll
-      for (int m = 0; m < 4; ++m) bx[u][m] = zero8;
-  }
-}
-
-// W13 (gate rows [0, I), up rows [I, 2I)) + SwiGLU.  KS waves split K = H, NU = H/(128 KS).
-template <int NCT, int NU, int KS>
-__global__ __launch_bounds__(64 * KS) void k_moe_w13(MoeArgs a) {
-  __shared__ f32x4_t red[KS > 1 ? KS - 1 : 1][2][NCT][64];
-  if ((int)blockIdx.y >= a.active[a.E]) return;
-  const int e = a.active[blockIdx.y];
-  const int nt = blockIdx.x;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int i = lane & 15, G = lane >> 4;
-  const int K = a.H;
-  const int kw0 = wave * (NU * 128);
-  const size_t rowg = (size_t)e * 2 * a.I + nt * 16 + i;
-  const size_t rowu = rowg + a.I;
-  RowSlice<NU> wg, wu;
-  load_slice<NU>(wg, a.w13_codes + rowg * (K >> 1), a.w13_scales + rowg * (K >> 4), kw0, G);
-  load_slice<NU>(wu, a.w13_codes + rowu * (K >> 1), a.w13_scales + rowu * (K >> 4), kw0, G);
-  const int Te = a.counts[e];
-  const int off = a.offsets[e];
-  const int nct = (Te + 7) >> 3;
-  f32x4_t ag[NCT], au[NCT];
-#pragma unroll
-  for (int c = 0; c < NCT; ++c) ag[c] = au[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int c = 0; c < NCT; ++c) {
-    if (c >= nct) break;
-    const int slot = 8 * c + (i & 7);
+  __shared__ int s_wc[4], s_wa[4];
+  const int ntiles = (a.E + 15) >> 4;
+  const int nt = blockIdx.x % ntiles, ks = blockIdx.x / ntiles;
+  const int KS = gridDim.x / ntiles;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, tid = threadIdx.x;
+  const int i = lane & 15, g = lane >> 4;
+  const int KT = a.H >> 5;
+  const int kt0 = ks * 8 + wave * 2;
+  {
+    const uint32_t xbytes = (uint32_t)(a.b * a.H * 2);
+    const auto rh = rsrc(a.x, xbytes);
+    const auto rl = rsrc(a.x_lo != nullptr ? a.x_lo : a.x, a.x_lo != nullptr ? xbytes : 0);
     const bool lo = (i >> 3) != 0;
-    const bool valid = slot < Te && (!lo || a.x16_lo != nullptr);
-    const _Float16* base = (lo && a.x16_lo != nullptr) ? a.x16_lo : a.x16;
-    // the tile's 8 token ids through uniform (scalar) loads, which do not queue behind the
-    // weight loads; each lane then selects its own
-    int tok = 0;
+    const uint16_t* wt = a.w + ((size_t)nt * KT + kt0) * 512 + lane * 8;
+    const bf16x8_t a0 = __builtin_nontemporal_load((const bf16x8_t*)wt);
+    const bf16x8_t a1 = __builtin_nontemporal_load((const bf16x8_t*)(wt + 512));
+    bf16x8_t b0[NCT], b1[NCT];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int t = (8 * c + j < Te) ? a.tos[off + 8 * c + j] : 0;
-      tok = ((i & 7) == j) ? t : tok;
+    for (int c = 0; c < NCT; ++c) {
+      const int row = 8 * c + (i & 7);
+      const uint32_t ob = row < a.b ? (uint32_t)((row * a.H + kt0 * 32 + 8 * g) * 2) : kOob;
+      const uint32_t oh = lo ? kOob : ob, ol = lo ? ob : kOob;
+      b0[c] = __builtin_bit_cast(bf16x8_t, buf_load16(rh, oh) | buf_load16(rl, ol));
+      b1[c] = __builtin_bit_cast(bf16x8_t, buf_load16(rh, oh + 64) | buf_load16(rl, ol + 64));
     }
-    tok = valid ? tok : 0;
-    f16x8_t bx[NU][4];
-    load_b<NU>(bx, base + (size_t)tok * K + kw0 + 32 * G, valid);
+    f32x4_t acc[NCT];
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      f16x8_t dg[4], du[4];
-      sd::dequant_unit(wg.codes[u], wg.scales[u], dg);
-      sd::dequant_unit(wu.codes[u], wu.scales[u], du);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        ag[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dg[m], bx[u][m], ag[c], 0, 0, 0);
-        au[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(du[m], bx[u][m], au[c], 0, 0, 0);
-      }
+    for (int c = 0; c < NCT; ++c) {
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0[c], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1[c], acc[c], 0, 0, 0);
     }
-  }
-  if (KS > 1) {
-    if (wave > 0) {
-#pragma unroll
-      for (int c = 0; c < NCT; ++c) {
-        red[wave - 1][0][c][lane] = ag[c];
-        red[wave - 1][1][c][lane] = au[c];
-      }
-    }
-    __syncthreads();
-    if (wave != 0) return;
-#pragma unroll
-    for (int c = 0; c < NCT; ++c)
-#pragma unroll
-      for (int w = 0; w < KS - 1; ++w) {
-        ag[c] += red[w][0][c][lane];
-        au[c] += red[w][1][c][lane];
-      }
-  }
-  // hi + lo columns
-#pragma unroll
-  for (int c = 0; c < NCT; ++c)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      ag[c][r] += __shfl_xor(ag[c][r], 8, 64);
-      au[c][r] += __shfl_xor(au[c][r], 8, 64);
-    }
-  if (i >= 8) return;
-  const float sc = SD_X16_UNSCALE * a.w13_gscale[e];
-  const int n = nt * 16 + 4 * G;  // lane rows n .. n+3 of the gate (and up) block
-#pragma unroll
-  for (int c = 0; c < NCT; ++c) {
-    const int slot = 8 * c + i;
-    if (slot >= Te) continue;
-    const size_t o = (size_t)(off + slot) * a.I + n;
-    _Float16 hh[4], hl[4];
-    uint16_t hb[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float gv = ag[c][r] * sc, uv = au[c][r] * sc;
-      const float h = gv / (1.0f + __expf(-gv)) * uv;
-      sd::split_f16(h, hh[r], hl[r]);
-      hb[r] = sd::f2bf(h);
-    }
-    *(u32x2_t*)(a.h16 + o) = u32x2_t{__builtin_bit_cast(uint32_t, f16x2_t{hh[0], hh[1]}),
-                                     __builtin_bit_cast(uint32_t, f16x2_t{hh[2], hh[3]})};
-    *(u32x2_t*)(a.h16_lo + o) = u32x2_t{__builtin_bit_cast(uint32_t, f16x2_t{hl[0], hl[1]}),
-                                        __builtin_bit_cast(uint32_t, f16x2_t{hl[2], hl[3]})};
-    if (a.h_bf16 != nullptr)
-      *(u32x2_t*)(a.h_bf16 + o) = u32x2_t{hb[0] | ((uint32_t)hb[1] << 16),
-                                          hb[2] | ((uint32_t)hb[3] << 16)};
-  }
-}
-
-// W2: y[slot, n] = h[slot] . W2_e[n], fp32.  KS waves split K = I, NU = I/(128 KS).
-template <int NCT, int NU, int KS>
-__global__ __launch_bounds__(64 * KS) void k_moe_w2(MoeArgs a) {
-  __shared__ f32x4_t red[KS > 1 ? KS - 1 : 1][NCT][64];
-  if ((int)blockIdx.y >= a.active[a.E]) return;
-  const int e = a.active[blockIdx.y];
-  const int nt = blockIdx.x;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int i = lane & 15, G = lane >> 4;
-  const int K = a.I;
-  const int kw0 = wave * (NU * 128);
-  const size_t row = (size_t)e * a.H + nt * 16 + i;
-  RowSlice<NU> wv;
-  load_slice<NU>(wv, a.w2_codes + row * (K >> 1), a.w2_scales + row * (K >> 4), kw0, G);
-  const int Te = a.counts[e];
-  const int off = a.offsets[e];
-  const int nct = (Te + 7) >> 3;
-  f32x4_t acc[NCT];
-#pragma unroll
-  for (int c = 0; c < NCT; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int c = 0; c < NCT; ++c) {
-    if (c >= nct) break;
-    const int slot = 8 * c + (i & 7);
-    const bool valid = slot < Te;
-    const _Float16* base = (i >> 3) ? a.h16_lo : a.h16;
-    f16x8_t bx[NU][4];
-    load_b<NU>(bx, base + (size_t)(off + (valid ? slot : 0)) * K + kw0 + 32 * G, valid);
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      f16x8_t dw[4];
-      sd::dequant_unit(wv.codes[u], wv.scales[u], dw);
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dw[m], bx[u][m], acc[c], 0, 0, 0);
-    }
-  }
-  if (KS > 1) {
     if (wave > 0) {
 #pragma unroll
       for (int c = 0; c < NCT; ++c) red[wave - 1][c][lane] = acc[c];
     }
     __syncthreads();
-    if (wave != 0) return;
+    if (wave == 0) {
 #pragma unroll
-    for (int c = 0; c < NCT; ++c)
+      for (int c = 0; c < NCT; ++c) {
+        acc[c] += red[0][c][lane];
+        acc[c] += red[1][c][lane];
+        acc[c] += red[2][c][lane];
 #pragma unroll
-      for (int w = 0; w < KS - 1; ++w) acc[c] += red[w][c][lane];
+        for (int r = 0; r < 4; ++r) acc[c][r] += __shfl_xor(acc[c][r], 8, 64);
+        const int row = 8 * c + i;
+        if (i < 8 && row < a.b) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int e = nt * 16 + 4 * g + r;
+            if (e < a.E) a.part[((size_t)ks * a.b + row) * a.E + e] = acc[c][r];
+          }
+        }
+      }
+    }
   }
+  // arrival: wave 0 wrote the partials; thread 0 releases them before counting, and the
+  // last arrival acquires every workgroup's partials before reading them
+  __syncthreads();
+  if (tid == 0) {
+    __threadfence();
+    s_last = atomicAdd(a.counter, 1) == (int)gridDim.x - 1;
+    if (s_last) __threadfence();
+  }
+  __syncthreads();
+  if (!s_last) return;
+
+  const int b = a.b, E = a.E, k = a.k;
+  // z = sum over ks in order + bias, every (row, expert) at once: one round of loads
+  const size_t st = (size_t)b * E;
+  for (int idx = tid; idx < b * E; idx += 256) {
+    float z = 0.f;
+#pragma unroll 16
+    for (int j = 0; j < KS; ++j) z += a.part[j * st + idx];
+    if (a.bias != nullptr) z += a.bias[idx];
+    if (a.logits != nullptr) a.logits[idx] = z;
+    s_z[idx] = z != z ? -INFINITY : z;  // NaN ranks with -inf
+  }
+  __syncthreads();
+  for (int t = wave; t < b; t += 4) {
+    float v[4];
 #pragma unroll
-  for (int c = 0; c < NCT; ++c)
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane + 64 * q;
+      v[q] = e < E ? s_z[t * E + e] : -INFINITY;
+    }
+    int taken = 0;
+    float sel[8];
+    int sid[8];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[c][r] += __shfl_xor(acc[c][r], 8, 64);
-  if (i >= 8) return;
-  const float sc = SD_X16_UNSCALE * a.w2_gscale[e];
-  const int n = nt * 16 + 4 * G;
+    for (int j = 0; j < 8; ++j) {
+      if (j >= k) break;
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
 #pragma unroll
-  for (int c = 0; c < NCT; ++c) {
-    const int slot = 8 * c + i;
-    if (slot >= Te) continue;
-    *(f32x4_t*)(a.y + (size_t)(off + slot) * a.H + n) = acc[c] * sc;
+      for (int q = 0; q < 4; ++q) {
+        const int e = lane + 64 * q;
+        if (e < E && !((taken >> q) & 1) && (v[q] > bv || (v[q] == bv && e < bi))) {
+          bv = v[q];
+          bi = e;
+        }
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        const float ov = __shfl_xor(bv, o, 64);
+        const int oi = __shfl_xor(bi, o, 64);
+        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+      }
+      if ((bi & 63) == lane) taken |= 1 << (bi >> 6);
+      sel[j] = bv;
+      sid[j] = bi;
+    }
+    if (lane == 0) {
+      float den = 0.f;
+      for (int j = 0; j < k; ++j) den += expf(sel[j] - sel[0]);
+      for (int j = 0; j < k; ++j) {
+        a.ids[t * k + j] = sid[j];
+        a.w_out[t * k + j] = expf(sel[j] - sel[0]) / den;
+        s_ids[t * k + j] = sid[j];
+      }
+    }
+  }
+  if (tid < E) s_mlo[tid] = s_mhi[tid] = 0u;
+  __syncthreads();
+  const int nk = b * k;
+  for (int p = tid; p < nk; p += 256) {
+    const int t = p / k;
+    atomicOr(t < 32 ? &s_mlo[s_ids[p]] : &s_mhi[s_ids[p]], 1u << (t & 31));
+  }
+  __syncthreads();
+  // counts, exclusive offsets and the active list: block scans over experts (tid = e)
+  const int e = tid;
+  const int cnt = e < E ? __popc(s_mlo[e]) + __popc(s_mhi[e]) : 0;
+  const int act = cnt > 0 ? 1 : 0;
+  int ic = cnt, ia = act;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int uc = __shfl_up(ic, d, 64), ua = __shfl_up(ia, d, 64);
+    if (lane >= d) { ic += uc; ia += ua; }
+  }
+  if (lane == 63) { s_wc[wave] = ic; s_wa[wave] = ia; }
+  __syncthreads();
+  int pc = 0, pa = 0;
+  for (int w = 0; w < wave; ++w) { pc += s_wc[w]; pa += s_wa[w]; }
+  const int total = s_wc[0] + s_wc[1] + s_wc[2] + s_wc[3];
+  const int n_act = s_wa[0] + s_wa[1] + s_wa[2] + s_wa[3];
+  const int off = pc + ic - cnt;
+  if (e < E) {
+    a.counts[e] = cnt;
+    a.offsets[e] = off;
+    s_off[e] = off;
+    if (act) a.active[pa + ia - 1] = e;
+    if (e >= n_act) a.active[e] = -1;
+  }
+  if (tid == 0) {
+    a.offsets[E] = total;
+    a.active[E] = n_act;
+  }
+  __syncthreads();
+  for (int p = tid; p < nk; p += 256) {
+    const int t = p / k, ex = s_ids[p];
+    const int rank = t < 32 ? __popc(s_mlo[ex] & ((1u << t) - 1u))
+                            : __popc(s_mlo[ex]) + __popc(s_mhi[ex] & ((1u << (t - 32)) - 1u));
+    const int slot = s_off[ex] + rank;
+    a.slot_of[p] = slot;
+    a.tos[slot] = t;
+  }
+  if (tid == 0) *a.counter = 0;  // ready for the next launch
+}
+
+__global__ void k_zero_i32(int* p) { *p = 0; }
+
+// ---------------------------------------------------------------- expert GEMMs
+// Weights are packed tiles of 16 rows x 128 weights (layout in sdverify.h): per tile 1 KB
+// of codes, lane l's 16 bytes holding weights 32(l/16) .. +31 of row l%16, and 128 B of
+// scales, lane l's 2 bytes at 2l.  Lane (i, G)'s four f16x8 operands of a tile cover k =
+// 32G + 8m, m = 0..3; the activation operand takes the same k order.
+//
+// A work unit is (active expert, 16-row tile); a persistent grid walks the units with KS
+// waves splitting K (NU tiles each).  The routing metadata is staged in LDS once per
+// workgroup, and the next unit's weights are loaded while the current unit is reduced, so
+// the weight stream does not drain between units.  Pooled tokens are the B operand, 8 per column tile as hi/lo fp16 terms (columns
+// 0-7 / 8-15); operand rows that do not exist are read through buffer loads whose range
+// check returns zero without a memory access.
+
+struct MoeMeta {
+  int active[257];
+  int cnt[256];
+  int off[256];
+  int tos[512];
+};
+
+__device__ __forceinline__ void stage_meta(const MoeArgs& a, MoeMeta& m) {
+  const int nk = a.b * a.k;
+  for (int p = threadIdx.x; p <= a.E; p += blockDim.x) m.active[p] = a.active[p];
+  for (int p = threadIdx.x; p < a.E; p += blockDim.x) {
+    m.cnt[p] = a.counts[p];
+    m.off[p] = a.offsets[p];
+  }
+  for (int p = threadIdx.x; p < nk; p += blockDim.x) m.tos[p] = a.tos[p];
+  __syncthreads();
+}
+
+template <int NU>
+struct Slice {
+  u32x4_t codes[NU];
+  uint32_t scales[NU];
+};
+
+// The wave's NU consecutive tiles starting at packed tile index `tile0`.
+template <int NU>
+__device__ __forceinline__ void load_slice(Slice<NU>& s, const uint8_t* codes,
+                                           const uint8_t* scales, size_t tile0, int lane) {
+  const uint8_t* cp = codes + tile0 * 1024 + 16 * lane;
+  const uint8_t* sp = scales + tile0 * 128 + 2 * lane;
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    s.codes[u] = __builtin_nontemporal_load((const u32x4_t*)(cp + 1024 * u));
+    s.scales[u] = *(const uint16_t*)(sp + 128 * u);
+  }
+}
+
+// B operand: f16x8 m of tile u at byte offset off + (128u + 8m) * 2 of the hi (lanes with
+// off_h in range) or lo buffer (off_l); the other buffer's offset is out of range.
+template <int NU>
+__device__ __forceinline__ void load_bx(f16x8_t (&bx)[NU][4], __amdgpu_buffer_rsrc_t rh,
+                                        __amdgpu_buffer_rsrc_t rl, uint32_t off_h,
+                                        uint32_t off_l) {
+#pragma unroll
+  for (int u = 0; u < NU; ++u)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t d = (uint32_t)(128 * u + 8 * m) * 2;
+      const u32x4_t h = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rh, off_h + d, 0, 0));
+      const u32x4_t l = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rl, off_l + d, 0, 0));
+      bx[u][m] = __builtin_bit_cast(f16x8_t, h | l);
+    }
+}
+
+struct Unit {
+  int e, nt, Te, off;
+};
+
+__device__ __forceinline__ Unit unit_of(const MoeMeta& m, int u, int NT) {
+  Unit r;
+  const int ai = u / NT;
+  r.nt = u - ai * NT;
+  r.e = __builtin_amdgcn_readfirstlane(m.active[ai]);
+  r.Te = __builtin_amdgcn_readfirstlane(m.cnt[r.e]);
+  r.off = __builtin_amdgcn_readfirstlane(m.off[r.e]);
+  return r;
+}
+
+// Workgroup w walks the contiguous unit range [begin, end): consecutive units mostly share
+// an expert, so the activation operand is reloaded only when the expert changes.
+__device__ __forceinline__ void unit_range(int n_units, int& begin, int& end) {
+  begin = (int)(((long)blockIdx.x * n_units) / gridDim.x);
+  end = (int)(((long)(blockIdx.x + 1) * n_units) / gridDim.x);
+}
+
+// W13 (gate rows [0, I), up rows [I, 2I)) + SwiGLU.  K = H = 128 * NU * KS.
+template <int NCT, int NU, int KS>
+__global__ __launch_bounds__(64 * KS) void k_moe_w13(MoeArgs a) {
+  constexpr bool PB = NCT == 1;  // activations prefetched with the weights
+  constexpr int NR = KS > 1 ? KS - 1 : 1;
+  __shared__ MoeMeta meta;
+  __shared__ f32x4_t red[PB ? 2 : 1][NR][2][NCT][64];
+  stage_meta(a, meta);
+  const int NT = a.I >> 4;
+  const int n_units = meta.active[a.E] * NT;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int i = lane & 15, G = lane >> 4;
+  const bool lo = (i >> 3) != 0;
+  const int K = a.H, KT = K >> 7, kw = wave * NU;
+  const int NT2 = 2 * NT;
+  const uint32_t xbytes = (uint32_t)(a.b * K * 2);
+  const auto rh = rsrc(a.x16, xbytes);
+  const auto rl = rsrc(a.x16_lo != nullptr ? a.x16_lo : a.x16, a.x16_lo != nullptr ? xbytes : 0);
+
+  // lane's B offsets for column tile c of unit U (hi and lo buffers)
+  auto b_off = [&](const Unit& U, int c, uint32_t& oh, uint32_t& ol) {
+    const int slot = 8 * c + (i & 7);
+    const uint32_t o = slot < U.Te
+                           ? (uint32_t)(((size_t)meta.tos[U.off + slot] * K + kw * 128 + 32 * G) * 2)
+                           : kOob;
+    oh = lo ? kOob : o;
+    ol = lo ? o : kOob;
+  };
+  auto load_a = [&](Slice<NU>& sg, Slice<NU>& su, const Unit& U) {
+    const size_t t0 = ((size_t)U.e * NT2 + U.nt) * KT + kw;
+    load_slice<NU>(sg, a.w13_codes, a.w13_scales, t0, lane);
+    load_slice<NU>(su, a.w13_codes, a.w13_scales, t0 + (size_t)NT * KT, lane);
+  };
+  auto load_b0 = [&](f16x8_t (&bx)[NU][4], const Unit& U) {
+    uint32_t oh, ol;
+    b_off(U, 0, oh, ol);
+    load_bx<NU>(bx, rh, rl, oh, ol);
+  };
+  auto compute = [&](const Slice<NU>& sg, const Slice<NU>& su, f16x8_t (&bx0)[NU][4],
+                     const Unit& U, int buf) {
+    f32x4_t ag[NCT], au[NCT];
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) ag[c] = au[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int nct = (U.Te + 7) >> 3;
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) {
+      if (c >= nct) break;
+      f16x8_t bl[NU][4];
+      if (!PB) {
+        uint32_t oh, ol;
+        b_off(U, c, oh, ol);
+        load_bx<NU>(bl, rh, rl, oh, ol);
+      }
+      f16x8_t (&bx)[NU][4] = PB ? bx0 : bl;
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        f16x8_t dg[4], du[4];
+        sd::dequant_unit(sg.codes[u], sg.scales[u], dg);
+        sd::dequant_unit(su.codes[u], su.scales[u], du);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          ag[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dg[m], bx[u][m], ag[c], 0, 0, 0);
+          au[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(du[m], bx[u][m], au[c], 0, 0, 0);
+        }
+      }
+    }
+    if (KS > 1) {
+      if (wave > 0) {
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) {
+          red[buf][wave - 1][0][c][lane] = ag[c];
+          red[buf][wave - 1][1][c][lane] = au[c];
+        }
+      }
+      __syncthreads();
+    }
+    if (wave == 0) {
+#pragma unroll
+      for (int c = 0; c < NCT; ++c) {
+#pragma unroll
+        for (int w = 0; w < KS - 1; ++w) {
+          ag[c] += red[buf][w][0][c][lane];
+          au[c] += red[buf][w][1][c][lane];
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {  // hi + lo columns
+          ag[c][r] += __shfl_xor(ag[c][r], 8, 64);
+          au[c][r] += __shfl_xor(au[c][r], 8, 64);
+        }
+      }
+      if (i < 8) {
+        const float sc = SD_X16_UNSCALE * a.w13_gscale[U.e];
+        const int n = U.nt * 16 + 4 * G;  // lane rows n .. n+3 of the gate (and up) block
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) {
+          const int slot = 8 * c + i;
+          if (slot >= U.Te) continue;
+          const size_t o = (size_t)(U.off + slot) * a.I + n;
+          _Float16 hh[4], hl[4];
+          uint16_t hb[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float gv = ag[c][r] * sc, uv = au[c][r] * sc;
+            const float h = gv / (1.0f + __expf(-gv)) * uv;
+            sd::split_f16(h, hh[r], hl[r]);
+            hb[r] = sd::f2bf(h);
+          }
+          *(u32x2_t*)(a.h16 + o) = u32x2_t{__builtin_bit_cast(uint32_t, f16x2_t{hh[0], hh[1]}),
+                                           __builtin_bit_cast(uint32_t, f16x2_t{hh[2], hh[3]})};
+          *(u32x2_t*)(a.h16_lo + o) = u32x2_t{__builtin_bit_cast(uint32_t, f16x2_t{hl[0], hl[1]}),
+                                              __builtin_bit_cast(uint32_t, f16x2_t{hl[2], hl[3]})};
+          if (a.h_bf16 != nullptr)
+            *(u32x2_t*)(a.h_bf16 + o) = u32x2_t{hb[0] | ((uint32_t)hb[1] << 16),
+                                                hb[2] | ((uint32_t)hb[3] << 16)};
+        }
+      }
+    }
+    if (!PB && KS > 1) __syncthreads();  // single-buffered reduction space
+  };
+
+  Slice<NU> g0, u0, g1, u1;
+  f16x8_t bx[NU][4];  // one column tile's activations (unused without PB)
+  int u, end;
+  unit_range(n_units, u, end);
+  if (u >= end) return;
+  if constexpr (!PB) {  // several column tiles: their accumulators leave no room to prefetch
+    for (; u < end; ++u) {
+      const Unit U = unit_of(meta, u, NT);
+      load_a(g0, u0, U);
+      compute(g0, u0, bx, U, 0);
+    }
+    return;
+  }
+  Unit U0 = unit_of(meta, u, NT), U1;
+  int be = -1;  // expert whose activations are in bx
+  load_a(g0, u0, U0);
+  while (true) {
+    if (PB && U0.e != be) { load_b0(bx, U0); be = U0.e; }
+    const int n1 = u + 1;
+    if (n1 < end) { U1 = unit_of(meta, n1, NT); load_a(g1, u1, U1); }
+    compute(g0, u0, bx, U0, 0);
+    if (n1 >= end) break;
+    if (PB && U1.e != be) { load_b0(bx, U1); be = U1.e; }
+    const int n2 = n1 + 1;
+    if (n2 < end) { U0 = unit_of(meta, n2, NT); load_a(g0, u0, U0); }
+    compute(g1, u1, bx, U1, PB ? 1 : 0);
+    if (n2 >= end) break;
+    u = n2;
+  }
+}
+
+// W2: y[slot, n] = h[slot] . W2_e[n], fp32.  K = I = 128 * NU * KS.
+template <int NCT, int NU, int KS>
+__global__ __launch_bounds__(64 * KS) void k_moe_w2(MoeArgs a) {
+  constexpr bool PB = NCT == 1;
+  constexpr int NR = KS > 1 ? KS - 1 : 1;
+  __shared__ MoeMeta meta;
+  __shared__ f32x4_t red[PB ? 2 : 1][NR][NCT][64];
+  stage_meta(a, meta);
+  const int NT = a.H >> 4;
+  const int n_units = meta.active[a.E] * NT;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int i = lane & 15, G = lane >> 4;
+  const bool lo = (i >> 3) != 0;
+  const int K = a.I, KT = K >> 7, kw = wave * NU;
+  const uint32_t hbytes = (uint32_t)(a.b * a.k * K * 2);
+  const auto rh = rsrc(a.h16, hbytes);
+  const auto rl = rsrc(a.h16_lo, hbytes);
+
+  auto b_off = [&](const Unit& U, int c, uint32_t& oh, uint32_t& ol) {
+    const int slot = 8 * c + (i & 7);
+    const uint32_t o =
+        slot < U.Te ? (uint32_t)(((size_t)(U.off + slot) * K + kw * 128 + 32 * G) * 2) : kOob;
+    oh = lo ? kOob : o;
+    ol = lo ? o : kOob;
+  };
+  auto load_a = [&](Slice<NU>& sw, const Unit& U) {
+    load_slice<NU>(sw, a.w2_codes, a.w2_scales, ((size_t)U.e * NT + U.nt) * KT + kw, lane);
+  };
+  auto load_b0 = [&](f16x8_t (&bx)[NU][4], const Unit& U) {
+    uint32_t oh, ol;
+    b_off(U, 0, oh, ol);
+    load_bx<NU>(bx, rh, rl, oh, ol);
+  };
+  auto compute = [&](const Slice<NU>& sw, f16x8_t (&bx0)[NU][4], const Unit& U, int buf) {
+    f32x4_t acc[NCT];
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int nct = (U.Te + 7) >> 3;
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) {
+      if (c >= nct) break;
+      f16x8_t bl[NU][4];
+      if (!PB) {
+        uint32_t oh, ol;
+        b_off(U, c, oh, ol);
+        load_bx<NU>(bl, rh, rl, oh, ol);
+      }
+      f16x8_t (&bx)[NU][4] = PB ? bx0 : bl;
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        f16x8_t dw[4];
+        sd::dequant_unit(sw.codes[u], sw.scales[u], dw);
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dw[m], bx[u][m], acc[c], 0, 0, 0);
+      }
+    }
+    if (KS > 1) {
+      if (wave > 0) {
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) red[buf][wave - 1][c][lane] = acc[c];
+      }
+      __syncthreads();
+    }
+    if (wave == 0) {
+#pragma unroll
+      for (int c = 0; c < NCT; ++c) {
+#pragma unroll
+        for (int w = 0; w < KS - 1; ++w) acc[c] += red[buf][w][c][lane];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[c][r] += __shfl_xor(acc[c][r], 8, 64);
+      }
+      if (i < 8) {
+        const float sc = SD_X16_UNSCALE * a.w2_gscale[U.e];
+        const int n = U.nt * 16 + 4 * G;
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) {
+          const int slot = 8 * c + i;
+          if (slot >= U.Te) continue;
+          *(f32x4_t*)(a.y + (size_t)(U.off + slot) * a.H + n) = acc[c] * sc;
+        }
+      }
+    }
+    if (!PB && KS > 1) __syncthreads();
+  };
+
+  Slice<NU> w0, w1;
+  f16x8_t bx[NU][4];  // one column tile's activations (unused without PB)
+  int u, end;
+  unit_range(n_units, u, end);
+  if (u >= end) return;
+  if constexpr (!PB) {
+    for (; u < end; ++u) {
+      const Unit U = unit_of(meta, u, NT);
+      load_a(w0, U);
+      compute(w0, bx, U, 0);
+    }
+    return;
+  }
+  Unit U0 = unit_of(meta, u, NT), U1;
+  int be = -1;
+  load_a(w0, U0);
+  while (true) {
+    if (PB && U0.e != be) { load_b0(bx, U0); be = U0.e; }
+    const int n1 = u + 1;
+    if (n1 < end) { U1 = unit_of(meta, n1, NT); load_a(w1, U1); }
+    compute(w0, bx, U0, 0);
+    if (n1 >= end) break;
+    if (PB && U1.e != be) { load_b0(bx, U1); be = U1.e; }
+    const int n2 = n1 + 1;
+    if (n2 < end) { U0 = unit_of(meta, n2, NT); load_a(w0, U0); }
+    compute(w1, bx, U1, PB ? 1 : 0);
+    if (n2 >= end) break;
+    u = n2;
   }
 }
 
@@ -342,7 +607,7 @@ __global__ __launch_bounds__(256) void k_debug_dequant(int n, int k, const uint8
     for (int e = 0; e < 8; ++e) o[8 * m + e] = (float)wv[m][e] * gscale;
 }
 
-// A K split of an expert GEMM: K = 128 * NU * KS with NU <= 4 groups per wave.
+// A K split of an expert GEMM: K = 128 * NU * KS with NU <= 4 tiles per wave.
 struct Split { int nu, ks; };
 Split split_for(int K) {
   const int g = K / 128;
@@ -354,14 +619,30 @@ Split split_for(int K) {
 #define SD_SPLITS(X) X(1, 1) X(1, 2) X(1, 4) X(1, 8) X(2, 1) X(2, 2) X(2, 4) X(2, 8) \
                      X(3, 1) X(3, 2) X(3, 4) X(3, 8) X(4, 1) X(4, 2) X(4, 4) X(4, 8)
 
+int cus() {
+  static int n[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (n[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        v <= 0)
+      v = 256;
+    n[dev] = v;
+  }
+  return n[dev];
+}
+
 template <int NCT>
 hipError_t launch_experts_nct(const MoeArgs& a, hipStream_t st) {
   const Split s13 = split_for(a.H), s2 = split_for(a.I);
-  const dim3 g13(a.I / 16, a.E), g2(a.H / 16, a.E);
+  // persistent grids: the live units are at most E * tiles
+  const int g13 = min(cus(), a.E * (a.I / 16));
+  const int g2 = min(2 * cus(), a.E * (a.H / 16));
   bool done = false;
 #define SD_W13(NU, KS)                                                                     \
   if (!done && s13.nu == NU && s13.ks == KS) {                                             \
-    hipLaunchKernelGGL((k_moe_w13<NCT, NU, KS>), g13, dim3(64 * KS), 0, st, a);            \
+    hipLaunchKernelGGL((k_moe_w13<NCT, NU, KS>), dim3(g13), dim3(64 * KS), 0, st, a);      \
     done = true;                                                                          \
   }
   SD_SPLITS(SD_W13)
@@ -372,7 +653,7 @@ hipError_t launch_experts_nct(const MoeArgs& a, hipStream_t st) {
   done = false;
 #define SD_W2(NU, KS)                                                                      \
   if (!done && s2.nu == NU && s2.ks == KS) {                                               \
-    hipLaunchKernelGGL((k_moe_w2<NCT, NU, KS>), g2, dim3(64 * KS), 0, st, a);              \
+    hipLaunchKernelGGL((k_moe_w2<NCT, NU, KS>), dim3(g2), dim3(64 * KS), 0, st, a);        \
     done = true;                                                                          \
   }
   SD_SPLITS(SD_W2)
@@ -385,11 +666,18 @@ hipError_t launch_experts_nct(const MoeArgs& a, hipStream_t st) {
 
 bool moe_shape_supported(int H, int I) { return split_for(H).nu > 0 && split_for(I).nu > 0; }
 
-hipError_t launch_route_pool(const float* z, int b, int E, int k, int* ids, float* w,
-                             int* counts, int* offsets, int* slot_of, int* tos, int* active,
-                             hipStream_t st) {
-  hipLaunchKernelGGL(k_route_pool, dim3(1), dim3(256), 0, st, z, b, E, k, ids, w, counts,
-                     offsets, slot_of, tos, active);
+hipError_t launch_router(const RouterArgs& a, hipStream_t st) {
+  const int ntiles = (a.E + 15) / 16, ks = a.H / 256;
+  const dim3 grid(ntiles * ks), block(256);
+  if (a.b <= 8) hipLaunchKernelGGL(k_router<1>, grid, block, 0, st, a);
+  else if (a.b <= 16) hipLaunchKernelGGL(k_router<2>, grid, block, 0, st, a);
+  else if (a.b <= 32) hipLaunchKernelGGL(k_router<4>, grid, block, 0, st, a);
+  else hipLaunchKernelGGL(k_router<8>, grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_i32(int* p, hipStream_t st) {
+  hipLaunchKernelGGL(k_zero_i32, dim3(1), dim3(1), 0, st, p);
   return hipGetLastError();
 }
 

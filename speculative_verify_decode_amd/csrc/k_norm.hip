@@ -10,7 +10,17 @@
 
 namespace {
 
-template <int EPT>  // elements per thread: H = 256 * EPT
+template <int VW>
+struct VecT;
+template <> struct VecT<1> { typedef float T; };
+template <> struct VecT<2> { typedef f32x2_t T; };
+template <> struct VecT<4> { typedef f32x4_t T; };
+
+// H = 256 * EPT.  Thread tid owns NV vectors of VW consecutive elements, vector v at
+// element (v * 256 + tid) * VW, so every load is coalesced and as wide as H allows.  All
+// inputs (branch, stream, both gains) are loaded before the first reduction, so the row
+// costs one round trip to memory.
+template <int EPT>
 __global__ __launch_bounds__(256) void k_dualnorm(int H, float* __restrict__ stream,
                                                   const float* __restrict__ branch,
                                                   const uint16_t* __restrict__ front,
@@ -19,52 +29,81 @@ __global__ __launch_bounds__(256) void k_dualnorm(int H, float* __restrict__ str
                                                   uint16_t* __restrict__ out,
                                                   uint16_t* __restrict__ out_lo,
                                                   _Float16* __restrict__ x16,
-                                                  _Float16* __restrict__ x16_lo) {
+                                                  _Float16* __restrict__ x16_lo,
+                                                  int* __restrict__ zero) {
+  constexpr int VW = EPT % 4 == 0 ? 4 : (EPT % 2 == 0 ? 2 : 1);
+  constexpr int NV = EPT / VW;
+  typedef typename VecT<VW>::T V;
   __shared__ float red[4];
   const int row = blockIdx.x, tid = threadIdx.x;
+  if (zero != nullptr && row == 0 && tid == 0) *zero = 0;
   const size_t base = (size_t)row * H;
   const float inv_h = 1.0f / (float)H;
-  float s[EPT];
+  float s[EPT], gq[EPT];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int i0 = (v * 256 + tid) * VW;
+    const V q = *(const V*)(g_pre + i0);
+#pragma unroll
+    for (int j = 0; j < VW; ++j) gq[v * VW + j] = ((const float*)&q)[j];
+  }
   if (branch != nullptr) {
-    float u[EPT];
+    float u[EPT], gp[EPT];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int i0 = (v * 256 + tid) * VW;
+      const V bu = *(const V*)(branch + base + i0);
+      const V bs = *(const V*)(stream + base + i0);
+      const V bg = *(const V*)(g_post + i0);
+#pragma unroll
+      for (int j = 0; j < VW; ++j) {
+        u[v * VW + j] = ((const float*)&bu)[j];
+        s[v * VW + j] = ((const float*)&bs)[j];
+        gp[v * VW + j] = ((const float*)&bg)[j];
+      }
+    }
     float ss = 0.f;
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      u[e] = branch[base + e * 256 + tid];
-      ss += u[e] * u[e];
-    }
+    for (int e = 0; e < EPT; ++e) ss += u[e] * u[e];
     ss = sd::block_sum<4>(ss, red);
     const float r = rsqrtf(ss * inv_h + eps);
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      const int i = e * 256 + tid;
-      s[e] = stream[base + i] + u[e] * r * g_post[i];
-    }
+    for (int e = 0; e < EPT; ++e) s[e] += u[e] * r * gp[e];
   } else {
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) s[e] = sd::bf2f(front[base + e * 256 + tid]);
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+      for (int j = 0; j < VW; ++j) s[v * VW + j] = sd::bf2f(front[base + (v * 256 + tid) * VW + j]);
   }
   float ss = 0.f;
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    stream[base + e * 256 + tid] = s[e];
-    ss += s[e] * s[e];
+  for (int v = 0; v < NV; ++v) {
+    V o;
+#pragma unroll
+    for (int j = 0; j < VW; ++j) {
+      ((float*)&o)[j] = s[v * VW + j];
+      ss += s[v * VW + j] * s[v * VW + j];
+    }
+    *(V*)(stream + base + (v * 256 + tid) * VW) = o;
   }
   ss = sd::block_sum<4>(ss, red);
   const float r = rsqrtf(ss * inv_h + eps);
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    const int i = e * 256 + tid;
-    const float x = s[e] * r * g_pre[i];
-    uint16_t hi, lo;
-    sd::split_bf16(x, hi, lo);
-    out[base + i] = hi;
-    if (out_lo != nullptr) out_lo[base + i] = lo;
-    if (x16 != nullptr) {
-      _Float16 h16, l16;
-      sd::split_f16(x, h16, l16);
-      x16[base + i] = h16;
-      x16_lo[base + i] = l16;
+  for (int v = 0; v < NV; ++v) {
+    const size_t i0 = base + (size_t)(v * 256 + tid) * VW;
+#pragma unroll
+    for (int j = 0; j < VW; ++j) {
+      const float x = s[v * VW + j] * r * gq[v * VW + j];
+      uint16_t hi, lo;
+      sd::split_bf16(x, hi, lo);
+      out[i0 + j] = hi;
+      if (out_lo != nullptr) out_lo[i0 + j] = lo;
+      if (x16 != nullptr) {
+        _Float16 h16, l16;
+        sd::split_f16(x, h16, l16);
+        x16[i0 + j] = h16;
+        x16_lo[i0 + j] = l16;
+      }
     }
   }
 }
@@ -81,14 +120,14 @@ __global__ __launch_bounds__(256) void k_to_f16(int n, const uint16_t* __restric
 hipError_t launch_dualnorm(int b, int H, float* stream, const float* branch,
                            const uint16_t* front, const float* g_post, const float* g_pre,
                            float eps, uint16_t* out, uint16_t* out_lo, _Float16* x16,
-                           _Float16* x16_lo, hipStream_t st) {
+                           _Float16* x16_lo, int* zero, hipStream_t st) {
   if ((x16 == nullptr) != (x16_lo == nullptr)) return hipErrorInvalidValue;
   const dim3 grid(b), block(256);
   switch (H / 256) {
 #define SD_NORM_CASE(E)                                                                   \
   case E:                                                                                 \
     hipLaunchKernelGGL(k_dualnorm<E>, grid, block, 0, st, H, stream, branch, front, g_post, \
-                       g_pre, eps, out, out_lo, x16, x16_lo);                              \
+                       g_pre, eps, out, out_lo, x16, x16_lo, zero);                        \
     break;
     SD_NORM_CASE(1)
     SD_NORM_CASE(2)

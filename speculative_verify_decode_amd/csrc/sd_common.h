@@ -125,19 +125,20 @@ __device__ __forceinline__ void dequant_unit(u32x4_t codes, uint32_t scales2, f1
 // branch: fp32 [b, H] (null: front mode, the stream becomes the bf16 `front` rows).
 // out: bf16 pre-norm output (hi term); out_lo (optional): its bf16 lo term; x16 / x16_lo
 // (optional): fp16 hi / lo terms of the pre-norm output * 2^-8 (the expert input).
+// zero (optional): an int set to 0, for a later kernel's arrival counter.
 hipError_t launch_dualnorm(int b, int H, float* stream, const float* branch,
                            const uint16_t* front, const float* g_post, const float* g_pre,
                            float eps, uint16_t* out, uint16_t* out_lo, _Float16* x16,
-                           _Float16* x16_lo, hipStream_t st);
+                           _Float16* x16_lo, int* zero, hipStream_t st);
 
-enum GemmMode { GEMM_F32 = 0, GEMM_BF16 = 1, GEMM_F32_BIAS = 2, GEMM_HEAD = 3 };
+enum GemmMode { GEMM_F32 = 0, GEMM_F32_BIAS = 2, GEMM_HEAD = 3 };
 
 struct GemmArgs {
   int M, N, K;
   const uint16_t* x;   // bf16 [M, K]
   const uint16_t* x_lo; // optional bf16 lo terms of x [M, K] (column-split MFMA)
-  const uint16_t* w;   // bf16 [N, K]
-  void* y;             // fp32 or bf16 [M, N] (GEMM_HEAD: optional fp32 tau)
+  const uint16_t* w;   // bf16 [N, K] in packed 16 x 32 tiles
+  void* y;             // fp32 [M, N] (GEMM_HEAD: optional fp32 tau)
   const float* bias;   // [M, N] for GEMM_F32_BIAS (may be null)
   float* head_val;     // GEMM_HEAD: per (m, tile) best logit
   int* head_idx;       // GEMM_HEAD: per (m, tile) its index
@@ -145,13 +146,18 @@ struct GemmArgs {
 };
 hipError_t launch_gemm(GemmMode mode, const GemmArgs& a, hipStream_t st);
 
+// Weight packing (layouts in sdverify.h).
+hipError_t launch_pack_dense(int N, int K, const uint16_t* src, uint16_t* dst, hipStream_t st);
+hipError_t launch_pack_fp4(int E, int N, int K, const uint8_t* codes, const uint8_t* scales,
+                           uint8_t* codes_out, uint8_t* scales_out, hipStream_t st);
+
 hipError_t launch_qkv_post(const float* qkv, int b, int Hq, int Hkv, int D, int qk_norm,
                            float eps, float theta, const int* positions, const int64_t* slots,
                            uint16_t* q_out, uint16_t* q_lo, uint16_t* k_cache,
                            uint16_t* v_cache, hipStream_t st);
 
 struct AttnPlan {
-  int chunk_blocks;   // blocks per workgroup (even)
+  int chunk_blocks;   // blocks per workgroup (a multiple of 8)
   int n_chunks;       // chunks per (request, kv head) at max_seq_len
   int qg;             // queries per (request, kv head) = group * q_rows
 };
@@ -163,7 +169,8 @@ struct AttnArgs {
   const uint16_t* k_cache;
   const uint16_t* v_cache;
   const int* block_table;
-  int max_blocks;
+  int max_blocks;             // entries per block-table row
+  int num_blocks;             // blocks in the pool (block ids are clamped below it)
   const int* seq_lens;
   const int* positions;
   int n_req, Hq, Hkv, D, q_rows;
@@ -177,9 +184,23 @@ struct AttnArgs {
 };
 hipError_t launch_attention(const AttnArgs& a, const AttnPlan& p, hipStream_t st);
 
-hipError_t launch_route_pool(const float* z, int b, int E, int k, int* ids, float* w,
-                             int* counts, int* offsets, int* slot_of, int* tos, int* active,
-                             hipStream_t st);
+// Router GEMM + top-k + softmax + pooler in one launch: workgroups compute split-K
+// partial logits; the last to arrive (counter) reduces them and routes.
+struct RouterArgs {
+  int b, H, E, k;
+  const uint16_t* x;     // bf16 [b, H] hi terms
+  const uint16_t* x_lo;  // bf16 [b, H] lo terms (may be null)
+  const uint16_t* w;     // packed bf16 [E, H]
+  const float* bias;     // fp32 [b, E] (may be null)
+  float* part;           // fp32 [H / 256, b, E] scratch
+  int* counter;          // 0 at launch; the kernel leaves it 0
+  float* logits;         // fp32 [b, E] (may be null)
+  int* ids;
+  float* w_out;
+  int *counts, *offsets, *slot_of, *tos, *active;
+};
+hipError_t launch_router(const RouterArgs& a, hipStream_t st);
+hipError_t launch_zero_i32(int* p, hipStream_t st);
 
 struct MoeArgs {
   int b, H, I, E, k;

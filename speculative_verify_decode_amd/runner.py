@@ -16,11 +16,21 @@ def to_dev(t, device):
     return None if t is None else t.to(device).contiguous()
 
 
+def pack_layer(t):
+    """Replace the row-major weights of a device layer dict by their packed copies."""
+    for k in ("w_qkv", "w_o", "w_router"):
+        t[k] = B.pack_dense(t[k])
+    t["w13_codes"], t["w13_scales"] = B.pack_fp4(t["w13_codes"], t["w13_scales"])
+    t["w2_codes"], t["w2_scales"] = B.pack_fp4(t["w2_codes"], t["w2_scales"])
+
+
 class DeviceLayer:
-    """One layer's weights, KV pool and step metadata on the device, with its C structs."""
+    """One layer's weights (packed), KV pool and step metadata on the device, with its C
+    structs."""
 
     def __init__(self, lay, device):
         self.t = {k: to_dev(lay[k], device) for k in LAYER_TENSORS}
+        pack_layer(self.t)
         for k in ("num_blocks", "max_blocks", "max_seq_len"):
             self.t[k] = lay[k]
         self.weights = B.make_layer_weights(self.t)
@@ -64,7 +74,7 @@ class StepRunner:
         self.head = None
         if wk.get("head") is not None:
             h = wk["head"]
-            self.head = dict(w_lm=to_dev(h["w_lm"], device), g_final=to_dev(h["g_final"], device),
+            self.head = dict(w_lm=B.pack_dense(to_dev(h["w_lm"], device)), g_final=to_dev(h["g_final"], device),
                              d2t=to_dev(h["d2t"], device), multiplier=h["multiplier"],
                              soft_cap=h["soft_cap"])
             V = h["w_lm"].shape[0]

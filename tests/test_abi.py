@@ -55,7 +55,7 @@ def test_no_extra_exports_beyond_header(lib):
 
 
 def test_abi_version(lib):
-    assert B.abi_version() == 1
+    assert B.abi_version() == 2
 
 
 def test_workspace_bytes_host_only(lib):
@@ -164,6 +164,26 @@ def test_debug_dequant_validation(lib):
     L = B.lib()
     assert L.sd_debug_dequant(4, 48, FAKE, FAKE, 1.0, FAKE, None) == -1
     assert L.sd_debug_dequant(4, 64, FAKE + 1, FAKE, 1.0, FAKE, None) == -1
+
+
+def test_packed_dense_bytes(lib):
+    L = B.lib()
+    assert L.sd_packed_dense_bytes(10240, 4096) == 10240 * 4096 * 2
+    assert L.sd_packed_dense_bytes(40, 96) == 48 * 96 * 2      # rows padded to 16
+    assert L.sd_packed_dense_bytes(16, 48) == 0                # k % 32 != 0
+    assert L.sd_packed_dense_bytes(0, 64) == 0
+
+
+def test_pack_validation(lib):
+    L = B.lib()
+    assert L.sd_pack_dense(16, 48, FAKE, FAKE + 4096, None) == -1
+    assert L.sd_pack_dense(16, 64, FAKE + 8, FAKE + 4096, None) == -1   # misaligned
+    assert L.sd_pack_dense(16, 64, FAKE, FAKE, None) == -1              # in place
+    assert "in place" in L.sd_last_error().decode() or "out of place" in L.sd_last_error().decode()
+    assert L.sd_pack_fp4(2, 24, 128, FAKE, FAKE, FAKE + 4096, FAKE + 8192, None) == -1  # n % 16
+    assert L.sd_pack_fp4(2, 32, 96, FAKE, FAKE, FAKE + 4096, FAKE + 8192, None) == -1   # k % 128
+    assert L.sd_pack_fp4(2, 32, 128, FAKE, FAKE + 1, FAKE + 4096, FAKE + 8192, None) == -1
+    assert L.sd_pack_fp4(2, 32, 128, None, FAKE, FAKE + 4096, FAKE + 8192, None) == -1
 
 
 def test_product_path_never_imports_the_oracle():

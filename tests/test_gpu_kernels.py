@@ -39,6 +39,51 @@ def test_debug_dequant_is_bit_exact():
         assert np.array_equal(out.cpu().numpy().astype(np.float64), ref), gscale
 
 
+# ------------------------------------------------------------------------ weight packing
+# Expected layouts are the header's tile definitions, written as numpy reshapes.
+def packed_dense_ref(w):
+    n, k = w.shape
+    npad = -(-n // 16) * 16
+    full = np.zeros((npad, k), dtype=w.dtype)
+    full[:n] = w
+    # tile (nt, kt), lane l = 16 g + i, element j  <-  W[16 nt + i, 32 kt + 8 g + j]
+    return full.reshape(npad // 16, 16, k // 32, 4, 8).transpose(0, 2, 3, 1, 4).reshape(-1)
+
+
+def packed_fp4_ref(codes, scales):
+    e, n, kh = codes.shape
+    nt, kt = n // 16, (2 * kh) // 128
+    # lane l = 16 g + i of tile (e, nt, kt): code bytes 64 kt + 16 g .., scale bytes 8 kt + 2 g ..
+    c = codes.reshape(e, nt, 16, kt, 4, 16).transpose(0, 1, 3, 4, 2, 5).reshape(-1)
+    s = scales.reshape(e, nt, 16, kt, 4, 2).transpose(0, 1, 3, 4, 2, 5).reshape(-1)
+    return c, s
+
+
+@pytest.mark.parametrize("n,k", [(40, 96), (48, 4096), (10240, 4096)])
+def test_pack_dense_layout_is_exact(n, k):
+    require_lib()
+    rng = np.random.default_rng(n + k)
+    w = rng.integers(0, 1 << 16, (n, k), dtype=np.uint16)
+    dev = torch.from_numpy(w.view(np.int16)).to(DEV).view(torch.bfloat16)
+    out = B.pack_dense(dev)
+    torch.cuda.synchronize()
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1)
+    assert np.array_equal(got, packed_dense_ref(w))
+
+
+@pytest.mark.parametrize("e,n,k", [(3, 32, 128), (2, 3072, 4096), (4, 4096, 1536)])
+def test_pack_fp4_layout_is_exact(e, n, k):
+    require_lib()
+    rng = np.random.default_rng(e * n + k)
+    codes = rng.integers(0, 256, (e, n, k // 2), dtype=np.uint8)
+    scales = rng.integers(0, 256, (e, n, k // 16), dtype=np.uint8)
+    co, so = B.pack_fp4(torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV))
+    torch.cuda.synchronize()
+    c_ref, s_ref = packed_fp4_ref(codes, scales)
+    assert np.array_equal(co.cpu().numpy().reshape(-1), c_ref)
+    assert np.array_equal(so.cpu().numpy().reshape(-1), s_ref)
+
+
 # ------------------------------------------------------------------------ dual norm
 @pytest.mark.parametrize("name", ["tiny_b8_ctx128", "h4096_b8_ctx8k"])
 def test_boundary_dualnorm_modes(name):
@@ -170,7 +215,7 @@ def test_draft_head_full_size_matches_oracle():
     hd = synth.make_head(w, 0)
     H, V, b = w.hidden, w.draft_vocab, w.b
     h = synth._bf16(synth._normal(0, "head_probe_h", (b, H)))
-    w_lm, d2t = hd["w_lm"].to(DEV), hd["d2t"].to(DEV)
+    w_lm, d2t = B.pack_dense(hd["w_lm"].to(DEV)), hd["d2t"].to(DEV)
     ws = torch.empty(B.draft_head_workspace_bytes(H, V, b), dtype=torch.uint8, device=DEV)
     tau = torch.empty(b, V, dtype=torch.float32, device=DEV)
     ids = torch.empty(b, dtype=torch.int32, device=DEV)
@@ -202,6 +247,7 @@ def test_draft_head_ties_take_the_lower_index():
     ws = torch.empty(B.draft_head_workspace_bytes(H, V, b), dtype=torch.uint8, device=DEV)
     ids = torch.empty(b, dtype=torch.int32, device=DEV)
     tgt = torch.empty(b, dtype=torch.int64, device=DEV)
-    B.draft_head(H, V, b, h.to(DEV), w.to(DEV), 0.25, 30.0, d2t.to(DEV), None, ids, tgt, ws)
+    B.draft_head(H, V, b, h.to(DEV), B.pack_dense(w.to(DEV)), 0.25, 30.0, d2t.to(DEV), None, ids,
+                 tgt, ws)
     torch.cuda.synchronize()
     assert ids.cpu().tolist() == [5] * b and tgt.cpu().tolist() == [38] * b
