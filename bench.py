@@ -39,8 +39,37 @@ def algorithmic_bytes(wk, counts_per_layer):
     return total, int((counts_per_layer[0] > 0).sum()) * per_expert
 
 
+TRAFFIC_FILE = "profiles/moe_experts_{workload}_traffic.txt"
+KERNEL_SOURCES = ("speculative_verify_decode_amd/csrc/k_moe.hip",
+                  "speculative_verify_decode_amd/csrc/sd_common.h")
+
+
+def measured_traffic(workload):
+    """HBM bytes per sd_moe_experts launch from the committed FETCH_SIZE / WRITE_SIZE
+    summary, or None if there is none for this workload or the expert kernels' sources
+    have changed since the counters were taken."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(root, TRAFFIC_FILE.format(workload=workload))
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch", "source_sha256"):
+            k, v = line.split(":", 1)
+            fields[k] = v.split()[0]
+    h = hashlib.sha256()
+    for fn in KERNEL_SOURCES:
+        with open(os.path.join(root, fn), "rb") as f:
+            h.update(f.read())
+    if fields.get("source_sha256") != h.hexdigest():
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(wk):
-    """The oracle, as it stands, on one full layer step of the workload."""
+    """The oracle, as it stands, on full layer steps of the workload, repeated until about
+    10 s of host time (at most 4 steps); the mean per step."""
     import threadpoolctl
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     import oracle
@@ -48,12 +77,15 @@ def cpu_baseline(wk):
     lay, act, d = wk["layers"][0], wk["act"], wk["dims"]
     inp = oracle_layer_inputs(lay, act)
     threads = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()), default=1)
-    t0 = time.perf_counter()
-    oracle.layer_step(inp, d, branch_in=np64(act["branch_in"]))
-    dt = time.perf_counter() - t0
-    return {"value": dt * 1e6, "unit": "us per layer-step", "cores": int(threads), "kind": "oracle",
-            "sample": f"one full layer step of {wk['workload'].name} (fp64 NumPy oracle), "
-                      f"{len(os.sched_getaffinity(0))} host cores visible"}
+    times = []
+    while len(times) < 4 and sum(times) < 10.0:
+        t0 = time.perf_counter()
+        oracle.layer_step(inp, d, branch_in=np64(act["branch_in"]))
+        times.append(time.perf_counter() - t0)
+    return {"value": float(np.mean(times)) * 1e6, "unit": "us per layer-step", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{len(times)} full layer steps of {wk['workload'].name} (fp64 NumPy oracle, "
+                      f"{sum(times):.1f} s), {len(os.sched_getaffinity(0))} host cores visible"}
 
 
 def main():
@@ -139,25 +171,34 @@ def main():
     torch.cuda.synchronize()
     hot_us = h0.elapsed_time(h1) * 1e3 / 50
 
-    # dominant kernels: the routed-expert GEMMs (sd_moe_experts), timed live with HIP events
-    # on their launch stream, rotating over the copies like the step
+    # dominant kernels: the routed-expert GEMMs (sd_moe_experts: k_moe_w13 then k_moe_w2),
+    # timed live with HIP events on their launch stream, rotating over the copies like the
+    # step; their input is the attention boundary's expert-input form of the same rows
     d, b = wk["dims"], wk["workload"].b
-    y = torch.empty(b * d["top_k"], d["hidden"], dtype=torch.float32, device=dev)
-    x = [r.act["front_embed"] for r in runners]
+    H = d["hidden"]
+    y = torch.empty(b * d["top_k"], H, dtype=torch.float32, device=dev)
+    x = []
+    for r in runners:
+        x16 = torch.empty(2, b, H, dtype=torch.float16, device=dev)
+        hb = torch.empty(b, H, dtype=torch.bfloat16, device=dev)
+        sb = r.act["stream"].clone()
+        B.boundary_dualnorm(r.dims, b, sb, r.act["branch_in"], None, r.layers[0].t["g_post_prev"],
+                            r.layers[0].t["g_pre_ffn"], hb, out16=x16)
+        x.append(x16)
+    torch.cuda.synchronize()
     n_it = args.roofline_iters
-    e0 = [torch.cuda.Event(enable_timing=True) for _ in range(n_it)]
-    e1 = [torch.cuda.Event(enable_timing=True) for _ in range(n_it)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(st):
         for i in range(10):
             r = runners[i % R]
             B.moe_experts(r.dims, b, x[i % R], r.layers[0].moe_w, r.route, y, None, r.ws, stream=st)
+        e0.record(st)
         for i in range(n_it):
             r = runners[i % R]
-            e0[i].record(st)
             B.moe_experts(r.dims, b, x[i % R], r.layers[0].moe_w, r.route, y, None, r.ws, stream=st)
-            e1[i].record(st)
+        e1.record(st)
     torch.cuda.synchronize()
-    exp_us = float(np.mean([e0[i].elapsed_time(e1[i]) for i in range(n_it)])) * 1e3
+    exp_us = e0.elapsed_time(e1) * 1e3 / n_it      # average per launch, back to back
     achieved = expert_bytes / (exp_us * 1e-6) / 1e9
 
     out = {
@@ -184,9 +225,11 @@ def main():
         "tokens_per_s": round(b * 1e6 / us, 1),
         "us_p10_p50_p90": [round(float(np.percentile(per, q)), 3) for q in (10, 50, 90)],
         "hot_cache_us": round(hot_us, 3),
-        "roofline": {"bound": "hbm", "kernel": "routed-expert GEMMs (sd_moe_experts)",
+        "roofline": {"bound": "hbm",
+                     "kernel": "routed-expert GEMMs (sd_moe_experts: k_moe_w13 + k_moe_w2)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(args.workload),
                      "launch_us": round(exp_us, 3), "bytes_per_launch": int(expert_bytes)},
     }
     if not args.no_cpu_baseline:

@@ -164,13 +164,15 @@ size_t sd_workspace_bytes(const sd_dims *dims, int32_t b, int32_t n_req, int32_t
 /* Input boundary / front / final boundary ([DEC] module docstring: the first layer's front,
  * the input boundary's dual norm, the final boundary; order from [DSP]
  * MuseSparkDSparkDecoderLayer.forward).  stream fp32 [b, H] in/out.
- *   branch != NULL: stream += RMSNorm(branch; g_post); out = bf16(RMSNorm(stream; g_pre)).
- *   branch == NULL (front): stream = front_embed; out = bf16(RMSNorm(stream; g_pre)).
+ *   branch != NULL: stream += RMSNorm(branch; g_post); y = RMSNorm(stream; g_pre).
+ *   branch == NULL (front): stream = front_embed; y = RMSNorm(stream; g_pre).
  * branch fp32 [b, H] (the branches between blocks are fp32); front_embed bf16 [b, H];
- * gains fp32 [H]; out bf16 [b, H] (e.g. the final hidden cast for the draft head). */
+ * gains fp32 [H]; out bf16 [b, H] = bf16(y) (e.g. the final hidden cast for the draft
+ * head); out16 (may be NULL) fp16 [2, b, H] = the expert-input form of y: hi terms, then
+ * lo terms, of y * 2^-8 (y * 2^-8 ~ hi + lo to about 2^-22 relative). */
 int sd_boundary_dualnorm(const sd_dims *dims, int32_t b, float *stream, const float *branch,
                          const void *front_embed, const float *g_post, const float *g_pre,
-                         void *out, void *stream_handle);
+                         void *out, void *out16, void *stream_handle);
 
 /* Attention of one layer ([DEC] module docstring: QKV front -> attn2 -> o_proj):
  * stacked QKV projection of x (bf16 [b, H]); weightless per-head RMSNorm of q and k when
@@ -191,10 +193,11 @@ int sd_moe_route(const sd_dims *dims, int32_t b, const void *x, const void *w_ro
 /* Routed experts over pooled slots ([DEC] module docstring: routed experts; [RT] module
  * list: NVFP4 routed experts): for slot s = (row t, expert e), y[s] = W2_e * h[s] with
  * h[s] = silu(g) * u and [g | u] = W13_e * x[t], weights dequantised exactly, fp32
- * accumulation, h kept at near-fp32 precision between the two GEMMs.  x bf16 [b, H];
- * route as produced by sd_moe_route; y_slots fp32 [b * k, H]; h_slots (may be NULL)
- * receives bf16(h) [b * k, I]. */
-int sd_moe_experts(const sd_dims *dims, int32_t b, const void *x, const sd_moe_weights *w,
+ * accumulation, h kept at near-fp32 precision between the two GEMMs.  x16 fp16 [2, b, H]:
+ * the expert input x as sd_boundary_dualnorm's out16 gives it (hi terms, then lo terms, of
+ * x * 2^-8); route as produced by sd_moe_route; y_slots fp32 [b * k, H]; h_slots (may be
+ * NULL) receives bf16(h) [b * k, I]. */
+int sd_moe_experts(const sd_dims *dims, int32_t b, const void *x16, const sd_moe_weights *w,
                    const sd_route *route, void *y_slots, void *h_slots, void *ws,
                    size_t ws_bytes, void *stream_handle);
 

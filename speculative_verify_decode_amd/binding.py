@@ -59,7 +59,7 @@ SYMBOLS = {
                             c_void_p]),
     "sd_workspace_bytes": (c_size_t, [ctypes.POINTER(SdDims), c_int, c_int, c_int]),
     "sd_boundary_dualnorm": (c_int, [ctypes.POINTER(SdDims), c_int, c_void_p, c_void_p, c_void_p,
-                                     c_void_p, c_void_p, c_void_p, c_void_p]),
+                                     c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "sd_attn_verify": (c_int, [ctypes.POINTER(SdDims), c_int, c_void_p,
                                ctypes.POINTER(SdAttnWeights), ctypes.POINTER(SdKv), c_void_p,
                                c_void_p, c_size_t, c_void_p]),
@@ -195,10 +195,11 @@ def workspace_bytes(dims, b, n_req, max_seq_len):
     return lib().sd_workspace_bytes(ctypes.byref(dims), b, n_req, max_seq_len)
 
 
-def boundary_dualnorm(dims, b, stream_buf, branch, front_embed, g_post, g_pre, out, stream=None):
+def boundary_dualnorm(dims, b, stream_buf, branch, front_embed, g_post, g_pre, out, stream=None,
+                      out16=None):
     _check(lib().sd_boundary_dualnorm(ctypes.byref(dims), b, ptr(stream_buf), ptr(branch),
                                       ptr(front_embed), ptr(g_post), ptr(g_pre), ptr(out),
-                                      cur_stream(stream)))
+                                      ptr(out16), cur_stream(stream)))
 
 
 def attn_verify(dims, b, x, attn_w, kv, out, ws, stream=None):
@@ -213,8 +214,8 @@ def moe_route(dims, b, x, w_router, logit_bias, route, logits_out, ws, stream=No
                               ws.numel() * ws.element_size(), cur_stream(stream)))
 
 
-def moe_experts(dims, b, x, moe_w, route, y_slots, h_slots, ws, stream=None):
-    _check(lib().sd_moe_experts(ctypes.byref(dims), b, ptr(x), ctypes.byref(moe_w),
+def moe_experts(dims, b, x16, moe_w, route, y_slots, h_slots, ws, stream=None):
+    _check(lib().sd_moe_experts(ctypes.byref(dims), b, ptr(x16), ctypes.byref(moe_w),
                                 ctypes.byref(route), ptr(y_slots), ptr(h_slots), ptr(ws),
                                 ws.numel() * ws.element_size(), cur_stream(stream)))
 

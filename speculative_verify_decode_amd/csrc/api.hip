@@ -352,17 +352,21 @@ size_t sd_workspace_bytes(const sd_dims* dims, int32_t b, int32_t n_req, int32_t
 
 int sd_boundary_dualnorm(const sd_dims* dims, int32_t b, float* stream, const float* branch,
                          const void* front_embed, const float* g_post, const float* g_pre,
-                         void* out, void* stream_handle) {
+                         void* out, void* out16, void* stream_handle) {
   SD_CHECK(check_dims(dims));
   SD_CHECK(check_rows(dims, b));
   if (!stream || !out || !g_pre) return fail(SD_EINVAL, "stream, out or g_pre is null");
   if (branch == nullptr && front_embed == nullptr)
     return fail(SD_EINVAL, "front mode needs front_embed");
   if (branch != nullptr && g_post == nullptr) return fail(SD_EINVAL, "g_post is null");
-  if (branch != nullptr && !aligned16(branch)) return fail(SD_EINVAL, "branch misaligned");
+  if (!aligned16(stream) || (branch != nullptr && !aligned16(branch)) || !aligned16(g_pre) ||
+      (g_post != nullptr && !aligned16(g_post)) || (out16 != nullptr && !aligned16(out16)))
+    return fail(SD_EINVAL, "stream, branch, gains and out16 must be 16-byte aligned");
+  _Float16* x16 = (_Float16*)out16;
   SD_LAUNCH(launch_dualnorm(b, dims->hidden, stream, (const float*)branch,
                             (const uint16_t*)front_embed, g_post, g_pre, dims->eps,
-                            (uint16_t*)out, nullptr, nullptr, nullptr, nullptr,
+                            (uint16_t*)out, nullptr, x16,
+                            x16 ? x16 + (size_t)b * dims->hidden : nullptr, nullptr,
                             (hipStream_t)stream_handle),
             "dual norm");
   return ok();
@@ -401,24 +405,22 @@ int sd_moe_route(const sd_dims* dims, int32_t b, const void* x, const void* w_ro
   return ok();
 }
 
-int sd_moe_experts(const sd_dims* dims, int32_t b, const void* x, const sd_moe_weights* w,
+int sd_moe_experts(const sd_dims* dims, int32_t b, const void* x16, const sd_moe_weights* w,
                    const sd_route* route, void* y_slots, void* h_slots, void* ws,
                    size_t ws_bytes, void* stream_handle) {
   SD_CHECK(check_dims(dims));
   SD_CHECK(check_rows(dims, b));
   SD_CHECK(check_moe_weights(w, false, true));
   SD_CHECK(check_route(route));
-  if (!x || !y_slots) return fail(SD_EINVAL, "x or y_slots is null");
-  if (!aligned16(y_slots) || (h_slots && !aligned16(h_slots)))
-    return fail(SD_EINVAL, "y_slots / h_slots must be 16-byte aligned");
+  if (!x16 || !y_slots) return fail(SD_EINVAL, "x16 or y_slots is null");
+  if (!aligned16(x16) || !aligned16(y_slots) || (h_slots && !aligned16(h_slots)))
+    return fail(SD_EINVAL, "x16, y_slots and h_slots must be 16-byte aligned");
   SD_CHECK(check_ws(dims, b, b / dims->q_rows, dims->q_rows, ws, ws_bytes));
   const Ws L = ws_layout(*dims, b, b / dims->q_rows, dims->q_rows);
-  hipStream_t st = (hipStream_t)stream_handle;
-  _Float16* x16 = at<_Float16>(ws, L.x16);
-  // a bf16 input is exact as one fp16 term (no lo term)
-  SD_LAUNCH(launch_to_f16(b * dims->hidden, (const uint16_t*)x, x16, st), "expert input");
-  SD_CHECK(run_experts(dims, b, x16, nullptr, w, route, (float*)y_slots, (uint16_t*)h_slots,
-                       at<_Float16>(ws, L.h16), at<_Float16>(ws, L.h16_lo), st));
+  const _Float16* hi = (const _Float16*)x16;
+  SD_CHECK(run_experts(dims, b, hi, hi + (size_t)b * dims->hidden, w, route, (float*)y_slots,
+                       (uint16_t*)h_slots, at<_Float16>(ws, L.h16), at<_Float16>(ws, L.h16_lo),
+                       (hipStream_t)stream_handle));
   return ok();
 }
 

@@ -91,13 +91,13 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a, int cb, int n_ch
       const int pb = (tw >> 4) ? pb1 : pb0;
       const uint16_t* kp = a.k_cache + ((size_t)pb * a.Hkv + g) * kvh + (size_t)(tw & 15) * D + G * DL;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) W.k[t][c] = __builtin_nontemporal_load((const bf16x8_t*)(kp + 8 * c));
+      for (int c = 0; c < NC; ++c) W.k[t][c] = *(const bf16x8_t*)(kp + 8 * c);
     }
     // V^T rows: dim 16 dt + i, window tokens 8G .. 8G+7
     const int pb = (G >> 1) ? pb1 : pb0;
     const uint16_t* vp = a.v_cache + ((size_t)pb * a.Hkv + g) * kvh + (size_t)i * 16 + 8 * (G & 1);
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) W.v[dt] = __builtin_nontemporal_load((const bf16x8_t*)(vp + (size_t)dt * 256));
+    for (int dt = 0; dt < NDT; ++dt) W.v[dt] = *(const bf16x8_t*)(vp + (size_t)dt * 256);
   };
 
   float mrun[NQT], lsum[NQT];
@@ -175,17 +175,19 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a, int cb, int n_ch
     }
   };
 
+  // two-deep pipeline; the prefetch past a wave's last window re-reads that window (an L2
+  // hit) instead of branching, so each wait covers exactly the window it uses
   Win W0, W1;
   int wb = blk_begin + 2 * wave;
   if (wb < blk_end) {
     load_win(W0, wb);
     while (true) {
       const int w1 = wb + 8;
-      if (w1 < blk_end) load_win(W1, w1);
+      load_win(W1, w1 < blk_end ? w1 : wb);
       compute(W0, wb);
       if (w1 >= blk_end) break;
       const int w2 = w1 + 8;
-      if (w2 < blk_end) load_win(W0, w2);
+      load_win(W0, w2 < blk_end ? w2 : w1);
       compute(W1, w1);
       if (w2 >= blk_end) break;
       wb = w2;

@@ -115,11 +115,15 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_res(GemmArgs a, int ntiles) {
 #pragma unroll
   for (int u = 0; u < S; ++u) bv[u] = load_b<SPLIT>(rh, rl, oh + 64 * u, ol + 64 * u);
 
+  // weights through a buffer resource: a tile index past the last loads zeros without a
+  // memory access, so the prefetch of a missing next tile needs no branch and every wait
+  // before a tile's MFMAs covers exactly that tile
+  const auto rw = rsrc(a.w, (uint32_t)((size_t)ntiles * KT * 1024));
   bf16x8_t A0[S], A1[S];
   auto load = [&](bf16x8_t (&A)[S], int tile) {
-    const uint16_t* wt = a.w + ((size_t)tile * KT + kt0) * 512 + lane * 8;
+    const uint32_t o0 = tile < ntiles ? (uint32_t)(((size_t)tile * KT + kt0) * 1024 + lane * 16) : kOob;
 #pragma unroll
-    for (int u = 0; u < S; ++u) A[u] = __builtin_nontemporal_load((const bf16x8_t*)(wt + 512 * u));
+    for (int u = 0; u < S; ++u) A[u] = buf_load8(rw, o0 + 1024 * u);
   };
   auto finish = [&](bf16x8_t (&A)[S], int tile, int buf) {
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -141,11 +145,11 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_res(GemmArgs a, int ntiles) {
   load(A0, t);
   while (true) {
     const int t1 = t + gridDim.x;
-    if (t1 < ntiles) load(A1, t1);
+    load(A1, t1);
     finish(A0, t, 0);
     if (t1 >= ntiles) break;
     const int t2 = t1 + gridDim.x;
-    if (t2 < ntiles) load(A0, t2);
+    load(A0, t2);
     finish(A1, t1, 1);
     if (t2 >= ntiles) break;
     t = t2;
@@ -238,6 +242,7 @@ template <int NW, int MODE, bool SPLIT>
 bool try_res(const GemmArgs& a, int ntiles, hipStream_t st) {
   const int KT = a.K / 32;
   if (KT % NW) return false;
+  if ((size_t)ntiles * KT * 1024 >= 0x80000000u) return false;  // buffer offsets are 32-bit
   const int grid = min(ntiles, cu_count());
   const dim3 block(64 * NW);
   switch (KT / NW) {

@@ -28,14 +28,16 @@ __device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t
 // Phase 1, every workgroup: partial logits of one 16-expert tile over 256 columns of H
 // (4 waves x 2 MFMA steps; rows as bf16 hi/lo terms in columns 0-7 / 8-15 of NCT tiles),
 // written to part[ks, t, e].  Phase 2, the last workgroup to arrive: z = sum over ks in
-// order + bias; top-k per row by (-z, index) with one wave per row; weights = softmax
-// over the selected logits; pooler = stable counting sort of (row, choice) by expert,
+// order + bias; top-k per row by (-z, index), each (row, expert) finding its own rank;
+// weights = softmax over the selected logits; pooler = stable counting sort of (row,
+// choice) by expert,
 // through per-expert row bitmasks (a row picks an expert at most once, so an entry's
 // rank within its expert is the number of earlier rows in the expert's mask).
 template <int NCT>
 __global__ __launch_bounds__(256) void k_router(RouterArgs a) {
   __shared__ f32x4_t red[3][NCT][64];
-  __shared__ float s_z[64 * 256];
+  __shared__ uint32_t s_key[64 * 256];
+  __shared__ float s_sel[512];
   __shared__ int s_last;
   __shared__ int s_ids[512];
   __shared__ uint32_t s_mlo[256], s_mhi[256];
@@ -108,7 +110,8 @@ __global__ __launch_bounds__(256) void k_router(RouterArgs a) {
   if (!s_last) return;
 
   const int b = a.b, E = a.E, k = a.k;
-  // z = sum over ks in order + bias, every (row, expert) at once: one round of loads
+  // z = sum over ks in order + bias, every (row, expert) at once: one round of loads.  The
+  // LDS copy is an order key: larger key = earlier in (-z, index) order, NaN last.
   const size_t st = (size_t)b * E;
   for (int idx = tid; idx < b * E; idx += 256) {
     float z = 0.f;
@@ -116,51 +119,36 @@ __global__ __launch_bounds__(256) void k_router(RouterArgs a) {
     for (int j = 0; j < KS; ++j) z += a.part[j * st + idx];
     if (a.bias != nullptr) z += a.bias[idx];
     if (a.logits != nullptr) a.logits[idx] = z;
-    s_z[idx] = z != z ? -INFINITY : z;  // NaN ranks with -inf
+    const uint32_t u = __float_as_uint(z == 0.f ? 0.f : z);  // -0 ties with +0
+    s_key[idx] = z != z ? 0u : (u & 0x80000000u ? ~u : u | 0x80000000u);
   }
   __syncthreads();
-  for (int t = wave; t < b; t += 4) {
-    float v[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = lane + 64 * q;
-      v[q] = e < E ? s_z[t * E + e] : -INFINITY;
+  // top-k by rank: (t, e) is choice number rank(t, e) if that is < k, where rank counts the
+  // experts of row t ordered before e (larger key, or equal key and lower index)
+  for (int p = tid; p < b * E; p += 256) {
+    const int t = p / E, e = p - t * E;
+    const uint32_t* kr = s_key + t * E;
+    const uint32_t ke = kr[e];
+    int rank = 0;
+    for (int j = 0; j < E; ++j) {
+      const uint32_t kj = kr[j];
+      rank += (kj > ke || (kj == ke && j < e)) ? 1 : 0;
     }
-    int taken = 0;
-    float sel[8];
-    int sid[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j >= k) break;
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int e = lane + 64 * q;
-        if (e < E && !((taken >> q) & 1) && (v[q] > bv || (v[q] == bv && e < bi))) {
-          bv = v[q];
-          bi = e;
-        }
-      }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, 64);
-        const int oi = __shfl_xor(bi, o, 64);
-        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-      }
-      if ((bi & 63) == lane) taken |= 1 << (bi >> 6);
-      sel[j] = bv;
-      sid[j] = bi;
+    if (rank < k) {  // the logit back from its key (key 0: NaN)
+      s_ids[t * k + rank] = e;
+      s_sel[t * k + rank] = ke == 0u ? __uint_as_float(0x7fc00000u)
+                                     : __uint_as_float(ke & 0x80000000u ? ke & 0x7fffffffu : ~ke);
     }
-    if (lane == 0) {
-      float den = 0.f;
-      for (int j = 0; j < k; ++j) den += expf(sel[j] - sel[0]);
-      for (int j = 0; j < k; ++j) {
-        a.ids[t * k + j] = sid[j];
-        a.w_out[t * k + j] = expf(sel[j] - sel[0]) / den;
-        s_ids[t * k + j] = sid[j];
-      }
-    }
+  }
+  __syncthreads();
+  // weights: softmax over the k selected logits of the row
+  for (int p = tid; p < b * k; p += 256) {
+    const int t = p / k;
+    const float m = s_sel[t * k];
+    float den = 0.f;
+    for (int j = 0; j < k; ++j) den += expf(s_sel[t * k + j] - m);
+    a.ids[p] = s_ids[p];
+    a.w_out[p] = expf(s_sel[p] - m) / den;
   }
   if (tid < E) s_mlo[tid] = s_mhi[tid] = 0u;
   __syncthreads();
@@ -249,34 +237,44 @@ struct Slice {
   uint32_t scales[NU];
 };
 
-// The wave's NU consecutive tiles starting at packed tile index `tile0`.
+// Packed weights of one expert as buffer resources (codes, scales).
+struct ExpertRes {
+  __amdgpu_buffer_rsrc_t c, s;
+};
+
+__device__ __forceinline__ ExpertRes expert_res(const uint8_t* codes, const uint8_t* scales,
+                                                size_t code_bytes, int e) {
+  ExpertRes r;
+  r.c = rsrc(codes + (size_t)e * code_bytes, (uint32_t)code_bytes);
+  r.s = rsrc(scales + (size_t)e * (code_bytes / 8), (uint32_t)(code_bytes / 8));
+  return r;
+}
+
+// The wave's NU consecutive tiles from tile index `t0` of the expert; t0 < 0 loads zeros
+// without touching memory (a prefetch past the last unit), so the load count never
+// depends on a branch and every wait stays exact.
 template <int NU>
-__device__ __forceinline__ void load_slice(Slice<NU>& s, const uint8_t* codes,
-                                           const uint8_t* scales, size_t tile0, int lane) {
-  const uint8_t* cp = codes + tile0 * 1024 + 16 * lane;
-  const uint8_t* sp = scales + tile0 * 128 + 2 * lane;
+__device__ __forceinline__ void load_slice(Slice<NU>& s, const ExpertRes& r, int t0, int lane) {
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
-    s.codes[u] = __builtin_nontemporal_load((const u32x4_t*)(cp + 1024 * u));
-    s.scales[u] = *(const uint16_t*)(sp + 128 * u);
+    const uint32_t oc = t0 < 0 ? kOob : (uint32_t)(t0 + u) * 1024u + 16u * lane;
+    const uint32_t os = t0 < 0 ? kOob : (uint32_t)(t0 + u) * 128u + 2u * lane;
+    s.codes[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r.c, oc, 0, 0));
+    s.scales[u] = __builtin_amdgcn_raw_buffer_load_b16(r.s, os, 0, 0);
   }
 }
 
-// B operand: f16x8 m of tile u at byte offset off + (128u + 8m) * 2 of the hi (lanes with
-// off_h in range) or lo buffer (off_l); the other buffer's offset is out of range.
+// B operand: f16x8 m of tile u at byte offset off + (128u + 8m) * 2 of one buffer that
+// holds the hi terms and, lo_off bytes further, the lo terms (each lane's offset picks).
 template <int NU>
-__device__ __forceinline__ void load_bx(f16x8_t (&bx)[NU][4], __amdgpu_buffer_rsrc_t rh,
-                                        __amdgpu_buffer_rsrc_t rl, uint32_t off_h,
-                                        uint32_t off_l) {
+__device__ __forceinline__ void load_bx(f16x8_t (&bx)[NU][4], __amdgpu_buffer_rsrc_t r,
+                                        uint32_t off) {
 #pragma unroll
   for (int u = 0; u < NU; ++u)
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const uint32_t d = (uint32_t)(128 * u + 8 * m) * 2;
-      const u32x4_t h = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rh, off_h + d, 0, 0));
-      const u32x4_t l = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rl, off_l + d, 0, 0));
-      bx[u][m] = __builtin_bit_cast(f16x8_t, h | l);
-    }
+    for (int m = 0; m < 4; ++m)
+      bx[u][m] = __builtin_bit_cast(
+          f16x8_t, __builtin_amdgcn_raw_buffer_load_b128(r, off + (uint32_t)(128 * u + 8 * m) * 2, 0, 0));
 }
 
 struct Unit {
@@ -315,30 +313,26 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w13(MoeArgs a) {
   const int i = lane & 15, G = lane >> 4;
   const bool lo = (i >> 3) != 0;
   const int K = a.H, KT = K >> 7, kw = wave * NU;
-  const int NT2 = 2 * NT;
+  const size_t code_bytes = (size_t)a.I * K;  // 2I rows x K/2 bytes per expert
+  // hi terms at x16, lo terms x16_lo_off bytes further in the same buffer (or none)
   const uint32_t xbytes = (uint32_t)(a.b * K * 2);
-  const auto rh = rsrc(a.x16, xbytes);
-  const auto rl = rsrc(a.x16_lo != nullptr ? a.x16_lo : a.x16, a.x16_lo != nullptr ? xbytes : 0);
+  const auto rx = rsrc(a.x16, a.x16_lo_off + xbytes);
 
-  // lane's B offsets for column tile c of unit U (hi and lo buffers)
-  auto b_off = [&](const Unit& U, int c, uint32_t& oh, uint32_t& ol) {
+  // lane's B byte offset for column tile c of unit U
+  auto b_off = [&](const Unit& U, int c) -> uint32_t {
     const int slot = 8 * c + (i & 7);
-    const uint32_t o = slot < U.Te
-                           ? (uint32_t)(((size_t)meta.tos[U.off + slot] * K + kw * 128 + 32 * G) * 2)
-                           : kOob;
-    oh = lo ? kOob : o;
-    ol = lo ? o : kOob;
+    if (slot >= U.Te || (lo && a.x16_lo_off == 0)) return kOob;
+    return (lo ? a.x16_lo_off : 0u) +
+           (uint32_t)(((size_t)meta.tos[U.off + slot] * K + kw * 128 + 32 * G) * 2);
   };
-  auto load_a = [&](Slice<NU>& sg, Slice<NU>& su, const Unit& U) {
-    const size_t t0 = ((size_t)U.e * NT2 + U.nt) * KT + kw;
-    load_slice<NU>(sg, a.w13_codes, a.w13_scales, t0, lane);
-    load_slice<NU>(su, a.w13_codes, a.w13_scales, t0 + (size_t)NT * KT, lane);
+  // weights of unit U (valid == false: zeros, no memory traffic)
+  auto load_a = [&](Slice<NU>& sg, Slice<NU>& su, const Unit& U, bool valid) {
+    const ExpertRes r = expert_res(a.w13_codes, a.w13_scales, code_bytes, U.e);
+    const int t0 = U.nt * KT + kw;
+    load_slice<NU>(sg, r, valid ? t0 : -1, lane);
+    load_slice<NU>(su, r, valid ? t0 + NT * KT : -1, lane);
   };
-  auto load_b0 = [&](f16x8_t (&bx)[NU][4], const Unit& U) {
-    uint32_t oh, ol;
-    b_off(U, 0, oh, ol);
-    load_bx<NU>(bx, rh, rl, oh, ol);
-  };
+  auto load_b0 = [&](f16x8_t (&bx)[NU][4], const Unit& U) { load_bx<NU>(bx, rx, b_off(U, 0)); };
   auto compute = [&](const Slice<NU>& sg, const Slice<NU>& su, f16x8_t (&bx0)[NU][4],
                      const Unit& U, int buf) {
     f32x4_t ag[NCT], au[NCT];
@@ -349,11 +343,7 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w13(MoeArgs a) {
     for (int c = 0; c < NCT; ++c) {
       if (c >= nct) break;
       f16x8_t bl[NU][4];
-      if (!PB) {
-        uint32_t oh, ol;
-        b_off(U, c, oh, ol);
-        load_bx<NU>(bl, rh, rl, oh, ol);
-      }
+      if (!PB) load_bx<NU>(bl, rx, b_off(U, c));
       f16x8_t (&bx)[NU][4] = PB ? bx0 : bl;
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
@@ -429,23 +419,27 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w13(MoeArgs a) {
   if constexpr (!PB) {  // several column tiles: their accumulators leave no room to prefetch
     for (; u < end; ++u) {
       const Unit U = unit_of(meta, u, NT);
-      load_a(g0, u0, U);
+      load_a(g0, u0, U, true);
       compute(g0, u0, bx, U, 0);
     }
     return;
   }
+  // two-deep pipeline: every load is unconditional (a missing next unit loads zeros from
+  // no memory), so the wait before each compute covers exactly the unit it uses
   Unit U0 = unit_of(meta, u, NT), U1;
   int be = -1;  // expert whose activations are in bx
-  load_a(g0, u0, U0);
+  load_a(g0, u0, U0, true);
   while (true) {
     if (PB && U0.e != be) { load_b0(bx, U0); be = U0.e; }
     const int n1 = u + 1;
-    if (n1 < end) { U1 = unit_of(meta, n1, NT); load_a(g1, u1, U1); }
+    U1 = unit_of(meta, min(n1, end - 1), NT);
+    load_a(g1, u1, U1, n1 < end);
     compute(g0, u0, bx, U0, 0);
     if (n1 >= end) break;
     if (PB && U1.e != be) { load_b0(bx, U1); be = U1.e; }
     const int n2 = n1 + 1;
-    if (n2 < end) { U0 = unit_of(meta, n2, NT); load_a(g0, u0, U0); }
+    U0 = unit_of(meta, min(n2, end - 1), NT);
+    load_a(g0, u0, U0, n2 < end);
     compute(g1, u1, bx, U1, PB ? 1 : 0);
     if (n2 >= end) break;
     u = n2;
@@ -467,25 +461,21 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w2(MoeArgs a) {
   const int i = lane & 15, G = lane >> 4;
   const bool lo = (i >> 3) != 0;
   const int K = a.I, KT = K >> 7, kw = wave * NU;
+  const size_t code_bytes = (size_t)a.H * K / 2;
+  // hi terms at h16, lo terms h16_lo_off bytes further in the same buffer
   const uint32_t hbytes = (uint32_t)(a.b * a.k * K * 2);
-  const auto rh = rsrc(a.h16, hbytes);
-  const auto rl = rsrc(a.h16_lo, hbytes);
+  const auto rx = rsrc(a.h16, a.h16_lo_off + hbytes);
 
-  auto b_off = [&](const Unit& U, int c, uint32_t& oh, uint32_t& ol) {
+  auto b_off = [&](const Unit& U, int c) -> uint32_t {
     const int slot = 8 * c + (i & 7);
-    const uint32_t o =
-        slot < U.Te ? (uint32_t)(((size_t)(U.off + slot) * K + kw * 128 + 32 * G) * 2) : kOob;
-    oh = lo ? kOob : o;
-    ol = lo ? o : kOob;
+    if (slot >= U.Te) return kOob;
+    return (lo ? a.h16_lo_off : 0u) + (uint32_t)(((size_t)(U.off + slot) * K + kw * 128 + 32 * G) * 2);
   };
-  auto load_a = [&](Slice<NU>& sw, const Unit& U) {
-    load_slice<NU>(sw, a.w2_codes, a.w2_scales, ((size_t)U.e * NT + U.nt) * KT + kw, lane);
+  auto load_a = [&](Slice<NU>& sw, const Unit& U, bool valid) {
+    const ExpertRes r = expert_res(a.w2_codes, a.w2_scales, code_bytes, U.e);
+    load_slice<NU>(sw, r, valid ? U.nt * KT + kw : -1, lane);
   };
-  auto load_b0 = [&](f16x8_t (&bx)[NU][4], const Unit& U) {
-    uint32_t oh, ol;
-    b_off(U, 0, oh, ol);
-    load_bx<NU>(bx, rh, rl, oh, ol);
-  };
+  auto load_b0 = [&](f16x8_t (&bx)[NU][4], const Unit& U) { load_bx<NU>(bx, rx, b_off(U, 0)); };
   auto compute = [&](const Slice<NU>& sw, f16x8_t (&bx0)[NU][4], const Unit& U, int buf) {
     f32x4_t acc[NCT];
 #pragma unroll
@@ -495,11 +485,7 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w2(MoeArgs a) {
     for (int c = 0; c < NCT; ++c) {
       if (c >= nct) break;
       f16x8_t bl[NU][4];
-      if (!PB) {
-        uint32_t oh, ol;
-        b_off(U, c, oh, ol);
-        load_bx<NU>(bl, rh, rl, oh, ol);
-      }
+      if (!PB) load_bx<NU>(bl, rx, b_off(U, c));
       f16x8_t (&bx)[NU][4] = PB ? bx0 : bl;
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
@@ -547,23 +533,25 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w2(MoeArgs a) {
   if constexpr (!PB) {
     for (; u < end; ++u) {
       const Unit U = unit_of(meta, u, NT);
-      load_a(w0, U);
+      load_a(w0, U, true);
       compute(w0, bx, U, 0);
     }
     return;
   }
   Unit U0 = unit_of(meta, u, NT), U1;
   int be = -1;
-  load_a(w0, U0);
+  load_a(w0, U0, true);
   while (true) {
     if (PB && U0.e != be) { load_b0(bx, U0); be = U0.e; }
     const int n1 = u + 1;
-    if (n1 < end) { U1 = unit_of(meta, n1, NT); load_a(w1, U1); }
+    U1 = unit_of(meta, min(n1, end - 1), NT);
+    load_a(w1, U1, n1 < end);
     compute(w0, bx, U0, 0);
     if (n1 >= end) break;
     if (PB && U1.e != be) { load_b0(bx, U1); be = U1.e; }
     const int n2 = n1 + 1;
-    if (n2 < end) { U0 = unit_of(meta, n2, NT); load_a(w0, U0); }
+    U0 = unit_of(meta, min(n2, end - 1), NT);
+    load_a(w0, U0, n2 < end);
     compute(w1, bx, U1, PB ? 1 : 0);
     if (n2 >= end) break;
     u = n2;
@@ -681,7 +669,20 @@ hipError_t launch_zero_i32(int* p, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_moe_experts(const MoeArgs& a, hipStream_t st) {
+hipError_t launch_moe_experts(const MoeArgs& in, hipStream_t st) {
+  MoeArgs a = in;
+  const size_t xb = (size_t)a.b * a.H * 2, hb = (size_t)a.b * a.k * a.I * 2;
+  // lo terms must follow the hi terms in one buffer (the workspace lays them out so)
+  if (a.x16_lo != nullptr) {
+    if (a.x16_lo < a.x16 + (size_t)a.b * a.H || (size_t)((const char*)a.x16_lo - (const char*)a.x16) + xb >= 0x80000000u)
+      return hipErrorInvalidValue;
+    a.x16_lo_off = (uint32_t)((const char*)a.x16_lo - (const char*)a.x16);
+  } else {
+    a.x16_lo_off = 0;
+  }
+  if (a.h16_lo < a.h16 + (size_t)a.b * a.k * a.I || (size_t)((const char*)a.h16_lo - (const char*)a.h16) + hb >= 0x80000000u)
+    return hipErrorInvalidValue;
+  a.h16_lo_off = (uint32_t)((const char*)a.h16_lo - (const char*)a.h16);
   // a token chooses an expert at most once, so an expert holds at most b pooled tokens;
   // b <= 8 fits one column tile, larger batches take up to 8 tiles (64 tokens)
   if (a.b <= 8) return launch_experts_nct<1>(a, st);

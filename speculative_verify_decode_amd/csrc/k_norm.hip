@@ -108,13 +108,6 @@ __global__ __launch_bounds__(256) void k_dualnorm(int H, float* __restrict__ str
   }
 }
 
-// bf16 -> fp16 hi term of x * 2^-8 (exact for |x| >= 2^-6, so no lo term is kept).
-__global__ __launch_bounds__(256) void k_to_f16(int n, const uint16_t* __restrict__ x,
-                                                _Float16* __restrict__ out) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < n) out[i] = (_Float16)(sd::bf2f(x[i]) * SD_X16_SCALE);
-}
-
 }  // namespace
 
 hipError_t launch_dualnorm(int b, int H, float* stream, const float* branch,
@@ -142,10 +135,5 @@ hipError_t launch_dualnorm(int b, int H, float* stream, const float* branch,
     default:
       return hipErrorInvalidValue;
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_to_f16(int n, const uint16_t* x, _Float16* out, hipStream_t st) {
-  hipLaunchKernelGGL(k_to_f16, dim3((n + 255) / 256), dim3(256), 0, st, n, x, out);
   return hipGetLastError();
 }

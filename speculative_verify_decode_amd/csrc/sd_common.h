@@ -205,7 +205,7 @@ hipError_t launch_zero_i32(int* p, hipStream_t st);
 struct MoeArgs {
   int b, H, I, E, k;
   const _Float16* x16;        // [b, H] hi terms of the expert input * 2^-8
-  const _Float16* x16_lo;     // [b, H] lo terms (may be null: the input is exact in fp16)
+  const _Float16* x16_lo;     // [b, H] lo terms after x16 in one buffer (null: exact in fp16)
   const uint8_t *w13_codes, *w13_scales;
   const float* w13_gscale;
   const uint8_t *w2_codes, *w2_scales;
@@ -213,17 +213,17 @@ struct MoeArgs {
   const int *counts, *offsets, *tos;
   const int* active;          // [E + 1]: active expert ids ascending, then their number
   _Float16* h16;              // [b*k, I] scratch: hi terms of the SwiGLU output * 2^-8
-  _Float16* h16_lo;           // [b*k, I] scratch: lo terms
+  _Float16* h16_lo;           // [b*k, I] scratch: lo terms, after h16 in one buffer
   uint16_t* h_bf16;           // [b*k, I] optional bf16 copy of the SwiGLU output
   float* y;                   // fp32 [b*k, H]
+  uint32_t x16_lo_off;        // set by the launcher: bytes from x16 to x16_lo (0: none)
+  uint32_t h16_lo_off;        // set by the launcher: bytes from h16 to h16_lo
 };
 hipError_t launch_moe_experts(const MoeArgs& a, hipStream_t st);
 bool moe_shape_supported(int H, int I);  // the expert GEMMs' K splits exist for H and I
 
 hipError_t launch_unpool(int b, int H, int k, const float* y, const float* w,
                          const int* slot_of, float* out, hipStream_t st);
-
-hipError_t launch_to_f16(int n, const uint16_t* x, _Float16* out, hipStream_t st);
 
 hipError_t launch_head_argmax(int b, int n_tiles, const float* val, const int* idx,
                               const int64_t* d2t, int32_t* ids, int64_t* target,

@@ -70,7 +70,7 @@ def test_workspace_bytes_host_only(lib):
 def _rc_dualnorm(d, b=8, stream=FAKE, branch=FAKE, front=None, g_post=FAKE, g_pre=FAKE, out=FAKE):
     L = B.lib()
     return L.sd_boundary_dualnorm(ctypes.byref(d) if d is not None else None, b, stream, branch,
-                                  front, g_post, g_pre, out, None)
+                                  front, g_post, g_pre, out, None, None)
 
 
 @pytest.mark.parametrize("kw,code,text", [

@@ -13,8 +13,8 @@ from oracle.formats import dequant_nvfp4
 from speculative_verify_decode_amd import binding as B
 from speculative_verify_decode_amd import synth
 from speculative_verify_decode_amd.runner import alloc_route
-from tests.gpu_util import (DEV, check_route_stage_a, head_flags, require_lib, runner, say,
-                            workload)
+from tests.gpu_util import (DEV, check_route_stage_a, expert_input, head_flags, require_lib,
+                            runner, say, workload)
 from tests.helpers import assert_close, np64
 
 pytestmark = pytest.mark.gpu
@@ -93,13 +93,18 @@ def test_boundary_dualnorm_modes(name):
     dims, b, H = B.make_dims(d), wk["workload"].b, d["hidden"]
     s = act["stream"].to(DEV).clone()
     out = torch.empty(b, H, dtype=torch.bfloat16, device=DEV)
+    out16 = torch.empty(2, b, H, dtype=torch.float16, device=DEV)
     gp, gq = lay["g_post_prev"].to(DEV), lay["g_pre_attn"].to(DEV)
-    B.boundary_dualnorm(dims, b, s, act["branch_in"].float().to(DEV), None, gp, gq, out)
+    B.boundary_dualnorm(dims, b, s, act["branch_in"].float().to(DEV), None, gp, gq, out,
+                        out16=out16)
     torch.cuda.synchronize()
     s_ref, x_ref = oracle.dual_norm(np64(act["stream"]), np64(act["branch_in"]), np64(lay["g_post_prev"]),
                                     np64(lay["g_pre_attn"]), d["eps"])
     assert_close(np64(s), s_ref, "stream")
     assert_close(np64(out), x_ref, "pre-norm output")
+    # the expert-input form: hi + lo = y * 2^-8 to fp32 accuracy
+    terms = np64(out16)
+    assert_close((terms[0] + terms[1]) * 256.0, x_ref, "expert-input terms", tol=1e-4)
     # front mode: the stream becomes the embedding
     B.boundary_dualnorm(dims, b, s, None, act["front_embed"].to(DEV), None, gq, out)
     torch.cuda.synchronize()
@@ -187,7 +192,7 @@ def test_moe_experts_and_unpool_match_oracle(name):
     B.moe_route(r.dims, b, x.to(DEV), r.layers[0].t["w_router"], r.act["logit_bias"], r.route, None, r.ws)
     y = torch.empty(b * k, H, dtype=torch.float32, device=DEV)
     h = torch.empty(b * k, I, dtype=torch.bfloat16, device=DEV)
-    B.moe_experts(r.dims, b, x.to(DEV), r.layers[0].moe_w, r.route, y, h, r.ws)
+    B.moe_experts(r.dims, b, expert_input(x).to(DEV), r.layers[0].moe_w, r.route, y, h, r.ws)
     m = torch.empty(b, H, dtype=torch.float32, device=DEV)
     B.moe_unpool(r.dims, b, y, r.route, m)
     torch.cuda.synchronize()
