@@ -6,7 +6,8 @@ A step is one whole layer step (input boundary -> attention -> attention boundar
 router/routing/pooler -> experts -> unpooler) of b = 8 verify rows at hidden 4096 with an
 8192-token paged context, replayed from a HIP graph.  Inputs are resident in HBM before the
 timed region.  To keep the 256 MB MALL and the L2s from serving repeat reads, steps rotate
-over R independent copies of the weights and KV (R * touched bytes >= 1 GB).  Prints one
+over R independent copies of the weights and KV (R * touched bytes >= 1 GB); one graph holds
+the R copies' steps back to back, as a serving graph holds consecutive layers.  Prints one
 JSON line.
 """
 
@@ -126,37 +127,49 @@ def main():
     print(f"[bench] {R} rotation copies, {step_bytes / 1e6:.1f} MB algorithmic per step",
           file=sys.stderr, flush=True)
 
-    # one captured graph per copy, on a side stream
+    # Graphs on a side stream: one graph holds the R copies' layer steps back to back (as a
+    # serving graph holds a model's consecutive layers), so replays rotate through the copies
+    # and no graph launch separates two steps inside it; K % R leftover steps replay
+    # single-step graphs.  Every replay step is a whole layer step.
     st = torch.cuda.Stream()
-    graphs, streams = [], []
-    for r in runners:
-        sb = r.act["stream"].clone()
-        streams.append(sb)
-        with torch.cuda.stream(st):
+    streams = [r.act["stream"].clone() for r in runners]
+    with torch.cuda.stream(st):
+        for r, sb in zip(runners, streams):
             r.layer_step(0, sb, r.act["branch_in"], stream=st)      # warm (lazy module load)
-        torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    g_all = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_all, stream=st):
+        for r, sb in zip(runners, streams):
+            r.layer_step(0, sb, r.act["branch_in"], stream=st)
+    singles = []
+    for r, sb in zip(runners, streams):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=st):
             r.layer_step(0, sb, r.act["branch_in"], stream=st)
-        graphs.append(g)
+        singles.append(g)
     torch.cuda.synchronize()
 
     with torch.cuda.stream(st):
-        for i in range(args.warmup):
-            graphs[i % R].replay()
+        for i in range(max(1, args.warmup // R)):
+            g_all.replay()
     torch.cuda.synchronize()
     K = args.steps
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    n_all, n_rest = K // R, K % R
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_all + n_rest + 1)]
     torch.cuda.synchronize()
     with torch.cuda.stream(st):
         ev[0].record(st)
-        for i in range(K):
-            graphs[i % R].replay()
+        for i in range(n_all):
+            g_all.replay()
             ev[i + 1].record(st)
+        for i in range(n_rest):
+            singles[i].replay()
+            ev[n_all + i + 1].record(st)
     torch.cuda.synchronize()
-    total_ms = ev[0].elapsed_time(ev[K])
-    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(K)]) * 1e3   # us
+    total_ms = ev[0].elapsed_time(ev[n_all + n_rest])
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) / R for i in range(n_all)]) * 1e3  # us per step
     us = total_ms * 1e3 / K
+    graphs = singles
 
     # hot-cache number (same copy every step), labelled separately
     with torch.cuda.stream(st):

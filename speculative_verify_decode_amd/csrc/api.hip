@@ -45,6 +45,9 @@ int hip_fail(hipError_t e, const char* what) {
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 constexpr int kMaxRows = 64;
+// K slices of the QKV and o_proj GEMMs inside a layer step: each writes this many fp32
+// partials, which their consumers (the QKV epilogue, the attention boundary) sum in order.
+constexpr int kDenseSplit = 4;
 
 bool norm_width_ok(int H) {
   if (H <= 0 || H % 256) return false;
@@ -100,8 +103,8 @@ int check_rows(const sd_dims* d, int b) {
 }
 
 struct Ws {
-  size_t x_a, x_a_lo, qkv, q, q_lo, part_acc, part_ml, o, o_lo, a, x_m, x_m_lo, x16, x16_lo,
-      zpart, counter, ids, w, counts, offsets, slot_of, tos, active, h16, h16_lo, y, total;
+  size_t x_a, x_a_lo, qkv, q, q_lo, gate, part_acc, part_ml, o, o_lo, a, x_m, x_m_lo, x16,
+      x16_lo, zpart, counter, ids, w, counts, offsets, slot_of, tos, active, h16, h16_lo, y, total;
 };
 
 size_t up(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -117,14 +120,15 @@ Ws ws_layout(const sd_dims& d, int b, int n_req, int max_seq_len) {
   auto take = [&](size_t bytes) { size_t at = o; o += up(bytes); return at; };
   w.x_a = take(B * H * 2);
   w.x_a_lo = take(B * H * 2);
-  w.qkv = take(B * N * 4);
+  w.qkv = take(kDenseSplit * B * N * 4);
   w.q = take(B * Hq * D * 2);
   w.q_lo = take(B * Hq * D * 2);
+  w.gate = take(B * Hq * D * 4);
   w.part_acc = take(parts * p.qg * D * 4);
   w.part_ml = take(parts * p.qg * 2 * 4);
   w.o = take(B * Hq * D * 2);
   w.o_lo = take(B * Hq * D * 2);
-  w.a = take(B * H * 4);
+  w.a = take(kDenseSplit * B * H * 4);
   w.x_m = take(B * H * 2);
   w.x_m_lo = take(B * H * 2);
   w.x16 = take(B * H * 2);
@@ -190,22 +194,27 @@ float scale_of(const sd_dims* d) {
   } while (0)
 
 // ---- launch sequences (validated arguments only) ----
-// x (bf16 hi terms) and x_lo (bf16 lo terms, may be null) -> out fp32 [b, H].
+// x (bf16 hi terms) and x_lo (bf16 lo terms after x in one buffer, may be null) -> out fp32
+// [out_parts, b, H]: out_parts = 1 gives the attention output itself; more leaves K-slice
+// partials of o_proj for a consumer that sums them.  Returns the partial count used.
 int run_attention(const sd_dims* d, int b, const uint16_t* x, const uint16_t* x_lo,
-                  const sd_attn_weights* w, const sd_kv* kv, float* out, void* ws, const Ws& L,
-                  hipStream_t st) {
+                  const sd_attn_weights* w, const sd_kv* kv, float* out, int out_parts,
+                  void* ws, const Ws& L, hipStream_t st, int* parts_used) {
   const int H = d->hidden, D = d->head_dim, Hq = d->n_q_heads, Hkv = d->n_kv_heads;
   const int N = (2 * Hq + 2 * Hkv) * D;
+  const bool lo = x_lo != nullptr;
   float* qkv = at<float>(ws, L.qkv);
   GemmArgs g{};
   g.M = b; g.N = N; g.K = H; g.x = x; g.x_lo = x_lo; g.w = (const uint16_t*)w->w_qkv;
   g.y = qkv;
+  g.ksplit = gemm_split_ok(b, N, H, lo, kDenseSplit) ? kDenseSplit : 1;
   SD_LAUNCH(launch_gemm(GEMM_F32, g, st), "qkv projection");
   uint16_t* q = at<uint16_t>(ws, L.q);
   uint16_t* q_lo = at<uint16_t>(ws, L.q_lo);
-  SD_LAUNCH(launch_qkv_post(qkv, b, Hq, Hkv, D, d->qk_norm, d->eps, d->rope_theta,
-                            kv->positions, kv->slot_mapping, q, q_lo, (uint16_t*)kv->k_cache,
-                            (uint16_t*)kv->v_cache, st),
+  float* gate = at<float>(ws, L.gate);
+  SD_LAUNCH(launch_qkv_post(qkv, g.ksplit, b, Hq, Hkv, D, d->qk_norm, d->eps, d->rope_theta,
+                            kv->positions, kv->slot_mapping, q, q_lo, gate,
+                            (uint16_t*)kv->k_cache, (uint16_t*)kv->v_cache, st),
             "qkv front epilogue");
   const AttnPlan p = attn_plan(*d, kv->n_req, kv->max_seq_len);
   AttnArgs aa{};
@@ -216,7 +225,7 @@ int run_attention(const sd_dims* d, int b, const uint16_t* x, const uint16_t* x_
   aa.positions = kv->positions; aa.n_req = kv->n_req; aa.Hq = Hq; aa.Hkv = Hkv; aa.D = D;
   aa.q_rows = d->q_rows; aa.scale = scale_of(d);
   aa.part_acc = at<float>(ws, L.part_acc); aa.part_ml = at<float>(ws, L.part_ml);
-  aa.gate = qkv + (size_t)(Hq + 2 * Hkv) * D; aa.gate_stride = N;
+  aa.gate = gate; aa.gate_stride = Hq * D;
   uint16_t* o = at<uint16_t>(ws, L.o);
   uint16_t* o_lo = at<uint16_t>(ws, L.o_lo);
   aa.out = o; aa.out_lo = o_lo;
@@ -224,7 +233,9 @@ int run_attention(const sd_dims* d, int b, const uint16_t* x, const uint16_t* x_
   GemmArgs go{};
   go.M = b; go.N = H; go.K = Hq * D; go.x = o; go.x_lo = o_lo; go.w = (const uint16_t*)w->w_o;
   go.y = out;
+  go.ksplit = (out_parts > 1 && gemm_split_ok(b, H, Hq * D, true, out_parts)) ? out_parts : 1;
   SD_LAUNCH(launch_gemm(GEMM_F32, go, st), "o_proj");
+  if (parts_used) *parts_used = go.ksplit;
   return SD_OK;
 }
 
@@ -363,7 +374,7 @@ int sd_boundary_dualnorm(const sd_dims* dims, int32_t b, float* stream, const fl
       (g_post != nullptr && !aligned16(g_post)) || (out16 != nullptr && !aligned16(out16)))
     return fail(SD_EINVAL, "stream, branch, gains and out16 must be 16-byte aligned");
   _Float16* x16 = (_Float16*)out16;
-  SD_LAUNCH(launch_dualnorm(b, dims->hidden, stream, (const float*)branch,
+  SD_LAUNCH(launch_dualnorm(b, dims->hidden, stream, (const float*)branch, 1,
                             (const uint16_t*)front_embed, g_post, g_pre, dims->eps,
                             (uint16_t*)out, nullptr, x16,
                             x16 ? x16 + (size_t)b * dims->hidden : nullptr, nullptr,
@@ -382,8 +393,8 @@ int sd_attn_verify(const sd_dims* dims, int32_t b, const void* x, const sd_attn_
     return fail(SD_EINVAL, "x or out null or misaligned");
   SD_CHECK(check_ws(dims, b, kv->n_req, kv->max_seq_len, ws, ws_bytes));
   const Ws L = ws_layout(*dims, b, kv->n_req, kv->max_seq_len);
-  SD_CHECK(run_attention(dims, b, (const uint16_t*)x, nullptr, w, kv, (float*)out, ws, L,
-                         (hipStream_t)stream_handle));
+  SD_CHECK(run_attention(dims, b, (const uint16_t*)x, nullptr, w, kv, (float*)out, 1, ws, L,
+                         (hipStream_t)stream_handle, nullptr));
   return ok();
 }
 
@@ -462,17 +473,20 @@ int sd_layer_step(const sd_dims* dims, int32_t b, float* stream, const float* br
   const int H = dims->hidden;
   uint16_t* x_a = at<uint16_t>(ws, L.x_a);
   uint16_t* x_a_lo = at<uint16_t>(ws, L.x_a_lo);
-  SD_LAUNCH(launch_dualnorm(b, H, stream, (const float*)branch_in,
+  SD_LAUNCH(launch_dualnorm(b, H, stream, (const float*)branch_in, 1,
                             (const uint16_t*)front_embed, w->g_post_prev, w->g_pre_attn,
                             dims->eps, x_a, x_a_lo, nullptr, nullptr, nullptr, st),
             "input boundary");
   float* a = at<float>(ws, L.a);
-  SD_CHECK(run_attention(dims, b, x_a, x_a_lo, &w->attn, kv, a, ws, L, st));
+  int a_parts = 1;
+  SD_CHECK(run_attention(dims, b, x_a, x_a_lo, &w->attn, kv, a, kDenseSplit, ws, L, st,
+                         &a_parts));
   uint16_t* x_m = at<uint16_t>(ws, L.x_m);
   uint16_t* x_m_lo = at<uint16_t>(ws, L.x_m_lo);
   _Float16* x16 = at<_Float16>(ws, L.x16);
   _Float16* x16_lo = at<_Float16>(ws, L.x16_lo);
-  SD_LAUNCH(launch_dualnorm(b, H, stream, a, nullptr, w->g_post_attn, w->g_pre_ffn, dims->eps,
+  SD_LAUNCH(launch_dualnorm(b, H, stream, a, a_parts, nullptr, w->g_post_attn, w->g_pre_ffn,
+                            dims->eps,
                             x_m, x_m_lo, x16, x16_lo, at<int>(ws, L.counter), st),
             "attention boundary");
   const sd_route r = route_out ? *route_out : ws_route(ws, L);
@@ -515,7 +529,7 @@ int sd_draft_head(int32_t hidden, int32_t draft_vocab, int32_t b, const void* h,
   float* val = (float*)ws;
   int* idx = (int*)((char*)ws + up((size_t)b * tiles * 4));
   GemmArgs g{};
-  g.M = b; g.N = draft_vocab; g.K = hidden; g.x = (const uint16_t*)h;
+  g.M = b; g.N = draft_vocab; g.K = hidden; g.x = (const uint16_t*)h; g.ksplit = 1;
   g.w = (const uint16_t*)w_lm; g.y = tau_out; g.head_val = val; g.head_idx = idx;
   g.multiplier = multiplier; g.soft_cap = soft_cap;
   SD_LAUNCH(launch_gemm(GEMM_HEAD, g, st), "lm_head");

@@ -38,17 +38,6 @@ __device__ __forceinline__ uint32_t x_off(int m, int M, int K, int k) {
   return m < M ? (uint32_t)(((size_t)m * K + k) * 2) : kOob;
 }
 
-// B operand of column tile c at byte offset `off` (+ du bytes per step): for SPLIT, lanes
-// 8..15 of each 16 read the lo terms, the others the hi terms.
-template <bool SPLIT>
-__device__ __forceinline__ bf16x8_t load_b(__amdgpu_buffer_rsrc_t rh, __amdgpu_buffer_rsrc_t rl,
-                                           uint32_t off_h, uint32_t off_l) {
-  if (!SPLIT) return buf_load8(rh, off_h);
-  const u32x4_t h = __builtin_bit_cast(u32x4_t, buf_load8(rh, off_h));
-  const u32x4_t l = __builtin_bit_cast(u32x4_t, buf_load8(rl, off_l));
-  return __builtin_bit_cast(bf16x8_t, h | l);  // one of the two is zero
-}
-
 // Epilogue of one 16-feature tile: lane (i, g) holds y[m = RPC*c + i][n = 16 t + 4g + r].
 template <int MODE>
 __device__ __forceinline__ void store_tile(const GemmArgs& a, int m, int tile, int ntiles,
@@ -96,6 +85,9 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, int m, int tile, i
 }
 
 // Persistent kernel, one column tile: wave w owns K steps [w S, (w+1) S) of every tile.
+// Workgroup w owns K slice ks = w % ksplit (wave v: steps ks * KT / ksplit + v S ..) of the
+// tiles w / ksplit + j * (grid / ksplit); slice ks writes partial ks of the output, which
+// the consumer sums in slice order.
 template <int NW, int S, int MODE, bool SPLIT>
 __global__ __launch_bounds__(64 * NW) void k_gemm_res(GemmArgs a, int ntiles) {
   __shared__ f32x4_t red[2][NW - 1][64];
@@ -103,17 +95,21 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_res(GemmArgs a, int ntiles) {
   const int lane = threadIdx.x & 63;
   const int i = lane & 15, g = lane >> 4;
   const int KT = a.K >> 5;
-  const int kt0 = wave * S;
+  const int ks = blockIdx.x % a.ksplit, grp = blockIdx.x / a.ksplit;
+  const int ngrp = gridDim.x / a.ksplit;
+  const int kt0 = ks * (KT / a.ksplit) + wave * S;
+  // activations: hi terms at x, lo terms x_lo_off bytes further in the same buffer
   const uint32_t xbytes = (uint32_t)(a.M * a.K * 2);
-  const auto rh = rsrc(a.x, xbytes);
-  const auto rl = rsrc(SPLIT ? a.x_lo : a.x, xbytes);
+  const auto rx = rsrc(a.x, (SPLIT ? a.x_lo_off : 0u) + xbytes);
   const int m = SPLIT ? (i & 7) : i;
   const bool lo = SPLIT && (i >> 3);
   const uint32_t ob = x_off(m, a.M, a.K, kt0 * 32 + 8 * g);
-  const uint32_t oh = lo ? kOob : ob, ol = lo ? ob : kOob;
+  const uint32_t ox = ob == kOob ? kOob : ob + (lo ? a.x_lo_off : 0u);
   bf16x8_t bv[S];
 #pragma unroll
-  for (int u = 0; u < S; ++u) bv[u] = load_b<SPLIT>(rh, rl, oh + 64 * u, ol + 64 * u);
+  for (int u = 0; u < S; ++u) bv[u] = buf_load8(rx, ox + 64 * u);
+  GemmArgs ap = a;
+  if (MODE != GEMM_HEAD) ap.y = (float*)a.y + (size_t)ks * a.M * a.N;
 
   // weights through a buffer resource: a tile index past the last loads zeros without a
   // memory access, so the prefetch of a missing next tile needs no branch and every wait
@@ -138,17 +134,18 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_res(GemmArgs a, int ntiles) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[r] += __shfl_xor(acc[r], 8, 64);
       }
-      if (!SPLIT || i < 8) store_tile<MODE>(a, m, tile, ntiles, g, acc);
+      if (!SPLIT || i < 8) store_tile<MODE>(ap, m, tile, ntiles, g, acc);
     }
   };
-  int t = blockIdx.x;  // the grid never exceeds ntiles
+  int t = grp;
+  if (t >= ntiles) return;  // uniform per workgroup
   load(A0, t);
   while (true) {
-    const int t1 = t + gridDim.x;
+    const int t1 = t + ngrp;
     load(A1, t1);
     finish(A0, t, 0);
     if (t1 >= ntiles) break;
-    const int t2 = t1 + gridDim.x;
+    const int t2 = t1 + ngrp;
     load(A0, t2);
     finish(A1, t1, 1);
     if (t2 >= ntiles) break;
@@ -170,15 +167,13 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_tile(GemmArgs a) {
   const int KTW = KT / NW;  // steps per wave
   const int kt0 = wave * KTW;
   const uint32_t xbytes = (uint32_t)(a.M * a.K * 2);
-  const auto rh = rsrc(a.x, xbytes);
-  const auto rl = rsrc(SPLIT ? a.x_lo : a.x, xbytes);
+  const auto rx = rsrc(a.x, (SPLIT ? a.x_lo_off : 0u) + xbytes);
   const bool lo = SPLIT && (i >> 3);
-  uint32_t oh[NCT], ol[NCT];
+  uint32_t ox[NCT];
 #pragma unroll
   for (int c = 0; c < NCT; ++c) {
     const uint32_t ob = x_off(RPC * c + (SPLIT ? (i & 7) : i), a.M, a.K, kt0 * 32 + 8 * g);
-    oh[c] = lo ? kOob : ob;
-    ol[c] = lo ? ob : kOob;
+    ox[c] = ob == kOob ? kOob : ob + (lo ? a.x_lo_off : 0u);
   }
   const uint16_t* wt = a.w + ((size_t)tile * KT + kt0) * 512 + lane * 8;
   f32x4_t acc[NCT];
@@ -195,8 +190,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_tile(GemmArgs a) {
     for (int u = 0; u < S; ++u)
 #pragma unroll
       for (int c = 0; c < NCT; ++c) {
-        const uint32_t d = (uint32_t)(p * S + u) * 64;
-        bv[u][c] = load_b<SPLIT>(rh, rl, oh[c] + d, ol[c] + d);
+        bv[u][c] = buf_load8(rx, ox[c] + (uint32_t)(p * S + u) * 64);
       }
 #pragma unroll
     for (int u = 0; u < S; ++u)
@@ -241,14 +235,19 @@ int cu_count() {
 template <int NW, int MODE, bool SPLIT>
 bool try_res(const GemmArgs& a, int ntiles, hipStream_t st) {
   const int KT = a.K / 32;
-  if (KT % NW) return false;
+  if (KT % (NW * a.ksplit)) return false;
   if ((size_t)ntiles * KT * 1024 >= 0x80000000u) return false;  // buffer offsets are 32-bit
-  const int grid = min(ntiles, cu_count());
+  const int grid = (min(ntiles * a.ksplit, cu_count()) / a.ksplit) * a.ksplit;
+  if (grid < a.ksplit) return false;
   const dim3 block(64 * NW);
-  switch (KT / NW) {
+  switch (KT / (NW * a.ksplit)) {
     case 16:
-      if (NW > 8) return false;  // 16 waves x 16 resident steps do not fit the registers
-      hipLaunchKernelGGL((k_gemm_res<NW, 16, MODE, SPLIT>), dim3(grid), block, 0, st, a, ntiles); return true;
+      if constexpr (NW > 8) {
+        return false;  // 16 waves x 16 resident steps do not fit the registers
+      } else {
+        hipLaunchKernelGGL((k_gemm_res<NW, 16, MODE, SPLIT>), dim3(grid), block, 0, st, a, ntiles);
+        return true;
+      }
     case 8: hipLaunchKernelGGL((k_gemm_res<NW, 8, MODE, SPLIT>), dim3(grid), block, 0, st, a, ntiles); return true;
     case 4: hipLaunchKernelGGL((k_gemm_res<NW, 4, MODE, SPLIT>), dim3(grid), block, 0, st, a, ntiles); return true;
     case 2: hipLaunchKernelGGL((k_gemm_res<NW, 2, MODE, SPLIT>), dim3(grid), block, 0, st, a, ntiles); return true;
@@ -283,16 +282,28 @@ hipError_t launch_tile(const GemmArgs& a, int ntiles, hipStream_t st) {
 }
 
 template <int MODE>
-hipError_t launch_m(const GemmArgs& a, hipStream_t st) {
+hipError_t launch_m(const GemmArgs& in, hipStream_t st) {
+  GemmArgs a = in;
   const int ntiles = (a.N + 15) / 16;
+  if (a.ksplit < 1 || (MODE == GEMM_HEAD && a.ksplit != 1)) return hipErrorInvalidValue;
   if (a.x_lo != nullptr) {
-    if (MODE == GEMM_HEAD) return hipErrorInvalidValue;
+    // lo terms must follow the hi terms in one buffer (the workspace lays them out so)
+    const ptrdiff_t off = (const char*)a.x_lo - (const char*)a.x;
+    if (MODE == GEMM_HEAD || off < (ptrdiff_t)a.M * a.K * 2 || off + (ptrdiff_t)a.M * a.K * 2 >= 0x80000000LL)
+      return hipErrorInvalidValue;
+    a.x_lo_off = (uint32_t)off;
+  } else {
+    a.x_lo_off = 0;
+  }
+  // the persistent kernel takes any K slicing; the per-tile kernel only whole K
+  if (a.x_lo != nullptr) {
     if (a.M <= 8) {
       if (try_res<8, MODE, true>(a, ntiles, st) || try_res<16, MODE, true>(a, ntiles, st) ||
           try_res<4, MODE, true>(a, ntiles, st))
         return hipGetLastError();
-      return launch_tile<1, MODE, true>(a, ntiles, st);
     }
+    if (a.ksplit != 1) return hipErrorInvalidValue;
+    if (a.M <= 8) return launch_tile<1, MODE, true>(a, ntiles, st);
     if (a.M <= 16) return launch_tile<2, MODE, true>(a, ntiles, st);
     if (a.M <= 32) return launch_tile<4, MODE, true>(a, ntiles, st);
     return launch_tile<8, MODE, true>(a, ntiles, st);
@@ -301,8 +312,9 @@ hipError_t launch_m(const GemmArgs& a, hipStream_t st) {
     if (try_res<8, MODE, false>(a, ntiles, st) || try_res<16, MODE, false>(a, ntiles, st) ||
         try_res<4, MODE, false>(a, ntiles, st))
       return hipGetLastError();
-    return launch_tile<1, MODE, false>(a, ntiles, st);
   }
+  if (a.ksplit != 1) return hipErrorInvalidValue;
+  if (a.M <= 16) return launch_tile<1, MODE, false>(a, ntiles, st);
   if (a.M <= 32) return launch_tile<2, MODE, false>(a, ntiles, st);
   return launch_tile<4, MODE, false>(a, ntiles, st);
 }
@@ -345,13 +357,17 @@ __global__ __launch_bounds__(256) void k_pack_fp4(int N, int K, const uint8_t* _
   }
 }
 
-// One wave per (row, head).  Lane d < D/2 owns the rotate-half pair (d, d + D/2).
-__global__ __launch_bounds__(64) void k_qkv_post(const float* __restrict__ qkv, int Hq, int Hkv,
+// One wave per (row, head).  Lane d < D/2 owns the rotate-half pair (d, d + D/2).  The
+// projection arrives as nparts K-slice partials (stride part_stride floats), summed here in
+// slice order; query-head waves also write the summed output gate of their head.
+__global__ __launch_bounds__(64) void k_qkv_post(const float* __restrict__ qkv, int nparts,
+                                                 size_t part_stride, int Hq, int Hkv,
                                                  int D, int qk_norm, float eps, float theta,
                                                  const int* __restrict__ positions,
                                                  const int64_t* __restrict__ slots,
                                                  uint16_t* __restrict__ q_out,
                                                  uint16_t* __restrict__ q_lo,
+                                                 float* __restrict__ gate_out,
                                                  uint16_t* __restrict__ k_cache,
                                                  uint16_t* __restrict__ v_cache) {
   const int h = blockIdx.x, t = blockIdx.y, d = threadIdx.x;
@@ -361,8 +377,24 @@ __global__ __launch_bounds__(64) void k_qkv_post(const float* __restrict__ qkv, 
   const bool act = d < half;
   const bool is_q = h < Hq;
   const int kvh = h - Hq;
-  const float* src = is_q ? row + h * D : row + Hq * D + kvh * D;
-  float x1 = act ? src[d] : 0.f, x2 = act ? src[d + half] : 0.f;
+  const int c0 = is_q ? h * D : Hq * D + kvh * D;              // q or k columns
+  const int cv = Hq * D + Hkv * D + kvh * D;                     // v columns (k heads)
+  const int cg = (Hq + 2 * Hkv) * D + h * D;                     // gate columns (q heads)
+  float x1 = 0.f, x2 = 0.f, v1 = 0.f, v2 = 0.f, g1 = 0.f, g2 = 0.f;
+  if (act) {
+    for (int p = 0; p < nparts; ++p) {
+      const float* rp = row + p * part_stride;
+      x1 += rp[c0 + d];
+      x2 += rp[c0 + d + half];
+      if (is_q) {
+        g1 += rp[cg + d];
+        g2 += rp[cg + d + half];
+      } else {
+        v1 += rp[cv + d];
+        v2 += rp[cv + d + half];
+      }
+    }
+  }
   if (qk_norm) {
     const float ss = sd::wave_sum(x1 * x1 + x2 * x2);
     const float r = rsqrtf(ss / (float)D + eps);
@@ -375,7 +407,7 @@ __global__ __launch_bounds__(64) void k_qkv_post(const float* __restrict__ qkv, 
     const double ang = (double)positions[t] * freq;
     const float c = (float)cos(ang), s = (float)sin(ang);
     const float y1 = x1 * c - x2 * s, y2 = x2 * c + x1 * s;
-    if (is_q) {  // q as bf16 hi/lo terms
+    if (is_q) {  // q as bf16 hi/lo terms, and the gate
       const size_t o = ((size_t)t * Hq + h) * D;
       uint16_t h1, l1, h2, l2;
       sd::split_bf16(y1, h1, l1);
@@ -384,6 +416,8 @@ __global__ __launch_bounds__(64) void k_qkv_post(const float* __restrict__ qkv, 
       q_out[o + d + half] = h2;
       q_lo[o + d] = l1;
       q_lo[o + d + half] = l2;
+      gate_out[o + d] = g1;
+      gate_out[o + d + half] = g2;
     } else if (slots[t] >= 0) {  // a negative slot writes nothing
       const int64_t slot = slots[t];
       const int64_t blk = slot >> 4;
@@ -391,10 +425,9 @@ __global__ __launch_bounds__(64) void k_qkv_post(const float* __restrict__ qkv, 
       uint16_t* kp = k_cache + ((size_t)(blk * Hkv + kvh) * 16 + off) * D;
       kp[d] = sd::f2bf(y1);
       kp[d + half] = sd::f2bf(y2);
-      const float* vs = row + Hq * D + Hkv * D + kvh * D;
       uint16_t* vp = v_cache + (size_t)(blk * Hkv + kvh) * D * 16 + off;
-      vp[(size_t)d * 16] = sd::f2bf(vs[d]);
-      vp[(size_t)(d + half) * 16] = sd::f2bf(vs[d + half]);
+      vp[(size_t)d * 16] = sd::f2bf(v1);
+      vp[(size_t)(d + half) * 16] = sd::f2bf(v2);
     }
   }
 }
@@ -461,13 +494,29 @@ hipError_t launch_pack_fp4(int E, int N, int K, const uint8_t* codes, const uint
   return hipGetLastError();
 }
 
-hipError_t launch_qkv_post(const float* qkv, int b, int Hq, int Hkv, int D, int qk_norm,
-                           float eps, float theta, const int* positions, const int64_t* slots,
-                           uint16_t* q_out, uint16_t* q_lo, uint16_t* k_cache,
-                           uint16_t* v_cache, hipStream_t st) {
-  hipLaunchKernelGGL(k_qkv_post, dim3(Hq + Hkv, b), dim3(64), 0, st, qkv, Hq, Hkv, D, qk_norm,
-                     eps, theta, positions, slots, q_out, q_lo, k_cache, v_cache);
+hipError_t launch_qkv_post(const float* qkv, int nparts, int b, int Hq, int Hkv, int D,
+                           int qk_norm, float eps, float theta, const int* positions,
+                           const int64_t* slots, uint16_t* q_out, uint16_t* q_lo,
+                           float* gate_out, uint16_t* k_cache, uint16_t* v_cache,
+                           hipStream_t st) {
+  const size_t part_stride = (size_t)b * (2 * Hq + 2 * Hkv) * D;
+  hipLaunchKernelGGL(k_qkv_post, dim3(Hq + Hkv, b), dim3(64), 0, st, qkv, nparts, part_stride, Hq,
+                     Hkv, D, qk_norm, eps, theta, positions, slots, q_out, q_lo, gate_out, k_cache,
+                     v_cache);
   return hipGetLastError();
+}
+
+bool gemm_split_ok(int M, int N, int K, bool lo, int ksplit) {
+  if (ksplit == 1) return true;
+  if (M > (lo ? 8 : 16) || K % 32) return false;
+  const int KT = K / 32, ntiles = (N + 15) / 16;
+  if ((size_t)ntiles * KT * 1024 >= 0x80000000u || ntiles * ksplit < ksplit) return false;
+  for (int nw : {8, 16, 4}) {
+    if (KT % (nw * ksplit)) continue;
+    const int S = KT / (nw * ksplit);
+    if (S == 1 || S == 2 || S == 4 || S == 8 || (S == 16 && nw <= 8)) return true;
+  }
+  return false;
 }
 
 hipError_t launch_head_argmax(int b, int n_tiles, const float* val, const int* idx,

@@ -23,6 +23,7 @@ template <> struct VecT<4> { typedef f32x4_t T; };
 template <int EPT>
 __global__ __launch_bounds__(256) void k_dualnorm(int H, float* __restrict__ stream,
                                                   const float* __restrict__ branch,
+                                                  int nbranch, size_t branch_stride,
                                                   const uint16_t* __restrict__ front,
                                                   const float* __restrict__ g_post,
                                                   const float* __restrict__ g_pre, float eps,
@@ -52,7 +53,8 @@ __global__ __launch_bounds__(256) void k_dualnorm(int H, float* __restrict__ str
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
       const int i0 = (v * 256 + tid) * VW;
-      const V bu = *(const V*)(branch + base + i0);
+      V bu = *(const V*)(branch + base + i0);
+      for (int p = 1; p < nbranch; ++p) bu += *(const V*)(branch + p * branch_stride + base + i0);
       const V bs = *(const V*)(stream + base + i0);
       const V bg = *(const V*)(g_post + i0);
 #pragma unroll
@@ -110,16 +112,18 @@ __global__ __launch_bounds__(256) void k_dualnorm(int H, float* __restrict__ str
 
 }  // namespace
 
-hipError_t launch_dualnorm(int b, int H, float* stream, const float* branch,
+hipError_t launch_dualnorm(int b, int H, float* stream, const float* branch, int nbranch,
                            const uint16_t* front, const float* g_post, const float* g_pre,
                            float eps, uint16_t* out, uint16_t* out_lo, _Float16* x16,
                            _Float16* x16_lo, int* zero, hipStream_t st) {
   if ((x16 == nullptr) != (x16_lo == nullptr)) return hipErrorInvalidValue;
+  if (branch != nullptr && nbranch < 1) return hipErrorInvalidValue;
   const dim3 grid(b), block(256);
   switch (H / 256) {
 #define SD_NORM_CASE(E)                                                                   \
   case E:                                                                                 \
-    hipLaunchKernelGGL(k_dualnorm<E>, grid, block, 0, st, H, stream, branch, front, g_post, \
+    hipLaunchKernelGGL(k_dualnorm<E>, grid, block, 0, st, H, stream, branch, nbranch,        \
+                       (size_t)b * H, front, g_post,                                       \
                        g_pre, eps, out, out_lo, x16, x16_lo, zero);                        \
     break;
     SD_NORM_CASE(1)

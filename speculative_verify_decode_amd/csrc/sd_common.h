@@ -122,11 +122,12 @@ __device__ __forceinline__ void dequant_unit(u32x4_t codes, uint32_t scales2, f1
 // ---------------------------------------------------------------------------- launches
 // Every launcher enqueues on `st` and returns the launch status (hipGetLastError).
 
-// branch: fp32 [b, H] (null: front mode, the stream becomes the bf16 `front` rows).
+// branch: fp32 [nbranch, b, H], nbranch partials summed in order (null: front mode, the
+// stream becomes the bf16 `front` rows).
 // out: bf16 pre-norm output (hi term); out_lo (optional): its bf16 lo term; x16 / x16_lo
 // (optional): fp16 hi / lo terms of the pre-norm output * 2^-8 (the expert input).
 // zero (optional): an int set to 0, for a later kernel's arrival counter.
-hipError_t launch_dualnorm(int b, int H, float* stream, const float* branch,
+hipError_t launch_dualnorm(int b, int H, float* stream, const float* branch, int nbranch,
                            const uint16_t* front, const float* g_post, const float* g_pre,
                            float eps, uint16_t* out, uint16_t* out_lo, _Float16* x16,
                            _Float16* x16_lo, int* zero, hipStream_t st);
@@ -136,7 +137,9 @@ enum GemmMode { GEMM_F32 = 0, GEMM_F32_BIAS = 2, GEMM_HEAD = 3 };
 struct GemmArgs {
   int M, N, K;
   const uint16_t* x;   // bf16 [M, K]
-  const uint16_t* x_lo; // optional bf16 lo terms of x [M, K] (column-split MFMA)
+  const uint16_t* x_lo; // optional bf16 lo terms of x [M, K], after x in one buffer
+  int ksplit;          // K slices: y holds ksplit partials [ksplit, M, N] (1: one output)
+  uint32_t x_lo_off;   // set by the launcher
   const uint16_t* w;   // bf16 [N, K] in packed 16 x 32 tiles
   void* y;             // fp32 [M, N] (GEMM_HEAD: optional fp32 tau)
   const float* bias;   // [M, N] for GEMM_F32_BIAS (may be null)
@@ -144,17 +147,23 @@ struct GemmArgs {
   int* head_idx;       // GEMM_HEAD: per (m, tile) its index
   float multiplier, soft_cap;
 };
+// ksplit > 1 is taken only by the persistent kernel (M <= 8 with lo terms, M <= 16
+// without); otherwise the launch fails with hipErrorInvalidValue.
 hipError_t launch_gemm(GemmMode mode, const GemmArgs& a, hipStream_t st);
+bool gemm_split_ok(int M, int N, int K, bool lo, int ksplit);
 
 // Weight packing (layouts in sdverify.h).
 hipError_t launch_pack_dense(int N, int K, const uint16_t* src, uint16_t* dst, hipStream_t st);
 hipError_t launch_pack_fp4(int E, int N, int K, const uint8_t* codes, const uint8_t* scales,
                            uint8_t* codes_out, uint8_t* scales_out, hipStream_t st);
 
-hipError_t launch_qkv_post(const float* qkv, int b, int Hq, int Hkv, int D, int qk_norm,
-                           float eps, float theta, const int* positions, const int64_t* slots,
-                           uint16_t* q_out, uint16_t* q_lo, uint16_t* k_cache,
-                           uint16_t* v_cache, hipStream_t st);
+// qkv: nparts K-slice partials of the stacked projection [nparts, b, (2Hq + 2Hkv) D];
+// gate_out fp32 [b, Hq D] receives the summed output gate.
+hipError_t launch_qkv_post(const float* qkv, int nparts, int b, int Hq, int Hkv, int D,
+                           int qk_norm, float eps, float theta, const int* positions,
+                           const int64_t* slots, uint16_t* q_out, uint16_t* q_lo,
+                           float* gate_out, uint16_t* k_cache, uint16_t* v_cache,
+                           hipStream_t st);
 
 struct AttnPlan {
   int chunk_blocks;   // blocks per workgroup (a multiple of 8)
