@@ -370,7 +370,7 @@ int sd_boundary_dualnorm(const sd_dims* dims, int32_t b, float* stream, const fl
   if (branch == nullptr && front_embed == nullptr)
     return fail(SD_EINVAL, "front mode needs front_embed");
   if (branch != nullptr && g_post == nullptr) return fail(SD_EINVAL, "g_post is null");
-  if (!aligned16(stream) || (branch != nullptr && !aligned16(branch)) || !aligned16(g_pre) ||
+  if (!aligned16(stream) || !aligned16(out) || (branch != nullptr && !aligned16(branch)) || !aligned16(g_pre) ||
       (g_post != nullptr && !aligned16(g_post)) || (out16 != nullptr && !aligned16(out16)))
     return fail(SD_EINVAL, "stream, branch, gains and out16 must be 16-byte aligned");
   _Float16* x16 = (_Float16*)out16;

@@ -7,7 +7,9 @@
 // are causal: row j sees positions 0 .. p_j of its request.
 //
 // Work split: workgroup (chunk, kv head g, request r) covers `chunk_blocks` KV blocks; its
-// 4 waves take 32-token windows (two blocks) in turn.  Every window is read once and
+// 4 waves take 32-token windows (two blocks) in turn.  In MFMA step c over the head dim,
+// lane group G holds dims 32c + 8G .. +7 of K and of Q (any dim order serves if both
+// operands share it), so each K load instruction reads 64 contiguous bytes of 16 rows.  Every window is read once and
 // shared by all QG = (Hq/Hkv) * q_rows queries of (r, g) through MFMA:
 //   S^T[token, query] = K[token, :] . Q^T       (A = K rows, B = Q^T; 16x16x32 bf16)
 //   O^T[dim, query]  += V^T[dim, token] . P^T   (A = V^T, B = P^T)
@@ -36,7 +38,6 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a, int cb, int n_ch
   constexpr int QG = 16 * NQT;
   constexpr int NC = D / 32;   // MFMA steps over the head dim
   constexpr int NDT = D / 16;  // output dim tiles
-  constexpr int DL = D / 4;    // dims per lane group
   constexpr int QP = D + 8;    // padded LDS row of the query terms
   constexpr int AP = D + 4;    // padded LDS row of the cross-wave accumulators
   __shared__ float s_acc[4][QG][AP];
@@ -50,10 +51,44 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a, int cb, int n_ch
   const int i = lane & 15, G = lane >> 4;
   const int group = a.Hq / a.Hkv;
   const int blk_begin = chunk * cb;
-  // stage block ids and queries; neither depends on the request length
+  const float sl2 = a.scale * LOG2E;
+  const size_t kvh = (size_t)16 * D;  // elements per (block, head)
   const int* btr = a.block_table + (size_t)r * a.max_blocks;
+
+  struct Win {
+    bf16x8_t k[2][NC];
+    bf16x8_t v[NDT];
+  };
+  // window of blocks (pb0, pb1): 32 tokens, K rows and V^T rows in MFMA operand order
+  auto load_win = [&](Win& W, int pb0, int pb1) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      // K rows: tile t, row i <-> window token 8 * (i / 4) + 4 t + i % 4
+      const int tw = 8 * (i >> 2) + 4 * t + (i & 3);
+      const int pb = (tw >> 4) ? pb1 : pb0;
+      const uint16_t* kp = a.k_cache + ((size_t)pb * a.Hkv + g) * kvh + (size_t)(tw & 15) * D + 8 * G;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) W.k[t][c] = *(const bf16x8_t*)(kp + 32 * c);
+    }
+    // V^T rows: dim 16 dt + i, window tokens 8G .. 8G+7
+    const int pb = (G >> 1) ? pb1 : pb0;
+    const uint16_t* vp = a.v_cache + ((size_t)pb * a.Hkv + g) * kvh + (size_t)i * 16 + 8 * (G & 1);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) W.v[dt] = *(const bf16x8_t*)(vp + (size_t)dt * 256);
+  };
+  auto clamp_blk = [&](int id) { return min(max(id, 0), a.num_blocks - 1); };
+
+  // the wave's first window starts loading at once, its block ids read straight from the
+  // table (uniform loads); ids are clamped into the pool and tokens past the request's end
+  // are masked, so a window past the end reads harmless data
+  Win W0, W1;
+  const int wb0 = blk_begin + 2 * wave;
+  load_win(W0, clamp_blk(btr[min(wb0, a.max_blocks - 1)]),
+           clamp_blk(btr[min(wb0 + 1, a.max_blocks - 1)]));
+
+  // stage block ids and queries; neither depends on the request length
   const int ncb = min(cb, a.max_blocks - blk_begin);  // >= 1: the grid covers max_blocks
-  for (int j = tid; j < ncb; j += 256) s_bt[j] = min(max(btr[blk_begin + j], 0), a.num_blocks - 1);
+  for (int j = tid; j < ncb; j += 256) s_bt[j] = clamp_blk(btr[blk_begin + j]);
   constexpr int QCH = QG * D / 8;  // 16-byte pieces of one query term
   for (int c = tid; c < 2 * QCH; c += 256) {
     const int term = c / QCH, rem = c - term * QCH;
@@ -73,31 +108,10 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a, int cb, int n_ch
   const int nblk = (L + 15) >> 4;
   if (blk_begin >= nblk) return;  // past this request's end (uniform per workgroup)
   const int blk_end = min(blk_begin + cb, nblk);
-  const float sl2 = a.scale * LOG2E;
-  const size_t kvh = (size_t)16 * D;  // elements per (block, head)
-
-  struct Win {
-    bf16x8_t k[2][NC];
-    bf16x8_t v[NDT];
-  };
-  // window at block wb (wb + 1 may be past blk_end: then it re-reads block wb, masked)
-  auto load_win = [&](Win& W, int wb) {
+  // later windows take their block ids from LDS (wb + 1 past blk_end re-reads block wb)
+  auto load_at = [&](Win& W, int wb) {
     const int pb0 = s_bt[wb - blk_begin];
-    const int pb1 = wb + 1 < blk_end ? s_bt[wb + 1 - blk_begin] : pb0;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      // K rows: tile t, row i <-> window token 8 * (i / 4) + 4 t + i % 4
-      const int tw = 8 * (i >> 2) + 4 * t + (i & 3);
-      const int pb = (tw >> 4) ? pb1 : pb0;
-      const uint16_t* kp = a.k_cache + ((size_t)pb * a.Hkv + g) * kvh + (size_t)(tw & 15) * D + G * DL;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) W.k[t][c] = *(const bf16x8_t*)(kp + 8 * c);
-    }
-    // V^T rows: dim 16 dt + i, window tokens 8G .. 8G+7
-    const int pb = (G >> 1) ? pb1 : pb0;
-    const uint16_t* vp = a.v_cache + ((size_t)pb * a.Hkv + g) * kvh + (size_t)i * 16 + 8 * (G & 1);
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) W.v[dt] = *(const bf16x8_t*)(vp + (size_t)dt * 256);
+    load_win(W, pb0, wb + 1 < blk_end ? s_bt[wb + 1 - blk_begin] : pb0);
   };
 
   float mrun[NQT], lsum[NQT];
@@ -128,8 +142,8 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a, int cb, int n_ch
       for (int t = 0; t < 2; ++t) sh[t] = slo[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const bf16x8_t qh = *(const bf16x8_t*)&s_q[0][16 * qt + i][G * DL + 8 * c];
-        const bf16x8_t ql = *(const bf16x8_t*)&s_q[1][16 * qt + i][G * DL + 8 * c];
+        const bf16x8_t qh = *(const bf16x8_t*)&s_q[0][16 * qt + i][32 * c + 8 * G];
+        const bf16x8_t ql = *(const bf16x8_t*)&s_q[1][16 * qt + i][32 * c + 8 * G];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           sh[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(W.k[t][c], qh, sh[t], 0, 0, 0);
@@ -150,8 +164,12 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a, int cb, int n_ch
         }
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mnew = fmaxf(mrun[qt], mx);
-      const float alpha = mnew == -INFINITY ? 1.f : exp2f(mrun[qt] - mnew);
+      // lazy rescaling: a column's reference maximum moves only when a score exceeds it by
+      // more than 2^8 (in exp2 units), so p <= 256 and the accumulators are rescaled rarely;
+      // exp2(s - m) with any fixed m gives the same normalised result
+      const bool grow = mx > mrun[qt] + 8.0f;
+      const float mnew = grow ? mx : mrun[qt];
+      const float alpha = (grow && mrun[qt] != -INFINITY) ? exp2f(mrun[qt] - mnew) : 1.f;
       bf16x8_t pb, pbl;
       float psum = 0.f;
 #pragma unroll
@@ -166,28 +184,27 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a, int cb, int n_ch
         }
       lsum[qt] = lsum[qt] * alpha + psum;
       mrun[qt] = mnew;
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {  // wave-uniform
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) acc[dt][qt] *= alpha;
+      }
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        acc[dt][qt] *= alpha;
         acc[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(W.v[dt], pb, acc[dt][qt], 0, 0, 0);
         acc[dt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(W.v[dt], pbl, acc[dt][qt], 0, 0, 0);
       }
     }
   };
 
-  // two-deep pipeline; the prefetch past a wave's last window re-reads that window (an L2
-  // hit) instead of branching, so each wait covers exactly the window it uses
-  Win W0, W1;
-  int wb = blk_begin + 2 * wave;
+  int wb = wb0;
   if (wb < blk_end) {
-    load_win(W0, wb);
     while (true) {
       const int w1 = wb + 8;
-      load_win(W1, w1 < blk_end ? w1 : wb);
+      load_at(W1, w1 < blk_end ? w1 : wb);
       compute(W0, wb);
       if (w1 >= blk_end) break;
       const int w2 = w1 + 8;
-      load_win(W0, w2 < blk_end ? w2 : w1);
+      load_at(W0, w2 < blk_end ? w2 : w1);
       compute(W1, w1);
       if (w2 >= blk_end) break;
       wb = w2;
@@ -248,6 +265,7 @@ __global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a, int cb, int n_
   const size_t p0 = ((size_t)r * a.Hkv + g) * n_chunks;
   const float* pa = a.part_acc + (p0 * qg + qi) * a.D + d;
   const size_t cs = (size_t)qg * a.D;  // chunk stride
+  const float gate = a.gate[(size_t)t * a.gate_stride + h * a.D + d];  // in flight early
   float vals[PASS];
 #pragma unroll
   for (int u = 0; u < PASS; ++u) vals[u] = pa[min(u, nc - 1) * cs];
@@ -280,7 +298,6 @@ __global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a, int cb, int n_
     }
   }
   o /= l;
-  const float gate = a.gate[(size_t)t * a.gate_stride + h * a.D + d];
   const float sig = 1.0f / (1.0f + __expf(-gate));
   uint16_t hi, lo;
   sd::split_bf16(o * sig, hi, lo);

@@ -360,7 +360,8 @@ __global__ __launch_bounds__(256) void k_pack_fp4(int N, int K, const uint8_t* _
 // One wave per (row, head).  Lane d < D/2 owns the rotate-half pair (d, d + D/2).  The
 // projection arrives as nparts K-slice partials (stride part_stride floats), summed here in
 // slice order; query-head waves also write the summed output gate of their head.
-__global__ __launch_bounds__(64) void k_qkv_post(const float* __restrict__ qkv, int nparts,
+template <int NP>
+__global__ __launch_bounds__(64) void k_qkv_post(const float* __restrict__ qkv,
                                                  size_t part_stride, int Hq, int Hkv,
                                                  int D, int qk_norm, float eps, float theta,
                                                  const int* __restrict__ positions,
@@ -382,7 +383,8 @@ __global__ __launch_bounds__(64) void k_qkv_post(const float* __restrict__ qkv, 
   const int cg = (Hq + 2 * Hkv) * D + h * D;                     // gate columns (q heads)
   float x1 = 0.f, x2 = 0.f, v1 = 0.f, v2 = 0.f, g1 = 0.f, g2 = 0.f;
   if (act) {
-    for (int p = 0; p < nparts; ++p) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {  // all partials' loads in flight together
       const float* rp = row + p * part_stride;
       x1 += rp[c0 + d];
       x2 += rp[c0 + d + half];
@@ -500,9 +502,16 @@ hipError_t launch_qkv_post(const float* qkv, int nparts, int b, int Hq, int Hkv,
                            float* gate_out, uint16_t* k_cache, uint16_t* v_cache,
                            hipStream_t st) {
   const size_t part_stride = (size_t)b * (2 * Hq + 2 * Hkv) * D;
-  hipLaunchKernelGGL(k_qkv_post, dim3(Hq + Hkv, b), dim3(64), 0, st, qkv, nparts, part_stride, Hq,
-                     Hkv, D, qk_norm, eps, theta, positions, slots, q_out, q_lo, gate_out, k_cache,
-                     v_cache);
+  const dim3 grid(Hq + Hkv, b), block(64);
+#define SD_QKV_POST(NPV)                                                                    \
+  hipLaunchKernelGGL(k_qkv_post<NPV>, grid, block, 0, st, qkv, part_stride, Hq, Hkv, D,       \
+                     qk_norm, eps, theta, positions, slots, q_out, q_lo, gate_out, k_cache,   \
+                     v_cache)
+  if (nparts == 1) SD_QKV_POST(1);
+  else if (nparts == 2) SD_QKV_POST(2);
+  else if (nparts == 4) SD_QKV_POST(4);
+  else return hipErrorInvalidValue;
+#undef SD_QKV_POST
   return hipGetLastError();
 }
 

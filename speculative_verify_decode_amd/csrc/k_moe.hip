@@ -559,20 +559,29 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w2(MoeArgs a) {
 }
 
 // ---------------------------------------------------------------- unpooler
-// out[t, n] = sum_j w[t, j] * y[slot_of[t, j], n], j in order, fp32.  4 features/thread.
-__global__ __launch_bounds__(256) void k_unpool(int H, int k, const float* __restrict__ y,
+// out[t, n] = sum_j w[t, j] * y[slot_of[t, j], n], j in order, fp32.  4 features/thread;
+// K = top_k is a template parameter so every slot id, then every row, is in flight at once.
+template <int K>
+__global__ __launch_bounds__(256) void k_unpool(int H, const float* __restrict__ y,
                                                 const float* __restrict__ w,
                                                 const int* __restrict__ slot_of,
                                                 float* __restrict__ out) {
   const int t = blockIdx.y;
   const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (n >= H) return;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
-    const float wj = w[t * k + j];
-    const f32x4_t v = *(const f32x4_t*)(y + (size_t)slot_of[t * k + j] * H + n);
-    acc += wj * v;
+  int sl[K];
+  float wj[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    sl[j] = slot_of[t * K + j];
+    wj[j] = w[t * K + j];
   }
+  f32x4_t v[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) v[j] = *(const f32x4_t*)(y + (size_t)sl[j] * H + n);
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < K; ++j) acc += wj[j] * v[j];
   *(f32x4_t*)(out + (size_t)t * H + n) = acc;
 }
 
@@ -626,7 +635,7 @@ hipError_t launch_experts_nct(const MoeArgs& a, hipStream_t st) {
   const Split s13 = split_for(a.H), s2 = split_for(a.I);
   // persistent grids: the live units are at most E * tiles
   const int g13 = min(cus(), a.E * (a.I / 16));
-  const int g2 = min(2 * cus(), a.E * (a.H / 16));
+  const int g2 = min(4 * cus(), a.E * (a.H / 16));
   bool done = false;
 #define SD_W13(NU, KS)                                                                     \
   if (!done && s13.nu == NU && s13.ks == KS) {                                             \
@@ -691,8 +700,15 @@ hipError_t launch_moe_experts(const MoeArgs& in, hipStream_t st) {
 
 hipError_t launch_unpool(int b, int H, int k, const float* y, const float* w, const int* slot_of,
                          float* out, hipStream_t st) {
-  hipLaunchKernelGGL(k_unpool, dim3((H / 4 + 255) / 256, b), dim3(256), 0, st, H, k, y, w,
-                     slot_of, out);
+  const dim3 grid((H / 4 + 255) / 256, b), block(256);
+  switch (k) {
+#define SD_UNPOOL(KV) \
+  case KV: hipLaunchKernelGGL(k_unpool<KV>, grid, block, 0, st, H, y, w, slot_of, out); break;
+    SD_UNPOOL(1) SD_UNPOOL(2) SD_UNPOOL(3) SD_UNPOOL(4)
+    SD_UNPOOL(5) SD_UNPOOL(6) SD_UNPOOL(7) SD_UNPOOL(8)
+#undef SD_UNPOOL
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

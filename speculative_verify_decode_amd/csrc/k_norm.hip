@@ -10,6 +10,18 @@
 
 namespace {
 
+// VW consecutive 16-bit values as one store (VW = 1, 2 or 4).
+template <int VW>
+__device__ __forceinline__ void store16(uint16_t* p, const uint16_t* v) {
+  if constexpr (VW == 4) {
+    *(u32x2_t*)p = u32x2_t{v[0] | ((uint32_t)v[1] << 16), v[2] | ((uint32_t)v[3] << 16)};
+  } else if constexpr (VW == 2) {
+    *(uint32_t*)p = v[0] | ((uint32_t)v[1] << 16);
+  } else {
+    *p = v[0];
+  }
+}
+
 template <int VW>
 struct VecT;
 template <> struct VecT<1> { typedef float T; };
@@ -18,12 +30,12 @@ template <> struct VecT<4> { typedef f32x4_t T; };
 
 // H = 256 * EPT.  Thread tid owns NV vectors of VW consecutive elements, vector v at
 // element (v * 256 + tid) * VW, so every load is coalesced and as wide as H allows.  All
-// inputs (branch, stream, both gains) are loaded before the first reduction, so the row
-// costs one round trip to memory.
-template <int EPT>
+// inputs (the NB branch partials, stream, both gains) are loaded before the first
+// reduction, so the row costs one round trip to memory; outputs leave as packed stores.
+template <int EPT, int NB>
 __global__ __launch_bounds__(256) void k_dualnorm(int H, float* __restrict__ stream,
                                                   const float* __restrict__ branch,
-                                                  int nbranch, size_t branch_stride,
+                                                  size_t branch_stride,
                                                   const uint16_t* __restrict__ front,
                                                   const float* __restrict__ g_post,
                                                   const float* __restrict__ g_pre, float eps,
@@ -54,7 +66,8 @@ __global__ __launch_bounds__(256) void k_dualnorm(int H, float* __restrict__ str
     for (int v = 0; v < NV; ++v) {
       const int i0 = (v * 256 + tid) * VW;
       V bu = *(const V*)(branch + base + i0);
-      for (int p = 1; p < nbranch; ++p) bu += *(const V*)(branch + p * branch_stride + base + i0);
+#pragma unroll
+      for (int p = 1; p < NB; ++p) bu += *(const V*)(branch + p * branch_stride + base + i0);
       const V bs = *(const V*)(stream + base + i0);
       const V bg = *(const V*)(g_post + i0);
 #pragma unroll
@@ -93,19 +106,19 @@ __global__ __launch_bounds__(256) void k_dualnorm(int H, float* __restrict__ str
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
     const size_t i0 = base + (size_t)(v * 256 + tid) * VW;
+    uint16_t hi[VW], lo[VW];
+    _Float16 h16[VW], l16[VW];
 #pragma unroll
     for (int j = 0; j < VW; ++j) {
       const float x = s[v * VW + j] * r * gq[v * VW + j];
-      uint16_t hi, lo;
-      sd::split_bf16(x, hi, lo);
-      out[i0 + j] = hi;
-      if (out_lo != nullptr) out_lo[i0 + j] = lo;
-      if (x16 != nullptr) {
-        _Float16 h16, l16;
-        sd::split_f16(x, h16, l16);
-        x16[i0 + j] = h16;
-        x16_lo[i0 + j] = l16;
-      }
+      sd::split_bf16(x, hi[j], lo[j]);
+      sd::split_f16(x, h16[j], l16[j]);
+    }
+    store16<VW>(out + i0, hi);
+    if (out_lo != nullptr) store16<VW>(out_lo + i0, lo);
+    if (x16 != nullptr) {
+      store16<VW>((uint16_t*)x16 + i0, (const uint16_t*)h16);
+      store16<VW>((uint16_t*)x16_lo + i0, (const uint16_t*)l16);
     }
   }
 }
@@ -119,13 +132,19 @@ hipError_t launch_dualnorm(int b, int H, float* stream, const float* branch, int
   if ((x16 == nullptr) != (x16_lo == nullptr)) return hipErrorInvalidValue;
   if (branch != nullptr && nbranch < 1) return hipErrorInvalidValue;
   const dim3 grid(b), block(256);
-  switch (H / 256) {
+  const size_t bs = (size_t)b * H;
+  if (branch == nullptr) nbranch = 1;
+  if (nbranch != 1 && nbranch != 2 && nbranch != 4) return hipErrorInvalidValue;
+#define SD_NORM_NB(E, NBV)                                                                 \
+  hipLaunchKernelGGL((k_dualnorm<E, NBV>), grid, block, 0, st, H, stream, branch, bs, front, \
+                     g_post, g_pre, eps, out, out_lo, x16, x16_lo, zero)
 #define SD_NORM_CASE(E)                                                                   \
   case E:                                                                                 \
-    hipLaunchKernelGGL(k_dualnorm<E>, grid, block, 0, st, H, stream, branch, nbranch,        \
-                       (size_t)b * H, front, g_post,                                       \
-                       g_pre, eps, out, out_lo, x16, x16_lo, zero);                        \
+    if (nbranch == 1) SD_NORM_NB(E, 1);                                                   \
+    else if (nbranch == 2) SD_NORM_NB(E, 2);                                              \
+    else SD_NORM_NB(E, 4);                                                                \
     break;
+  switch (H / 256) {
     SD_NORM_CASE(1)
     SD_NORM_CASE(2)
     SD_NORM_CASE(4)
@@ -135,9 +154,10 @@ hipError_t launch_dualnorm(int b, int H, float* stream, const float* branch, int
     SD_NORM_CASE(20)
     SD_NORM_CASE(24)
     SD_NORM_CASE(32)
-#undef SD_NORM_CASE
     default:
       return hipErrorInvalidValue;
   }
+#undef SD_NORM_CASE
+#undef SD_NORM_NB
   return hipGetLastError();
 }
