@@ -249,11 +249,13 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a, int cb, int n_ch
 }
 
 // One workgroup of D threads per (row, query head): LSE-combine the chunks, normalise,
-// apply the output gate o * sigmoid(o_gate), store bf16 hi/lo terms.  Chunk statistics go
-// to LDS while each thread's chunk values for its dim are already in flight (32 per pass).
+// apply the output gate o * sigmoid(o_gate), store bf16 hi/lo terms.  Every thread's chunk
+// values for its dim are in flight at once (32 per pass) while thread c turns chunk c's
+// statistics into its weight exp2(m_c - M) (in LDS) and w_c * l_c (block-summed).
 __global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a, int cb, int n_chunks, int qg) {
   constexpr int PASS = 32;
-  __shared__ float s_m[1024], s_l[1024], s_red[2];
+  __shared__ __align__(16) float s_w[1024];
+  __shared__ float s_red[4];
   const int t = blockIdx.x / a.Hq, h = blockIdx.x - t * a.Hq;
   const int d = threadIdx.x;
   const int r = t / a.q_rows, jr = t - r * a.q_rows;
@@ -261,7 +263,7 @@ __global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a, int cb, int n_
   const int g = h / group, hh = h - g * group;
   const int qi = hh * a.q_rows + jr;
   const int L = min(a.seq_lens[r], a.max_blocks * 16);
-  const int nc = min((((L + 15) >> 4) + cb - 1) / cb, n_chunks);
+  const int nc = max(min((((L + 15) >> 4) + cb - 1) / cb, n_chunks), 1);
   const size_t p0 = ((size_t)r * a.Hkv + g) * n_chunks;
   const float* pa = a.part_acc + (p0 * qg + qi) * a.D + d;
   const size_t cs = (size_t)qg * a.D;  // chunk stride
@@ -269,32 +271,41 @@ __global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a, int cb, int n_
   float vals[PASS];
 #pragma unroll
   for (int u = 0; u < PASS; ++u) vals[u] = pa[min(u, nc - 1) * cs];
+  // chunk statistics: thread c holds (m_c, l_c) of chunks c, c + D, ...
   float mloc = -INFINITY;
   for (int c = d; c < nc; c += blockDim.x) {
     const float m = a.part_ml[((p0 + c) * qg + qi) * 2];
-    s_m[c] = m;
-    s_l[c] = a.part_ml[((p0 + c) * qg + qi) * 2 + 1];
+    s_w[c] = m;
     mloc = fmaxf(mloc, m);
   }
   mloc = sd::wave_max(mloc);
   if ((d & 63) == 0) s_red[d >> 6] = mloc;
   __syncthreads();
   const float M = blockDim.x > 64 ? fmaxf(s_red[0], s_red[1]) : s_red[0];
-  float o = 0.f, l = 0.f;
+  float wl = 0.f;
+  for (int c = d; c < nc; c += blockDim.x) {
+    const float m = s_w[c];
+    const float w = m == -INFINITY ? 0.f : exp2f(m - M);
+    s_w[c] = w;
+    wl += w * a.part_ml[((p0 + c) * qg + qi) * 2 + 1];
+  }
+  wl = sd::wave_sum(wl);
+  __syncthreads();  // s_red reuse and s_w complete
+  if ((d & 63) == 0) s_red[2 + (d >> 6)] = wl;
+  __syncthreads();
+  const float l = blockDim.x > 64 ? s_red[2] + s_red[3] : s_red[2];
+  float o = 0.f;
   for (int c0 = 0; c0 < nc; c0 += PASS) {
     if (c0 > 0) {
 #pragma unroll
       for (int u = 0; u < PASS; ++u) vals[u] = pa[min(c0 + u, nc - 1) * cs];
     }
 #pragma unroll
-    for (int u = 0; u < PASS; ++u) {
-      const int c = c0 + u;
-      if (c < nc) {
-        const float m = s_m[c];
-        const float w = m == -INFINITY ? 0.f : exp2f(m - M);
-        o += w * vals[u];
-        l += w * s_l[c];
-      }
+    for (int u4 = 0; u4 < PASS / 4; ++u4) {
+      const f32x4_t w4 = *(const f32x4_t*)&s_w[c0 + 4 * u4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (c0 + 4 * u4 + j < nc) o += w4[j] * vals[4 * u4 + j];
     }
   }
   o /= l;
