@@ -241,9 +241,9 @@ int run_attention(const sd_dims* d, int b, const uint16_t* x, const uint16_t* x_
 
 // The router kernel's arrival counter must be 0 at launch: in a layer step the attention
 // boundary's norm kernel zeroes it; a standalone call zeroes it first.
-int run_route(const sd_dims* d, int b, const uint16_t* x, const uint16_t* x_lo,
-              const void* w_router, const float* bias, const sd_route* r, float* logits,
-              void* ws, const Ws& L, hipStream_t st) {
+RouterArgs router_args(const sd_dims* d, int b, const uint16_t* x, const uint16_t* x_lo,
+                       const void* w_router, const float* bias, const sd_route* r, float* logits,
+                       void* ws, const Ws& L) {
   RouterArgs ra{};
   ra.b = b; ra.H = d->hidden; ra.E = d->n_experts; ra.k = d->top_k;
   ra.x = x; ra.x_lo = x_lo; ra.w = (const uint16_t*)w_router; ra.bias = bias;
@@ -251,6 +251,13 @@ int run_route(const sd_dims* d, int b, const uint16_t* x, const uint16_t* x_lo,
   ra.ids = r->topk_ids; ra.w_out = r->topk_w; ra.counts = r->expert_counts;
   ra.offsets = r->expert_offsets; ra.slot_of = r->slot_of; ra.tos = r->token_of_slot;
   ra.active = r->active_experts;
+  return ra;
+}
+
+int run_route(const sd_dims* d, int b, const uint16_t* x, const uint16_t* x_lo,
+              const void* w_router, const float* bias, const sd_route* r, float* logits,
+              void* ws, const Ws& L, hipStream_t st) {
+  const RouterArgs ra = router_args(d, b, x, x_lo, w_router, bias, r, logits, ws, L);
   SD_LAUNCH(launch_router(ra, st), "router, routing and pooler");
   return SD_OK;
 }
@@ -475,7 +482,8 @@ int sd_layer_step(const sd_dims* dims, int32_t b, float* stream, const float* br
   uint16_t* x_a_lo = at<uint16_t>(ws, L.x_a_lo);
   SD_LAUNCH(launch_dualnorm(b, H, stream, (const float*)branch_in, 1,
                             (const uint16_t*)front_embed, w->g_post_prev, w->g_pre_attn,
-                            dims->eps, x_a, x_a_lo, nullptr, nullptr, nullptr, st),
+                            dims->eps, x_a, x_a_lo, nullptr, nullptr, at<int>(ws, L.counter),
+                            st),
             "input boundary");
   float* a = at<float>(ws, L.a);
   int a_parts = 1;
@@ -485,13 +493,24 @@ int sd_layer_step(const sd_dims* dims, int32_t b, float* stream, const float* br
   uint16_t* x_m_lo = at<uint16_t>(ws, L.x_m_lo);
   _Float16* x16 = at<_Float16>(ws, L.x16);
   _Float16* x16_lo = at<_Float16>(ws, L.x16_lo);
-  SD_LAUNCH(launch_dualnorm(b, H, stream, a, a_parts, nullptr, w->g_post_attn, w->g_pre_ffn,
-                            dims->eps,
-                            x_m, x_m_lo, x16, x16_lo, at<int>(ws, L.counter), st),
-            "attention boundary");
   const sd_route r = route_out ? *route_out : ws_route(ws, L);
-  SD_CHECK(run_route(dims, b, x_m, x_m_lo, w->moe.w_router, logit_bias, &r, nullptr, ws, L,
-                     st));
+  if (norm_router_parts(H, dims->n_experts, b, dims->top_k) > 0 && (a_parts == 1 || a_parts == 4)) {
+    // attention boundary and router in one launch (the input boundary zeroed the counter)
+    NormRouterArgs nr{};
+    nr.H = H; nr.branch = a; nr.branch_stride = (size_t)b * H; nr.stream = stream;
+    nr.g_post = w->g_post_attn; nr.g_pre = w->g_pre_ffn; nr.eps = dims->eps;
+    nr.out = nullptr; nr.out_lo = nullptr;  // the bf16 row feeds only the router
+    nr.x16 = x16; nr.x16_lo = x16_lo;
+    nr.r = router_args(dims, b, nullptr, nullptr, w->moe.w_router, logit_bias, &r, nullptr, ws, L);
+    nr.r.part = at<float>(ws, L.zpart);
+    SD_LAUNCH(launch_norm_router(nr, a_parts, st), "attention boundary and router");
+  } else {
+    SD_LAUNCH(launch_dualnorm(b, H, stream, a, a_parts, nullptr, w->g_post_attn, w->g_pre_ffn,
+                              dims->eps, x_m, x_m_lo, x16, x16_lo, at<int>(ws, L.counter), st),
+              "attention boundary");
+    SD_CHECK(run_route(dims, b, x_m, x_m_lo, w->moe.w_router, logit_bias, &r, nullptr, ws, L,
+                       st));
+  }
   float* y = at<float>(ws, L.y);
   SD_CHECK(run_experts(dims, b, x16, x16_lo, &w->moe, &r, y, nullptr, at<_Float16>(ws, L.h16),
                        at<_Float16>(ws, L.h16_lo), st));

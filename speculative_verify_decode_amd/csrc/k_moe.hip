@@ -33,16 +33,156 @@ __device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t
 // choice) by expert,
 // through per-expert row bitmasks (a row picks an expert at most once, so an entry's
 // rank within its expert is the number of earlier rows in the expert's mask).
+// The routing of the last router workgroup: z = sum over ks < KS of part[ks] (in order) +
+// bias; top-k per row by (-z, index) with each (row, expert) finding its own rank; weights
+// = softmax over the selected logits; pooler = stable counting sort of (row, choice) by
+// expert through per-expert row bitmasks (a row picks an expert at most once, so an
+// entry's rank within its expert is the number of earlier rows in the expert's mask).
+// 256 threads.
+struct RouteLds {
+  uint32_t key[64 * 256];  // order keys: larger = earlier in (-z, index) order, NaN last
+  float sel[512 + 8];      // 8 spare: unrolled reads of a row's k values stay in the array
+  int ids[512];
+  uint32_t mlo[256], mhi[256];
+  int off[257];
+  int wc[4], wa[4];
+};
+
+// EMAX > 0: E <= EMAX and k <= 8, ranks and weights from fully unrolled LDS reads.
+template <int EMAX>
+__device__ void route_phase2(const RouterArgs& a, int KS, RouteLds& R) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int b = a.b, E = a.E, k = a.k;
+  // z = sum over ks in order + bias, every (row, expert) at once: one round of loads.  The
+  // LDS copy is an order key: larger key = earlier in (-z, index) order, NaN last.
+  const size_t st = (size_t)b * E;
+  for (int idx = tid; idx < b * E; idx += 256) {
+    float z = 0.f;
+#pragma unroll 16
+    for (int j = 0; j < KS; ++j) z += a.part[j * st + idx];
+    if (a.bias != nullptr) z += a.bias[idx];
+    if (a.logits != nullptr) a.logits[idx] = z;
+    const uint32_t u = __float_as_uint(z == 0.f ? 0.f : z);  // -0 ties with +0
+    R.key[idx] = z != z ? 0u : (u & 0x80000000u ? ~u : u | 0x80000000u);
+  }
+  if (tid < E) R.mlo[tid] = R.mhi[tid] = 0u;
+  __syncthreads();
+  // top-k by rank: (t, e) is choice number rank(t, e) if that is < k, where rank counts the
+  // experts of row t ordered before e (larger key, or equal key and lower index).  The
+  // logit comes back from its key (key 0: NaN); the softmax sums in rank order.
+  auto key_value = [](uint32_t ke) {
+    return ke == 0u ? __uint_as_float(0x7fc00000u)
+                    : __uint_as_float(ke & 0x80000000u ? ke & 0x7fffffffu : ~ke);
+  };
+  const int nk = b * k;
+  if constexpr (EMAX > 0) {
+    for (int p = tid; p < b * E; p += 256) {
+      const int t = p / E, e = p - t * E;
+      const uint32_t* kr = R.key + t * E;  // reads past the row stay in the array, masked
+      const uint32_t ke = kr[e];
+      uint32_t kk[EMAX];
+#pragma unroll
+      for (int j = 0; j < EMAX; ++j) kk[j] = kr[j];
+      int rank = 0;
+#pragma unroll
+      for (int j = 0; j < EMAX; ++j) rank += (j < E && (kk[j] > ke || (kk[j] == ke && j < e))) ? 1 : 0;
+      if (rank < k) {
+        R.ids[t * k + rank] = e;
+        R.sel[t * k + rank] = key_value(ke);
+      }
+    }
+    __syncthreads();
+    for (int p = tid; p < nk; p += 256) {
+      const int t = p / k;
+      float sv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sv[j] = R.sel[t * k + j];
+      const float m = sv[0];
+      float den = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j < k) den += expf(sv[j] - m);
+      const int ex = R.ids[p];
+      a.ids[p] = ex;
+      a.w_out[p] = expf(R.sel[p] - m) / den;
+      atomicOr(t < 32 ? &R.mlo[ex] : &R.mhi[ex], 1u << (t & 31));
+    }
+  } else {
+    for (int p = tid; p < b * E; p += 256) {
+      const int t = p / E, e = p - t * E;
+      const uint32_t* kr = R.key + t * E;
+      const uint32_t ke = kr[e];
+      int rank = 0;
+      for (int j = 0; j < E; ++j) {
+        const uint32_t kj = kr[j];
+        rank += (kj > ke || (kj == ke && j < e)) ? 1 : 0;
+      }
+      if (rank < k) {
+        R.ids[t * k + rank] = e;
+        R.sel[t * k + rank] = key_value(ke);
+      }
+    }
+    __syncthreads();
+    for (int p = tid; p < nk; p += 256) {
+      const int t = p / k;
+      const float m = R.sel[t * k];
+      float den = 0.f;
+      for (int j = 0; j < k; ++j) den += expf(R.sel[t * k + j] - m);
+      a.ids[p] = R.ids[p];
+      a.w_out[p] = expf(R.sel[p] - m) / den;
+    }
+    for (int p = tid; p < nk; p += 256) {
+      const int t = p / k;
+      atomicOr(t < 32 ? &R.mlo[R.ids[p]] : &R.mhi[R.ids[p]], 1u << (t & 31));
+    }
+  }
+  __syncthreads();
+  // counts, exclusive offsets and the active list: block scans over experts (tid = e)
+  const int e = tid;
+  const int cnt = e < E ? __popc(R.mlo[e]) + __popc(R.mhi[e]) : 0;
+  const int act = cnt > 0 ? 1 : 0;
+  int ic = cnt, ia = act;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int uc = __shfl_up(ic, d, 64), ua = __shfl_up(ia, d, 64);
+    if (lane >= d) { ic += uc; ia += ua; }
+  }
+  if (lane == 63) { R.wc[wave] = ic; R.wa[wave] = ia; }
+  __syncthreads();
+  int pc = 0, pa = 0;
+  for (int w = 0; w < wave; ++w) { pc += R.wc[w]; pa += R.wa[w]; }
+  const int total = R.wc[0] + R.wc[1] + R.wc[2] + R.wc[3];
+  const int n_act = R.wa[0] + R.wa[1] + R.wa[2] + R.wa[3];
+  const int off = pc + ic - cnt;
+  if (e < E) {
+    a.counts[e] = cnt;
+    a.offsets[e] = off;
+    R.off[e] = off;
+    if (act) a.active[pa + ia - 1] = e;
+    if (e >= n_act) a.active[e] = -1;
+  }
+  if (tid == 0) {
+    a.offsets[E] = total;
+    a.active[E] = n_act;
+  }
+  __syncthreads();
+  for (int p = tid; p < nk; p += 256) {
+    const int t = p / k, ex = R.ids[p];
+    const int rank = t < 32 ? __popc(R.mlo[ex] & ((1u << t) - 1u))
+                            : __popc(R.mlo[ex]) + __popc(R.mhi[ex] & ((1u << (t - 32)) - 1u));
+    const int slot = R.off[ex] + rank;
+    a.slot_of[p] = slot;
+    a.tos[slot] = t;
+  }
+  if (tid == 0) *a.counter = 0;  // ready for the next launch
+}
+
 template <int NCT>
 __global__ __launch_bounds__(256) void k_router(RouterArgs a) {
   __shared__ f32x4_t red[3][NCT][64];
-  __shared__ uint32_t s_key[64 * 256];
-  __shared__ float s_sel[512];
+  __shared__ RouteLds R;
   __shared__ int s_last;
-  __shared__ int s_ids[512];
-  __shared__ uint32_t s_mlo[256], s_mhi[256];
-  __shared__ int s_off[257];
-  __shared__ int s_wc[4], s_wa[4];
   const int ntiles = (a.E + 15) >> 4;
   const int nt = blockIdx.x % ntiles, ks = blockIdx.x / ntiles;
   const int KS = gridDim.x / ntiles;
@@ -109,93 +249,183 @@ __global__ __launch_bounds__(256) void k_router(RouterArgs a) {
   __syncthreads();
   if (!s_last) return;
 
-  const int b = a.b, E = a.E, k = a.k;
-  // z = sum over ks in order + bias, every (row, expert) at once: one round of loads.  The
-  // LDS copy is an order key: larger key = earlier in (-z, index) order, NaN last.
-  const size_t st = (size_t)b * E;
-  for (int idx = tid; idx < b * E; idx += 256) {
-    float z = 0.f;
-#pragma unroll 16
-    for (int j = 0; j < KS; ++j) z += a.part[j * st + idx];
-    if (a.bias != nullptr) z += a.bias[idx];
-    if (a.logits != nullptr) a.logits[idx] = z;
-    const uint32_t u = __float_as_uint(z == 0.f ? 0.f : z);  // -0 ties with +0
-    s_key[idx] = z != z ? 0u : (u & 0x80000000u ? ~u : u | 0x80000000u);
+  route_phase2<0>(a, KS, R);
+}
+
+// Attention boundary fused with the router, for the layer step.  Workgroup (row t, part q)
+// of RS per row redoes the row's dual norm (latency-bound, so the repeat costs nothing
+// measurable), writes its RS-th of the boundary's outputs, and computes in fp32 the logits
+// of experts e = q + RS j (j < EPW) as the normalised row times the packed router rows.
+// The last of the b * RS workgroups to arrive routes (route_phase2 over one partial).
+template <int VW>
+__device__ __forceinline__ void load_bf16v(const uint16_t* p, float* out) {
+  if constexpr (VW == 4) {
+    const u32x2_t v = *(const u32x2_t*)p;
+    out[0] = __uint_as_float(v[0] << 16); out[1] = __uint_as_float(v[0] & 0xffff0000u);
+    out[2] = __uint_as_float(v[1] << 16); out[3] = __uint_as_float(v[1] & 0xffff0000u);
+  } else if constexpr (VW == 2) {
+    const uint32_t v = *(const uint32_t*)p;
+    out[0] = __uint_as_float(v << 16); out[1] = __uint_as_float(v & 0xffff0000u);
+  } else {
+    out[0] = sd::bf2f(p[0]);
   }
-  __syncthreads();
-  // top-k by rank: (t, e) is choice number rank(t, e) if that is < k, where rank counts the
-  // experts of row t ordered before e (larger key, or equal key and lower index)
-  for (int p = tid; p < b * E; p += 256) {
-    const int t = p / E, e = p - t * E;
-    const uint32_t* kr = s_key + t * E;
-    const uint32_t ke = kr[e];
-    int rank = 0;
-    for (int j = 0; j < E; ++j) {
-      const uint32_t kj = kr[j];
-      rank += (kj > ke || (kj == ke && j < e)) ? 1 : 0;
-    }
-    if (rank < k) {  // the logit back from its key (key 0: NaN)
-      s_ids[t * k + rank] = e;
-      s_sel[t * k + rank] = ke == 0u ? __uint_as_float(0x7fc00000u)
-                                     : __uint_as_float(ke & 0x80000000u ? ke & 0x7fffffffu : ~ke);
-    }
+}
+
+template <int VW>
+__device__ __forceinline__ void load_f32v(const float* p, float* out) {
+  if constexpr (VW == 4) {
+    const f32x4_t v = *(const f32x4_t*)p;
+    out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
+  } else if constexpr (VW == 2) {
+    const f32x2_t v = *(const f32x2_t*)p;
+    out[0] = v[0]; out[1] = v[1];
+  } else {
+    out[0] = p[0];
   }
-  __syncthreads();
-  // weights: softmax over the k selected logits of the row
-  for (int p = tid; p < b * k; p += 256) {
-    const int t = p / k;
-    const float m = s_sel[t * k];
-    float den = 0.f;
-    for (int j = 0; j < k; ++j) den += expf(s_sel[t * k + j] - m);
-    a.ids[p] = s_ids[p];
-    a.w_out[p] = expf(s_sel[p] - m) / den;
+}
+
+template <int VW>
+__device__ __forceinline__ void store16v(uint16_t* p, const uint16_t* v) {
+  if constexpr (VW == 4) {
+    *(u32x2_t*)p = u32x2_t{v[0] | ((uint32_t)v[1] << 16), v[2] | ((uint32_t)v[3] << 16)};
+  } else if constexpr (VW == 2) {
+    *(uint32_t*)p = v[0] | ((uint32_t)v[1] << 16);
+  } else {
+    *p = v[0];
   }
-  if (tid < E) s_mlo[tid] = s_mhi[tid] = 0u;
-  __syncthreads();
-  const int nk = b * k;
-  for (int p = tid; p < nk; p += 256) {
-    const int t = p / k;
-    atomicOr(t < 32 ? &s_mlo[s_ids[p]] : &s_mhi[s_ids[p]], 1u << (t & 31));
-  }
-  __syncthreads();
-  // counts, exclusive offsets and the active list: block scans over experts (tid = e)
-  const int e = tid;
-  const int cnt = e < E ? __popc(s_mlo[e]) + __popc(s_mhi[e]) : 0;
-  const int act = cnt > 0 ? 1 : 0;
-  int ic = cnt, ia = act;
+}
+
+template <int EPT, int NB, int RS>
+__global__ __launch_bounds__(256) void k_norm_router(NormRouterArgs A) {
+  constexpr int VW = EPT % 4 == 0 ? 4 : (EPT % 2 == 0 ? 2 : 1);
+  constexpr int NV = EPT / VW;
+  static_assert(NV % RS == 0, "each part writes whole vectors");
+  __shared__ float red[4];
+  __shared__ float s_z[4][8];
+  __shared__ float s_x[256 * EPT];
+  __shared__ RouteLds R;
+  __shared__ int s_last;
+  const RouterArgs& a = A.r;
+  const int t = blockIdx.x / RS, q = blockIdx.x - t * RS;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int H = A.H;
+  const size_t base = (size_t)t * H;
+  const float inv_h = 1.0f / (float)H;
+  // Every load is issued before the first use: the row (branch partials, stream, gains)
+  // first, as it is needed first, then the router lines.  Part q scores experts 8q .. 8q+7:
+  // rows 8(q&1) .. +7 of 16-row tile q>>1, which fill one 128-byte line of every 8-wide k
+  // group of the packed router weight.  Lane l of wave w takes line (it*4 + w)*8 + l/8
+  // (k = 8 x line .. +7) and expert 8q + l%8, so each load instruction reads 1 KB of whole
+  // lines.
+  float pb[NB][EPT], s[EPT], gp[EPT], gq[EPT];
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int uc = __shfl_up(ic, d, 64), ua = __shfl_up(ia, d, 64);
-    if (lane >= d) { ic += uc; ia += ua; }
+  for (int v = 0; v < NV; ++v) {
+    const int i0 = (v * 256 + tid) * VW;
+#pragma unroll
+    for (int p = 0; p < NB; ++p) load_f32v<VW>(A.branch + p * A.branch_stride + base + i0, &pb[p][v * VW]);
+    load_f32v<VW>(A.stream + base + i0, &s[v * VW]);
+    load_f32v<VW>(A.g_post + i0, &gp[v * VW]);
+    load_f32v<VW>(A.g_pre + i0, &gq[v * VW]);
   }
-  if (lane == 63) { s_wc[wave] = ic; s_wa[wave] = ia; }
+  const int KT = H >> 5;
+  const auto rw = rsrc(a.w, (uint32_t)((size_t)((a.E + 15) >> 4) * KT * 1024));
+  u32x4_t wv[EPT];
+#pragma unroll
+  for (int it = 0; it < EPT; ++it) {
+    const int line = (it * 4 + wave) * 8 + (lane >> 3);
+    const uint32_t off = (uint32_t)(((q >> 1) * KT + (line >> 2)) * 1024 + (line & 3) * 256 +
+                                    (q & 1) * 128 + (lane & 7) * 16);
+    wv[it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  float u[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    u[e] = pb[0][e];
+#pragma unroll
+    for (int p = 1; p < NB; ++p) u[e] += pb[p][e];
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) ss += u[e] * u[e];
+  ss = sd::block_sum<4>(ss, red);
+  const float r1 = rsqrtf(ss * inv_h + A.eps);
+  ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    s[e] += u[e] * r1 * gp[e];
+    ss += s[e] * s[e];
+  }
+  ss = sd::block_sum<4>(ss, red);
+  const float r2 = rsqrtf(ss * inv_h + A.eps);
+  float x[EPT];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) x[e] = s[e] * r2 * gq[e];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int i0 = (v * 256 + tid) * VW;
+#pragma unroll
+    for (int jj = 0; jj < VW; ++jj) s_x[i0 + jj] = x[v * VW + jj];
+  }
+  // this part's share of the outputs: vectors v with v % RS == q
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    if (v % RS != q) continue;
+    const size_t i0 = base + (size_t)(v * 256 + tid) * VW;
+    uint16_t hi[VW], lo[VW];
+    _Float16 h16[VW], l16[VW];
+    if constexpr (VW == 4) {
+      *(f32x4_t*)(A.stream + i0) = f32x4_t{s[v * 4], s[v * 4 + 1], s[v * 4 + 2], s[v * 4 + 3]};
+    } else {
+#pragma unroll
+      for (int jj = 0; jj < VW; ++jj) A.stream[i0 + jj] = s[v * VW + jj];
+    }
+#pragma unroll
+    for (int jj = 0; jj < VW; ++jj) {
+      sd::split_bf16(x[v * VW + jj], hi[jj], lo[jj]);
+      sd::split_f16(x[v * VW + jj], h16[jj], l16[jj]);
+    }
+    if (A.out != nullptr) {
+      store16v<VW>(A.out + i0, hi);
+      store16v<VW>(A.out_lo + i0, lo);
+    }
+    store16v<VW>((uint16_t*)A.x16 + i0, (const uint16_t*)h16);
+    store16v<VW>((uint16_t*)A.x16_lo + i0, (const uint16_t*)l16);
+  }
   __syncthreads();
-  int pc = 0, pa = 0;
-  for (int w = 0; w < wave; ++w) { pc += s_wc[w]; pa += s_wa[w]; }
-  const int total = s_wc[0] + s_wc[1] + s_wc[2] + s_wc[3];
-  const int n_act = s_wa[0] + s_wa[1] + s_wa[2] + s_wa[3];
-  const int off = pc + ic - cnt;
-  if (e < E) {
-    a.counts[e] = cnt;
-    a.offsets[e] = off;
-    s_off[e] = off;
-    if (act) a.active[pa + ia - 1] = e;
-    if (e >= n_act) a.active[e] = -1;
+  // logits of the part's experts from the normalised row: fp32 products, lane sums over
+  // its lines, then the 8 lanes of an expert, then the 4 waves
+  float acc = 0.f;
+#pragma unroll
+  for (int it = 0; it < EPT; ++it) {
+    const int k0 = ((it * 4 + wave) * 8 + (lane >> 3)) * 8;
+    const f32x4_t x0 = *(const f32x4_t*)(s_x + k0), x1 = *(const f32x4_t*)(s_x + k0 + 4);
+    const u32x4_t w = wv[it];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const float wl = __uint_as_float(w[h] << 16), wh = __uint_as_float(w[h] & 0xffff0000u);
+      const float xl = h < 2 ? x0[2 * h] : x1[2 * h - 4], xh = h < 2 ? x0[2 * h + 1] : x1[2 * h - 3];
+      acc += wl * xl;
+      acc += wh * xh;
+    }
   }
+  acc += __shfl_xor(acc, 8, 64);
+  acc += __shfl_xor(acc, 16, 64);
+  acc += __shfl_xor(acc, 32, 64);
+  if (lane < 8) s_z[wave][lane] = acc;
+  __syncthreads();
+  if (tid < 8 && 8 * q + tid < a.E)
+    a.part[(size_t)t * a.E + 8 * q + tid] = (s_z[0][tid] + s_z[1][tid]) + (s_z[2][tid] + s_z[3][tid]);
+  // arrival: the logits are released before counting; the last arrival acquires them all
+  __syncthreads();
   if (tid == 0) {
-    a.offsets[E] = total;
-    a.active[E] = n_act;
+    __threadfence();
+    s_last = atomicAdd(a.counter, 1) == (int)gridDim.x - 1;
+    if (s_last) __threadfence();
   }
   __syncthreads();
-  for (int p = tid; p < nk; p += 256) {
-    const int t = p / k, ex = s_ids[p];
-    const int rank = t < 32 ? __popc(s_mlo[ex] & ((1u << t) - 1u))
-                            : __popc(s_mlo[ex]) + __popc(s_mhi[ex] & ((1u << (t - 32)) - 1u));
-    const int slot = s_off[ex] + rank;
-    a.slot_of[p] = slot;
-    a.tos[slot] = t;
-  }
-  if (tid == 0) *a.counter = 0;  // ready for the next launch
+  if (!s_last) return;
+  route_phase2<32>(a, 1, R);
 }
 
 __global__ void k_zero_i32(int* p) { *p = 0; }
@@ -671,6 +901,33 @@ hipError_t launch_router(const RouterArgs& a, hipStream_t st) {
   else if (a.b <= 32) hipLaunchKernelGGL(k_router<4>, grid, block, 0, st, a);
   else hipLaunchKernelGGL(k_router<8>, grid, block, 0, st, a);
   return hipGetLastError();
+}
+
+int norm_router_parts(int H, int E, int b, int k) {
+  if (H % 256 || b > 64 || b * k > 512 || k > 8) return 0;
+  const int ept = H / 256;
+  if (ept != 16 && ept != 1) return 0;  // instantiated widths: H = 4096 and H = 256
+  const int vw = ept % 4 == 0 ? 4 : (ept % 2 == 0 ? 2 : 1), nv = ept / vw;
+  // RS parts of 8 experts each; an odd part would leave half of its tile's lines to nobody
+  for (int rs : {1, 2, 4})
+    if (nv % rs == 0 && E <= 8 * rs) return rs;
+  return 0;
+}
+
+hipError_t launch_norm_router(const NormRouterArgs& a, int nbranch, hipStream_t st) {
+  const int rs = norm_router_parts(a.H, a.r.E, a.r.b, a.r.k);
+  if (rs == 0 || (nbranch != 1 && nbranch != 4)) return hipErrorInvalidValue;
+  if ((a.out == nullptr) != (a.out_lo == nullptr)) return hipErrorInvalidValue;
+  const dim3 grid(a.r.b * rs), block(256);
+#define SD_NR(EPT, NB, RS)                                                             \
+  if (a.H == 256 * EPT && nbranch == NB && rs == RS) {                                 \
+    hipLaunchKernelGGL((k_norm_router<EPT, NB, RS>), grid, block, 0, st, a);           \
+    return hipGetLastError();                                                          \
+  }
+  SD_NR(16, 4, 4) SD_NR(16, 1, 4) SD_NR(16, 4, 2) SD_NR(16, 1, 2) SD_NR(16, 4, 1) SD_NR(16, 1, 1)
+  SD_NR(1, 4, 1) SD_NR(1, 1, 1)
+#undef SD_NR
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_zero_i32(int* p, hipStream_t st) {

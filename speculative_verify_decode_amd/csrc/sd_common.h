@@ -209,6 +209,22 @@ struct RouterArgs {
   int *counts, *offsets, *slot_of, *tos, *active;
 };
 hipError_t launch_router(const RouterArgs& a, hipStream_t st);
+
+// Attention boundary (dual norm over nbranch partials of the attention branch) fused with
+// the router; r.part holds [b, E] logits, r.x / r.x_lo are unused, r.counter must be 0.
+struct NormRouterArgs {
+  int H;
+  const float* branch;     // fp32 [nbranch, b, H]
+  size_t branch_stride;    // floats between partials
+  float* stream;
+  const float *g_post, *g_pre;
+  float eps;
+  uint16_t *out, *out_lo;  // bf16 hi / lo terms of the pre-FFN norm output
+  _Float16 *x16, *x16_lo;  // fp16 hi / lo terms of it * 2^-8 (the expert input)
+  RouterArgs r;
+};
+int norm_router_parts(int H, int E, int b, int k);  // 0: shape not served by the fusion
+hipError_t launch_norm_router(const NormRouterArgs& a, int nbranch, hipStream_t st);
 hipError_t launch_zero_i32(int* p, hipStream_t st);
 
 struct MoeArgs {
