@@ -7,8 +7,9 @@ router/routing/pooler -> experts -> unpooler) of b = 8 verify rows at hidden 409
 8192-token paged context, replayed from a HIP graph.  Inputs are resident in HBM before the
 timed region.  To keep the 256 MB MALL and the L2s from serving repeat reads, steps rotate
 over R independent copies of the weights and KV (R * touched bytes >= 1 GB); one graph holds
-the R copies' steps back to back, as a serving graph holds consecutive layers.  Prints one
-JSON line.
+the R copies' steps back to back, as a serving graph holds consecutive layers.  For a
+workload with a draft head (the 4-layer chain) a step is the whole chain: every layer, the
+final boundary and the head.  Prints one JSON line.
 """
 
 import argparse
@@ -37,6 +38,9 @@ def algorithmic_bytes(wk, counts_per_layer):
         lens = wk["layers"][li]["seq_lens"].numpy().astype(np.int64)
         kv = lens.sum() * Hkv * D * 2 * 2 + b * Hkv * D * 2 * 2
         total += dense + int((counts > 0).sum()) * per_expert + kv
+    if wk.get("head") is not None and len(counts_per_layer) == len(wk["layers"]):
+        V = wk["head"]["w_lm"].shape[0]
+        total += 2 * V * H + 8 * V + 8 * H      # head weight, d2t, final and last post gains
     return total, int((counts_per_layer[0] > 0).sum()) * per_expert
 
 
@@ -115,15 +119,38 @@ def main():
     wk = synth.make_workload(args.workload)
     print(f"[bench] generated {args.workload} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
-    # first copy: one eager step to learn the routing (touched experts) and the byte count
-    r0 = StepRunner(wk, dev)
+    # A step is one layer step, or for a workload with a draft head the whole chain (every
+    # layer, the final boundary and the head).
+    chain = wk.get("head") is not None
+    H = wk["dims"]["hidden"]
+
+    def make_runner():
+        r = StepRunner(wk, dev)
+        r.chain_bufs = [torch.empty(wk["workload"].b, H, dtype=torch.float32, device=dev)
+                        for _ in r.layers]
+        return r
+
+    def run_step(r, sb, stream=None):
+        if chain:
+            r.chain(sb, r.act["branch_in"], r.chain_bufs, with_tau=False, stream=stream)
+        else:
+            r.layer_step(0, sb, r.act["branch_in"], stream=stream)
+
+    # first copy: eager layer steps to learn the routing (touched experts) and the byte count
+    r0 = make_runner()
     s = r0.act["stream"].clone()
-    r0.layer_step(0, s, r0.act["branch_in"])
-    torch.cuda.synchronize()
-    counts = r0.route_t["expert_counts"].cpu().numpy()
-    step_bytes, expert_bytes = algorithmic_bytes(wk, [counts])
-    R = args.copies or max(2, math.ceil(1.0e9 / step_bytes))
-    runners = [r0] + [StepRunner(wk, dev) for _ in range(R - 1)]
+    u = r0.act["branch_in"]
+    counts_per_layer = []
+    for i in range(len(r0.layers) if chain else 1):
+        u = r0.layer_step(i, s, u, branch_out=r0.chain_bufs[i])
+        torch.cuda.synchronize()
+        counts_per_layer.append(r0.route_t["expert_counts"].cpu().numpy())
+    counts = counts_per_layer[0]
+    step_bytes, expert_bytes = algorithmic_bytes(wk, counts_per_layer)
+    # (at most 16 copies: a step small enough to need more is launch-bound, not HBM-bound)
+    R = args.copies or min(16, max(2, math.ceil(1.0e9 / step_bytes)))
+    R = max(1, min(R, args.steps))
+    runners = [r0] + [make_runner() for _ in range(R - 1)]
     print(f"[bench] {R} rotation copies, {step_bytes / 1e6:.1f} MB algorithmic per step",
           file=sys.stderr, flush=True)
 
@@ -135,17 +162,17 @@ def main():
     streams = [r.act["stream"].clone() for r in runners]
     with torch.cuda.stream(st):
         for r, sb in zip(runners, streams):
-            r.layer_step(0, sb, r.act["branch_in"], stream=st)      # warm (lazy module load)
+            run_step(r, sb, stream=st)      # warm (lazy module load)
     torch.cuda.synchronize()
     g_all = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g_all, stream=st):
         for r, sb in zip(runners, streams):
-            r.layer_step(0, sb, r.act["branch_in"], stream=st)
+            run_step(r, sb, stream=st)
     singles = []
     for r, sb in zip(runners, streams):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=st):
-            r.layer_step(0, sb, r.act["branch_in"], stream=st)
+            run_step(r, sb, stream=st)
         singles.append(g)
     torch.cuda.synchronize()
 
@@ -215,7 +242,9 @@ def main():
     achieved = expert_bytes / (exp_us * 1e-6) / 1e9
 
     out = {
-        "metric": "µs per decode layer-step (b=8 verify) + achieved HBM GB/s vs peak",
+        "metric": ("µs per decode chain (every layer, final boundary, draft head) + achieved HBM "
+                   "GB/s vs peak" if chain else
+                   "µs per decode layer-step (b=8 verify) + achieved HBM GB/s vs peak"),
         "value": round(us, 3),
         "unit": "us",
         "n_gpus": 1,
@@ -231,7 +260,9 @@ def main():
                    "n_q_heads": d["n_q_heads"], "n_kv_heads": d["n_kv_heads"],
                    "head_dim": d["head_dim"], "experts": d["n_experts"], "top_k": d["top_k"],
                    "inter": d["inter"], "context": int(wk["layers"][0]["seq_lens"].sum()),
-                   "touched_experts": int((counts > 0).sum()), "rotation_copies": R},
+                   "touched_experts": [int((c > 0).sum()) for c in counts_per_layer] if chain
+                   else int((counts > 0).sum()),
+                   "layers": len(counts_per_layer), "rotation_copies": R},
         "step_bytes": int(step_bytes),
         "step_GBps": round(step_bytes / (us * 1e-6) / 1e9, 1),
         "step_frac_hbm": round(step_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define SD_ABI_VERSION 2
+#define SD_ABI_VERSION 3
 
 enum {
   SD_OK = 0,
@@ -118,7 +118,11 @@ typedef struct sd_layer_weights {
  * request including its q_rows verify tokens; positions int32 [b] (row j of request r is
  * at seq_lens[r] - q_rows + j); slot_mapping int64 [b] = block * 16 + offset where that
  * row's K/V is written (a negative slot writes nothing).  max_seq_len bounds seq_lens
- * (host value, sizes the launch; device seq_lens are clamped to max_blocks * 16). */
+ * (host value, sizes the launch; device seq_lens are clamped to max_blocks * 16).
+ * window: the layer's sliding window ([DEC] SpecializedDecode.plan: attn2 serves each
+ * layer's sliding window).  0 = full causal attention; w > 0 = a row at position p sees
+ * positions max(0, p - w + 1) .. p only.  The blocks a request's rows cannot see are not
+ * read; which blocks those are follows from seq_lens and the positions contract above. */
 typedef struct sd_kv {
   void *k_cache, *v_cache;
   int32_t num_blocks;
@@ -128,6 +132,7 @@ typedef struct sd_kv {
   const int32_t *positions;
   const int64_t *slot_mapping;
   int32_t n_req, max_seq_len;
+  int32_t window;
 } sd_kv;
 
 /* Routing outputs.  topk_ids int32 [b, k] (descending logit, ties to the lower expert
@@ -178,7 +183,8 @@ int sd_boundary_dualnorm(const sd_dims *dims, int32_t b, float *stream, const fl
  * stacked QKV projection of x (bf16 [b, H]); weightless per-head RMSNorm of q and k when
  * dims->qk_norm; RoPE at each row's position; bf16 K/V written to the cache at
  * slot_mapping (the cache is modified there and nowhere else); causal GQA attention of each
- * row over positions 0..p of its request; output gate o * sigmoid(o_gate); o_proj.
+ * row over positions 0..p of its request (the last kv->window of them when window > 0);
+ * output gate o * sigmoid(o_gate); o_proj.
  * out fp32 [b, H] (the attention branch). */
 int sd_attn_verify(const sd_dims *dims, int32_t b, const void *x, const sd_attn_weights *w,
                    const sd_kv *kv, float *out, void *ws, size_t ws_bytes, void *stream_handle);

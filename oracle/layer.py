@@ -145,14 +145,16 @@ def gather_request_kv(k_cache, v_cache, block_table_row, length):
     return k, v
 
 
-def paged_attention(q, k_cache, v_cache, block_table, positions, q_rows, scale=None):
+def paged_attention(q, k_cache, v_cache, block_table, positions, q_rows, scale=None, window=0):
     """Causal GQA attention of each verify row over its request's paged KV.
 
     Row t belongs to request r = t // q_rows and sits at position p = positions[t];
     it attends to tokens 0..p of that request (the draft layers are causal, [DSP]
     ``MuseSparkDSparkDecoderLayer.__init__``; attn2 reads the paged cache through the
-    block table, [DEC] ``plan``).  Query head h uses KV head h // (Hq / Hkv).
-    softmax(scale * q . K^T) . V with scale = D**-1/2 unless given.
+    block table, [DEC] ``plan``).  With a sliding window w > 0 (attn2 serves each layer's
+    sliding window, [DEC] ``plan``; the pages give no size or convention) the row sees only
+    the w most recent positions, max(0, p - w + 1)..p.  Query head h uses KV head
+    h // (Hq / Hkv).  softmax(scale * q . K^T) . V with scale = D**-1/2 unless given.
     q: [b, Hq, D] -> o [b, Hq, D], fp64.
     """
     q = np.asarray(q, dtype=np.float64)
@@ -164,7 +166,9 @@ def paged_attention(q, k_cache, v_cache, block_table, positions, q_rows, scale=N
     o = np.zeros_like(q)
     for t in range(b):
         r, p = t // q_rows, int(positions[t])
+        lo = max(0, p - window + 1) if window > 0 else 0
         k, v = gather_request_kv(k_cache, v_cache, block_table[r], p + 1)
+        k, v = k[lo:], v[lo:]
         for h in range(hq):
             g = h // group
             sc = scale * (k[:, g, :] @ q[t, h])
@@ -328,7 +332,8 @@ def layer_step(inp, dims, branch_in=None, front_embed=None, route_override=None)
                               d["n_kv_heads"], d["head_dim"], eps, d["rope_theta"],
                               bool(d.get("qk_norm", True)))
     kc, vc = kv_write(inp["k_cache"], inp["v_cache"], k, v, inp["slot_mapping"])
-    o = paged_attention(q, kc, vc, inp["block_table"], inp["positions"], d["q_rows"])
+    o = paged_attention(q, kc, vc, inp["block_table"], inp["positions"], d["q_rows"],
+                        window=int(inp.get("window", 0)))
     a = gate_oproj(o, gate, inp["w_o"])
     s, x_m = dual_norm(s, a, inp["g_post_attn"], inp["g_pre_ffn"], eps)
     z = router_logits(x_m, inp["w_router"], inp.get("logit_bias"))

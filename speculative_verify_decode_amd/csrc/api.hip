@@ -110,11 +110,12 @@ struct Ws {
 size_t up(size_t v) { return (v + 255) & ~(size_t)255; }
 
 Ws ws_layout(const sd_dims& d, int b, int n_req, int max_seq_len) {
-  const AttnPlan p = attn_plan(d, n_req, max_seq_len);
+  const AttnPlan p = attn_plan(d, n_req, max_seq_len, 0);
+  const size_t n_chunks = attn_chunk_bound(d, n_req, max_seq_len);  // any window fits
   const size_t H = d.hidden, D = d.head_dim, Hq = d.n_q_heads, Hkv = d.n_kv_heads;
   const size_t E = d.n_experts, k = d.top_k, I = d.inter, B = b;
   const size_t N = (2 * Hq + 2 * Hkv) * D;
-  const size_t parts = (size_t)n_req * Hkv * p.n_chunks;
+  const size_t parts = (size_t)n_req * Hkv * n_chunks;
   Ws w;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o += up(bytes); return at; };
@@ -171,6 +172,7 @@ int check_kv(const sd_dims* d, int b, const sd_kv* kv) {
   if (kv->max_blocks * 16 < kv->max_seq_len)
     return fail(SD_EINVAL, "block table of %d blocks per request cannot hold %d tokens",
                 kv->max_blocks, kv->max_seq_len);
+  if (kv->window < 0) return fail(SD_EINVAL, "sliding window %d is negative", kv->window);
   return SD_OK;
 }
 
@@ -216,14 +218,17 @@ int run_attention(const sd_dims* d, int b, const uint16_t* x, const uint16_t* x_
                             kv->positions, kv->slot_mapping, q, q_lo, gate,
                             (uint16_t*)kv->k_cache, (uint16_t*)kv->v_cache, st),
             "qkv front epilogue");
-  const AttnPlan p = attn_plan(*d, kv->n_req, kv->max_seq_len);
+  const AttnPlan p = attn_plan(*d, kv->n_req, kv->max_seq_len, kv->window);
+  if (p.n_chunks > attn_chunk_bound(*d, kv->n_req, kv->max_seq_len))
+    return fail(SD_EHIP, "internal: attention plan of %d chunks exceeds the workspace's",
+                p.n_chunks);
   AttnArgs aa{};
   aa.q = q; aa.q_lo = q_lo;
   aa.k_cache = (const uint16_t*)kv->k_cache; aa.v_cache = (const uint16_t*)kv->v_cache;
   aa.block_table = kv->block_table; aa.max_blocks = kv->max_blocks; aa.seq_lens = kv->seq_lens;
   aa.num_blocks = kv->num_blocks;
   aa.positions = kv->positions; aa.n_req = kv->n_req; aa.Hq = Hq; aa.Hkv = Hkv; aa.D = D;
-  aa.q_rows = d->q_rows; aa.scale = scale_of(d);
+  aa.q_rows = d->q_rows; aa.window = kv->window; aa.scale = scale_of(d);
   aa.part_acc = at<float>(ws, L.part_acc); aa.part_ml = at<float>(ws, L.part_ml);
   aa.gate = gate; aa.gate_stride = Hq * D;
   uint16_t* o = at<uint16_t>(ws, L.o);

@@ -27,6 +27,14 @@ namespace {
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr int kMaxChunkBlocks = 2048;
 
+// The first block a request's rows can see: with a sliding window w, the lowest position
+// of the request's rows (seq_len - q_rows) minus w - 1; block 0 otherwise.
+__device__ __forceinline__ int first_block(const AttnArgs& a, int r) {
+  if (a.window <= 0) return 0;
+  const int L = min(a.seq_lens[r], a.max_blocks * 16);
+  return max(0, L - a.q_rows - a.window + 1) >> 4;
+}
+
 // Workgroup (chunk, kv head g, request r): blocks [chunk * cb, +cb) of the request, one
 // workgroup per CU at most.  The chunk's block ids (clamped to the pool) and the query
 // group (hi/lo) are staged in LDS first; each of the 4 waves then streams 2-block windows
@@ -50,7 +58,8 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a, int cb, int n_ch
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int i = lane & 15, G = lane >> 4;
   const int group = a.Hq / a.Hkv;
-  const int blk_begin = chunk * cb;
+  // chunks start at the request's first visible block (block 0 without a window)
+  const int blk_begin = first_block(a, r) + chunk * cb;
   const float sl2 = a.scale * LOG2E;
   const size_t kvh = (size_t)16 * D;  // elements per (block, head)
   const int* btr = a.block_table + (size_t)r * a.max_blocks;
@@ -87,7 +96,7 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a, int cb, int n_ch
            clamp_blk(btr[min(wb0 + 1, a.max_blocks - 1)]));
 
   // stage block ids and queries; neither depends on the request length
-  const int ncb = min(cb, a.max_blocks - blk_begin);  // >= 1: the grid covers max_blocks
+  const int ncb = min(cb, a.max_blocks - blk_begin);  // <= 0 only past the table's end
   for (int j = tid; j < ncb; j += 256) s_bt[j] = clamp_blk(btr[blk_begin + j]);
   constexpr int QCH = QG * D / 8;  // 16-byte pieces of one query term
   for (int c = tid; c < 2 * QCH; c += 256) {
@@ -98,11 +107,12 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a, int cb, int n_ch
     *(u32x4_t*)&s_q[term][qi][d8] = *(const u32x4_t*)((term ? a.q_lo : a.q) + qo);
   }
   const int L = min(a.seq_lens[r], a.max_blocks * 16);  // never read past the table row
-  int qpos[NQT];
+  int qpos[NQT], qlow[NQT];  // visible tokens: qlow < tok <= qpos
 #pragma unroll
   for (int qt = 0; qt < NQT; ++qt) {
     const int qi = 16 * qt + i;
     qpos[qt] = a.positions[r * a.q_rows + (qi - (qi / a.q_rows) * a.q_rows)];
+    qlow[qt] = a.window > 0 ? qpos[qt] - a.window : -1;
   }
   __syncthreads();
   const int nblk = (L + 15) >> 4;
@@ -158,7 +168,8 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a, int cb, int n_ch
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int tok = tok_base + 8 * G + 4 * t + rr;
-          const float v = tok <= qpos[qt] ? (sh[t][rr] + slo[t][rr]) * sl2 : -INFINITY;
+          const float v = (tok <= qpos[qt] && tok > qlow[qt]) ? (sh[t][rr] + slo[t][rr]) * sl2
+                                                               : -INFINITY;
           sc[t][rr] = v;
           mx = fmaxf(mx, v);
         }
@@ -263,7 +274,7 @@ __global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a, int cb, int n_
   const int g = h / group, hh = h - g * group;
   const int qi = hh * a.q_rows + jr;
   const int L = min(a.seq_lens[r], a.max_blocks * 16);
-  const int nc = max(min((((L + 15) >> 4) + cb - 1) / cb, n_chunks), 1);
+  const int nc = max(min((((L + 15) >> 4) - first_block(a, r) + cb - 1) / cb, n_chunks), 1);
   const size_t p0 = ((size_t)r * a.Hkv + g) * n_chunks;
   const float* pa = a.part_acc + (p0 * qg + qi) * a.D + d;
   const size_t cs = (size_t)qg * a.D;  // chunk stride
@@ -319,17 +330,27 @@ __global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a, int cb, int n_
 
 }  // namespace
 
-AttnPlan attn_plan(const sd_dims& d, int n_req, int max_seq_len) {
+AttnPlan attn_plan(const sd_dims& d, int n_req, int max_seq_len, int window) {
   AttnPlan p;
-  const int max_blocks = (max_seq_len + 15) / 16;
-  const long units = (long)n_req * d.n_kv_heads * max_blocks;
+  int span = (max_seq_len + 15) / 16;
+  if (window > 0) span = min(span, (int)(((long)window + d.q_rows - 1 + 15) / 16) + 1);
+  const long units = (long)n_req * d.n_kv_heads * span;
   // about one workgroup per CU (4 waves x 2-block windows, so a multiple of 8 blocks)
   int cb = 8;
   while (units / cb > 256 && cb < kMaxChunkBlocks) cb *= 2;
   p.chunk_blocks = cb;
-  p.n_chunks = (max_blocks + cb - 1) / cb;
+  p.n_chunks = (span + cb - 1) / cb;
   p.qg = (d.n_q_heads / d.n_kv_heads) * d.q_rows;
   return p;
+}
+
+int attn_chunk_bound(const sd_dims& d, int n_req, int max_seq_len) {
+  // a plan's chunks are at most units / cb + 1 <= 256 / (n_req * Hkv) + 1 when cb stops
+  // below the cap, and span / kMaxChunkBlocks + 1 at the cap; the full span is one plan
+  const int full = attn_plan(d, n_req, max_seq_len, 0).n_chunks;
+  const int small = 256 / max(1, n_req * d.n_kv_heads) + 1;
+  const int capped = (max_seq_len + 15) / 16 / kMaxChunkBlocks + 1;
+  return max(full, max(small, capped));
 }
 
 hipError_t launch_attention(const AttnArgs& a, const AttnPlan& p, hipStream_t st) {

@@ -167,10 +167,14 @@ hipError_t launch_qkv_post(const float* qkv, int nparts, int b, int Hq, int Hkv,
 
 struct AttnPlan {
   int chunk_blocks;   // blocks per workgroup (a multiple of 8)
-  int n_chunks;       // chunks per (request, kv head) at max_seq_len
+  int n_chunks;       // chunks per (request, kv head) over the visible span
   int qg;             // queries per (request, kv head) = group * q_rows
 };
-AttnPlan attn_plan(const sd_dims& d, int n_req, int max_seq_len);
+// window 0: the span is every block up to max_seq_len; window w > 0: the blocks a request's
+// rows can see, at most ceil((w + q_rows - 1) / 16) + 1 starting at the first visible one
+AttnPlan attn_plan(const sd_dims& d, int n_req, int max_seq_len, int window);
+// chunks per (request, kv head) that no window can exceed at this max_seq_len
+int attn_chunk_bound(const sd_dims& d, int n_req, int max_seq_len);
 
 struct AttnArgs {
   const uint16_t* q;          // bf16 hi terms [b, Hq, D]
@@ -183,6 +187,7 @@ struct AttnArgs {
   const int* seq_lens;
   const int* positions;
   int n_req, Hq, Hkv, D, q_rows;
+  int window;                 // 0: causal; w > 0: positions p - w + 1 .. p
   float scale;
   float* part_acc;            // [n_req * Hkv * n_chunks, qg, D]
   float* part_ml;             // [n_req * Hkv * n_chunks, qg, 2]

@@ -45,6 +45,7 @@ class Workload:
     target_vocab: int = 0
     base_width: int = 1024            # head multiplier = (hidden / base_width) ** -1
     soft_cap: float = 30.0
+    window: int = 0                   # sliding window of every layer (0: full causal)
     seed: int = 0
 
     @property
@@ -75,6 +76,8 @@ WORKLOADS = {
                                  pool_blocks=4096, skew_rows=0.25, **_BIG),
     "h4096_b8_ctx131k": Workload("h4096_b8_ctx131k", n_req=1, ctx=(131072,),
                                  pool_blocks=8192 + 64, **_BIG),
+    "h4096_b8_ctx131k_win8k": Workload("h4096_b8_ctx131k_win8k", n_req=1, ctx=(131072,),
+                                       pool_blocks=8192 + 64, window=8192, **_BIG),
     "h4096_chain4_head": Workload("h4096_chain4_head", n_req=1, ctx=(8192,), pool_blocks=4096,
                                   n_layers=4, draft_vocab=32768, target_vocab=131072, **_BIG),
 }
@@ -148,7 +151,8 @@ def make_kv(w: Workload, seed, tag=""):
     return dict(k_cache=_bf16(k), v_cache=_bf16(v), block_table=torch.from_numpy(bt),
                 seq_lens=torch.from_numpy(lens.astype(np.int32)),
                 positions=torch.from_numpy(positions), slot_mapping=torch.from_numpy(slots),
-                num_blocks=nb, max_blocks=max_blocks, max_seq_len=int(lens.max()))
+                num_blocks=nb, max_blocks=max_blocks, max_seq_len=int(lens.max()),
+                window=int(w.window))
 
 
 def make_layer_weights(w: Workload, seed, tag=""):

@@ -26,6 +26,7 @@ def oracle_layer_inputs(lay, act, stream=None):
     inp = {k: np64(lay[k]) for k in LAYER_KEYS}
     inp["stream"] = np64(act["stream"]) if stream is None else stream
     inp["logit_bias"] = np64(act.get("logit_bias"))
+    inp["window"] = int(lay.get("window", 0))
     return inp
 
 

@@ -55,7 +55,7 @@ def test_no_extra_exports_beyond_header(lib):
 
 
 def test_abi_version(lib):
-    assert B.abi_version() == 2
+    assert B.abi_version() == 3
 
 
 def test_workspace_bytes_host_only(lib):
@@ -121,6 +121,8 @@ def test_attention_validation(lib):
     assert _rc_attn(d, _kv(max_blocks=4)) == -1                   # table too short
     assert _rc_attn(d, _kv(k_cache=FAKE + 2)) == -1                # misaligned cache
     assert _rc_attn(d, _kv(seq_lens=None)) == -1
+    assert _rc_attn(d, _kv(window=-1)) == -1                      # negative sliding window
+    assert "window" in lib.sd_last_error().decode()
     assert _rc_attn(d, _kv()) == -4                               # no workspace
     assert _rc_attn(d, _kv(), ws=FAKE, ws_bytes=1024) == -4        # too small
     assert "need" in lib.sd_last_error().decode()

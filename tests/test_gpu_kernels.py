@@ -149,6 +149,38 @@ def test_attn_verify_matches_oracle(name):
         assert_close(got[mask], want[mask], key)
 
 
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,windows", [
+    ("tiny_b8_ctx128", (1, 9, 40, 300)),
+    ("h4096_b8_ctx8k", (1, 100, 4096, 8184, 9000)),
+    ("h4096_b64_ragged", (2048,)),
+    ("h4096_b8_ctx131k", (8192,)),
+])
+def test_attn_sliding_window_matches_oracle(name, windows):
+    """Sliding windows from one visible token (the row's own) past the whole context."""
+    wk = workload(name)
+    r = runner(wk)
+    lay, d, b = wk["layers"][0], wk["dims"], r.b
+    x = wk["act"]["front_embed"]
+    L = r.layers[0]
+    q, k, v, gate = oracle.qkv_front(np64(x), np64(lay["w_qkv"]), np64(lay["positions"]),
+                                     d["n_q_heads"], d["n_kv_heads"], d["head_dim"], d["eps"],
+                                     d["rope_theta"], bool(d["qk_norm"]))
+    kc, vc = oracle.kv_write(np64(lay["k_cache"]), np64(lay["v_cache"]), k, v, np64(lay["slot_mapping"]))
+    for window in windows:
+        say(f"[gpu-test] attn_verify {name} window {window}")
+        kv = B.SdKv.from_buffer_copy(L.kv)
+        kv.window = window
+        out = torch.empty(b, d["hidden"], dtype=torch.float32, device=DEV)
+        B.attn_verify(r.dims, b, x.to(DEV), L.attn_w, kv, out, r.ws)
+        torch.cuda.synchronize()
+        o = oracle.paged_attention(q, kc, vc, np64(lay["block_table"]), np64(lay["positions"]),
+                                   d["q_rows"], window=window)
+        a = oracle.gate_oproj(o, gate, np64(lay["w_o"]))
+        w = assert_close(np64(out), a, f"attention output, window {window}")
+        say(f"[gpu-test] attn {name} window {window}: worst scaled err {w:.2e}")
+
+
 # ------------------------------------------------------------------------ routing
 @pytest.mark.parametrize("name", ["tiny_b8_ctx128", "h4096_b8_ctx8k", "h4096_b64_ragged"])
 def test_moe_route_matches_oracle(name):

@@ -53,7 +53,7 @@ def run_and_compare(wk, front=False):
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["tiny_b8_ctx128", "h4096_b8_ctx8k", "h4096_b64_ragged",
-                                  "h4096_b8_ctx131k"])
+                                  "h4096_b8_ctx131k", "h4096_b8_ctx131k_win8k"])
 def test_layer_step_end_to_end(name):
     say(f"[gpu-test] layer step {name}")
     run_and_compare(workload(name))
@@ -73,6 +73,14 @@ def test_layer_step_ragged_and_minimal_contexts(ctx):
 def test_layer_step_max_rows_tiny():
     w = synth.with_overrides(synth.WORKLOADS["tiny_b8_ctx128"], n_req=8,
                              ctx=(128, 9, 64, 300, 33, 16, 250, 100), name="tiny_b64")
+    run_and_compare(synth.make_workload(w))
+
+
+@pytest.mark.parametrize("window", [1, 20, 64])
+def test_layer_step_sliding_window_ragged_tiny(window):
+    # two requests of different lengths: the first visible block differs per request
+    w = synth.with_overrides(synth.WORKLOADS["tiny_b8_ctx128"], n_req=2, ctx=(45, 200),
+                             window=window, name=f"tiny_win{window}")
     run_and_compare(synth.make_workload(w))
 
 

@@ -155,7 +155,7 @@ def _attn_case(n_req=2, q_rows=8, hq=4, hkv=2, d=16, lens=(45, 70), nb=16, seed=
     return q, kc, vc, bt, pos
 
 
-def _sdpa_reference(q, kc, vc, bt, pos, q_rows):
+def _sdpa_reference(q, kc, vc, bt, pos, q_rows, window=0):
     b, hq, d = q.shape
     hkv = kc.shape[1]
     out = np.zeros_like(q)
@@ -166,7 +166,10 @@ def _sdpa_reference(q, kc, vc, bt, pos, q_rows):
         k = torch.from_numpy(kc[bt[r, t // 16], :, t % 16, :]).permute(1, 0, 2)
         v = torch.from_numpy(vc[bt[r, t // 16], :, :, t % 16]).permute(1, 0, 2)
         k, v = k.repeat_interleave(hq // hkv, 0), v.repeat_interleave(hq // hkv, 0)
-        mask = torch.from_numpy(t[None, :] <= pos[rows][:, None])
+        mask = t[None, :] <= pos[rows][:, None]
+        if window > 0:                                  # band of the w most recent positions
+            mask &= t[None, :] > pos[rows][:, None] - window
+        mask = torch.from_numpy(mask)
         qq = torch.from_numpy(q[rows]).permute(1, 0, 2)
         out[rows] = F.scaled_dot_product_attention(qq, k, v, attn_mask=mask).permute(1, 0, 2).numpy()
     return out
@@ -176,6 +179,31 @@ def test_paged_attention_matches_sdpa_on_gathered_kv():
     q, kc, vc, bt, pos = _attn_case()
     got = oracle.paged_attention(q, kc, vc, bt, pos, 8)
     assert np.allclose(got, _sdpa_reference(q, kc, vc, bt, pos, 8), atol=1e-12)
+
+
+@pytest.mark.parametrize("window", [1, 2, 7, 16, 23, 40])
+def test_sliding_window_matches_sdpa_with_band_mask(window):
+    q, kc, vc, bt, pos = _attn_case(seed=11)
+    got = oracle.paged_attention(q, kc, vc, bt, pos, 8, window=window)
+    assert np.allclose(got, _sdpa_reference(q, kc, vc, bt, pos, 8, window=window), atol=1e-12)
+
+
+def test_window_of_one_returns_the_rows_own_value():
+    # one visible key: softmax weight 1, so the output is V at the row's own position
+    q, kc, vc, bt, pos = _attn_case(hq=4, hkv=2, seed=12)
+    got = oracle.paged_attention(q, kc, vc, bt, pos, 8, window=1)
+    for t in range(q.shape[0]):
+        p = int(pos[t])
+        blk = bt[t // 8, p // 16]
+        for h in range(4):
+            assert np.array_equal(got[t, h], vc[blk, h // 2, :, p % 16])
+
+
+def test_window_covering_the_context_equals_full_causal():
+    q, kc, vc, bt, pos = _attn_case(seed=13)
+    full = oracle.paged_attention(q, kc, vc, bt, pos, 8)
+    for w in (int(pos.max()) + 1, 10 ** 6):
+        assert np.array_equal(oracle.paged_attention(q, kc, vc, bt, pos, 8, window=w), full)
 
 
 def test_paged_attention_block_table_permutation_invariant():

@@ -37,8 +37,12 @@ def _dual_norm_plain_add(stream, branch, g_post, g_pre, eps):
     return s, OL.rmsnorm(s, g_pre, eps)
 
 
-def _attn_off_by_one(q, kc, vc, bt, pos, q_rows, scale=None):
-    return ORIG_ATTN(q, kc, vc, bt, np.asarray(pos) - 1, q_rows, scale)
+def _attn_off_by_one(q, kc, vc, bt, pos, q_rows, scale=None, window=0):
+    return ORIG_ATTN(q, kc, vc, bt, np.asarray(pos) - 1, q_rows, scale, window)
+
+
+def _window_one_too_wide(q, kc, vc, bt, pos, q_rows, scale=None, window=0):
+    return ORIG_ATTN(q, kc, vc, bt, pos, q_rows, scale, window + 1 if window > 0 else 0)
 
 
 def _gate_dropped(o, gate, w_o):
@@ -63,12 +67,15 @@ MUTANTS = [
     ("topk_route", _topk_high_index, [TL.test_topk_ties_go_to_lower_index]),
     ("dual_norm", _dual_norm_plain_add, [TL.test_dual_norm_post_norm_on_branch_then_pre_norm]),
     ("paged_attention", _attn_off_by_one, [TL.test_paged_attention_matches_sdpa_on_gathered_kv]),
+    ("paged_attention", _window_one_too_wide,
+     [TL.test_window_of_one_returns_the_rows_own_value,
+      lambda: TL.test_sliding_window_matches_sdpa_with_band_mask(7)]),
     ("gate_oproj", _gate_dropped, [TL.test_gate_limits]),
     ("pooler", _pooler_reversed, [TL.test_pooler_is_stable_counting_sort]),
 ]
 
 
-@pytest.mark.parametrize("name,mutant,pins", MUTANTS, ids=[m[0] for m in MUTANTS])
+@pytest.mark.parametrize("name,mutant,pins", MUTANTS, ids=[m[1].__name__.strip("_") for m in MUTANTS])
 def test_pins_catch_planted_mistake(monkeypatch, name, mutant, pins):
     monkeypatch.setattr(oracle, name, mutant)
     monkeypatch.setattr(OL, name, mutant)
