@@ -36,6 +36,9 @@ def algorithmic_bytes(wk, counts_per_layer):
     total = 0.0
     for li, counts in enumerate(counts_per_layer):
         lens = wk["layers"][li]["seq_lens"].numpy().astype(np.int64)
+        window = int(wk["layers"][li].get("window", 0))
+        if window > 0:                          # a request's rows see its last w + q - 1 tokens
+            lens = np.minimum(lens, window + w.q_rows - 1)
         kv = lens.sum() * Hkv * D * 2 * 2 + b * Hkv * D * 2 * 2
         total += dense + int((counts > 0).sum()) * per_expert + kv
     if wk.get("head") is not None and len(counts_per_layer) == len(wk["layers"]):

@@ -40,7 +40,7 @@ __device__ __forceinline__ int first_block(const AttnArgs& a, int r) {
 // group (hi/lo) are staged in LDS first; each of the 4 waves then streams 2-block windows
 // w = 2 * wave + 8 j, loading window j + 1 while window j is in the matrix cores.  Loads
 // are unconditional: tokens past the request's end are masked after loading (scores by
-// selection to -inf, V by selection to 0).
+// selection to -inf, V by selection to 0).  K and V are read once: non-temporal loads.
 template <int D, int NQT>
 __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a, int cb, int n_chunks) {
   constexpr int QG = 16 * NQT;
@@ -77,13 +77,13 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a, int cb, int n_ch
       const int pb = (tw >> 4) ? pb1 : pb0;
       const uint16_t* kp = a.k_cache + ((size_t)pb * a.Hkv + g) * kvh + (size_t)(tw & 15) * D + 8 * G;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) W.k[t][c] = *(const bf16x8_t*)(kp + 32 * c);
+      for (int c = 0; c < NC; ++c) W.k[t][c] = __builtin_nontemporal_load((const bf16x8_t*)(kp + 32 * c));
     }
     // V^T rows: dim 16 dt + i, window tokens 8G .. 8G+7
     const int pb = (G >> 1) ? pb1 : pb0;
     const uint16_t* vp = a.v_cache + ((size_t)pb * a.Hkv + g) * kvh + (size_t)i * 16 + 8 * (G & 1);
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) W.v[dt] = *(const bf16x8_t*)(vp + (size_t)dt * 256);
+    for (int dt = 0; dt < NDT; ++dt) W.v[dt] = __builtin_nontemporal_load((const bf16x8_t*)(vp + (size_t)dt * 256));
   };
   auto clamp_blk = [&](int id) { return min(max(id, 0), a.num_blocks - 1); };
 

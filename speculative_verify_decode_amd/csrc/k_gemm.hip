@@ -30,6 +30,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t b
 __device__ __forceinline__ bf16x8_t buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+// Weights are read once per step: non-temporal loads (cache policy bit 1) stream them
+// without displacing reusable lines, which measurably raises the achieved HBM rate.
+constexpr int kStream = 2;
+__device__ __forceinline__ bf16x8_t buf_load8_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kStream));
+}
 
 constexpr uint32_t kOob = 0x80000000u;  // a byte offset past every activation buffer
 
@@ -119,7 +125,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_res(GemmArgs a, int ntiles) {
   auto load = [&](bf16x8_t (&A)[S], int tile) {
     const uint32_t o0 = tile < ntiles ? (uint32_t)(((size_t)tile * KT + kt0) * 1024 + lane * 16) : kOob;
 #pragma unroll
-    for (int u = 0; u < S; ++u) A[u] = buf_load8(rw, o0 + 1024 * u);
+    for (int u = 0; u < S; ++u) A[u] = buf_load8_nt(rw, o0 + 1024 * u);
   };
   auto finish = [&](bf16x8_t (&A)[S], int tile, int buf) {
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};

@@ -24,6 +24,9 @@ constexpr uint32_t kOob = 0x80000000u;  // a byte offset past every activation b
 __device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+// Weights are read once per step: non-temporal loads (cache policy bit 1) stream them
+// without displacing reusable lines, which measurably raises the achieved HBM rate.
+constexpr int kStream = 2;
 
 // Phase 1, every workgroup: partial logits of one 16-expert tile over 256 columns of H
 // (4 waves x 2 MFMA steps; rows as bf16 hi/lo terms in columns 0-7 / 8-15 of NCT tiles),
@@ -335,7 +338,7 @@ __global__ __launch_bounds__(256) void k_norm_router(NormRouterArgs A) {
     const int line = (it * 4 + wave) * 8 + (lane >> 3);
     const uint32_t off = (uint32_t)(((q >> 1) * KT + (line >> 2)) * 1024 + (line & 3) * 256 +
                                     (q & 1) * 128 + (lane & 7) * 16);
-    wv[it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0));
+    wv[it] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, kStream));
   }
   __builtin_amdgcn_sched_barrier(0);
   float u[EPT];
@@ -489,8 +492,8 @@ __device__ __forceinline__ void load_slice(Slice<NU>& s, const ExpertRes& r, int
   for (int u = 0; u < NU; ++u) {
     const uint32_t oc = t0 < 0 ? kOob : (uint32_t)(t0 + u) * 1024u + 16u * lane;
     const uint32_t os = t0 < 0 ? kOob : (uint32_t)(t0 + u) * 128u + 2u * lane;
-    s.codes[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r.c, oc, 0, 0));
-    s.scales[u] = __builtin_amdgcn_raw_buffer_load_b16(r.s, os, 0, 0);
+    s.codes[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r.c, oc, 0, kStream));
+    s.scales[u] = __builtin_amdgcn_raw_buffer_load_b16(r.s, os, 0, kStream);
   }
 }
 
