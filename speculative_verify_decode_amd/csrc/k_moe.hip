@@ -451,6 +451,8 @@ struct MoeMeta {
   int cnt[256];
   int off[256];
   int tos[512];
+  float g13[256], g2[256];  // per-expert global scales: an LDS read in the epilogue, not a
+                            // global load queued behind the next unit's weights
 };
 
 __device__ __forceinline__ void stage_meta(const MoeArgs& a, MoeMeta& m) {
@@ -459,6 +461,8 @@ __device__ __forceinline__ void stage_meta(const MoeArgs& a, MoeMeta& m) {
   for (int p = threadIdx.x; p < a.E; p += blockDim.x) {
     m.cnt[p] = a.counts[p];
     m.off[p] = a.offsets[p];
+    m.g13[p] = a.w13_gscale[p];
+    m.g2[p] = a.w2_gscale[p];
   }
   for (int p = threadIdx.x; p < nk; p += blockDim.x) m.tos[p] = a.tos[p];
   __syncthreads();
@@ -615,7 +619,7 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w13(MoeArgs a) {
         }
       }
       if (i < 8) {
-        const float sc = SD_X16_UNSCALE * a.w13_gscale[U.e];
+        const float sc = SD_X16_UNSCALE * meta.g13[U.e];
         const int n = U.nt * 16 + 4 * G;  // lane rows n .. n+3 of the gate (and up) block
 #pragma unroll
         for (int c = 0; c < NCT; ++c) {
@@ -745,7 +749,7 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w2(MoeArgs a) {
         for (int r = 0; r < 4; ++r) acc[c][r] += __shfl_xor(acc[c][r], 8, 64);
       }
       if (i < 8) {
-        const float sc = SD_X16_UNSCALE * a.w2_gscale[U.e];
+        const float sc = SD_X16_UNSCALE * meta.g2[U.e];
         const int n = U.nt * 16 + 4 * G;
 #pragma unroll
         for (int c = 0; c < NCT; ++c) {
