@@ -87,41 +87,64 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a, int cb, int n_ch
   };
   auto clamp_blk = [&](int id) { return min(max(id, 0), a.num_blocks - 1); };
 
-  // the wave's first window starts loading at once, its block ids read straight from the
-  // table (uniform loads); ids are clamped into the pool and tokens past the request's end
-  // are masked, so a window past the end reads harmless data
-  Win W0, W1;
-  const int wb0 = blk_begin + 2 * wave;
-  load_win(W0, clamp_blk(btr[min(wb0, a.max_blocks - 1)]),
-           clamp_blk(btr[min(wb0 + 1, a.max_blocks - 1)]));
-
-  // stage block ids and queries; neither depends on the request length
-  const int ncb = min(cb, a.max_blocks - blk_begin);  // <= 0 only past the table's end
-  for (int j = tid; j < ncb; j += 256) s_bt[j] = clamp_blk(btr[blk_begin + j]);
-  constexpr int QCH = QG * D / 8;  // 16-byte pieces of one query term
-  for (int c = tid; c < 2 * QCH; c += 256) {
+  // Issue order matters: loads complete in order, so the small loads the staging barrier
+  // needs (query terms, the chunk's block ids) go first, then the wave's first two windows,
+  // whose block ids come straight from the table (uniform loads).  Ids are clamped into the
+  // pool and tokens past the request's end are masked, so a window past the end reads
+  // harmless data; a second window past the end re-reads the first one's blocks, which merge
+  // with the loads in flight.
+  constexpr int QCH = QG * D / 8;                 // 16-byte pieces of one query term
+  constexpr int NQP = (2 * QCH + 255) / 256;      // pieces per thread
+  u32x4_t qv[NQP];
+#pragma unroll
+  for (int n = 0; n < NQP; ++n) {
+    const int c = min(tid + 256 * n, 2 * QCH - 1);
     const int term = c / QCH, rem = c - term * QCH;
     const int qi = rem / (D / 8), d8 = (rem - qi * (D / 8)) * 8;
     const int hh = qi / a.q_rows, jr = qi - hh * a.q_rows;
     const size_t qo = ((size_t)(r * a.q_rows + jr) * a.Hq + g * group + hh) * D + d8;
-    *(u32x4_t*)&s_q[term][qi][d8] = *(const u32x4_t*)((term ? a.q_lo : a.q) + qo);
+    qv[n] = *(const u32x4_t*)((term ? a.q_lo : a.q) + qo);
   }
-  const int L = min(a.seq_lens[r], a.max_blocks * 16);  // never read past the table row
+  const int ncb = min(cb, a.max_blocks - blk_begin);  // <= 0 only past the table's end
+  const int bt0 = btr[min(blk_begin + min(tid, max(ncb - 1, 0)), a.max_blocks - 1)];
   int qpos[NQT], qlow[NQT];  // visible tokens: qlow < tok <= qpos
 #pragma unroll
   for (int qt = 0; qt < NQT; ++qt) {
     const int qi = 16 * qt + i;
     qpos[qt] = a.positions[r * a.q_rows + (qi - (qi / a.q_rows) * a.q_rows)];
-    qlow[qt] = a.window > 0 ? qpos[qt] - a.window : -1;
   }
-  __syncthreads();
+  const int L = min(a.seq_lens[r], a.max_blocks * 16);  // never read past the table row
   const int nblk = (L + 15) >> 4;
+  Win W0, W1;
+  const int wb0 = blk_begin + 2 * wave, wb1 = wb0 + 8;
+  const int mb = a.max_blocks - 1;
+  const int id0 = btr[min(wb0, mb)], id1 = btr[min(wb0 + 1, mb)];
+  const bool w1_in = wb1 < nblk;
+  __builtin_amdgcn_sched_barrier(0);  // the small loads above stay ahead of the windows
+  load_win(W0, clamp_blk(id0), clamp_blk(id1));
+  load_win(W1, clamp_blk(w1_in ? btr[min(wb1, mb)] : id0), clamp_blk(w1_in ? btr[min(wb1 + 1, mb)] : id1));
+
+  // stage block ids and queries
+#pragma unroll
+  for (int n = 0; n < NQP; ++n) {
+    const int c = tid + 256 * n;
+    if (c < 2 * QCH) {
+      const int term = c / QCH, rem = c - term * QCH;
+      const int qi = rem / (D / 8), d8 = (rem - qi * (D / 8)) * 8;
+      *(u32x4_t*)&s_q[term][qi][d8] = qv[n];
+    }
+  }
+  if (tid < ncb) s_bt[tid] = clamp_blk(bt0);
+  for (int j = tid + 256; j < ncb; j += 256) s_bt[j] = clamp_blk(btr[blk_begin + j]);  // long chunks
+#pragma unroll
+  for (int qt = 0; qt < NQT; ++qt) qlow[qt] = a.window > 0 ? qpos[qt] - a.window : -1;
+  __syncthreads();
   if (blk_begin >= nblk) return;  // past this request's end (uniform per workgroup)
   const int blk_end = min(blk_begin + cb, nblk);
-  // later windows take their block ids from LDS (wb + 1 past blk_end re-reads block wb)
+  // later windows take their block ids from LDS (a window's second block past blk_end
+  // re-reads its first)
   auto load_at = [&](Win& W, int wb) {
-    const int pb0 = s_bt[wb - blk_begin];
-    load_win(W, pb0, wb + 1 < blk_end ? s_bt[wb + 1 - blk_begin] : pb0);
+    load_win(W, s_bt[wb - blk_begin], s_bt[min(wb + 1, blk_end - 1) - blk_begin]);
   };
 
   float mrun[NQT], lsum[NQT];
@@ -207,17 +230,27 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a, int cb, int n_ch
     }
   };
 
+  // W0 holds window wb and W1 window wb + 8; each prefetch sits on its own path, so every
+  // wait before a compute covers exactly the window it uses
   int wb = wb0;
   if (wb < blk_end) {
     while (true) {
-      const int w1 = wb + 8;
-      load_at(W1, w1 < blk_end ? w1 : wb);
       compute(W0, wb);
+      const int w1 = wb + 8;
       if (w1 >= blk_end) break;
       const int w2 = w1 + 8;
-      load_at(W0, w2 < blk_end ? w2 : w1);
+      if (w2 >= blk_end) {
+        compute(W1, w1);
+        break;
+      }
+      load_at(W0, w2);
       compute(W1, w1);
-      if (w2 >= blk_end) break;
+      const int w3 = w2 + 8;
+      if (w3 >= blk_end) {
+        compute(W0, w2);
+        break;
+      }
+      load_at(W1, w3);
       wb = w2;
     }
   }
