@@ -46,6 +46,8 @@ class Workload:
     base_width: int = 1024            # head multiplier = (hidden / base_width) ** -1
     soft_cap: float = 30.0
     window: int = 0                   # sliding window of every layer (0: full causal)
+    dense_inter: int = 0              # > 0: layers also carry a dense feed-forward (draft)
+    n_ctx: int = 0                    # > 0: context rows for the context-K/V store
     seed: int = 0
 
     @property
@@ -61,7 +63,8 @@ class Workload:
         return dict(hidden=self.hidden, n_q_heads=self.n_q_heads, n_kv_heads=self.n_kv_heads,
                     head_dim=self.head_dim, q_rows=self.q_rows, block_size=BLOCK,
                     n_experts=self.n_experts, top_k=self.top_k, inter=self.inter,
-                    qk_norm=self.qk_norm, eps=self.eps, rope_theta=self.rope_theta)
+                    qk_norm=self.qk_norm, eps=self.eps, rope_theta=self.rope_theta,
+                    dense_inter=self.dense_inter)
 
 
 _BIG = dict(hidden=4096, n_q_heads=32, n_kv_heads=8, head_dim=128, n_experts=32, top_k=4,
@@ -78,6 +81,11 @@ WORKLOADS = {
                                  pool_blocks=8192 + 64, **_BIG),
     "h4096_b8_ctx131k_win8k": Workload("h4096_b8_ctx131k_win8k", n_req=1, ctx=(131072,),
                                        pool_blocks=8192 + 64, window=8192, **_BIG),
+    "tiny_dense": Workload("tiny_dense", hidden=256, n_q_heads=4, n_kv_heads=1, head_dim=64,
+                           n_experts=8, top_k=2, inter=128, n_req=1, ctx=(128,), pool_blocks=64,
+                           dense_inter=512, n_layers=2, n_ctx=8),
+    "h4096_b8_ctx8k_dense": Workload("h4096_b8_ctx8k_dense", n_req=1, ctx=(8192,),
+                                     pool_blocks=4096, dense_inter=8192, n_ctx=8, **_BIG),
     "h4096_chain4_head": Workload("h4096_chain4_head", n_req=1, ctx=(8192,), pool_blocks=4096,
                                   n_layers=4, draft_vocab=32768, target_vocab=131072, **_BIG),
 }
@@ -179,7 +187,28 @@ def make_layer_weights(w: Workload, seed, tag=""):
     out["w2_codes"] = torch.from_numpy(r.integers(0, 256, (E, H, I // 2), dtype=np.uint8))
     out["w2_scales"] = _e4m3_codes(np.abs(_normal(seed, tag + "w2_scales", (E, H, I // 16), 0.05)))
     out["w2_gscale"] = torch.ones(E, dtype=torch.float32)
+    if w.dense_inter:
+        Id = w.dense_inter
+        out["w_gate_up"] = _bf16(_normal(seed, tag + "w_gate_up", (2 * Id, H), H ** -0.5))
+        out["w_down"] = _bf16(_normal(seed, tag + "w_down", (H, Id), Id ** -0.5))
     return out
+
+
+def make_context(w: Workload, seed, layers):
+    """Context rows for the context-K/V store: hidden taps ~ N(0,1) bf16 [n_ctx, H], the
+    hidden-norm gain, and per layer the slots of the request's last n_ctx context
+    positions before its verify rows (their prefilled K/V are overwritten)."""
+    H, n = w.hidden, w.n_ctx
+    L0 = int(layers[0]["seq_lens"][0])
+    pos = np.arange(L0 - w.q_rows - n, L0 - w.q_rows, dtype=np.int32)
+    slots = []
+    for lay in layers:
+        bt = lay["block_table"].numpy()
+        slots.append(torch.from_numpy(np.array([int(bt[0, p // BLOCK]) * BLOCK + p % BLOCK
+                                                for p in pos], dtype=np.int64)))
+    return dict(states=_bf16(_normal(seed, "context_states", (n, H))),
+                g_hidden=torch.from_numpy(1.0 + _normal(seed, "g_hidden", (H,), 0.1)),
+                positions=torch.from_numpy(pos), slot_mappings=slots)
 
 
 def make_activations(w: Workload, seed):
@@ -226,7 +255,8 @@ def make_workload(name_or_w, seed=None):
             lay["g_post_prev"] = layers[i - 1]["g_post_ffn"]
         layers.append(lay)
     return dict(workload=w, dims=w.dims(), act=make_activations(w, seed), layers=layers,
-                head=make_head(w, seed) if w.draft_vocab else None)
+                head=make_head(w, seed) if w.draft_vocab else None,
+                context=make_context(w, seed, layers) if w.n_ctx else None)
 
 
 def with_overrides(w: Workload, **kw):

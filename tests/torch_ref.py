@@ -44,14 +44,13 @@ def bf16(x):
     return t64(x).to(torch.float32).to(torch.bfloat16).to(D64)
 
 
-def layer(lay, act, dims, branch_in):
-    """The layer step of one workload; returns a dict of the main intermediates."""
+def attn_block(lay, x_a, dims):
+    """QKV front, cache write, paged attention (causal, or a sliding window), gate, o_proj."""
     eps, theta = dims["eps"], dims["rope_theta"]
     hq, hkv, d, qr = dims["n_q_heads"], dims["n_kv_heads"], dims["head_dim"], dims["q_rows"]
-    b = act["stream"].shape[0]
-    s = t64(act["stream"]) + rms(branch_in, lay["g_post_prev"], eps)
-    x_a = rms(s, lay["g_pre_attn"], eps)
-    y = x_a @ t64(lay["w_qkv"]).T
+    window = int(lay.get("window", 0))
+    b = x_a.shape[0]
+    y = t64(x_a) @ t64(lay["w_qkv"]).T
     q, k, v, gate = torch.split(y, [hq * d, hkv * d, hkv * d, hq * d], dim=1)
     q, k, v = q.reshape(b, hq, d), k.reshape(b, hkv, d), v.reshape(b, hkv, d)
     if dims.get("qk_norm", 1):
@@ -74,10 +73,22 @@ def layer(lay, act, dims, branch_in):
         kk = kk.repeat_interleave(hq // hkv, dim=0)
         vv = vv.repeat_interleave(hq // hkv, dim=0)
         mask = tok[None, :] <= pos[rows][:, None]                    # [qr, L]
+        if window > 0:
+            mask &= tok[None, :] > pos[rows][:, None] - window
         qq = q[rows].permute(1, 0, 2)                                # [hq, qr, d]
         o[rows] = F.scaled_dot_product_attention(qq, kk, vv, attn_mask=mask).permute(1, 0, 2)
     a = (o.reshape(b, -1) * torch.sigmoid(gate)) @ t64(lay["w_o"]).T
-    s = s + rms(a, lay["g_post_attn"], eps)
+    return dict(q=q, k=k, v=v, gate=gate, o=o, a=a)
+
+
+def layer(lay, act, dims, branch_in):
+    """The layer step of one workload; returns a dict of the main intermediates."""
+    eps = dims["eps"]
+    b = act["stream"].shape[0]
+    s = t64(act["stream"]) + rms(branch_in, lay["g_post_prev"], eps)
+    x_a = rms(s, lay["g_pre_attn"], eps)
+    at = attn_block(lay, x_a, dims)
+    s = s + rms(at["a"], lay["g_post_attn"], eps)
     x_m = rms(s, lay["g_pre_ffn"], eps)
     z = x_m @ t64(lay["w_router"]).T
     if act.get("logit_bias") is not None:
@@ -93,5 +104,35 @@ def layer(lay, act, dims, branch_in):
         gu = x_m[rows] @ w13.T
         h = F.silu(gu[:, :inter]) * gu[:, inter:]
         m[rows] += w[rows, js][:, None] * (h @ w2.T)
-    return dict(x_a=x_a, q=q, k=k, v=v, gate=gate, o=o, a=a, stream=s, x_m=x_m, z=z,
-                ids=ids, w=w, m=m)
+    return dict(x_a=x_a, q=at["q"], k=at["k"], v=at["v"], gate=at["gate"], o=at["o"], a=at["a"],
+                stream=s, x_m=x_m, z=z, ids=ids, w=w, m=m)
+
+
+def dense_layer(lay, stream, dims):
+    """The draft's dense layer: bf16 stream into each pre-norm, bf16 pre-norm outputs,
+    F.silu(gate) * up between the stacked projection and down_proj."""
+    eps, Id = dims["eps"], dims["dense_inter"]
+    s = t64(stream)
+    x_a = bf16(rms(bf16(s), lay["g_pre_attn"], eps))
+    at = attn_block(lay, x_a, dims)
+    s = s + rms(at["a"], lay["g_post_attn"], eps)
+    x_f = bf16(rms(bf16(s), lay["g_pre_ffn"], eps))
+    gu = x_f @ t64(lay["w_gate_up"]).T
+    h = F.silu(gu[:, :Id]) * gu[:, Id:]
+    y = h @ t64(lay["w_down"]).T
+    s = s + rms(y, lay["g_post_ffn"], eps)
+    return dict(x_a=x_a, a=at["a"], x_f=x_f, h=h, y=y, stream=s)
+
+
+def context_kv(states, g_hidden, g_pre, w_kv, positions, hkv, d, eps, theta):
+    """Context K/V of every layer: hidden norm, per-layer norms, one batched matmul over
+    the stacked K/V rows, fp32-style K norm cast back to bf16, complex RoPE."""
+    fc = bf16(rms(states, g_hidden, eps))
+    per_layer = torch.stack([bf16(rms(fc, g, eps)) for g in t64(g_pre)])      # [L, n, H]
+    kv = bf16(torch.bmm(per_layer, t64(w_kv).transpose(1, 2)))                  # [L, n, 2 hkv d]
+    nl, n = kv.shape[0], kv.shape[1]
+    k = kv[..., :hkv * d].reshape(nl, n, hkv, d)
+    v = kv[..., hkv * d:].reshape(nl, n, hkv, d)
+    k = bf16(k * torch.rsqrt(k.pow(2).mean(-1, keepdim=True) + eps))
+    k = torch.stack([bf16(rope_complex(k[i], positions.to(torch.int64), theta)) for i in range(nl)])
+    return k, v
