@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define SD_ABI_VERSION 3
+#define SD_ABI_VERSION 4
 
 enum {
   SD_OK = 0,
@@ -239,6 +239,57 @@ int sd_draft_head(int32_t hidden, int32_t draft_vocab, int32_t b, const void *h,
 
 /* Bytes of workspace sd_draft_head needs. */
 size_t sd_draft_head_workspace_bytes(int32_t hidden, int32_t draft_vocab, int32_t b);
+
+/* ---- Draft side ([DSP] MuseSparkDSparkDecoderLayer, MuseSparkDSparkModel) ---- */
+
+/* One dense draft layer.  Gains fp32 [H] (the layer's own sandwich norms); attention
+ * weights as for sd_attn_verify; w_gate_up packed bf16 [2 * inter, H] with the gate rows
+ * first ([DSP] hf_to_vllm_mapper: gate_proj and up_proj stacked as shards 0 and 1);
+ * w_down packed bf16 [H, inter]; inter % 128 == 0. */
+typedef struct sd_dense_layer_weights {
+  const float *g_pre_attn, *g_post_attn, *g_pre_ffn, *g_post_ffn;
+  sd_attn_weights attn;
+  const void *w_gate_up, *w_down;
+  int32_t inter;
+} sd_dense_layer_weights;
+
+/* Bytes of workspace sd_dense_layer_step needs. */
+size_t sd_dense_workspace_bytes(const sd_dims *dims, int32_t b, int32_t n_req,
+                                int32_t max_seq_len, int32_t inter);
+
+/* One dense draft layer on the fp32 stream [b, H] (in/out), in the order of [DSP]
+ * MuseSparkDSparkDecoderLayer.forward: x = bf16(RMSNorm(bf16(stream); g_pre_attn));
+ * attention as sd_attn_verify (K/V written at kv->slot_mapping); stream +=
+ * RMSNorm(attention; g_post_attn); x = bf16(RMSNorm(bf16(stream); g_pre_ffn));
+ * stream += RMSNorm(down(silu(gate(x)) * up(x)); g_post_ffn).  The bf16 casts are the
+ * ones the forward spells out; the branches and the SwiGLU output stay near fp32. */
+int sd_dense_layer_step(const sd_dims *dims, int32_t b, float *stream,
+                        const sd_dense_layer_weights *w, const sd_kv *kv, void *ws,
+                        size_t ws_bytes, void *stream_handle);
+
+/* One layer of the context-K/V store: its pre-QKV norm gain fp32 [H], its packed w_qkv
+ * (the K/V rows [Hq D, Hq D + 2 Hkv D) are the ones read), its caches (as sd_kv) and
+ * num_blocks, and slot_mapping int64 [n_ctx] (a negative slot writes nothing). */
+typedef struct sd_ctx_layer {
+  const float *g_pre_attn;
+  const void *w_qkv;
+  void *k_cache, *v_cache;
+  int32_t num_blocks;
+  const int64_t *slot_mapping;
+} sd_ctx_layer;
+
+/* Bytes of workspace sd_context_kv needs. */
+size_t sd_context_kv_workspace_bytes(const sd_dims *dims, int32_t n_ctx, int32_t n_layers);
+
+/* Context-K/V store of n_layers draft layers ([DSP] _project_muse_context_kv,
+ * precompute_and_store_context_kv): fc = bf16(RMSNorm(states; g_hidden)); per layer
+ * x = bf16(RMSNorm(fc; g_pre_attn)), kv = bf16(x W_kv^T), K = bf16(weightless RMSNorm(K))
+ * (when dims->qk_norm) then RoPE at positions, bf16 K and V written at the layer's slots.
+ * states bf16 [n_ctx, H] (1 <= n_ctx <= 64); g_hidden fp32 [H]; layers: HOST array of
+ * n_layers (1 .. 16) descriptors; positions int32 [n_ctx]. */
+int sd_context_kv(const sd_dims *dims, int32_t n_ctx, int32_t n_layers, const void *states,
+                  const float *g_hidden, const sd_ctx_layer *layers, const int32_t *positions,
+                  void *ws, size_t ws_bytes, void *stream_handle);
 
 /* Test entry: dequantise row-major block-scaled FP4 rows [n, k] exactly as the expert
  * kernels do, into out fp32 [n, k] (codes [n, k/2], scales [n, k/16], one gscale).

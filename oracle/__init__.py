@@ -48,4 +48,5 @@ from .layer import (  # noqa: F401
     layer_step,
 )
 from .head import final_boundary, draft_head, chain_step  # noqa: F401
-from .draft import dense_ffn, dense_layer_step, context_kv, context_kv_store  # noqa: F401
+from .draft import (dense_ffn, dense_layer_step, context_kv, context_kv_store,  # noqa: F401
+                    context_rows, context_project)

@@ -72,29 +72,26 @@ def dense_layer_step(inp, dims):
                 stream_mid=s_mid, x_f=x_f, h=h, y=y, stream=s)
 
 
-def context_kv(context_states, g_hidden, g_pre, w_kv, positions, n_kv_heads, head_dim, eps,
-               theta, qk_norm=True):
-    """K/V of context tokens for every draft layer ([DSP] ``_project_muse_context_kv`` and
-    ``precompute_and_store_context_kv``), with the dtype flow those functions show:
-
-      fc  = bf16(RMSNorm(context; g_hidden))               the hidden norm
-      x_l = bf16(RMSNorm(fc; g_pre[l]))                    each layer's pre-QKV norm
-      kv  = bf16(x_l W_kv[l]^T)                            stacked k | v rows, one bmm
-      k   = bf16(weightless RMSNorm(k) in fp32), then RoPE at the context positions, bf16
-      v   = kv's v rows
-
-    context_states: [n, H]; g_pre: [L, H]; w_kv: [L, 2 Hkv D, H] (k rows then v rows, the
-    layer's qkv_proj rows after q).  Returns (k, v), each [L, n, Hkv, D] bf16 values in
-    fp64."""
+def context_rows(context_states, g_hidden, g_pre, eps):
+    """The per-layer inputs of the context K/V product ([DSP] ``_project_muse_context_kv``):
+    fc = bf16(RMSNorm(context; g_hidden)), x_l = bf16(RMSNorm(fc; g_pre[l])).
+    context_states: [n, H]; g_pre: [L, H].  Returns x [L, n, H] (bf16 values in fp64)."""
     ctx = np.asarray(context_states, dtype=np.float64)
-    n = ctx.shape[0]
-    w_kv = np.asarray(w_kv, dtype=np.float64)
-    nl = w_kv.shape[0]
     fc = bf16_round(rmsnorm(ctx, g_hidden, eps))
+    return np.stack([bf16_round(rmsnorm(fc, g, eps)) for g in np.asarray(g_pre)])
+
+
+def context_project(x, w_kv, positions, n_kv_heads, head_dim, eps, theta, qk_norm=True):
+    """K/V of the context rows x [L, n, H] ([DSP] ``precompute_and_store_context_kv``):
+    kv = bf16(x_l W_kv[l]^T) (stacked k | v rows, one bmm); K through the weightless
+    RMSNorm (fp32 arithmetic, cast back to bf16), then RoPE at the context positions,
+    bf16; V as the product returns it.  Returns (k, v), each [L, n, Hkv, D]."""
+    x = np.asarray(x, dtype=np.float64)
+    w_kv = np.asarray(w_kv, dtype=np.float64)
+    nl, n = x.shape[0], x.shape[1]
     ks, vs = [], []
     for li in range(nl):
-        x = bf16_round(rmsnorm(fc, np.asarray(g_pre)[li], eps))
-        kv = bf16_round(x @ w_kv[li].T)
+        kv = bf16_round(x[li] @ w_kv[li].T)
         k = kv[:, :n_kv_heads * head_dim].reshape(n, n_kv_heads, head_dim)
         v = kv[:, n_kv_heads * head_dim:].reshape(n, n_kv_heads, head_dim)
         if qk_norm:
@@ -103,6 +100,18 @@ def context_kv(context_states, g_hidden, g_pre, w_kv, positions, n_kv_heads, hea
         ks.append(k)
         vs.append(v)
     return np.stack(ks), np.stack(vs)
+
+
+def context_kv(context_states, g_hidden, g_pre, w_kv, positions, n_kv_heads, head_dim, eps,
+               theta, qk_norm=True):
+    """K/V of context tokens for every draft layer ([DSP] ``_project_muse_context_kv`` and
+    ``precompute_and_store_context_kv``): ``context_rows`` then ``context_project``.
+
+    context_states: [n, H]; g_pre: [L, H]; w_kv: [L, 2 Hkv D, H] (k rows then v rows, the
+    layer's qkv_proj rows after q).  Returns (k, v), each [L, n, Hkv, D] bf16 values in
+    fp64."""
+    x = context_rows(context_states, g_hidden, g_pre, eps)
+    return context_project(x, w_kv, positions, n_kv_heads, head_dim, eps, theta, qk_norm)
 
 
 def context_kv_store(k_caches, v_caches, k, v, slot_mappings):

@@ -50,6 +50,17 @@ class SdRoute(ctypes.Structure):
                                         "slot_of", "token_of_slot", "active_experts")]
 
 
+class SdDenseLayerWeights(ctypes.Structure):
+    _fields_ = [("g_pre_attn", c_void_p), ("g_post_attn", c_void_p), ("g_pre_ffn", c_void_p),
+                ("g_post_ffn", c_void_p), ("attn", SdAttnWeights), ("w_gate_up", c_void_p),
+                ("w_down", c_void_p), ("inter", c_int)]
+
+
+class SdCtxLayer(ctypes.Structure):
+    _fields_ = [("g_pre_attn", c_void_p), ("w_qkv", c_void_p), ("k_cache", c_void_p),
+                ("v_cache", c_void_p), ("num_blocks", c_int), ("slot_mapping", c_void_p)]
+
+
 SYMBOLS = {
     "sd_abi_version": (c_int, []),
     "sd_last_error": (ctypes.c_char_p, []),
@@ -78,6 +89,14 @@ SYMBOLS = {
                               c_void_p]),
     "sd_draft_head_workspace_bytes": (c_size_t, [c_int, c_int, c_int]),
     "sd_debug_dequant": (c_int, [c_int, c_int, c_void_p, c_void_p, c_float, c_void_p, c_void_p]),
+    "sd_dense_workspace_bytes": (c_size_t, [ctypes.POINTER(SdDims), c_int, c_int, c_int, c_int]),
+    "sd_dense_layer_step": (c_int, [ctypes.POINTER(SdDims), c_int, c_void_p,
+                                    ctypes.POINTER(SdDenseLayerWeights), ctypes.POINTER(SdKv),
+                                    c_void_p, c_size_t, c_void_p]),
+    "sd_context_kv_workspace_bytes": (c_size_t, [ctypes.POINTER(SdDims), c_int, c_int]),
+    "sd_context_kv": (c_int, [ctypes.POINTER(SdDims), c_int, c_int, c_void_p, c_void_p,
+                              ctypes.POINTER(SdCtxLayer), c_void_p, c_void_p, c_size_t,
+                              c_void_p]),
 }
 
 _lib = None
@@ -232,6 +251,46 @@ def layer_step(dims, b, stream_buf, branch_in, front_embed, layer_w, kv, logit_b
                                ptr(front_embed), ctypes.byref(layer_w), ctypes.byref(kv),
                                ptr(logit_bias), ptr(branch_out),
                                ctypes.byref(route) if route is not None else None, ptr(ws),
+                               ws.numel() * ws.element_size(), cur_stream(stream)))
+
+
+def make_dense_layer_weights(lay):
+    """Dense draft layer (gains, attention, packed w_gate_up and w_down); the intermediate
+    size is read from w_down's shape."""
+    return SdDenseLayerWeights(g_pre_attn=ptr(lay["g_pre_attn"]), g_post_attn=ptr(lay["g_post_attn"]),
+                               g_pre_ffn=ptr(lay["g_pre_ffn"]), g_post_ffn=ptr(lay["g_post_ffn"]),
+                               attn=make_attn_weights(lay), w_gate_up=ptr(lay["w_gate_up"]),
+                               w_down=ptr(lay["w_down"]), inter=int(lay["w_down"].shape[1]))
+
+
+def dense_workspace_bytes(dims, b, n_req, max_seq_len, inter):
+    return lib().sd_dense_workspace_bytes(ctypes.byref(dims), b, n_req, max_seq_len, inter)
+
+
+def dense_layer_step(dims, b, stream_buf, dense_w, kv, ws, stream=None):
+    _check(lib().sd_dense_layer_step(ctypes.byref(dims), b, ptr(stream_buf), ctypes.byref(dense_w),
+                                     ctypes.byref(kv), ptr(ws), ws.numel() * ws.element_size(),
+                                     cur_stream(stream)))
+
+
+def make_ctx_layers(layers, slot_mappings):
+    """Host array of context-store layer descriptors (each layer dict holds g_pre_attn,
+    the packed w_qkv, its caches and num_blocks)."""
+    arr = (SdCtxLayer * len(layers))()
+    for i, (lay, sm) in enumerate(zip(layers, slot_mappings)):
+        arr[i] = SdCtxLayer(g_pre_attn=ptr(lay["g_pre_attn"]), w_qkv=ptr(lay["w_qkv"]),
+                            k_cache=ptr(lay["k_cache"]), v_cache=ptr(lay["v_cache"]),
+                            num_blocks=int(lay["num_blocks"]), slot_mapping=ptr(sm))
+    return arr
+
+
+def context_kv_workspace_bytes(dims, n_ctx, n_layers):
+    return lib().sd_context_kv_workspace_bytes(ctypes.byref(dims), n_ctx, n_layers)
+
+
+def context_kv(dims, n_ctx, states, g_hidden, ctx_layers, positions, ws, stream=None):
+    _check(lib().sd_context_kv(ctypes.byref(dims), n_ctx, len(ctx_layers), ptr(states),
+                               ptr(g_hidden), ctx_layers, ptr(positions), ptr(ws),
                                ws.numel() * ws.element_size(), cur_stream(stream)))
 
 

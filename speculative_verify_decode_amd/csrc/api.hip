@@ -524,6 +524,154 @@ int sd_layer_step(const sd_dims* dims, int32_t b, float* stream, const float* br
   return ok();
 }
 
+// ------------------------------------------------------------------------ draft side
+namespace {
+
+struct DenseWs {
+  Ws L;  // the attention regions of the layer step
+  size_t x_f, gu, h, h_lo, y, total;
+};
+
+DenseWs dense_layout(const sd_dims& d, int b, int n_req, int max_seq_len, int inter) {
+  DenseWs w;
+  w.L = ws_layout(d, b, n_req, max_seq_len);
+  size_t o = w.L.total;
+  auto take = [&](size_t bytes) { size_t at = o; o += up(bytes); return at; };
+  const size_t B = b, H = d.hidden, I = inter;
+  w.x_f = take(B * H * 2);
+  w.gu = take(kDenseSplit * B * 2 * I * 4);
+  w.h = take(B * I * 2);     // bf16 hi terms of h, then
+  w.h_lo = take(B * I * 2);  // its lo terms, one buffer for the down projection
+  w.y = take(kDenseSplit * B * H * 4);
+  w.total = o;
+  return w;
+}
+
+int ctx_parts(const sd_dims& d, int n) {
+  const int N = 2 * d.n_kv_heads * d.head_dim;
+  return gemm_split_ok(n, N, d.hidden, false, kDenseSplit) ? kDenseSplit : 1;
+}
+
+}  // namespace
+
+size_t sd_dense_workspace_bytes(const sd_dims* dims, int32_t b, int32_t n_req,
+                                int32_t max_seq_len, int32_t inter) {
+  if (dims == nullptr || b <= 0 || n_req <= 0 || max_seq_len <= 0 || inter <= 0) return 0;
+  return dense_layout(*dims, b, n_req, max_seq_len, inter).total;
+}
+
+int sd_dense_layer_step(const sd_dims* dims, int32_t b, float* stream,
+                        const sd_dense_layer_weights* w, const sd_kv* kv, void* ws,
+                        size_t ws_bytes, void* stream_handle) {
+  SD_CHECK(check_dims(dims));
+  SD_CHECK(check_rows(dims, b));
+  if (w == nullptr) return fail(SD_EINVAL, "dense layer weights are null");
+  if (!w->g_pre_attn || !w->g_post_attn || !w->g_pre_ffn || !w->g_post_ffn)
+    return fail(SD_EINVAL, "a dense layer gain is null");
+  SD_CHECK(check_attn_weights(&w->attn));
+  if (!w->w_gate_up || !w->w_down || !aligned16(w->w_gate_up) || !aligned16(w->w_down))
+    return fail(SD_EINVAL, "w_gate_up or w_down null or misaligned");
+  if (w->inter <= 0 || w->inter % 128)
+    return fail(SD_EUNSUPPORTED, "dense inter %d (need a positive multiple of 128)", w->inter);
+  SD_CHECK(check_kv(dims, b, kv));
+  if (!stream || !aligned16(stream)) return fail(SD_EINVAL, "stream null or misaligned");
+  const size_t need = sd_dense_workspace_bytes(dims, b, kv->n_req, kv->max_seq_len, w->inter);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(SD_EWORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, need);
+  if (!aligned16(ws)) return fail(SD_EINVAL, "workspace must be 16-byte aligned");
+  const DenseWs D = dense_layout(*dims, b, kv->n_req, kv->max_seq_len, w->inter);
+  hipStream_t st = (hipStream_t)stream_handle;
+  const int H = dims->hidden, I = w->inter;
+  const float eps = dims->eps;
+  uint16_t* x_a = at<uint16_t>(ws, D.L.x_a);
+  SD_LAUNCH(launch_draft_norm(0, b, H, stream, nullptr, 1, nullptr, w->g_pre_attn, eps, x_a, st),
+            "dense layer input norm");
+  float* a = at<float>(ws, D.L.a);
+  int a_parts = 1;
+  SD_CHECK(run_attention(dims, b, x_a, nullptr, &w->attn, kv, a, kDenseSplit, ws, D.L, st,
+                         &a_parts));
+  uint16_t* x_f = at<uint16_t>(ws, D.x_f);
+  SD_LAUNCH(launch_draft_norm(1, b, H, stream, a, a_parts, w->g_post_attn, w->g_pre_ffn, eps,
+                              x_f, st),
+            "dense layer attention boundary");
+  GemmArgs g{};
+  g.M = b; g.N = 2 * I; g.K = H; g.x = x_f; g.x_lo = nullptr;
+  g.w = (const uint16_t*)w->w_gate_up; g.y = at<float>(ws, D.gu);
+  g.ksplit = gemm_split_ok(b, 2 * I, H, false, kDenseSplit) ? kDenseSplit : 1;
+  SD_LAUNCH(launch_gemm(GEMM_F32, g, st), "gate_up projection");
+  uint16_t* h = at<uint16_t>(ws, D.h);
+  uint16_t* h_lo = at<uint16_t>(ws, D.h_lo);
+  SD_LAUNCH(launch_swiglu_dense(b, I, at<float>(ws, D.gu), g.ksplit, h, h_lo, st), "SwiGLU");
+  GemmArgs gd{};
+  gd.M = b; gd.N = H; gd.K = I; gd.x = h; gd.x_lo = h_lo;
+  gd.w = (const uint16_t*)w->w_down; gd.y = at<float>(ws, D.y);
+  gd.ksplit = gemm_split_ok(b, H, I, true, kDenseSplit) ? kDenseSplit : 1;
+  SD_LAUNCH(launch_gemm(GEMM_F32, gd, st), "down projection");
+  SD_LAUNCH(launch_draft_norm(2, b, H, stream, at<float>(ws, D.y), gd.ksplit, w->g_post_ffn,
+                              nullptr, eps, nullptr, st),
+            "dense layer output add");
+  return ok();
+}
+
+size_t sd_context_kv_workspace_bytes(const sd_dims* dims, int32_t n_ctx, int32_t n_layers) {
+  if (dims == nullptr || n_ctx <= 0 || n_ctx > 64 || n_layers <= 0 || n_layers > kMaxCtxLayers)
+    return 0;
+  const size_t H = dims->hidden, N = 2 * (size_t)dims->n_kv_heads * dims->head_dim;
+  const size_t parts = ctx_parts(*dims, n_ctx);
+  return up((size_t)n_layers * n_ctx * H * 2) + up((size_t)n_layers * parts * n_ctx * N * 4);
+}
+
+int sd_context_kv(const sd_dims* dims, int32_t n_ctx, int32_t n_layers, const void* states,
+                  const float* g_hidden, const sd_ctx_layer* layers, const int32_t* positions,
+                  void* ws, size_t ws_bytes, void* stream_handle) {
+  SD_CHECK(check_dims(dims));
+  if (n_ctx < 1 || n_ctx > 64) return fail(SD_EUNSUPPORTED, "n_ctx %d (need 1 .. 64)", n_ctx);
+  if (n_layers < 1 || n_layers > kMaxCtxLayers)
+    return fail(SD_EUNSUPPORTED, "n_layers %d (need 1 .. %d)", n_layers, kMaxCtxLayers);
+  if (!states || !g_hidden || !layers || !positions)
+    return fail(SD_EINVAL, "states, g_hidden, layers or positions is null");
+  if (!aligned16(states)) return fail(SD_EINVAL, "states must be 16-byte aligned");
+  CtxPtrs P{};
+  for (int l = 0; l < n_layers; ++l) {
+    const sd_ctx_layer& c = layers[l];
+    if (!c.g_pre_attn || !c.w_qkv || !c.k_cache || !c.v_cache || !c.slot_mapping)
+      return fail(SD_EINVAL, "a pointer of context layer %d is null", l);
+    if (!aligned16(c.w_qkv) || !aligned16(c.k_cache) || !aligned16(c.v_cache))
+      return fail(SD_EINVAL, "context layer %d: weights or caches misaligned", l);
+    if (c.num_blocks <= 0) return fail(SD_EINVAL, "context layer %d: num_blocks %d", l, c.num_blocks);
+    P.g_pre[l] = c.g_pre_attn;
+    P.k_cache[l] = (uint16_t*)c.k_cache;
+    P.v_cache[l] = (uint16_t*)c.v_cache;
+    P.slots[l] = c.slot_mapping;
+  }
+  const size_t need = sd_context_kv_workspace_bytes(dims, n_ctx, n_layers);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(SD_EWORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, need);
+  if (!aligned16(ws)) return fail(SD_EINVAL, "workspace must be 16-byte aligned");
+  hipStream_t st = (hipStream_t)stream_handle;
+  const int H = dims->hidden, Hq = dims->n_q_heads, Hkv = dims->n_kv_heads, D = dims->head_dim;
+  const int N = 2 * Hkv * D, parts = ctx_parts(*dims, n_ctx);
+  uint16_t* x = (uint16_t*)ws;
+  float* kv = at<float>(ws, up((size_t)n_layers * n_ctx * H * 2));
+  const size_t layer_stride = (size_t)parts * n_ctx * N;
+  SD_LAUNCH(launch_ctx_norm(n_ctx, n_layers, H, (const uint16_t*)states, g_hidden, P, dims->eps,
+                            x, st),
+            "context norms");
+  for (int l = 0; l < n_layers; ++l) {
+    GemmArgs g{};
+    g.M = n_ctx; g.N = N; g.K = H; g.x = x + (size_t)l * n_ctx * H; g.x_lo = nullptr;
+    // the packed K/V rows start at row Hq D: tiles of 16 rows keep them contiguous
+    g.w = (const uint16_t*)layers[l].w_qkv + (size_t)Hq * D * H;
+    g.y = kv + l * layer_stride;
+    g.ksplit = parts;
+    SD_LAUNCH(launch_gemm(GEMM_F32, g, st), "context K/V projection");
+  }
+  SD_LAUNCH(launch_ctx_kv_post(kv, layer_stride, parts, n_ctx, n_layers, Hkv, D, dims->qk_norm,
+                               dims->eps, dims->rope_theta, positions, P, st),
+            "context K/V norm, RoPE and store");
+  return ok();
+}
+
 size_t sd_draft_head_workspace_bytes(int32_t hidden, int32_t draft_vocab, int32_t b) {
   if (hidden <= 0 || draft_vocab <= 0 || b <= 0) return 0;
   const size_t tiles = (size_t)draft_vocab / 16;

@@ -165,6 +165,30 @@ hipError_t launch_qkv_post(const float* qkv, int nparts, int b, int Hq, int Hkv,
                            float* gate_out, uint16_t* k_cache, uint16_t* v_cache,
                            hipStream_t st);
 
+// ---- draft side (k_draft.hip)
+// mode 0: out = bf16(RMSNorm(bf16(stream); g_pre)); 1: stream += RMSNorm(sum of nbranch
+// branch partials; g_post), then as 0; 2: only the stream update.
+hipError_t launch_draft_norm(int mode, int b, int H, float* stream, const float* branch,
+                             int nbranch, const float* g_post, const float* g_pre, float eps,
+                             uint16_t* out, hipStream_t st);
+// h = silu(g) * u from nparts partials of [g | u] [nparts, b, 2I]; bf16 hi / lo terms out
+hipError_t launch_swiglu_dense(int b, int I, const float* gu, int nparts, uint16_t* h,
+                               uint16_t* h_lo, hipStream_t st);
+constexpr int kMaxCtxLayers = 16;
+struct CtxPtrs {  // per-layer pointers of the context-K/V store, passed by value
+  const float* g_pre[kMaxCtxLayers];
+  uint16_t* k_cache[kMaxCtxLayers];
+  uint16_t* v_cache[kMaxCtxLayers];
+  const int64_t* slots[kMaxCtxLayers];
+};
+// x [L, n, H] bf16 = each layer's pre-norm of the bf16 hidden norm of the context rows
+hipError_t launch_ctx_norm(int n, int L, int H, const uint16_t* states, const float* g_hidden,
+                           const CtxPtrs& P, float eps, uint16_t* x, hipStream_t st);
+// kv: per layer (stride layer_stride floats) nparts partials [nparts, n, 2 Hkv D]
+hipError_t launch_ctx_kv_post(const float* kv, size_t layer_stride, int nparts, int n, int L,
+                              int Hkv, int D, int qk_norm, float eps, float theta,
+                              const int* positions, const CtxPtrs& P, hipStream_t st);
+
 struct AttnPlan {
   int chunk_blocks;   // blocks per workgroup (a multiple of 8)
   int n_chunks;       // chunks per (request, kv head) over the visible span

@@ -16,10 +16,14 @@ def to_dev(t, device):
     return None if t is None else t.to(device).contiguous()
 
 
+DENSE_TENSORS = ("w_gate_up", "w_down")  # a dense (draft) layer's feed-forward, when present
+
+
 def pack_layer(t):
     """Replace the row-major weights of a device layer dict by their packed copies."""
-    for k in ("w_qkv", "w_o", "w_router"):
-        t[k] = B.pack_dense(t[k])
+    for k in ("w_qkv", "w_o", "w_router") + DENSE_TENSORS:
+        if t.get(k) is not None:
+            t[k] = B.pack_dense(t[k])
     t["w13_codes"], t["w13_scales"] = B.pack_fp4(t["w13_codes"], t["w13_scales"])
     t["w2_codes"], t["w2_scales"] = B.pack_fp4(t["w2_codes"], t["w2_scales"])
 
@@ -30,6 +34,9 @@ class DeviceLayer:
 
     def __init__(self, lay, device):
         self.t = {k: to_dev(lay[k], device) for k in LAYER_TENSORS}
+        for k in DENSE_TENSORS:
+            if lay.get(k) is not None:
+                self.t[k] = to_dev(lay[k], device)
         pack_layer(self.t)
         for k in ("num_blocks", "max_blocks", "max_seq_len"):
             self.t[k] = lay[k]
@@ -38,6 +45,7 @@ class DeviceLayer:
         self.kv = B.make_kv(self.t)
         self.attn_w = self.weights.attn
         self.moe_w = self.weights.moe
+        self.dense_w = B.make_dense_layer_weights(self.t) if "w_down" in self.t else None
 
 
 def alloc_route(b, k, E, device):
@@ -68,10 +76,23 @@ class StepRunner:
         self.ws_bytes = B.workspace_bytes(self.dims, self.b, self.w.n_req, max_seq)
         if self.ws_bytes == 0:
             raise B.SdError(-1, B.lib().sd_last_error().decode())
+        if self.w.dense_inter:
+            self.ws_bytes = max(self.ws_bytes, B.dense_workspace_bytes(
+                self.dims, self.b, self.w.n_req, max_seq, self.w.dense_inter))
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
         self.route_t, self.route = alloc_route(self.b, self.d["top_k"], self.d["n_experts"], device)
         H = self.d["hidden"]
         self.branch_out = torch.empty(self.b, H, dtype=torch.float32, device=device)
+        self.ctx = None
+        if wk.get("context") is not None:
+            c = wk["context"]
+            self.ctx = dict(states=to_dev(c["states"], device), g_hidden=to_dev(c["g_hidden"], device),
+                            positions=to_dev(c["positions"], device),
+                            slots=[to_dev(sm, device) for sm in c["slot_mappings"]])
+            self.ctx["layers"] = B.make_ctx_layers([l.t for l in self.layers], self.ctx["slots"])
+            n = int(c["states"].shape[0])
+            self.ctx["ws"] = torch.empty(B.context_kv_workspace_bytes(self.dims, n, len(self.layers)),
+                                         dtype=torch.uint8, device=device)
         self.head = None
         if wk.get("head") is not None:
             h = wk["head"]
@@ -94,6 +115,17 @@ class StepRunner:
                      self.act["logit_bias"], out, self.route if with_route else None, self.ws,
                      stream)
         return out
+
+    def dense_step(self, i, stream_buf, stream=None):
+        """Layer i as a dense draft layer on stream_buf (in place)."""
+        L = self.layers[i]
+        B.dense_layer_step(self.dims, self.b, stream_buf, L.dense_w, L.kv, self.ws, stream)
+
+    def context_kv(self, stream=None):
+        """The context-K/V store of every layer for the workload's context rows."""
+        c = self.ctx
+        B.context_kv(self.dims, int(c["states"].shape[0]), c["states"], c["g_hidden"],
+                     c["layers"], c["positions"], c["ws"], stream)
 
     def chain(self, stream_buf, branch_in, branch_bufs, with_tau=True, stream=None):
         """All layers through their input boundaries, the final boundary and the head.

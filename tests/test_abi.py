@@ -55,7 +55,7 @@ def test_no_extra_exports_beyond_header(lib):
 
 
 def test_abi_version(lib):
-    assert B.abi_version() == 3
+    assert B.abi_version() == 4
 
 
 def test_workspace_bytes_host_only(lib):
@@ -145,6 +145,42 @@ def test_layer_step_validation(lib):
     rc = L.sd_layer_step(ctypes.byref(d), 8, FAKE, FAKE, None, ctypes.byref(lw), ctypes.byref(kv),
                          None, FAKE, None, FAKE, 1 << 40, None)
     assert rc == -1 and "aligned" in L.sd_last_error().decode()
+
+
+def test_dense_layer_validation(lib):
+    d = dims()
+    attn = B.SdAttnWeights(w_qkv=FAKE, w_o=FAKE)
+    def rc(inter=8192, ws=FAKE, ws_bytes=1 << 40, g=FAKE, kv=None):
+        w = B.SdDenseLayerWeights(g_pre_attn=g, g_post_attn=FAKE, g_pre_ffn=FAKE, g_post_ffn=FAKE,
+                                  attn=attn, w_gate_up=FAKE, w_down=FAKE, inter=inter)
+        return lib.sd_dense_layer_step(ctypes.byref(d), 8, FAKE, ctypes.byref(w),
+                                       ctypes.byref(kv or _kv()), ws, ws_bytes, None)
+    assert rc(g=None) == -1                                       # a gain is null
+    assert rc(inter=1000) == -2 and "128" in lib.sd_last_error().decode()
+    assert rc(kv=_kv(window=-3)) == -1
+    assert rc(ws=None) == -4
+    need = B.dense_workspace_bytes(d, 8, 1, 8192, 8192)
+    assert need > B.workspace_bytes(d, 8, 1, 8192)                # the FFN regions on top
+    assert rc(ws_bytes=need - 1) == -4 and "need" in lib.sd_last_error().decode()
+
+
+def test_context_kv_validation(lib):
+    d = dims()
+    lay = (B.SdCtxLayer * 2)()
+    for i in range(2):
+        lay[i] = B.SdCtxLayer(g_pre_attn=FAKE, w_qkv=FAKE, k_cache=FAKE, v_cache=FAKE,
+                              num_blocks=64, slot_mapping=FAKE)
+    def rc(n=8, nl=2, ws=FAKE, ws_bytes=1 << 30, states=FAKE):
+        return lib.sd_context_kv(ctypes.byref(d), n, nl, states, FAKE, lay, FAKE, ws, ws_bytes, None)
+    assert rc(n=0) == -2 and rc(n=65) == -2
+    assert rc(nl=17) == -2
+    assert rc(states=None) == -1
+    assert rc(states=FAKE + 2) == -1                               # misaligned
+    assert rc(ws=None) == -4
+    assert B.context_kv_workspace_bytes(d, 0, 2) == 0
+    assert B.context_kv_workspace_bytes(d, 8, 2) > 0
+    lay[1].v_cache = None
+    assert rc() == -1 and "layer 1" in lib.sd_last_error().decode()
 
 
 def test_draft_head_validation(lib):

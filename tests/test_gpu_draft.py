@@ -1,0 +1,134 @@
+"""GPU parity of the draft side: the dense decoder layer and the context-K/V store, against
+the fp64 oracle on the same seeded inputs."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from speculative_verify_decode_amd import synth
+from tests.gpu_util import DEV, runner, say, workload
+from tests.helpers import assert_close, np64
+
+pytestmark = pytest.mark.gpu
+
+
+def _dense_inputs(lay, stream, window=0):
+    inp = {k: np64(lay[k]) for k in ("g_pre_attn", "g_post_attn", "g_pre_ffn", "g_post_ffn",
+                                     "w_qkv", "w_o", "w_gate_up", "w_down", "k_cache",
+                                     "v_cache", "block_table", "positions", "slot_mapping")}
+    inp["stream"] = np64(stream)
+    inp["window"] = window
+    return inp
+
+
+def _check_written(got_cache, ref_cache, slots, what, k_major, unit_scale=0.0):
+    """The cache equals the reference at the written slots up to bf16 rounding: a value on a
+    rounding midpoint may land one bf16 step away (2^-7 relative).  K rows have unit RMS
+    after their weightless norm and RoPE mixes pairs of them, so a rotated value that
+    cancels towards 0 inherits the step of its inputs: unit_scale adds that absolute
+    allowance (two steps at magnitude 1)."""
+    for j, slot in enumerate(slots):
+        blk, off = int(slot) // 16, int(slot) % 16
+        g = got_cache[blk, :, off, :] if k_major else got_cache[blk, :, :, off]
+        r = ref_cache[blk, :, off, :] if k_major else ref_cache[blk, :, :, off]
+        err = np.abs(g - r)
+        bound = np.abs(r) * 2.0 ** -7 + unit_scale * 2.0 ** -6 + 1e-30
+        i = np.unravel_index(np.argmax(err - bound), err.shape)
+        assert (err <= bound).all(), f"{what} slot {j}: at {i} got {g[i]} want {r[i]}"
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,window", [("tiny_dense", 0), ("tiny_dense", 24),
+                                         ("h4096_b8_ctx8k_dense", 0)])
+def test_dense_layer_step_matches_oracle(name, window):
+    wk = workload(name)                      # cached: not modified here
+    r = runner(wk)
+    r.layers[0].kv.window = window
+    lay, d = wk["layers"][0], wk["dims"]
+    say(f"[gpu-test] dense layer {name} window {window}")
+    s = r.act["stream"].clone()
+    r.dense_step(0, s)
+    torch.cuda.synchronize()
+    ref = oracle.dense_layer_step(_dense_inputs(lay, wk["act"]["stream"], window), d)
+    w = assert_close(np64(s), ref["stream"], "dense layer stream")
+    say(f"[gpu-test] dense {name}: worst scaled err {w:.2e}")
+    slots = np64(lay["slot_mapping"]).astype(np.int64)
+    _check_written(np64(r.layers[0].t["k_cache"]), ref["k_cache"], slots, "written K", True, 1.0)
+    _check_written(np64(r.layers[0].t["v_cache"]), ref["v_cache"], slots, "written V", False)
+
+
+@pytest.mark.timeout(900)
+def test_dense_layer_step_is_deterministic_and_graph_capturable():
+    wk = workload("tiny_dense")
+    r = runner(wk)
+    s0 = r.act["stream"].clone()
+    r.dense_step(0, s0)
+    torch.cuda.synchronize()
+    st = torch.cuda.Stream()
+    s1 = r.act["stream"].clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(st):
+        r.dense_step(0, s1, stream=st)            # warm
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=st):
+        r.dense_step(0, s1, stream=st)
+    for rep in range(3):
+        s1.copy_(r.act["stream"])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(s1.view(torch.int32), s0.view(torch.int32)), f"replay {rep}"
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["tiny_dense", "h4096_b8_ctx8k_dense"])
+def test_context_kv_store_matches_oracle(name):
+    """Staged: (A) the GPU's normalised context rows against the oracle's, one bf16 step;
+    (B) the oracle's projection, K norm, RoPE and store run on the GPU's own rows against the
+    GPU's cache, one bf16 step (a row element on a rounding midpoint in (A) moves every
+    product it enters, so end to end only a loose bound holds, checked last)."""
+    wk = workload(name)
+    r = runner(wk)
+    d, ctx, lays = wk["dims"], wk["context"], wk["layers"]
+    n, nl, H = int(ctx["states"].shape[0]), len(lays), d["hidden"]
+    say(f"[gpu-test] context K/V {name}: {nl} layers, {n} rows")
+    before = [(np64(l["k_cache"]), np64(l["v_cache"])) for l in lays]
+    r.context_kv()
+    torch.cuda.synchronize()
+    hkv, hd = d["n_kv_heads"], d["head_dim"]
+    qs = d["n_q_heads"] * hd
+    w_kv = np.stack([np64(l["w_qkv"])[qs:qs + 2 * hkv * hd] for l in lays])
+    g_pre = np.stack([np64(l["g_pre_attn"]) for l in lays])
+    # (A) the rows: the workspace starts with them, bf16 [L, n, H]
+    x_gpu = np64(r.ctx["ws"][:nl * n * H * 2].view(torch.bfloat16).reshape(nl, n, H))
+    x_ref = oracle.context_rows(np64(ctx["states"]), np64(ctx["g_hidden"]), g_pre, d["eps"])
+    assert (np.abs(x_gpu - x_ref) <= np.abs(x_ref) * 2.0 ** -7 + 1e-30).all(), "context rows"
+    say(f"[gpu-test] context {name}: rows {np.mean(x_gpu == x_ref):.4%} bit-exact")
+    # (B) from the GPU's rows
+    k, v = oracle.context_project(x_gpu, w_kv, np64(ctx["positions"]), hkv, hd, d["eps"],
+                                  d["rope_theta"], bool(d["qk_norm"]))
+    nk, nv = oracle.context_kv_store([b[0] for b in before], [b[1] for b in before], k, v,
+                                     [np64(sm) for sm in ctx["slot_mappings"]])
+    ke, ve = oracle.context_kv(np64(ctx["states"]), np64(ctx["g_hidden"]), g_pre, w_kv,
+                               np64(ctx["positions"]), hkv, hd, d["eps"], d["rope_theta"],
+                               bool(d["qk_norm"]))
+    for li, l in enumerate(r.layers):
+        slots = np64(ctx["slot_mappings"][li]).astype(np.int64)
+        gk, gv = np64(l.t["k_cache"]), np64(l.t["v_cache"])
+        _check_written(gk, nk[li], slots, f"layer {li} K", True, 1.0)
+        _check_written(gv, nv[li], slots, f"layer {li} V", False)
+        # nothing else changed
+        touched = set((slots // 16).tolist())
+        for blk in range(gk.shape[0]):
+            if blk not in touched:
+                assert np.array_equal(gk[blk], before[li][0][blk], equal_nan=True), (li, blk)
+                assert np.array_equal(gv[blk], before[li][1][blk], equal_nan=True), (li, blk)
+        # end to end against the oracle from the context states: K and V have unit scale
+        for j, slot in enumerate(slots):
+            got_k, got_v = gk[slot // 16, :, slot % 16, :], gv[slot // 16, :, :, slot % 16]
+            assert np.abs(got_k - ke[li, j]).max() <= 2.0 ** -4, (li, j, "K end to end")
+            assert np.abs(got_v - ve[li, j]).max() <= 2.0 ** -4, (li, j, "V end to end")
+        exact = np.mean([np.array_equal(gk[s // 16, :, s % 16, :], nk[li][s // 16, :, s % 16, :])
+                         for s in slots])
+        say(f"[gpu-test] context {name} layer {li}: {exact:.0%} of K rows bit-exact")
