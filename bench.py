@@ -33,6 +33,9 @@ def algorithmic_bytes(wk, counts_per_layer):
     E, I, b = d["n_experts"], d["inter"], w.b
     dense = 2 * (2 * Hq + 2 * Hkv) * D * H + 2 * H * Hq * D + 2 * E * H + 4 * 4 * H
     per_expert = 3 * H * I * (0.5 + 1.0 / 16) + 8
+    if w.dense_inter:  # a dense draft layer: no router, no experts; gate_up and down instead
+        dense += 2 * 3 * H * w.dense_inter - 2 * E * H
+        per_expert = 0.0
     total = 0.0
     for li, counts in enumerate(counts_per_layer):
         lens = wk["layers"][li]["seq_lens"].numpy().astype(np.int64)
@@ -96,6 +99,50 @@ def cpu_baseline(wk):
                       f"{sum(times):.1f} s), {len(os.sched_getaffinity(0))} host cores visible"}
 
 
+def print_dense(args, wk, R, us, per, hot_us, step_bytes, runners, st):
+    """The dense draft layer's line: the step (attention + dense SwiGLU, every weight byte
+    once) and, beside it, the context-K/V store of the workload's context rows."""
+    d, w = wk["dims"], wk["workload"]
+    ctx_us = None
+    if runners[0].ctx is not None:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(st):
+            runners[0].context_kv(stream=st)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=st):
+            runners[0].context_kv(stream=st)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(st):
+            for _ in range(5):
+                g.replay()
+            e0.record(st)
+            for _ in range(50):
+                g.replay()
+            e1.record(st)
+        torch.cuda.synchronize()
+        ctx_us = e0.elapsed_time(e1) * 1e3 / 50
+    out = {
+        "metric": "µs per dense draft layer-step (b=8 verify) + achieved HBM GB/s vs peak",
+        "value": round(us, 3), "unit": "us", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(us / 1e3, 6), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "b": w.b, "hidden": d["hidden"], "dense_inter": w.dense_inter,
+                   "context": int(wk["layers"][0]["seq_lens"].sum()), "rotation_copies": R},
+        "step_bytes": int(step_bytes),
+        "step_GBps": round(step_bytes / (us * 1e-6) / 1e9, 1),
+        "step_frac_hbm": round(step_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        "us_p10_p50_p90": [round(float(np.percentile(per, q)), 3) for q in (10, 50, 90)],
+        "hot_cache_us": round(hot_us, 3),
+        "roofline": {"bound": "hbm", "kernel": "whole dense layer step", "unit": "GB/s",
+                     "achieved": round(step_bytes / (us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBPS,
+                     "frac": round(step_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "traffic": None},
+        "context_kv_us": None if ctx_us is None else round(ctx_us, 3),
+        "context_kv_rows": None if runners[0].ctx is None else int(runners[0].ctx["states"].shape[0]),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -133,9 +180,13 @@ def main():
                         for _ in r.layers]
         return r
 
+    dense = wk["workload"].dense_inter > 0
+
     def run_step(r, sb, stream=None):
         if chain:
             r.chain(sb, r.act["branch_in"], r.chain_bufs, with_tau=False, stream=stream)
+        elif dense:
+            r.dense_step(0, sb, stream=stream)
         else:
             r.layer_step(0, sb, r.act["branch_in"], stream=stream)
 
@@ -145,6 +196,9 @@ def main():
     u = r0.act["branch_in"]
     counts_per_layer = []
     for i in range(len(r0.layers) if chain else 1):
+        if dense:
+            counts_per_layer.append(np.zeros(wk["dims"]["n_experts"], dtype=np.int64))
+            break
         u = r0.layer_step(i, s, u, branch_out=r0.chain_bufs[i])
         torch.cuda.synchronize()
         counts_per_layer.append(r0.route_t["expert_counts"].cpu().numpy())
@@ -219,6 +273,9 @@ def main():
     # step; their input is the attention boundary's expert-input form of the same rows
     d, b = wk["dims"], wk["workload"].b
     H = d["hidden"]
+    if dense:
+        print_dense(args, wk, R, us, per, hot_us, step_bytes, runners, st)
+        return
     y = torch.empty(b * d["top_k"], H, dtype=torch.float32, device=dev)
     x = []
     for r in runners:
