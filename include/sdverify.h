@@ -22,8 +22,11 @@
  *   - bf16 tensors are raw 16-bit bfloat16; fp32 are IEEE float; activations, caches and
  *     metadata are row-major and contiguous.  Weight matrices are in the packed layouts
  *     below, made once from row-major weights by sd_pack_dense / sd_pack_fp4.
- *   - b = rows of the step = n_req * q_rows, request-major (row t belongs to request
- *     t / q_rows).  q_rows = 1 + 7 verify tokens ([RT] unsupported; [DEC] decode_metadata).
+ *   - b = rows of the step, request-major.  q_rows = 1 + 7 verify tokens ([RT]
+ *     unsupported; [DEC] decode_metadata).  By default every request verifies q_rows tokens:
+ *     b = n_req * q_rows and row t belongs to request t / q_rows.  With sd_kv.query_start a
+ *     request verifies 1..q_rows tokens (partial drafts, below).  Entry points that take no
+ *     KV cache accept any b in 1..64.
  *   - Return 0 on success, a negative SD_E* code otherwise; nothing is enqueued on an
  *     error.  sd_last_error() gives the first failing reason in words (thread-local).
  *   - Validation happens on the host, before any launch: dims, sizes, null pointers,
@@ -42,7 +45,7 @@
 extern "C" {
 #endif
 
-#define SD_ABI_VERSION 4
+#define SD_ABI_VERSION 5
 
 enum {
   SD_OK = 0,
@@ -115,14 +118,22 @@ typedef struct sd_layer_weights {
  * the step's slot mapping).  k_cache bf16 [num_blocks, Hkv, 16, D] (token-major inside
  * a block); v_cache bf16 [num_blocks, Hkv, D, 16] (dim-major inside a block).
  * block_table int32 [n_req, max_blocks]; seq_lens int32 [n_req] count every token of the
- * request including its q_rows verify tokens; positions int32 [b] (row j of request r is
- * at seq_lens[r] - q_rows + j); slot_mapping int64 [b] = block * 16 + offset where that
+ * request including its verify tokens; positions int32 [b] (row j of request r is at
+ * seq_lens[r] - q_rows + j); slot_mapping int64 [b] = block * 16 + offset where that
  * row's K/V is written (a negative slot writes nothing).  max_seq_len bounds seq_lens
  * (host value, sizes the launch; device seq_lens are clamped to max_blocks * 16).
  * window: the layer's sliding window ([DEC] SpecializedDecode.plan: attn2 serves each
  * layer's sliding window).  0 = full causal attention; w > 0 = a row at position p sees
  * positions max(0, p - w + 1) .. p only.  The blocks a request's rows cannot see are not
- * read; which blocks those are follows from seq_lens and the positions contract above. */
+ * read; which blocks those are follows from seq_lens and the positions contract above.
+ * query_start: NULL, or int32 [n_req + 1] for partial drafts (requests that verify fewer
+ * than q_rows tokens; [DEC] SpecializedDecode.plan leaves them, and steps of several
+ * requests, to the stock forward).  Request r's rows are query_start[r] ..
+ * query_start[r + 1] - 1, q_r = their count in 1..q_rows, query_start[0] = 0 and
+ * query_start[n_req] = b; row j of request r is at position seq_lens[r] - q_r + j.  The
+ * host checks n_req <= b <= n_req * q_rows; the contents are the caller's contract, and
+ * every row index the kernels derive from them is clamped into 0 .. b - 1, so a bad array
+ * gives wrong rows, never an access out of range. */
 typedef struct sd_kv {
   void *k_cache, *v_cache;
   int32_t num_blocks;
@@ -133,6 +144,7 @@ typedef struct sd_kv {
   const int64_t *slot_mapping;
   int32_t n_req, max_seq_len;
   int32_t window;
+  const int32_t *query_start;
 } sd_kv;
 
 /* Routing outputs.  topk_ids int32 [b, k] (descending logit, ties to the lower expert

@@ -38,6 +38,7 @@ from .layer import (  # noqa: F401
     qkv_front,
     kv_write,
     paged_attention,
+    request_of_row,
     gate_oproj,
     router_logits,
     topk_route,

@@ -61,7 +61,7 @@ def dense_layer_step(inp, dims):
                               bool(d.get("qk_norm", True)))
     kc, vc = kv_write(inp["k_cache"], inp["v_cache"], k, v, inp["slot_mapping"])
     o = paged_attention(q, kc, vc, inp["block_table"], inp["positions"], d["q_rows"],
-                        window=int(inp.get("window", 0)))
+                        window=int(inp.get("window", 0)), query_start=inp.get("query_start"))
     a = gate_oproj(o, gate, inp["w_o"])
     s = s + rmsnorm(a, inp["g_post_attn"], eps)
     s_mid = s

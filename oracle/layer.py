@@ -4,7 +4,8 @@ Test infrastructure: see the package docstring for who may import this.
 
 Shapes: ``b`` rows = ``n_req`` requests x ``q_rows`` (= 1 + 7) verify tokens, request
 major ([DEC] module docstring: one request verifying 1 + 7 tokens; ``decode_metadata``:
-the step's token count equals q).  ``H`` hidden, ``Hq``/``Hkv`` query/KV heads, ``D``
+the step's token count equals q); with ``query_start`` (partial drafts) request r owns
+rows ``query_start[r] .. query_start[r+1] - 1``, 1..q_rows of them.  ``H`` hidden, ``Hq``/``Hkv`` query/KV heads, ``D``
 head dim, ``E`` experts, ``k`` top-k, ``I`` expert intermediate size.
 
 Cache layout (the library's boundary layout, read here as is):
@@ -145,10 +146,24 @@ def gather_request_kv(k_cache, v_cache, block_table_row, length):
     return k, v
 
 
-def paged_attention(q, k_cache, v_cache, block_table, positions, q_rows, scale=None, window=0):
+def request_of_row(t, q_rows, query_start=None):
+    """The request that row t belongs to.  Every request verifies q_rows tokens unless
+    query_start is given: then request r owns rows query_start[r] .. query_start[r+1] - 1
+    (partial drafts: requests verifying fewer tokens, which [DEC] ``plan`` hands to the
+    stock forward and this library serves)."""
+    if query_start is None:
+        return t // q_rows
+    for r in range(len(query_start) - 1):
+        if query_start[r] <= t < query_start[r + 1]:
+            return r
+    raise ValueError(f"row {t} lies in no request of {list(query_start)}")
+
+
+def paged_attention(q, k_cache, v_cache, block_table, positions, q_rows, scale=None, window=0,
+                    query_start=None):
     """Causal GQA attention of each verify row over its request's paged KV.
 
-    Row t belongs to request r = t // q_rows and sits at position p = positions[t];
+    Row t belongs to request r (``request_of_row``) and sits at position p = positions[t];
     it attends to tokens 0..p of that request (the draft layers are causal, [DSP]
     ``MuseSparkDSparkDecoderLayer.__init__``; attn2 reads the paged cache through the
     block table, [DEC] ``plan``).  With a sliding window w > 0 (attn2 serves each layer's
@@ -165,7 +180,7 @@ def paged_attention(q, k_cache, v_cache, block_table, positions, q_rows, scale=N
         scale = d ** -0.5
     o = np.zeros_like(q)
     for t in range(b):
-        r, p = t // q_rows, int(positions[t])
+        r, p = request_of_row(t, q_rows, query_start), int(positions[t])
         lo = max(0, p - window + 1) if window > 0 else 0
         k, v = gather_request_kv(k_cache, v_cache, block_table[r], p + 1)
         k, v = k[lo:], v[lo:]
@@ -333,7 +348,7 @@ def layer_step(inp, dims, branch_in=None, front_embed=None, route_override=None)
                               bool(d.get("qk_norm", True)))
     kc, vc = kv_write(inp["k_cache"], inp["v_cache"], k, v, inp["slot_mapping"])
     o = paged_attention(q, kc, vc, inp["block_table"], inp["positions"], d["q_rows"],
-                        window=int(inp.get("window", 0)))
+                        window=int(inp.get("window", 0)), query_start=inp.get("query_start"))
     a = gate_oproj(o, gate, inp["w_o"])
     s, x_m = dual_norm(s, a, inp["g_post_attn"], inp["g_pre_ffn"], eps)
     z = router_logits(x_m, inp["w_router"], inp.get("logit_bias"))

@@ -42,7 +42,7 @@ class SdKv(ctypes.Structure):
     _fields_ = [("k_cache", c_void_p), ("v_cache", c_void_p), ("num_blocks", c_int),
                 ("block_table", c_void_p), ("max_blocks", c_int), ("seq_lens", c_void_p),
                 ("positions", c_void_p), ("slot_mapping", c_void_p), ("n_req", c_int),
-                ("max_seq_len", c_int), ("window", c_int)]
+                ("max_seq_len", c_int), ("window", c_int), ("query_start", c_void_p)]
 
 
 class SdRoute(ctypes.Structure):
@@ -151,13 +151,16 @@ def make_dims(d):
 
 def make_kv(kv):
     """kv: dict with device tensors k_cache, v_cache, block_table, seq_lens, positions,
-    slot_mapping and ints num_blocks, max_blocks, max_seq_len (and window, default 0)."""
+    slot_mapping and ints num_blocks, max_blocks, max_seq_len (and window, default 0; and
+    query_start, a device int32 [n_req + 1] tensor for partial drafts, default none)."""
+    qs = kv.get("query_start")
     return SdKv(k_cache=ptr(kv["k_cache"]), v_cache=ptr(kv["v_cache"]),
                 num_blocks=kv["num_blocks"], block_table=ptr(kv["block_table"]),
                 max_blocks=kv["max_blocks"], seq_lens=ptr(kv["seq_lens"]),
                 positions=ptr(kv["positions"]), slot_mapping=ptr(kv["slot_mapping"]),
                 n_req=int(kv["seq_lens"].numel()), max_seq_len=kv["max_seq_len"],
-                window=int(kv.get("window", 0)))
+                window=int(kv.get("window", 0)),
+                query_start=ptr(qs) if qs is not None else None)
 
 
 def make_attn_weights(lay):

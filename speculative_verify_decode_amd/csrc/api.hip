@@ -96,11 +96,14 @@ int check_dims(const sd_dims* d) {
 }
 
 int check_rows(const sd_dims* d, int b) {
-  if (b <= 0 || b > kMaxRows || b % d->q_rows)
-    return fail(SD_EUNSUPPORTED, "b = %d rows (need a multiple of q_rows = %d, at most %d)", b,
-                d->q_rows, kMaxRows);
+  (void)d;
+  if (b <= 0 || b > kMaxRows) return fail(SD_EUNSUPPORTED, "b = %d rows (1..%d)", b, kMaxRows);
   return SD_OK;
 }
+
+// requests that b rows can belong to when no KV metadata says (sizes the unused attention
+// part of a workspace for the entry points without a KV cache)
+int requests_of(const sd_dims* d, int b) { return (b + d->q_rows - 1) / d->q_rows; }
 
 struct Ws {
   size_t x_a, x_a_lo, qkv, q, q_lo, gate, part_acc, part_ml, o, o_lo, a, x_m, x_m_lo, x16,
@@ -160,14 +163,19 @@ int check_kv(const sd_dims* d, int b, const sd_kv* kv) {
     return fail(SD_EINVAL, "a kv pointer is null");
   if (!aligned16(kv->k_cache) || !aligned16(kv->v_cache))
     return fail(SD_EINVAL, "KV caches must be 16-byte aligned");
-  if (kv->n_req * d->q_rows != b)
+  if (kv->n_req <= 0) return fail(SD_EINVAL, "n_req %d", kv->n_req);
+  if (kv->query_start == nullptr && kv->n_req * d->q_rows != b)
     return fail(SD_EUNSUPPORTED,
-                "b = %d but n_req = %d requests of %d verify rows (one step verifies q_rows "
-                "tokens of every request)",
+                "b = %d but n_req = %d requests of %d verify rows (without query_start a step "
+                "verifies q_rows tokens of every request)",
                 b, kv->n_req, d->q_rows);
-  if (kv->max_seq_len < d->q_rows)
-    return fail(SD_EINVAL, "max_seq_len %d shorter than the %d verify tokens", kv->max_seq_len,
+  if (kv->query_start != nullptr && (b < kv->n_req || b > kv->n_req * d->q_rows))
+    return fail(SD_EINVAL, "b = %d rows for %d requests of 1..%d verify rows", b, kv->n_req,
                 d->q_rows);
+  const int min_len = kv->query_start ? 1 : d->q_rows;  // a partial draft may verify one
+  if (kv->max_seq_len < min_len)
+    return fail(SD_EINVAL, "max_seq_len %d shorter than the %d verify tokens", kv->max_seq_len,
+                min_len);
   if (kv->num_blocks <= 0) return fail(SD_EINVAL, "num_blocks %d", kv->num_blocks);
   if (kv->max_blocks * 16 < kv->max_seq_len)
     return fail(SD_EINVAL, "block table of %d blocks per request cannot hold %d tokens",
@@ -229,6 +237,7 @@ int run_attention(const sd_dims* d, int b, const uint16_t* x, const uint16_t* x_
   aa.num_blocks = kv->num_blocks;
   aa.positions = kv->positions; aa.n_req = kv->n_req; aa.Hq = Hq; aa.Hkv = Hkv; aa.D = D;
   aa.q_rows = d->q_rows; aa.window = kv->window; aa.scale = scale_of(d);
+  aa.query_start = kv->query_start; aa.b = b;
   aa.part_acc = at<float>(ws, L.part_acc); aa.part_ml = at<float>(ws, L.part_ml);
   aa.gate = gate; aa.gate_stride = Hq * D;
   uint16_t* o = at<uint16_t>(ws, L.o);
@@ -419,8 +428,8 @@ int sd_moe_route(const sd_dims* dims, int32_t b, const void* x, const void* w_ro
   if (!x || !aligned16(x) || !w_router || !aligned16(w_router))
     return fail(SD_EINVAL, "x or w_router null or misaligned");
   if (logits_out && !aligned16(logits_out)) return fail(SD_EINVAL, "logits_out misaligned");
-  SD_CHECK(check_ws(dims, b, b / dims->q_rows, dims->q_rows, ws, ws_bytes));
-  const Ws L = ws_layout(*dims, b, b / dims->q_rows, dims->q_rows);
+  SD_CHECK(check_ws(dims, b, requests_of(dims, b), dims->q_rows, ws, ws_bytes));
+  const Ws L = ws_layout(*dims, b, requests_of(dims, b), dims->q_rows);
   hipStream_t st = (hipStream_t)stream_handle;
   SD_LAUNCH(launch_zero_i32(at<int>(ws, L.counter), st), "router counter");
   SD_CHECK(run_route(dims, b, (const uint16_t*)x, nullptr, w_router, logit_bias, route,
@@ -438,8 +447,8 @@ int sd_moe_experts(const sd_dims* dims, int32_t b, const void* x16, const sd_moe
   if (!x16 || !y_slots) return fail(SD_EINVAL, "x16 or y_slots is null");
   if (!aligned16(x16) || !aligned16(y_slots) || (h_slots && !aligned16(h_slots)))
     return fail(SD_EINVAL, "x16, y_slots and h_slots must be 16-byte aligned");
-  SD_CHECK(check_ws(dims, b, b / dims->q_rows, dims->q_rows, ws, ws_bytes));
-  const Ws L = ws_layout(*dims, b, b / dims->q_rows, dims->q_rows);
+  SD_CHECK(check_ws(dims, b, requests_of(dims, b), dims->q_rows, ws, ws_bytes));
+  const Ws L = ws_layout(*dims, b, requests_of(dims, b), dims->q_rows);
   const _Float16* hi = (const _Float16*)x16;
   SD_CHECK(run_experts(dims, b, hi, hi + (size_t)b * dims->hidden, w, route, (float*)y_slots,
                        (uint16_t*)h_slots, at<_Float16>(ws, L.h16), at<_Float16>(ws, L.h16_lo),

@@ -35,6 +35,18 @@ __device__ __forceinline__ int first_block(const AttnArgs& a, int r) {
   return max(0, L - a.q_rows - a.window + 1) >> 4;
 }
 
+// Rows of request r: the first row and the count.  Without query_start q_rows rows start
+// at r * q_rows; with it (partial drafts) the range query_start[r] .. query_start[r+1] - 1,
+// clamped so that base + j stays in 0 .. b - 1 for every j < n (and base itself when n = 0).
+struct ReqRows {
+  int base, n;
+};
+__device__ __forceinline__ ReqRows req_rows(const AttnArgs& a, int r) {
+  if (a.query_start == nullptr) return {r * a.q_rows, a.q_rows};
+  const int s0 = min(max(a.query_start[r], 0), a.b - 1);
+  return {s0, min(max(a.query_start[r + 1] - s0, 0), min(a.q_rows, a.b - s0))};
+}
+
 // Workgroup (chunk, kv head g, request r): blocks [chunk * cb, +cb) of the request, one
 // workgroup per CU at most.  The chunk's block ids (clamped to the pool) and the query
 // group (hi/lo) are staged in LDS first; each of the 4 waves then streams 2-block windows
@@ -95,6 +107,10 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a, int cb, int n_ch
   // with the loads in flight.
   constexpr int QCH = QG * D / 8;                 // 16-byte pieces of one query term
   constexpr int NQP = (2 * QCH + 255) / 256;      // pieces per thread
+  // query column jr of the group is row base + jr of the step; the columns of a partial
+  // draft past its count read its last row and are masked below (position -1)
+  const ReqRows rq = req_rows(a, r);
+  auto row_of = [&](int jr) { return rq.base + min(jr, max(rq.n - 1, 0)); };
   u32x4_t qv[NQP];
 #pragma unroll
   for (int n = 0; n < NQP; ++n) {
@@ -102,7 +118,7 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a, int cb, int n_ch
     const int term = c / QCH, rem = c - term * QCH;
     const int qi = rem / (D / 8), d8 = (rem - qi * (D / 8)) * 8;
     const int hh = qi / a.q_rows, jr = qi - hh * a.q_rows;
-    const size_t qo = ((size_t)(r * a.q_rows + jr) * a.Hq + g * group + hh) * D + d8;
+    const size_t qo = ((size_t)row_of(jr) * a.Hq + g * group + hh) * D + d8;
     qv[n] = *(const u32x4_t*)((term ? a.q_lo : a.q) + qo);
   }
   const int ncb = min(cb, a.max_blocks - blk_begin);  // <= 0 only past the table's end
@@ -110,8 +126,9 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a, int cb, int n_ch
   int qpos[NQT], qlow[NQT];  // visible tokens: qlow < tok <= qpos
 #pragma unroll
   for (int qt = 0; qt < NQT; ++qt) {
-    const int qi = 16 * qt + i;
-    qpos[qt] = a.positions[r * a.q_rows + (qi - (qi / a.q_rows) * a.q_rows)];
+    const int qi = 16 * qt + i, jr = qi - (qi / a.q_rows) * a.q_rows;
+    const int p = a.positions[row_of(jr)];
+    qpos[qt] = jr < rq.n ? p : -1;  // a column past the request's rows sees no token
   }
   const int L = min(a.seq_lens[r], a.max_blocks * 16);  // never read past the table row
   const int nblk = (L + 15) >> 4;
@@ -292,17 +309,20 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a, int cb, int n_ch
   }
 }
 
-// One workgroup of D threads per (row, query head): LSE-combine the chunks, normalise,
-// apply the output gate o * sigmoid(o_gate), store bf16 hi/lo terms.  Every thread's chunk
-// values for its dim are in flight at once (32 per pass) while thread c turns chunk c's
-// statistics into its weight exp2(m_c - M) (in LDS) and w_c * l_c (block-summed).
+// One workgroup of D threads per (query column, query head) of each request: LSE-combine
+// the chunks, normalise, apply the output gate o * sigmoid(o_gate), store bf16 hi/lo terms.
+// Every thread's chunk values for its dim are in flight at once (32 per pass) while thread
+// c turns chunk c's statistics, loaded together as one (m, l) pair, into its weight
+// exp2(m_c - M) (in LDS) and w_c * l_c (block-summed).  Columns past a partial draft's
+// rows exit after issuing their loads.
 __global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a, int cb, int n_chunks, int qg) {
   constexpr int PASS = 32;
   __shared__ __align__(16) float s_w[1024];
+  __shared__ float s_lc[1024];
   __shared__ float s_red[4];
-  const int t = blockIdx.x / a.Hq, h = blockIdx.x - t * a.Hq;
+  const int tp = blockIdx.x / a.Hq, h = blockIdx.x - tp * a.Hq;
   const int d = threadIdx.x;
-  const int r = t / a.q_rows, jr = t - r * a.q_rows;
+  const int r = tp / a.q_rows, jr = tp - r * a.q_rows;
   const int group = a.Hq / a.Hkv;
   const int g = h / group, hh = h - g * group;
   const int qi = hh * a.q_rows + jr;
@@ -311,16 +331,20 @@ __global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a, int cb, int n_
   const size_t p0 = ((size_t)r * a.Hkv + g) * n_chunks;
   const float* pa = a.part_acc + (p0 * qg + qi) * a.D + d;
   const size_t cs = (size_t)qg * a.D;  // chunk stride
-  const float gate = a.gate[(size_t)t * a.gate_stride + h * a.D + d];  // in flight early
   float vals[PASS];
 #pragma unroll
   for (int u = 0; u < PASS; ++u) vals[u] = pa[min(u, nc - 1) * cs];
+  const ReqRows rq = req_rows(a, r);
+  const int t = rq.base + min(jr, max(rq.n - 1, 0));  // the step row of this column
+  const float gate = a.gate[(size_t)t * a.gate_stride + h * a.D + d];
+  if (jr >= rq.n) return;  // uniform per workgroup, before any barrier
   // chunk statistics: thread c holds (m_c, l_c) of chunks c, c + D, ...
   float mloc = -INFINITY;
   for (int c = d; c < nc; c += blockDim.x) {
-    const float m = a.part_ml[((p0 + c) * qg + qi) * 2];
-    s_w[c] = m;
-    mloc = fmaxf(mloc, m);
+    const float2 ml = *(const float2*)&a.part_ml[((p0 + c) * qg + qi) * 2];
+    s_w[c] = ml.x;
+    s_lc[c] = ml.y;
+    mloc = fmaxf(mloc, ml.x);
   }
   mloc = sd::wave_max(mloc);
   if ((d & 63) == 0) s_red[d >> 6] = mloc;
@@ -331,7 +355,7 @@ __global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a, int cb, int n_
     const float m = s_w[c];
     const float w = m == -INFINITY ? 0.f : exp2f(m - M);
     s_w[c] = w;
-    wl += w * a.part_ml[((p0 + c) * qg + qi) * 2 + 1];
+    wl += w * s_lc[c];
   }
   wl = sd::wave_sum(wl);
   __syncthreads();  // s_red reuse and s_w complete
@@ -399,8 +423,7 @@ hipError_t launch_attention(const AttnArgs& a, const AttnPlan& p, hipStream_t st
 #undef SD_ATTN
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int b = a.n_req * a.q_rows;
-  hipLaunchKernelGGL(k_attn_combine, dim3(b * a.Hq), dim3(a.D), 0, st, a, p.chunk_blocks,
+  hipLaunchKernelGGL(k_attn_combine, dim3(a.n_req * a.q_rows * a.Hq), dim3(a.D), 0, st, a, p.chunk_blocks,
                      p.n_chunks, p.qg);
   return hipGetLastError();
 }

@@ -212,6 +212,8 @@ struct AttnArgs {
   const int* positions;
   int n_req, Hq, Hkv, D, q_rows;
   int window;                 // 0: causal; w > 0: positions p - w + 1 .. p
+  const int* query_start;     // null: q_rows rows per request; else [n_req + 1] row starts
+  int b;                      // rows of the step (query_start indices are clamped below it)
   float scale;
   float* part_acc;            // [n_req * Hkv * n_chunks, qg, D]
   float* part_ml;             // [n_req * Hkv * n_chunks, qg, 2]

@@ -41,6 +41,7 @@ class DeviceLayer:
         for k in ("num_blocks", "max_blocks", "max_seq_len"):
             self.t[k] = lay[k]
         self.t["window"] = int(lay.get("window", 0))
+        self.t["query_start"] = to_dev(lay.get("query_start"), device)  # partial drafts
         self.weights = B.make_layer_weights(self.t)
         self.kv = B.make_kv(self.t)
         self.attn_w = self.weights.attn

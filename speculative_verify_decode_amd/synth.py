@@ -48,11 +48,21 @@ class Workload:
     window: int = 0                   # sliding window of every layer (0: full causal)
     dense_inter: int = 0              # > 0: layers also carry a dense feed-forward (draft)
     n_ctx: int = 0                    # > 0: context rows for the context-K/V store
+    q_lens: tuple = ()                # partial drafts: verify rows per request (1..q_rows)
     seed: int = 0
 
     @property
+    def verify_rows(self):
+        """Verify rows of each request: q_lens, or q_rows for every request."""
+        if self.q_lens:
+            assert len(self.q_lens) == self.n_req
+            assert all(1 <= q <= self.q_rows for q in self.q_lens)
+            return tuple(int(q) for q in self.q_lens)
+        return (self.q_rows,) * self.n_req
+
+    @property
     def b(self):
-        return self.n_req * self.q_rows
+        return sum(self.verify_rows)
 
     @property
     def qkv_rows(self):
@@ -86,6 +96,11 @@ WORKLOADS = {
                            dense_inter=512, n_layers=2, n_ctx=8),
     "h4096_b8_ctx8k_dense": Workload("h4096_b8_ctx8k_dense", n_req=1, ctx=(8192,),
                                      pool_blocks=4096, dense_inter=8192, n_ctx=8, **_BIG),
+    "tiny_partial": Workload("tiny_partial", hidden=256, n_q_heads=4, n_kv_heads=1, head_dim=64,
+                             n_experts=8, top_k=2, inter=128, n_req=4, ctx=(128, 45, 20, 97),
+                             q_lens=(8, 3, 1, 5), pool_blocks=64),
+    "h4096_partial_drafts": Workload("h4096_partial_drafts", n_req=8, ctx_range=(1024, 32768),
+                                     q_lens=(8, 3, 1, 6, 8, 2, 5, 7), pool_blocks=4096, **_BIG),
     "h4096_chain4_head": Workload("h4096_chain4_head", n_req=1, ctx=(8192,), pool_blocks=4096,
                                   n_layers=4, draft_vocab=32768, target_vocab=131072, **_BIG),
 }
@@ -122,9 +137,10 @@ def make_kv(w: Workload, seed, tag=""):
 
     K cache [num_blocks, Hkv, 16, D]; V cache [num_blocks, Hkv, D, 16].  Each request's
     blocks are a seeded random choice from the pool with no aliasing.  Context tokens
-    (positions < L - 8) hold N(0,1); the 8 verify slots, every unused block and the tail
-    of each last partial block hold NaN, so a read before the write or past the end
-    shows up as NaN.
+    (positions < L - q_r, q_r the request's verify rows) hold N(0,1); the verify slots,
+    every unused block and the tail of each last partial block hold NaN, so a read before
+    the write or past the end shows up as NaN.  With partial drafts (q_lens) the metadata
+    also holds query_start, int32 [n_req + 1], the first row of each request.
     """
     lens = context_lengths(w, seed)
     need = [int(-(-L // BLOCK)) for L in lens]
@@ -139,8 +155,9 @@ def make_kv(w: Workload, seed, tag=""):
     hkv, d = w.n_kv_heads, w.head_dim
     k = np.full((nb, hkv, BLOCK, d), np.nan, dtype=np.float32)
     v = np.full((nb, hkv, d, BLOCK), np.nan, dtype=np.float32)
+    qn = w.verify_rows
     for r, L in enumerate(lens):
-        n_ctx = int(L) - w.q_rows
+        n_ctx = int(L) - qn[r]
         full, rem = n_ctx // BLOCK, n_ctx % BLOCK
         blocks = bt[r, :full]
         if full:
@@ -149,18 +166,20 @@ def make_kv(w: Workload, seed, tag=""):
         if rem:
             k[bt[r, full], :, :rem, :] = _normal(seed, f"{tag}kt{r}", (hkv, rem, d))
             v[bt[r, full], :, :, :rem] = _normal(seed, f"{tag}vt{r}", (hkv, d, rem))
+    starts = np.concatenate([[0], np.cumsum(qn)]).astype(np.int32)
     positions = np.zeros(w.b, dtype=np.int32)
     slots = np.zeros(w.b, dtype=np.int64)
     for r, L in enumerate(lens):
-        for j in range(w.q_rows):
-            p = int(L) - w.q_rows + j
-            positions[r * w.q_rows + j] = p
-            slots[r * w.q_rows + j] = int(bt[r, p // BLOCK]) * BLOCK + p % BLOCK
+        for j in range(qn[r]):
+            p = int(L) - qn[r] + j
+            positions[starts[r] + j] = p
+            slots[starts[r] + j] = int(bt[r, p // BLOCK]) * BLOCK + p % BLOCK
     return dict(k_cache=_bf16(k), v_cache=_bf16(v), block_table=torch.from_numpy(bt),
                 seq_lens=torch.from_numpy(lens.astype(np.int32)),
                 positions=torch.from_numpy(positions), slot_mapping=torch.from_numpy(slots),
                 num_blocks=nb, max_blocks=max_blocks, max_seq_len=int(lens.max()),
-                window=int(w.window))
+                window=int(w.window),
+                query_start=torch.from_numpy(starts) if w.q_lens else None)
 
 
 def make_layer_weights(w: Workload, seed, tag=""):

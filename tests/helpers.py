@@ -27,6 +27,8 @@ def oracle_layer_inputs(lay, act, stream=None):
     inp["stream"] = np64(act["stream"]) if stream is None else stream
     inp["logit_bias"] = np64(act.get("logit_bias"))
     inp["window"] = int(lay.get("window", 0))
+    qs = lay.get("query_start")
+    inp["query_start"] = None if qs is None else np.asarray(qs).astype(np.int64)
     return inp
 
 

@@ -55,7 +55,7 @@ def test_no_extra_exports_beyond_header(lib):
 
 
 def test_abi_version(lib):
-    assert B.abi_version() == 4
+    assert B.abi_version() == 5
 
 
 def test_workspace_bytes_host_only(lib):
@@ -64,7 +64,8 @@ def test_workspace_bytes_host_only(lib):
     assert n > 0 and n % 256 == 0
     assert B.workspace_bytes(d, 64, 8, 32768) > n
     assert B.workspace_bytes(dims(block_size=32), 8, 1, 8192) == 0
-    assert B.workspace_bytes(d, 7, 1, 8192) == 0
+    assert B.workspace_bytes(d, 7, 1, 8192) > 0            # a partial draft of 7 rows
+    assert B.workspace_bytes(d, 65, 9, 8192) == 0
 
 
 def _rc_dualnorm(d, b=8, stream=FAKE, branch=FAKE, front=None, g_post=FAKE, g_pre=FAKE, out=FAKE):
@@ -97,9 +98,13 @@ def test_null_dims_and_pointers(lib):
     assert "front" in lib.sd_last_error().decode()
 
 
-def test_rows_must_be_whole_verify_steps(lib):
-    assert _rc_dualnorm(dims(), b=12) == -2
+def test_row_count_limits(lib):
+    # entry points without a KV cache take any b in 1..64 (partial drafts give any count)
+    assert _rc_dualnorm(dims(), b=0) == -2
     assert _rc_dualnorm(dims(), b=72) == -2
+    d = dims()
+    assert lib.sd_workspace_bytes(ctypes.byref(d), 12, 2, 8192) > 0
+    assert lib.sd_workspace_bytes(ctypes.byref(d), 65, 9, 8192) == 0
 
 
 def _kv(**kw):
@@ -118,6 +123,12 @@ def _rc_attn(d, kv, ws=None, ws_bytes=0, b=8):
 def test_attention_validation(lib):
     d = dims()
     assert _rc_attn(d, _kv(n_req=2)) == -2                        # b != n_req * q_rows
+    assert _rc_attn(d, _kv(n_req=0)) == -1
+    # partial drafts: 1..q_rows rows per request
+    assert _rc_attn(d, _kv(n_req=2, query_start=FAKE), b=17) == -1  # more than 2 * 8 rows
+    assert "1..8 verify rows" in lib.sd_last_error().decode()
+    assert _rc_attn(d, _kv(n_req=3, query_start=FAKE), b=2) == -1   # fewer rows than requests
+    assert _rc_attn(d, _kv(n_req=2, query_start=FAKE), b=9) == -4   # valid rows: workspace next
     assert _rc_attn(d, _kv(max_blocks=4)) == -1                   # table too short
     assert _rc_attn(d, _kv(k_cache=FAKE + 2)) == -1                # misaligned cache
     assert _rc_attn(d, _kv(seq_lens=None)) == -1

@@ -155,13 +155,32 @@ def _attn_case(n_req=2, q_rows=8, hq=4, hkv=2, d=16, lens=(45, 70), nb=16, seed=
     return q, kc, vc, bt, pos
 
 
-def _sdpa_reference(q, kc, vc, bt, pos, q_rows, window=0):
+def _ragged_case(q_lens=(8, 3, 1, 5), lens=(45, 70, 20, 33), hq=4, hkv=2, d=16, nb=24, seed=0):
+    """Partial drafts: request r verifies q_lens[r] rows at positions L_r - q_r .. L_r - 1."""
+    rng = np.random.default_rng(seed)
+    need = [-(-L // 16) for L in lens]
+    perm = rng.permutation(nb)
+    bt = np.zeros((len(lens), max(need)), np.int64)
+    o = 0
+    for r, n in enumerate(need):
+        bt[r, :n] = perm[o:o + n]
+        o += n
+    kc = rng.standard_normal((nb, hkv, 16, d))
+    vc = rng.standard_normal((nb, hkv, d, 16))
+    pos = np.concatenate([np.arange(L - qn, L) for L, qn in zip(lens, q_lens)])
+    qs = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int64)
+    q = rng.standard_normal((int(qs[-1]), hq, d))
+    return q, kc, vc, bt, pos, qs
+
+
+def _sdpa_reference(q, kc, vc, bt, pos, q_rows, window=0, starts=None):
     b, hq, d = q.shape
     hkv = kc.shape[1]
     out = np.zeros_like(q)
-    for r in range(b // q_rows):
-        rows = slice(r * q_rows, (r + 1) * q_rows)
-        L = int(pos[r * q_rows + q_rows - 1]) + 1
+    starts = list(range(0, b + 1, q_rows)) if starts is None else [int(v) for v in starts]
+    for r in range(len(starts) - 1):
+        rows = slice(starts[r], starts[r + 1])
+        L = int(pos[starts[r + 1] - 1]) + 1
         t = np.arange(L)
         k = torch.from_numpy(kc[bt[r, t // 16], :, t % 16, :]).permute(1, 0, 2)
         v = torch.from_numpy(vc[bt[r, t // 16], :, :, t % 16]).permute(1, 0, 2)
@@ -186,6 +205,39 @@ def test_sliding_window_matches_sdpa_with_band_mask(window):
     q, kc, vc, bt, pos = _attn_case(seed=11)
     got = oracle.paged_attention(q, kc, vc, bt, pos, 8, window=window)
     assert np.allclose(got, _sdpa_reference(q, kc, vc, bt, pos, 8, window=window), atol=1e-12)
+
+
+def test_partial_drafts_match_sdpa_per_request():
+    q, kc, vc, bt, pos, qs = _ragged_case(seed=21)
+    got = oracle.paged_attention(q, kc, vc, bt, pos, 8, query_start=qs)
+    assert np.allclose(got, _sdpa_reference(q, kc, vc, bt, pos, 8, starts=qs), atol=1e-12)
+
+
+def test_partial_drafts_equal_each_request_run_alone():
+    # requests are independent: each one's rows, run as a one-request step on its own block
+    # table row, give exactly the rows of the ragged step
+    q, kc, vc, bt, pos, qs = _ragged_case(seed=22)
+    got = oracle.paged_attention(q, kc, vc, bt, pos, 8, query_start=qs)
+    for r in range(len(qs) - 1):
+        rows = slice(qs[r], qs[r + 1])
+        alone = oracle.paged_attention(q[rows], kc, vc, bt[r:r + 1], pos[rows], 8)
+        assert np.array_equal(got[rows], alone), r
+
+
+def test_uniform_query_start_is_the_default_split():
+    q, kc, vc, bt, pos = _attn_case(seed=23)
+    qs = np.arange(0, q.shape[0] + 1, 8)
+    assert np.array_equal(oracle.paged_attention(q, kc, vc, bt, pos, 8, query_start=qs),
+                          oracle.paged_attention(q, kc, vc, bt, pos, 8))
+
+
+def test_request_of_row_follows_query_start():
+    qs = [0, 8, 11, 12, 17]
+    want = [0] * 8 + [1] * 3 + [2] + [3] * 5
+    assert [oracle.request_of_row(t, 8, qs) for t in range(17)] == want
+    assert [oracle.request_of_row(t, 8) for t in range(17)] == [t // 8 for t in range(17)]
+    with pytest.raises(ValueError):
+        oracle.request_of_row(17, 8, qs)
 
 
 def test_window_of_one_returns_the_rows_own_value():
@@ -381,6 +433,19 @@ def test_tiny_layer_matches_independent_torch_composition():
         assert np.allclose(out[key], ref[key].numpy(), atol=1e-10), key
     assert np.array_equal(out["ids"], ref["ids"].numpy())
     assert np.isfinite(out["m"]).all() and np.isfinite(out["stream"]).all()
+
+
+def test_tiny_partial_drafts_layer_matches_independent_torch_composition():
+    wk = synth.make_workload("tiny_partial")
+    lay, act, dims = wk["layers"][0], wk["act"], wk["dims"]
+    assert lay["query_start"].tolist() == [0, 8, 11, 12, 17] and act["stream"].shape[0] == 17
+    ref = torch_ref.layer(lay, act, dims, act["branch_in"])
+    out = oracle.layer_step(oracle_layer_inputs(lay, act), dims, branch_in=np64(act["branch_in"]))
+    for key in ("o", "a", "stream", "m"):
+        r = ref[key].numpy().reshape(out[key].shape)
+        assert np.allclose(out[key], r, rtol=1e-10, atol=1e-10), key
+    assert np.array_equal(out["ids"], ref["ids"].numpy())
+    assert np.isfinite(out["m"]).all()
 
 
 def test_tiny_layer_slot_mapping_matches_block_table():

@@ -37,12 +37,17 @@ def _dual_norm_plain_add(stream, branch, g_post, g_pre, eps):
     return s, OL.rmsnorm(s, g_pre, eps)
 
 
-def _attn_off_by_one(q, kc, vc, bt, pos, q_rows, scale=None, window=0):
-    return ORIG_ATTN(q, kc, vc, bt, np.asarray(pos) - 1, q_rows, scale, window)
+def _attn_off_by_one(q, kc, vc, bt, pos, q_rows, scale=None, window=0, query_start=None):
+    return ORIG_ATTN(q, kc, vc, bt, np.asarray(pos) - 1, q_rows, scale, window, query_start)
 
 
-def _window_one_too_wide(q, kc, vc, bt, pos, q_rows, scale=None, window=0):
-    return ORIG_ATTN(q, kc, vc, bt, pos, q_rows, scale, window + 1 if window > 0 else 0)
+def _window_one_too_wide(q, kc, vc, bt, pos, q_rows, scale=None, window=0, query_start=None):
+    return ORIG_ATTN(q, kc, vc, bt, pos, q_rows, scale, window + 1 if window > 0 else 0,
+                     query_start)
+
+
+def _request_by_fixed_rows(t, q_rows, query_start=None):
+    return t // q_rows          # ignores the partial drafts' row starts
 
 
 def _gate_dropped(o, gate, w_o):
@@ -70,6 +75,10 @@ MUTANTS = [
     ("paged_attention", _window_one_too_wide,
      [TL.test_window_of_one_returns_the_rows_own_value,
       lambda: TL.test_sliding_window_matches_sdpa_with_band_mask(7)]),
+    ("request_of_row", _request_by_fixed_rows,
+     [TL.test_partial_drafts_match_sdpa_per_request,
+      TL.test_partial_drafts_equal_each_request_run_alone,
+      TL.test_tiny_partial_drafts_layer_matches_independent_torch_composition]),
     ("gate_oproj", _gate_dropped, [TL.test_gate_limits]),
     ("pooler", _pooler_reversed, [TL.test_pooler_is_stable_counting_sort]),
 ]

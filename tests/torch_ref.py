@@ -64,9 +64,11 @@ def attn_block(lay, x_a, dims):
     vc[slots // 16, :, slots % 16, :] = bf16(v)
     o = torch.empty(b, hq, d, dtype=D64)
     bt = lay["block_table"].to(torch.int64)
-    for r in range(b // qr):
-        rows = slice(r * qr, (r + 1) * qr)
-        L = int(pos[r * qr + qr - 1]) + 1
+    qs = lay.get("query_start")
+    starts = list(range(0, b + 1, qr)) if qs is None else [int(v) for v in qs]
+    for r in range(len(starts) - 1):
+        rows = slice(starts[r], starts[r + 1])
+        L = int(pos[starts[r + 1] - 1]) + 1
         tok = torch.arange(L)
         kk = kc[bt[r, tok // 16], :, tok % 16, :].permute(1, 0, 2)   # [hkv, L, d]
         vv = vc[bt[r, tok // 16], :, tok % 16, :].permute(1, 0, 2)
