@@ -53,7 +53,13 @@ __device__ __forceinline__ ReqRows req_rows(const AttnArgs& a, int r) {
 // w = 2 * wave + 8 j, loading window j + 1 while window j is in the matrix cores.  Loads
 // are unconditional: tokens past the request's end are masked after loading (scores by
 // selection to -inf, V by selection to 0).  K and V are read once: non-temporal loads.
-template <int D, int NQT>
+//
+// GEN selects the general form (a sliding window or partial drafts): the first visible
+// block and the request's rows then come from device metadata, one more scalar round trip
+// before the first window.  Without it the chunk's block range and rows follow from the
+// launch alone, and every scalar load the first two windows need (their four block ids,
+// seq_len) goes out in one batch right after the kernel arguments.
+template <int D, int NQT, bool GEN>
 __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a, int cb, int n_chunks) {
   constexpr int QG = 16 * NQT;
   constexpr int NC = D / 32;   // MFMA steps over the head dim
@@ -71,7 +77,7 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a, int cb, int n_ch
   const int i = lane & 15, G = lane >> 4;
   const int group = a.Hq / a.Hkv;
   // chunks start at the request's first visible block (block 0 without a window)
-  const int blk_begin = first_block(a, r) + chunk * cb;
+  const int blk_begin = (GEN ? first_block(a, r) : 0) + chunk * cb;
   const float sl2 = a.scale * LOG2E;
   const size_t kvh = (size_t)16 * D;  // elements per (block, head)
   const int* btr = a.block_table + (size_t)r * a.max_blocks;
@@ -109,7 +115,7 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a, int cb, int n_ch
   constexpr int NQP = (2 * QCH + 255) / 256;      // pieces per thread
   // query column jr of the group is row base + jr of the step; the columns of a partial
   // draft past its count read its last row and are masked below (position -1)
-  const ReqRows rq = req_rows(a, r);
+  const ReqRows rq = GEN ? req_rows(a, r) : ReqRows{r * a.q_rows, a.q_rows};
   auto row_of = [&](int jr) { return rq.base + min(jr, max(rq.n - 1, 0)); };
   u32x4_t qv[NQP];
 #pragma unroll
@@ -130,16 +136,19 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a, int cb, int n_ch
     const int p = a.positions[row_of(jr)];
     qpos[qt] = jr < rq.n ? p : -1;  // a column past the request's rows sees no token
   }
-  const int L = min(a.seq_lens[r], a.max_blocks * 16);  // never read past the table row
-  const int nblk = (L + 15) >> 4;
+  // the block ids of both windows are read unconditionally (each index is clamped into the
+  // table row), so no id load waits for seq_len
   Win W0, W1;
   const int wb0 = blk_begin + 2 * wave, wb1 = wb0 + 8;
   const int mb = a.max_blocks - 1;
   const int id0 = btr[min(wb0, mb)], id1 = btr[min(wb0 + 1, mb)];
+  const int id2 = btr[min(wb1, mb)], id3 = btr[min(wb1 + 1, mb)];
+  const int L = min(a.seq_lens[r], a.max_blocks * 16);  // never read past the table row
+  const int nblk = (L + 15) >> 4;
   const bool w1_in = wb1 < nblk;
   __builtin_amdgcn_sched_barrier(0);  // the small loads above stay ahead of the windows
   load_win(W0, clamp_blk(id0), clamp_blk(id1));
-  load_win(W1, clamp_blk(w1_in ? btr[min(wb1, mb)] : id0), clamp_blk(w1_in ? btr[min(wb1 + 1, mb)] : id1));
+  load_win(W1, clamp_blk(w1_in ? id2 : id0), clamp_blk(w1_in ? id3 : id1));
 
   // stage block ids and queries
 #pragma unroll
@@ -311,10 +320,14 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a, int cb, int n_ch
 
 // One workgroup of D threads per (query column, query head) of each request: LSE-combine
 // the chunks, normalise, apply the output gate o * sigmoid(o_gate), store bf16 hi/lo terms.
-// Every thread's chunk values for its dim are in flight at once (32 per pass) while thread
-// c turns chunk c's statistics, loaded together as one (m, l) pair, into its weight
-// exp2(m_c - M) (in LDS) and w_c * l_c (block-summed).  Columns past a partial draft's
-// rows exit after issuing their loads.
+// The first pass of chunk values (32 per thread), each thread's chunk statistics (one (m, l)
+// pair per load) and the gate are loaded before seq_len is known: they read the chunk slots
+// the launch allocates, and the slots past the request's chunk count are dropped by
+// selection afterwards, so whatever they hold never reaches the result.  Thread c turns
+// chunk c's statistics into its weight exp2(m_c - M) (in LDS) and w_c * l_c (block-summed).
+// GEN as for the split: partial drafts map the column to its row through query_start, and
+// columns past a request's rows exit after issuing their loads.
+template <bool GEN>
 __global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a, int cb, int n_chunks, int qg) {
   constexpr int PASS = 32;
   __shared__ __align__(16) float s_w[1024];
@@ -326,22 +339,24 @@ __global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a, int cb, int n_
   const int group = a.Hq / a.Hkv;
   const int g = h / group, hh = h - g * group;
   const int qi = hh * a.q_rows + jr;
-  const int L = min(a.seq_lens[r], a.max_blocks * 16);
-  const int nc = max(min((((L + 15) >> 4) - first_block(a, r) + cb - 1) / cb, n_chunks), 1);
   const size_t p0 = ((size_t)r * a.Hkv + g) * n_chunks;
   const float* pa = a.part_acc + (p0 * qg + qi) * a.D + d;
   const size_t cs = (size_t)qg * a.D;  // chunk stride
   float vals[PASS];
 #pragma unroll
-  for (int u = 0; u < PASS; ++u) vals[u] = pa[min(u, nc - 1) * cs];
-  const ReqRows rq = req_rows(a, r);
+  for (int u = 0; u < PASS; ++u) vals[u] = pa[min(u, n_chunks - 1) * cs];
+  const float2 ml0 = *(const float2*)&a.part_ml[((p0 + min(d, n_chunks - 1)) * qg + qi) * 2];
+  const ReqRows rq = GEN ? req_rows(a, r) : ReqRows{r * a.q_rows, a.q_rows};
   const int t = rq.base + min(jr, max(rq.n - 1, 0));  // the step row of this column
   const float gate = a.gate[(size_t)t * a.gate_stride + h * a.D + d];
+  const int L = min(a.seq_lens[r], a.max_blocks * 16);
+  const int nc = max(min((((L + 15) >> 4) - (GEN ? first_block(a, r) : 0) + cb - 1) / cb,
+                         n_chunks), 1);
   if (jr >= rq.n) return;  // uniform per workgroup, before any barrier
   // chunk statistics: thread c holds (m_c, l_c) of chunks c, c + D, ...
   float mloc = -INFINITY;
   for (int c = d; c < nc; c += blockDim.x) {
-    const float2 ml = *(const float2*)&a.part_ml[((p0 + c) * qg + qi) * 2];
+    const float2 ml = c == d ? ml0 : *(const float2*)&a.part_ml[((p0 + c) * qg + qi) * 2];
     s_w[c] = ml.x;
     s_lc[c] = ml.y;
     mloc = fmaxf(mloc, ml.x);
@@ -412,8 +427,16 @@ int attn_chunk_bound(const sd_dims& d, int n_req, int max_seq_len) {
 
 hipError_t launch_attention(const AttnArgs& a, const AttnPlan& p, hipStream_t st) {
   const dim3 grid(p.n_chunks, a.Hkv, a.n_req), block(256);
+  const bool gen = a.window > 0 || a.query_start != nullptr;
 #define SD_ATTN(DD, NQ)                                                                    \
-  hipLaunchKernelGGL((k_attn_split<DD, NQ>), grid, block, 0, st, a, p.chunk_blocks, p.n_chunks)
+  do {                                                                                     \
+    if (gen)                                                                               \
+      hipLaunchKernelGGL((k_attn_split<DD, NQ, true>), grid, block, 0, st, a,              \
+                         p.chunk_blocks, p.n_chunks);                                      \
+    else                                                                                   \
+      hipLaunchKernelGGL((k_attn_split<DD, NQ, false>), grid, block, 0, st, a,             \
+                         p.chunk_blocks, p.n_chunks);                                      \
+  } while (0)
   if (a.D == 128 && p.qg == 32) SD_ATTN(128, 2);
   else if (a.D == 128 && p.qg == 16) SD_ATTN(128, 1);
   else if (a.D == 64 && p.qg == 32) SD_ATTN(64, 2);
@@ -423,7 +446,12 @@ hipError_t launch_attention(const AttnArgs& a, const AttnPlan& p, hipStream_t st
 #undef SD_ATTN
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_attn_combine, dim3(a.n_req * a.q_rows * a.Hq), dim3(a.D), 0, st, a, p.chunk_blocks,
-                     p.n_chunks, p.qg);
+  const dim3 cgrid(a.n_req * a.q_rows * a.Hq), cblock(a.D);
+  if (gen)
+    hipLaunchKernelGGL(k_attn_combine<true>, cgrid, cblock, 0, st, a, p.chunk_blocks, p.n_chunks,
+                       p.qg);
+  else
+    hipLaunchKernelGGL(k_attn_combine<false>, cgrid, cblock, 0, st, a, p.chunk_blocks,
+                       p.n_chunks, p.qg);
   return hipGetLastError();
 }

@@ -872,7 +872,7 @@ hipError_t launch_experts_nct(const MoeArgs& a, hipStream_t st) {
   const Split s13 = split_for(a.H), s2 = split_for(a.I);
   // persistent grids: the live units are at most E * tiles
   const int g13 = min(cus(), a.E * (a.I / 16));
-  const int g2 = min(4 * cus(), a.E * (a.H / 16));
+  const int g2 = min(2 * cus(), a.E * (a.H / 16));  // two per CU: measured fastest
   bool done = false;
 #define SD_W13(NU, KS)                                                                     \
   if (!done && s13.nu == NU && s13.ks == KS) {                                             \
