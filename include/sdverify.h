@@ -120,7 +120,8 @@ typedef struct sd_layer_weights {
  * block_table int32 [n_req, max_blocks]; seq_lens int32 [n_req] count every token of the
  * request including its verify tokens; positions int32 [b] (row j of request r is at
  * seq_lens[r] - q_rows + j); slot_mapping int64 [b] = block * 16 + offset where that
- * row's K/V is written (a negative slot writes nothing).  max_seq_len bounds seq_lens
+ * row's K/V is written (a negative slot writes nothing, and attention then reads whatever
+ * the cache holds at that row's position).  max_seq_len bounds seq_lens
  * (host value, sizes the launch; device seq_lens are clamped to max_blocks * 16).
  * window: the layer's sliding window ([DEC] SpecializedDecode.plan: attn2 serves each
  * layer's sliding window).  0 = full causal attention; w > 0 = a row at position p sees

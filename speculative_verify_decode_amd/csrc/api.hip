@@ -7,6 +7,7 @@
 // input boundary -> attention -> attention boundary -> MoE.  Validation mirrors that page's
 // and page "vllm.models.muse_spark.nvidia.specialized_decode.runtime"'s host-only checks
 // (`unsupported`: the first failing reason, in words), before any launch.
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -106,7 +107,7 @@ int check_rows(const sd_dims* d, int b) {
 int requests_of(const sd_dims* d, int b) { return (b + d->q_rows - 1) / d->q_rows; }
 
 struct Ws {
-  size_t x_a, x_a_lo, qkv, q, q_lo, gate, part_acc, part_ml, o, o_lo, a, x_m, x_m_lo, x16,
+  size_t x_a, x_a_lo, qkv, part_acc, part_ml, o, o_lo, a, x_m, x_m_lo, x16,
       x16_lo, zpart, counter, ids, w, counts, offsets, slot_of, tos, active, h16, h16_lo, y, total;
 };
 
@@ -125,9 +126,6 @@ Ws ws_layout(const sd_dims& d, int b, int n_req, int max_seq_len) {
   w.x_a = take(B * H * 2);
   w.x_a_lo = take(B * H * 2);
   w.qkv = take(kDenseSplit * B * N * 4);
-  w.q = take(B * Hq * D * 2);
-  w.q_lo = take(B * Hq * D * 2);
-  w.gate = take(B * Hq * D * 4);
   w.part_acc = take(parts * p.qg * D * 4);
   w.part_ml = take(parts * p.qg * 2 * 4);
   w.o = take(B * Hq * D * 2);
@@ -219,27 +217,23 @@ int run_attention(const sd_dims* d, int b, const uint16_t* x, const uint16_t* x_
   g.y = qkv;
   g.ksplit = gemm_split_ok(b, N, H, lo, kDenseSplit) ? kDenseSplit : 1;
   SD_LAUNCH(launch_gemm(GEMM_F32, g, st), "qkv projection");
-  uint16_t* q = at<uint16_t>(ws, L.q);
-  uint16_t* q_lo = at<uint16_t>(ws, L.q_lo);
-  float* gate = at<float>(ws, L.gate);
-  SD_LAUNCH(launch_qkv_post(qkv, g.ksplit, b, Hq, Hkv, D, d->qk_norm, d->eps, d->rope_theta,
-                            kv->positions, kv->slot_mapping, q, q_lo, gate,
-                            (uint16_t*)kv->k_cache, (uint16_t*)kv->v_cache, st),
-            "qkv front epilogue");
   const AttnPlan p = attn_plan(*d, kv->n_req, kv->max_seq_len, kv->window);
   if (p.n_chunks > attn_chunk_bound(*d, kv->n_req, kv->max_seq_len))
     return fail(SD_EHIP, "internal: attention plan of %d chunks exceeds the workspace's",
                 p.n_chunks);
   AttnArgs aa{};
-  aa.q = q; aa.q_lo = q_lo;
-  aa.k_cache = (const uint16_t*)kv->k_cache; aa.v_cache = (const uint16_t*)kv->v_cache;
+  aa.qkv = qkv; aa.nparts = g.ksplit; aa.part_stride = (size_t)b * N;
+  aa.qk_norm = d->qk_norm; aa.eps = d->eps;
+  for (int i = 0; i < D / 2; ++i) aa.freq[i] = pow((double)d->rope_theta, -2.0 * i / D);
+  aa.slot_mapping = kv->slot_mapping;
+  aa.k_cache = (uint16_t*)kv->k_cache; aa.v_cache = (uint16_t*)kv->v_cache;
   aa.block_table = kv->block_table; aa.max_blocks = kv->max_blocks; aa.seq_lens = kv->seq_lens;
   aa.num_blocks = kv->num_blocks;
   aa.positions = kv->positions; aa.n_req = kv->n_req; aa.Hq = Hq; aa.Hkv = Hkv; aa.D = D;
   aa.q_rows = d->q_rows; aa.window = kv->window; aa.scale = scale_of(d);
   aa.query_start = kv->query_start; aa.b = b;
   aa.part_acc = at<float>(ws, L.part_acc); aa.part_ml = at<float>(ws, L.part_ml);
-  aa.gate = gate; aa.gate_stride = Hq * D;
+  aa.gate = qkv + (size_t)(Hq + 2 * Hkv) * D; aa.gate_stride = N;  // the o_gate columns
   uint16_t* o = at<uint16_t>(ws, L.o);
   uint16_t* o_lo = at<uint16_t>(ws, L.o_lo);
   aa.out = o; aa.out_lo = o_lo;

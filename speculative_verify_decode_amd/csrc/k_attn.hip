@@ -26,6 +26,17 @@ namespace {
 
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr int kMaxChunkBlocks = 2048;
+constexpr int kQRows = 8;  // verify rows per request (the host accepts only 8)
+
+// cos and sin of the RoPE angle pos * freq: the angle is reduced modulo 2 pi in double (it
+// reaches ~1.3e5 rad, where fp32 would lose ~1e-2 rad), the reduced angle taken in fp32.
+__device__ __forceinline__ void rope_cs(int pos, double freq, float& c, float& s) {
+  constexpr double kTwoPi = 6.283185307179586232, kTwoPiLo = 2.4492935982947064e-16;
+  const double ang = (double)pos * freq;
+  const double k = rint(ang * 0.15915494309189535);
+  const double r = fma(-k, kTwoPiLo, fma(-k, kTwoPi, ang));
+  sincosf((float)r, &s, &c);
+}
 
 // The first block a request's rows can see: with a sliding window w, the lowest position
 // of the request's rows (seq_len - q_rows) minus w - 1; block 0 otherwise.
@@ -59,8 +70,9 @@ __device__ __forceinline__ ReqRows req_rows(const AttnArgs& a, int r) {
 // before the first window.  Without it the chunk's block range and rows follow from the
 // launch alone, and every scalar load the first two windows need (their four block ids,
 // seq_len) goes out in one batch right after the kernel arguments.
-template <int D, int NQT, bool GEN>
-__global__ __launch_bounds__(256) void k_attn_split(AttnArgs a, int cb, int n_chunks) {
+template <int D, int NQT, bool GEN, int NP>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_attn_split(AttnArgs a, int cb, int n_chunks) {
   constexpr int QG = 16 * NQT;
   constexpr int NC = D / 32;   // MFMA steps over the head dim
   constexpr int NDT = D / 16;  // output dim tiles
@@ -70,6 +82,9 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a, int cb, int n_ch
   __shared__ float s_m[4][QG], s_l[4][QG];
   __shared__ uint16_t s_q[2][QG][QP];
   __shared__ int s_bt[kMaxChunkBlocks];
+  __shared__ float s_cos[kQRows][D / 2], s_sin[kQRows][D / 2];
+  __shared__ __align__(16) uint16_t s_kn[kQRows][D], s_vn[kQRows][D];  // new tokens' K, V
+  __shared__ int s_kok[kQRows];  // row j's new K/V is stored (its slot is not negative)
 
   const int chunk = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
   const int tid = threadIdx.x;
@@ -105,28 +120,19 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a, int cb, int n_ch
   };
   auto clamp_blk = [&](int id) { return min(max(id, 0), a.num_blocks - 1); };
 
-  // Issue order matters: loads complete in order, so the small loads the staging barrier
-  // needs (query terms, the chunk's block ids) go first, then the wave's first two windows,
-  // whose block ids come straight from the table (uniform loads).  Ids are clamped into the
-  // pool and tokens past the request's end are masked, so a window past the end reads
-  // harmless data; a second window past the end re-reads the first one's blocks, which merge
-  // with the loads in flight.
-  constexpr int QCH = QG * D / 8;                 // 16-byte pieces of one query term
-  constexpr int NQP = (2 * QCH + 255) / 256;      // pieces per thread
-  // query column jr of the group is row base + jr of the step; the columns of a partial
-  // draft past its count read its last row and are masked below (position -1)
+  // Order matters, as loads complete in order: the scalar loads (block ids of the first two
+  // windows, seq_len, positions), then the projection partials this workgroup needs, then
+  // the first window; the query terms (and, where this workgroup's blocks hold the new
+  // tokens, their K/V) are computed while the window is in flight.  The new tokens' K/V go
+  // into the cache and into LDS; after one barrier every later window (the second one
+  // included) reads them from the cache, and the first window, read before they were
+  // stored, is patched from LDS.  Block ids are clamped into the pool and tokens past the
+  // request's end are masked, so a window past the end reads harmless data; a second window
+  // past the end re-reads the first one's blocks, which merge with the loads in flight.
+  // Query column jr of the group is row base + jr of the step; the columns of a partial
+  // draft past its count read its last row and are masked below (position -1).
   const ReqRows rq = GEN ? req_rows(a, r) : ReqRows{r * a.q_rows, a.q_rows};
   auto row_of = [&](int jr) { return rq.base + min(jr, max(rq.n - 1, 0)); };
-  u32x4_t qv[NQP];
-#pragma unroll
-  for (int n = 0; n < NQP; ++n) {
-    const int c = min(tid + 256 * n, 2 * QCH - 1);
-    const int term = c / QCH, rem = c - term * QCH;
-    const int qi = rem / (D / 8), d8 = (rem - qi * (D / 8)) * 8;
-    const int hh = qi / a.q_rows, jr = qi - hh * a.q_rows;
-    const size_t qo = ((size_t)row_of(jr) * a.Hq + g * group + hh) * D + d8;
-    qv[n] = *(const u32x4_t*)((term ? a.q_lo : a.q) + qo);
-  }
   const int ncb = min(cb, a.max_blocks - blk_begin);  // <= 0 only past the table's end
   const int bt0 = btr[min(blk_begin + min(tid, max(ncb - 1, 0)), a.max_blocks - 1)];
   int qpos[NQT], qlow[NQT];  // visible tokens: qlow < tok <= qpos
@@ -146,24 +152,186 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a, int cb, int n_ch
   const int L = min(a.seq_lens[r], a.max_blocks * 16);  // never read past the table row
   const int nblk = (L + 15) >> 4;
   const bool w1_in = wb1 < nblk;
-  __builtin_amdgcn_sched_barrier(0);  // the small loads above stay ahead of the windows
-  load_win(W0, clamp_blk(id0), clamp_blk(id1));
-  load_win(W1, clamp_blk(w1_in ? id2 : id0), clamp_blk(w1_in ? id3 : id1));
 
-  // stage block ids and queries
+  // Projection partials.  Query terms: thread (column qi, part qp) takes the rotate-half
+  // pairs (d, d + D/2), d = qp + TPQ m, of its column's head and row.  New tokens: thread
+  // (row j, lane l) takes the pairs d = l + 32 m of K and V head g of the request's row j
+  // (every workgroup loads them; only those holding new tokens use them).
+  constexpr int HALF = D / 2;
+  constexpr int TPQ = 256 / QG;    // threads per query column
+  constexpr int DPT = HALF / TPQ;  // query pairs per thread
+  constexpr int KPT = HALF / 32;   // K/V pairs per thread
+  const int N = (2 * a.Hq + 2 * a.Hkv) * D;
+  const int qi_t = tid / TPQ, qp = tid - qi_t * TPQ;
+  const int hh_t = qi_t / a.q_rows, jr_t = qi_t - hh_t * a.q_rows;
+  const int jn = tid >> 5, ln = tid & 31;
+  const int krow = rq.base + min(jn, max(rq.n - 1, 0));
+  float uq[NP][2][DPT], uk[NP][2][KPT], uv[NP][2][KPT];
+  {
+    const float* qsrc = a.qkv + (size_t)row_of(jr_t) * N + (size_t)(g * group + hh_t) * D;
+    const float* ksrc = a.qkv + (size_t)krow * N + (size_t)(a.Hq + g) * D;
+    const float* vsrc = ksrc + (size_t)a.Hkv * D;
 #pragma unroll
-  for (int n = 0; n < NQP; ++n) {
-    const int c = tid + 256 * n;
-    if (c < 2 * QCH) {
-      const int term = c / QCH, rem = c - term * QCH;
-      const int qi = rem / (D / 8), d8 = (rem - qi * (D / 8)) * 8;
-      *(u32x4_t*)&s_q[term][qi][d8] = qv[n];
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+        for (int m = 0; m < DPT; ++m) uq[p][h2][m] = qsrc[p * a.part_stride + qp + TPQ * m + h2 * HALF];
+#pragma unroll
+        for (int m = 0; m < KPT; ++m) {
+          uk[p][h2][m] = ksrc[p * a.part_stride + ln + 32 * m + h2 * HALF];
+          uv[p][h2][m] = vsrc[p * a.part_stride + ln + 32 * m + h2 * HALF];
+        }
+      }
+  }
+  const int kpos = a.positions[krow];
+  const int64_t kslot = a.slot_mapping[krow];
+  constexpr int NE = (kQRows * HALF + 255) / 256;  // RoPE table entries per thread
+  int epos[NE];
+  double efreq[NE], kfreq[KPT];  // kernel-argument reads are memory loads too
+#pragma unroll
+  for (int e = 0; e < NE; ++e) {
+    const int idx = min(tid + 256 * e, kQRows * HALF - 1);
+    epos[e] = a.positions[row_of(idx / HALF)];
+    efreq[e] = a.freq[idx % HALF];
+  }
+#pragma unroll
+  for (int m = 0; m < KPT; ++m) kfreq[m] = a.freq[ln + 32 * m];
+  load_win(W0, clamp_blk(id0), clamp_blk(id1));
+
+  // query terms: slices summed in order from 0, per-head weightless RMSNorm over the
+  // column's TPQ aligned lanes
+  float x1[DPT], x2[DPT];
+#pragma unroll
+  for (int m = 0; m < DPT; ++m) {
+    x1[m] = 0.f;
+    x2[m] = 0.f;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      x1[m] += uq[p][0][m];
+      x2[m] += uq[p][1][m];
     }
+  }
+  if (a.qk_norm) {
+    float ss = 0.f;
+#pragma unroll
+    for (int m = 0; m < DPT; ++m) ss += x1[m] * x1[m] + x2[m] * x2[m];
+#pragma unroll
+    for (int o = 1; o < TPQ; o <<= 1) ss += __shfl_xor(ss, o, 64);
+    const float rn = rsqrtf(ss / (float)D + a.eps);
+#pragma unroll
+    for (int m = 0; m < DPT; ++m) {
+      x1[m] *= rn;
+      x2[m] *= rn;
+    }
+  }
+  // RoPE cos / sin of the request's rows: entry (jr, d) for the rotate-half pair d of row jr
+#pragma unroll
+  for (int e = 0; e < NE; ++e) {
+    const int idx = tid + 256 * e, jr = idx / HALF, d = idx - jr * HALF;
+    if (idx < kQRows * HALF) rope_cs(epos[e], efreq[e], s_cos[jr][d], s_sin[jr][d]);
   }
   if (tid < ncb) s_bt[tid] = clamp_blk(bt0);
   for (int j = tid + 256; j < ncb; j += 256) s_bt[j] = clamp_blk(btr[blk_begin + j]);  // long chunks
 #pragma unroll
   for (int qt = 0; qt < NQT; ++qt) qlow[qt] = a.window > 0 ? qpos[qt] - a.window : -1;
+
+  // the new tokens sit at positions L - n .. L - 1 of the request (one workgroup per KV
+  // head holds each of them)
+  const int Ln0 = L - rq.n;
+  const bool has_new = blk_begin < nblk && 16 * min(blk_begin + cb, nblk) > Ln0;
+  if (has_new) {  // uniform
+    float k1[KPT], k2[KPT];
+#pragma unroll
+    for (int m = 0; m < KPT; ++m) {
+      k1[m] = 0.f;
+      k2[m] = 0.f;
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        k1[m] += uk[p][0][m];
+        k2[m] += uk[p][1][m];
+      }
+    }
+    if (a.qk_norm) {  // each 32-lane group is one row
+      float sk = 0.f;
+#pragma unroll
+      for (int m = 0; m < KPT; ++m) sk += k1[m] * k1[m] + k2[m] * k2[m];
+#pragma unroll
+      for (int o = 1; o < 32; o <<= 1) sk += __shfl_xor(sk, o, 64);
+      const float rk = rsqrtf(sk / (float)D + a.eps);
+#pragma unroll
+      for (int m = 0; m < KPT; ++m) {
+        k1[m] *= rk;
+        k2[m] *= rk;
+      }
+    }
+    if (ln == 0) s_kok[jn] = jn < rq.n && kslot >= 0;
+    if (jn < rq.n) {
+      const bool store =
+          kslot >= 0 && (kpos >> 4) >= blk_begin && (kpos >> 4) < blk_begin + cb;
+      const int64_t blk = kslot >> 4;
+      const int off = (int)(kslot & 15);
+      uint16_t* kp = a.k_cache + ((size_t)(blk * a.Hkv + g) * 16 + off) * D;
+      uint16_t* vp = a.v_cache + (size_t)(blk * a.Hkv + g) * D * 16 + off;
+#pragma unroll
+      for (int m = 0; m < KPT; ++m) {
+        const int d = ln + 32 * m;
+        float c, sn, v1 = 0.f, v2 = 0.f;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          v1 += uv[p][0][m];
+          v2 += uv[p][1][m];
+        }
+        rope_cs(kpos, kfreq[m], c, sn);
+        const uint16_t ka = sd::f2bf(k1[m] * c - k2[m] * sn), kb = sd::f2bf(k2[m] * c + k1[m] * sn);
+        const uint16_t va = sd::f2bf(v1), vb = sd::f2bf(v2);
+        s_kn[jn][d] = ka;
+        s_kn[jn][d + HALF] = kb;
+        s_vn[jn][d] = va;
+        s_vn[jn][d + HALF] = vb;
+        if (store) {
+          kp[d] = ka;
+          kp[d + HALF] = kb;
+          vp[(size_t)d * 16] = va;
+          vp[(size_t)(d + HALF) * 16] = vb;
+        }
+      }
+    }
+  }
+  __syncthreads();  // angles and the new tokens' K/V staged; the new tokens stored
+  load_win(W1, clamp_blk(w1_in ? id2 : id0), clamp_blk(w1_in ? id3 : id1));
+  // the first window may hold the old cache contents of new tokens that are now stored
+  if (has_new && 16 * wb0 + 32 > Ln0) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int tk = 16 * wb0 + 8 * (i >> 2) + 4 * t + (i & 3) - Ln0;
+      if (tk >= 0 && tk < rq.n && s_kok[tk]) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) W0.k[t][c] = *(const bf16x8_t*)&s_kn[tk][32 * c + 8 * G];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int tv = 16 * wb0 + 8 * G + e - Ln0;
+      if (tv >= 0 && tv < rq.n && s_kok[tv]) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) W0.v[dt][e] = __builtin_bit_cast(__bf16, s_vn[tv][16 * dt + i]);
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < DPT; ++m) {  // rotated query terms as bf16 hi/lo in LDS
+    const int d = qp + TPQ * m;
+    const float c = s_cos[jr_t][d], sn = s_sin[jr_t][d];
+    const float y1 = x1[m] * c - x2[m] * sn, y2 = x2[m] * c + x1[m] * sn;
+    uint16_t h1, l1, h2, l2;
+    sd::split_bf16(y1, h1, l1);
+    sd::split_bf16(y2, h2, l2);
+    s_q[0][qi_t][d] = h1;
+    s_q[1][qi_t][d] = l1;
+    s_q[0][qi_t][d + HALF] = h2;
+    s_q[1][qi_t][d + HALF] = l2;
+  }
   __syncthreads();
   if (blk_begin >= nblk) return;  // past this request's end (uniform per workgroup)
   const int blk_end = min(blk_begin + cb, nblk);
@@ -348,7 +516,13 @@ __global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a, int cb, int n_
   const float2 ml0 = *(const float2*)&a.part_ml[((p0 + min(d, n_chunks - 1)) * qg + qi) * 2];
   const ReqRows rq = GEN ? req_rows(a, r) : ReqRows{r * a.q_rows, a.q_rows};
   const int t = rq.base + min(jr, max(rq.n - 1, 0));  // the step row of this column
-  const float gate = a.gate[(size_t)t * a.gate_stride + h * a.D + d];
+  float gate = 0.f;  // the output gate, slices summed in order
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float gp = a.gate[(size_t)min(p, a.nparts - 1) * a.part_stride +
+                            (size_t)t * a.gate_stride + h * a.D + d];
+    gate += p < a.nparts ? gp : 0.f;
+  }
   const int L = min(a.seq_lens[r], a.max_blocks * 16);
   const int nc = max(min((((L + 15) >> 4) - (GEN ? first_block(a, r) : 0) + cb - 1) / cb,
                          n_chunks), 1);
@@ -428,14 +602,20 @@ int attn_chunk_bound(const sd_dims& d, int n_req, int max_seq_len) {
 hipError_t launch_attention(const AttnArgs& a, const AttnPlan& p, hipStream_t st) {
   const dim3 grid(p.n_chunks, a.Hkv, a.n_req), block(256);
   const bool gen = a.window > 0 || a.query_start != nullptr;
-#define SD_ATTN(DD, NQ)                                                                    \
+  if (a.nparts != 1 && a.nparts != 4) return hipErrorInvalidValue;
+#define SD_ATTN_NP(DD, NQ, GN)                                                             \
   do {                                                                                     \
-    if (gen)                                                                               \
-      hipLaunchKernelGGL((k_attn_split<DD, NQ, true>), grid, block, 0, st, a,              \
+    if (a.nparts == 4)                                                                     \
+      hipLaunchKernelGGL((k_attn_split<DD, NQ, GN, 4>), grid, block, 0, st, a,             \
                          p.chunk_blocks, p.n_chunks);                                      \
     else                                                                                   \
-      hipLaunchKernelGGL((k_attn_split<DD, NQ, false>), grid, block, 0, st, a,             \
+      hipLaunchKernelGGL((k_attn_split<DD, NQ, GN, 1>), grid, block, 0, st, a,             \
                          p.chunk_blocks, p.n_chunks);                                      \
+  } while (0)
+#define SD_ATTN(DD, NQ)                                                                    \
+  do {                                                                                     \
+    if (gen) SD_ATTN_NP(DD, NQ, true);                                                     \
+    else SD_ATTN_NP(DD, NQ, false);                                                        \
   } while (0)
   if (a.D == 128 && p.qg == 32) SD_ATTN(128, 2);
   else if (a.D == 128 && p.qg == 16) SD_ATTN(128, 1);
@@ -444,6 +624,7 @@ hipError_t launch_attention(const AttnArgs& a, const AttnPlan& p, hipStream_t st
   else if (a.D == 64 && p.qg == 64) SD_ATTN(64, 4);
   else return hipErrorInvalidValue;
 #undef SD_ATTN
+#undef SD_ATTN_NP
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 cgrid(a.n_req * a.q_rows * a.Hq), cblock(a.D);

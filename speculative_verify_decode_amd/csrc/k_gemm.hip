@@ -363,83 +363,6 @@ __global__ __launch_bounds__(256) void k_pack_fp4(int N, int K, const uint8_t* _
   }
 }
 
-// One wave per (row, head).  Lane d < D/2 owns the rotate-half pair (d, d + D/2).  The
-// projection arrives as nparts K-slice partials (stride part_stride floats), summed here in
-// slice order; query-head waves also write the summed output gate of their head.
-template <int NP>
-__global__ __launch_bounds__(64) void k_qkv_post(const float* __restrict__ qkv,
-                                                 size_t part_stride, int Hq, int Hkv,
-                                                 int D, int qk_norm, float eps, float theta,
-                                                 const int* __restrict__ positions,
-                                                 const int64_t* __restrict__ slots,
-                                                 uint16_t* __restrict__ q_out,
-                                                 uint16_t* __restrict__ q_lo,
-                                                 float* __restrict__ gate_out,
-                                                 uint16_t* __restrict__ k_cache,
-                                                 uint16_t* __restrict__ v_cache) {
-  const int h = blockIdx.x, t = blockIdx.y, d = threadIdx.x;
-  const int half = D >> 1;
-  const int N = (2 * Hq + 2 * Hkv) * D;
-  const float* row = qkv + (size_t)t * N;
-  const bool act = d < half;
-  const bool is_q = h < Hq;
-  const int kvh = h - Hq;
-  const int c0 = is_q ? h * D : Hq * D + kvh * D;              // q or k columns
-  const int cv = Hq * D + Hkv * D + kvh * D;                     // v columns (k heads)
-  const int cg = (Hq + 2 * Hkv) * D + h * D;                     // gate columns (q heads)
-  float x1 = 0.f, x2 = 0.f, v1 = 0.f, v2 = 0.f, g1 = 0.f, g2 = 0.f;
-  if (act) {
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {  // all partials' loads in flight together
-      const float* rp = row + p * part_stride;
-      x1 += rp[c0 + d];
-      x2 += rp[c0 + d + half];
-      if (is_q) {
-        g1 += rp[cg + d];
-        g2 += rp[cg + d + half];
-      } else {
-        v1 += rp[cv + d];
-        v2 += rp[cv + d + half];
-      }
-    }
-  }
-  if (qk_norm) {
-    const float ss = sd::wave_sum(x1 * x1 + x2 * x2);
-    const float r = rsqrtf(ss / (float)D + eps);
-    x1 *= r;
-    x2 *= r;
-  }
-  if (act) {
-    // angle in double: positions reach 1e5 and fp32 would lose ~1e-2 rad
-    const double freq = pow((double)theta, -2.0 * (double)d / (double)D);
-    const double ang = (double)positions[t] * freq;
-    const float c = (float)cos(ang), s = (float)sin(ang);
-    const float y1 = x1 * c - x2 * s, y2 = x2 * c + x1 * s;
-    if (is_q) {  // q as bf16 hi/lo terms, and the gate
-      const size_t o = ((size_t)t * Hq + h) * D;
-      uint16_t h1, l1, h2, l2;
-      sd::split_bf16(y1, h1, l1);
-      sd::split_bf16(y2, h2, l2);
-      q_out[o + d] = h1;
-      q_out[o + d + half] = h2;
-      q_lo[o + d] = l1;
-      q_lo[o + d + half] = l2;
-      gate_out[o + d] = g1;
-      gate_out[o + d + half] = g2;
-    } else if (slots[t] >= 0) {  // a negative slot writes nothing
-      const int64_t slot = slots[t];
-      const int64_t blk = slot >> 4;
-      const int off = (int)(slot & 15);
-      uint16_t* kp = k_cache + ((size_t)(blk * Hkv + kvh) * 16 + off) * D;
-      kp[d] = sd::f2bf(y1);
-      kp[d + half] = sd::f2bf(y2);
-      uint16_t* vp = v_cache + (size_t)(blk * Hkv + kvh) * D * 16 + off;
-      vp[(size_t)d * 16] = sd::f2bf(v1);
-      vp[(size_t)(d + half) * 16] = sd::f2bf(v2);
-    }
-  }
-}
-
 // Argmax over the per-tile bests of one row (ties: lower index), then the d2t gather.
 __global__ __launch_bounds__(256) void k_head_argmax(int n_tiles, int n_vocab,
                                                      const float* __restrict__ val,
@@ -499,25 +422,6 @@ hipError_t launch_pack_fp4(int E, int N, int K, const uint8_t* codes, const uint
   const size_t blocks = (nlanes + 255) / 256;
   hipLaunchKernelGGL(k_pack_fp4, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256),
                      0, st, N, K, codes, scales, codes_out, scales_out, nlanes);
-  return hipGetLastError();
-}
-
-hipError_t launch_qkv_post(const float* qkv, int nparts, int b, int Hq, int Hkv, int D,
-                           int qk_norm, float eps, float theta, const int* positions,
-                           const int64_t* slots, uint16_t* q_out, uint16_t* q_lo,
-                           float* gate_out, uint16_t* k_cache, uint16_t* v_cache,
-                           hipStream_t st) {
-  const size_t part_stride = (size_t)b * (2 * Hq + 2 * Hkv) * D;
-  const dim3 grid(Hq + Hkv, b), block(64);
-#define SD_QKV_POST(NPV)                                                                    \
-  hipLaunchKernelGGL(k_qkv_post<NPV>, grid, block, 0, st, qkv, part_stride, Hq, Hkv, D,       \
-                     qk_norm, eps, theta, positions, slots, q_out, q_lo, gate_out, k_cache,   \
-                     v_cache)
-  if (nparts == 1) SD_QKV_POST(1);
-  else if (nparts == 2) SD_QKV_POST(2);
-  else if (nparts == 4) SD_QKV_POST(4);
-  else return hipErrorInvalidValue;
-#undef SD_QKV_POST
   return hipGetLastError();
 }
 

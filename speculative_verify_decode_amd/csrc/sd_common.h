@@ -157,14 +157,6 @@ hipError_t launch_pack_dense(int N, int K, const uint16_t* src, uint16_t* dst, h
 hipError_t launch_pack_fp4(int E, int N, int K, const uint8_t* codes, const uint8_t* scales,
                            uint8_t* codes_out, uint8_t* scales_out, hipStream_t st);
 
-// qkv: nparts K-slice partials of the stacked projection [nparts, b, (2Hq + 2Hkv) D];
-// gate_out fp32 [b, Hq D] receives the summed output gate.
-hipError_t launch_qkv_post(const float* qkv, int nparts, int b, int Hq, int Hkv, int D,
-                           int qk_norm, float eps, float theta, const int* positions,
-                           const int64_t* slots, uint16_t* q_out, uint16_t* q_lo,
-                           float* gate_out, uint16_t* k_cache, uint16_t* v_cache,
-                           hipStream_t st);
-
 // ---- draft side (k_draft.hip)
 // mode 0: out = bf16(RMSNorm(bf16(stream); g_pre)); 1: stream += RMSNorm(sum of nbranch
 // branch partials; g_post), then as 0; 2: only the stream update.
@@ -201,10 +193,17 @@ AttnPlan attn_plan(const sd_dims& d, int n_req, int max_seq_len, int window);
 int attn_chunk_bound(const sd_dims& d, int n_req, int max_seq_len);
 
 struct AttnArgs {
-  const uint16_t* q;          // bf16 hi terms [b, Hq, D]
-  const uint16_t* q_lo;       // bf16 lo terms [b, Hq, D]
-  const uint16_t* k_cache;
-  const uint16_t* v_cache;
+  // the stacked projection [q | k | v | o_gate] of the step's rows as nparts K-slice
+  // partials [nparts, b, (2Hq + 2Hkv) D], summed in slice order by the kernels
+  const float* qkv;
+  int nparts;                 // 1 .. 4
+  size_t part_stride;         // floats between partials
+  int qk_norm;                // weightless RMSNorm of q and k heads before RoPE
+  float eps;
+  double freq[64];            // RoPE frequencies theta^(-2d/D), d < D/2 (host, in double)
+  const int64_t* slot_mapping;  // cache slot of each row's new K/V (negative: not stored)
+  uint16_t* k_cache;
+  uint16_t* v_cache;
   const int* block_table;
   int max_blocks;             // entries per block-table row
   int num_blocks;             // blocks in the pool (block ids are clamped below it)
@@ -217,7 +216,7 @@ struct AttnArgs {
   float scale;
   float* part_acc;            // [n_req * Hkv * n_chunks, qg, D]
   float* part_ml;             // [n_req * Hkv * n_chunks, qg, 2]
-  const float* gate;          // row t at gate + t * gate_stride (fp32, Hq * D values)
+  const float* gate;          // row t of partial p at gate + p * part_stride + t * gate_stride
   int gate_stride;
   uint16_t* out;              // bf16 hi terms of the gated output [b, Hq * D]
   uint16_t* out_lo;           // bf16 lo terms
