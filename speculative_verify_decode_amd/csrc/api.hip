@@ -270,9 +270,11 @@ int run_route(const sd_dims* d, int b, const uint16_t* x, const uint16_t* x_lo,
   return SD_OK;
 }
 
+// route (may be null): the router's logits and map outputs, routed inside the W13 kernel
 int run_experts(const sd_dims* d, int b, const _Float16* x16, const _Float16* x16_lo,
                 const sd_moe_weights* w, const sd_route* r, float* y, uint16_t* h_bf16,
-                _Float16* h16, _Float16* h16_lo, hipStream_t st) {
+                _Float16* h16, _Float16* h16_lo, hipStream_t st,
+                const RouterArgs* route = nullptr) {
   MoeArgs m{};
   m.b = b; m.H = d->hidden; m.I = d->inter; m.E = d->n_experts; m.k = d->top_k;
   m.x16 = x16; m.x16_lo = x16_lo; m.h16_lo = h16_lo;
@@ -281,6 +283,10 @@ int run_experts(const sd_dims* d, int b, const _Float16* x16, const _Float16* x1
   m.counts = r->expert_counts; m.offsets = r->expert_offsets; m.tos = r->token_of_slot;
   m.active = r->active_experts;
   m.h16 = h16; m.h_bf16 = h_bf16; m.y = y;
+  if (route != nullptr) {
+    m.route = 1;
+    m.r = *route;
+  }
   SD_LAUNCH(launch_moe_experts(m, st), "routed experts");
   return SD_OK;
 }
@@ -502,9 +508,10 @@ int sd_layer_step(const sd_dims* dims, int32_t b, float* stream, const float* br
   _Float16* x16 = at<_Float16>(ws, L.x16);
   _Float16* x16_lo = at<_Float16>(ws, L.x16_lo);
   const sd_route r = route_out ? *route_out : ws_route(ws, L);
+  NormRouterArgs nr{};
+  const RouterArgs* route_in_experts = nullptr;  // the expert kernel routes from the logits
   if (norm_router_parts(H, dims->n_experts, b, dims->top_k) > 0 && (a_parts == 1 || a_parts == 4)) {
-    // attention boundary and router in one launch (the input boundary zeroed the counter)
-    NormRouterArgs nr{};
+    // attention boundary and the router's product in one launch
     nr.H = H; nr.branch = a; nr.branch_stride = (size_t)b * H; nr.stream = stream;
     nr.g_post = w->g_post_attn; nr.g_pre = w->g_pre_ffn; nr.eps = dims->eps;
     nr.out = nullptr; nr.out_lo = nullptr;  // the bf16 row feeds only the router
@@ -512,6 +519,7 @@ int sd_layer_step(const sd_dims* dims, int32_t b, float* stream, const float* br
     nr.r = router_args(dims, b, nullptr, nullptr, w->moe.w_router, logit_bias, &r, nullptr, ws, L);
     nr.r.part = at<float>(ws, L.zpart);
     SD_LAUNCH(launch_norm_router(nr, a_parts, st), "attention boundary and router");
+    route_in_experts = &nr.r;
   } else {
     SD_LAUNCH(launch_dualnorm(b, H, stream, a, a_parts, nullptr, w->g_post_attn, w->g_pre_ffn,
                               dims->eps, x_m, x_m_lo, x16, x16_lo, at<int>(ws, L.counter), st),
@@ -521,7 +529,7 @@ int sd_layer_step(const sd_dims* dims, int32_t b, float* stream, const float* br
   }
   float* y = at<float>(ws, L.y);
   SD_CHECK(run_experts(dims, b, x16, x16_lo, &w->moe, &r, y, nullptr, at<_Float16>(ws, L.h16),
-                       at<_Float16>(ws, L.h16_lo), st));
+                       at<_Float16>(ws, L.h16_lo), st, route_in_experts));
   SD_LAUNCH(launch_unpool(b, H, dims->top_k, y, r.topk_w, r.slot_of, (float*)branch_out, st),
             "unpooler");
   return ok();

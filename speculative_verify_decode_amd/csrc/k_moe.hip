@@ -42,30 +42,46 @@ constexpr int kStream = 2;
 // expert through per-expert row bitmasks (a row picks an expert at most once, so an
 // entry's rank within its expert is the number of earlier rows in the expert's mask).
 // 256 threads.
-struct RouteLds {
-  uint32_t key[64 * 256];  // order keys: larger = earlier in (-z, index) order, NaN last
+struct MoeMeta {
+  int active[257];
+  int cnt[256];
+  int off[256];
+  int tos[512];
+  float g13[256], g2[256];  // per-expert global scales: an LDS read in the epilogue, not a
+                            // global load queued behind the next unit's weights
+};
+
+template <int KEYS>
+struct RouteLdsT {
+  uint32_t key[KEYS];      // order keys: larger = earlier in (-z, index) order, NaN last
   float sel[512 + 8];      // 8 spare: unrolled reads of a row's k values stay in the array
   int ids[512];
   uint32_t mlo[256], mhi[256];
   int off[257];
-  int wc[4], wa[4];
+  int wc[16], wa[16];
 };
+using RouteLds = RouteLdsT<64 * 256>;  // b <= 64 rows, E <= 256 experts
 
-// EMAX > 0: E <= EMAX and k <= 8, ranks and weights from fully unrolled LDS reads.
-template <int EMAX>
-__device__ void route_phase2(const RouterArgs& a, int KS, RouteLds& R) {
+// EMAX > 0: E <= EMAX and k <= 8, ranks and weights from fully unrolled LDS reads.  NT
+// threads (a multiple of 64, at least E).  out: write the maps (and the logits) to memory;
+// meta (may be null): the expert GEMMs' copy of the maps in LDS (active list, counts,
+// offsets, token of each slot).
+template <int EMAX, int NT, class RL>
+__device__ void route_phase2(const RouterArgs& a, int KS, RL& R, bool out = true,
+                             MoeMeta* meta = nullptr) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  constexpr int NW = NT / 64;
   const int b = a.b, E = a.E, k = a.k;
   // z = sum over ks in order + bias, every (row, expert) at once: one round of loads.  The
   // LDS copy is an order key: larger key = earlier in (-z, index) order, NaN last.
   const size_t st = (size_t)b * E;
-  for (int idx = tid; idx < b * E; idx += 256) {
+  for (int idx = tid; idx < b * E; idx += NT) {
     float z = 0.f;
 #pragma unroll 16
     for (int j = 0; j < KS; ++j) z += a.part[j * st + idx];
     if (a.bias != nullptr) z += a.bias[idx];
-    if (a.logits != nullptr) a.logits[idx] = z;
+    if (out && a.logits != nullptr) a.logits[idx] = z;
     const uint32_t u = __float_as_uint(z == 0.f ? 0.f : z);  // -0 ties with +0
     R.key[idx] = z != z ? 0u : (u & 0x80000000u ? ~u : u | 0x80000000u);
   }
@@ -80,7 +96,7 @@ __device__ void route_phase2(const RouterArgs& a, int KS, RouteLds& R) {
   };
   const int nk = b * k;
   if constexpr (EMAX > 0) {
-    for (int p = tid; p < b * E; p += 256) {
+    for (int p = tid; p < b * E; p += NT) {
       const int t = p / E, e = p - t * E;
       const uint32_t* kr = R.key + t * E;  // reads past the row stay in the array, masked
       const uint32_t ke = kr[e];
@@ -96,7 +112,7 @@ __device__ void route_phase2(const RouterArgs& a, int KS, RouteLds& R) {
       }
     }
     __syncthreads();
-    for (int p = tid; p < nk; p += 256) {
+    for (int p = tid; p < nk; p += NT) {
       const int t = p / k;
       float sv[8];
 #pragma unroll
@@ -107,12 +123,14 @@ __device__ void route_phase2(const RouterArgs& a, int KS, RouteLds& R) {
       for (int j = 0; j < 8; ++j)
         if (j < k) den += expf(sv[j] - m);
       const int ex = R.ids[p];
-      a.ids[p] = ex;
-      a.w_out[p] = expf(R.sel[p] - m) / den;
+      if (out) {
+        a.ids[p] = ex;
+        a.w_out[p] = expf(R.sel[p] - m) / den;
+      }
       atomicOr(t < 32 ? &R.mlo[ex] : &R.mhi[ex], 1u << (t & 31));
     }
   } else {
-    for (int p = tid; p < b * E; p += 256) {
+    for (int p = tid; p < b * E; p += NT) {
       const int t = p / E, e = p - t * E;
       const uint32_t* kr = R.key + t * E;
       const uint32_t ke = kr[e];
@@ -127,22 +145,24 @@ __device__ void route_phase2(const RouterArgs& a, int KS, RouteLds& R) {
       }
     }
     __syncthreads();
-    for (int p = tid; p < nk; p += 256) {
+    for (int p = tid; p < nk; p += NT) {
       const int t = p / k;
       const float m = R.sel[t * k];
       float den = 0.f;
       for (int j = 0; j < k; ++j) den += expf(R.sel[t * k + j] - m);
-      a.ids[p] = R.ids[p];
-      a.w_out[p] = expf(R.sel[p] - m) / den;
+      if (out) {
+        a.ids[p] = R.ids[p];
+        a.w_out[p] = expf(R.sel[p] - m) / den;
+      }
     }
-    for (int p = tid; p < nk; p += 256) {
+    for (int p = tid; p < nk; p += NT) {
       const int t = p / k;
       atomicOr(t < 32 ? &R.mlo[R.ids[p]] : &R.mhi[R.ids[p]], 1u << (t & 31));
     }
   }
   __syncthreads();
   // counts, exclusive offsets and the active list: block scans over experts (tid = e)
-  const int e = tid;
+  const int e = tid;  // NT >= E
   const int cnt = e < E ? __popc(R.mlo[e]) + __popc(R.mhi[e]) : 0;
   const int act = cnt > 0 ? 1 : 0;
   int ic = cnt, ia = act;
@@ -153,32 +173,50 @@ __device__ void route_phase2(const RouterArgs& a, int KS, RouteLds& R) {
   }
   if (lane == 63) { R.wc[wave] = ic; R.wa[wave] = ia; }
   __syncthreads();
-  int pc = 0, pa = 0;
-  for (int w = 0; w < wave; ++w) { pc += R.wc[w]; pa += R.wa[w]; }
-  const int total = R.wc[0] + R.wc[1] + R.wc[2] + R.wc[3];
-  const int n_act = R.wa[0] + R.wa[1] + R.wa[2] + R.wa[3];
+  int pc = 0, pa = 0, total = 0, n_act = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    if (w < wave) { pc += R.wc[w]; pa += R.wa[w]; }
+    total += R.wc[w];
+    n_act += R.wa[w];
+  }
   const int off = pc + ic - cnt;
   if (e < E) {
-    a.counts[e] = cnt;
-    a.offsets[e] = off;
+    if (out) {
+      a.counts[e] = cnt;
+      a.offsets[e] = off;
+      if (act) a.active[pa + ia - 1] = e;
+      if (e >= n_act) a.active[e] = -1;
+    }
+    if (meta != nullptr) {
+      meta->cnt[e] = cnt;
+      meta->off[e] = off;
+      if (act) meta->active[pa + ia - 1] = e;
+      if (e >= n_act) meta->active[e] = -1;
+    }
     R.off[e] = off;
-    if (act) a.active[pa + ia - 1] = e;
-    if (e >= n_act) a.active[e] = -1;
   }
   if (tid == 0) {
-    a.offsets[E] = total;
-    a.active[E] = n_act;
+    if (out) {
+      a.offsets[E] = total;
+      a.active[E] = n_act;
+    }
+    if (meta != nullptr) meta->active[E] = n_act;
   }
   __syncthreads();
-  for (int p = tid; p < nk; p += 256) {
+  for (int p = tid; p < nk; p += NT) {
     const int t = p / k, ex = R.ids[p];
     const int rank = t < 32 ? __popc(R.mlo[ex] & ((1u << t) - 1u))
                             : __popc(R.mlo[ex]) + __popc(R.mhi[ex] & ((1u << (t - 32)) - 1u));
     const int slot = R.off[ex] + rank;
-    a.slot_of[p] = slot;
-    a.tos[slot] = t;
+    if (out) {
+      a.slot_of[p] = slot;
+      a.tos[slot] = t;
+    }
+    if (meta != nullptr) meta->tos[slot] = t;
   }
-  if (tid == 0) *a.counter = 0;  // ready for the next launch
+  if (out && tid == 0 && a.counter != nullptr) *a.counter = 0;  // ready for the next launch
+  if (meta != nullptr) __syncthreads();
 }
 
 template <int NCT>
@@ -252,7 +290,7 @@ __global__ __launch_bounds__(256) void k_router(RouterArgs a) {
   __syncthreads();
   if (!s_last) return;
 
-  route_phase2<0>(a, KS, R);
+  route_phase2<0, 256>(a, KS, R);
 }
 
 // Attention boundary fused with the router, for the layer step.  Workgroup (row t, part q)
@@ -306,8 +344,6 @@ __global__ __launch_bounds__(256) void k_norm_router(NormRouterArgs A) {
   __shared__ float red[4];
   __shared__ float s_z[4][8];
   __shared__ float s_x[256 * EPT];
-  __shared__ RouteLds R;
-  __shared__ int s_last;
   const RouterArgs& a = A.r;
   const int t = blockIdx.x / RS, q = blockIdx.x - t * RS;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -419,16 +455,6 @@ __global__ __launch_bounds__(256) void k_norm_router(NormRouterArgs A) {
   __syncthreads();
   if (tid < 8 && 8 * q + tid < a.E)
     a.part[(size_t)t * a.E + 8 * q + tid] = (s_z[0][tid] + s_z[1][tid]) + (s_z[2][tid] + s_z[3][tid]);
-  // arrival: the logits are released before counting; the last arrival acquires them all
-  __syncthreads();
-  if (tid == 0) {
-    __threadfence();
-    s_last = atomicAdd(a.counter, 1) == (int)gridDim.x - 1;
-    if (s_last) __threadfence();
-  }
-  __syncthreads();
-  if (!s_last) return;
-  route_phase2<32>(a, 1, R);
 }
 
 __global__ void k_zero_i32(int* p) { *p = 0; }
@@ -446,14 +472,6 @@ __global__ void k_zero_i32(int* p) { *p = 0; }
 // 0-7 / 8-15); operand rows that do not exist are read through buffer loads whose range
 // check returns zero without a memory access.
 
-struct MoeMeta {
-  int active[257];
-  int cnt[256];
-  int off[256];
-  int tos[512];
-  float g13[256], g2[256];  // per-expert global scales: an LDS read in the epilogue, not a
-                            // global load queued behind the next unit's weights
-};
 
 __device__ __forceinline__ void stage_meta(const MoeArgs& a, MoeMeta& m) {
   const int nk = a.b * a.k;
@@ -536,13 +554,24 @@ __device__ __forceinline__ void unit_range(int n_units, int& begin, int& end) {
 }
 
 // W13 (gate rows [0, I), up rows [I, 2I)) + SwiGLU.  K = H = 128 * NU * KS.
-template <int NCT, int NU, int KS>
+template <int NCT, int NU, int KS, bool RT>
 __global__ __launch_bounds__(64 * KS) void k_moe_w13(MoeArgs a) {
   constexpr bool PB = NCT == 1;  // activations prefetched with the weights
   constexpr int NR = KS > 1 ? KS - 1 : 1;
   __shared__ MoeMeta meta;
   __shared__ f32x4_t red[PB ? 2 : 1][NR][2][NCT][64];
-  stage_meta(a, meta);
+  if constexpr (RT) {
+    // every workgroup routes from the router's logits (the same arithmetic, so the same
+    // maps); workgroup 0 also writes the maps for the W2 kernel and the unpooler
+    __shared__ RouteLdsT<64 * 32> R;  // b <= 64 rows, E <= 32 experts
+    for (int p = threadIdx.x; p < a.E; p += blockDim.x) {
+      meta.g13[p] = a.w13_gscale[p];
+      meta.g2[p] = a.w2_gscale[p];
+    }
+    route_phase2<32, 64 * KS>(a.r, 1, R, blockIdx.x == 0, &meta);
+  } else {
+    stage_meta(a, meta);
+  }
   const int NT = a.I >> 4;
   const int n_units = meta.active[a.E] * NT;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -876,7 +905,10 @@ hipError_t launch_experts_nct(const MoeArgs& a, hipStream_t st) {
   bool done = false;
 #define SD_W13(NU, KS)                                                                     \
   if (!done && s13.nu == NU && s13.ks == KS) {                                             \
-    hipLaunchKernelGGL((k_moe_w13<NCT, NU, KS>), dim3(g13), dim3(64 * KS), 0, st, a);      \
+    if (a.route)                                                                           \
+      hipLaunchKernelGGL((k_moe_w13<NCT, NU, KS, true>), dim3(g13), dim3(64 * KS), 0, st, a); \
+    else                                                                                   \
+      hipLaunchKernelGGL((k_moe_w13<NCT, NU, KS, false>), dim3(g13), dim3(64 * KS), 0, st, a); \
     done = true;                                                                          \
   }
   SD_SPLITS(SD_W13)

@@ -241,7 +241,8 @@ struct RouterArgs {
 hipError_t launch_router(const RouterArgs& a, hipStream_t st);
 
 // Attention boundary (dual norm over nbranch partials of the attention branch) fused with
-// the router; r.part holds [b, E] logits, r.x / r.x_lo are unused, r.counter must be 0.
+// the router's product: r.part receives the [b, E] logits (no bias); r.x / r.x_lo are
+// unused.  The routing itself runs in the expert kernel (MoeArgs::route).
 struct NormRouterArgs {
   int H;
   const float* branch;     // fp32 [nbranch, b, H]
@@ -273,6 +274,10 @@ struct MoeArgs {
   float* y;                   // fp32 [b*k, H]
   uint32_t x16_lo_off;        // set by the launcher: bytes from x16 to x16_lo (0: none)
   uint32_t h16_lo_off;        // set by the launcher: bytes from h16 to h16_lo
+  // route != 0: the W13 kernel first routes from the logits r.part [b, E] (+ r.bias), E <=
+  // 32, and writes r's maps, which counts / offsets / tos / active must point to
+  int route;
+  RouterArgs r;
 };
 hipError_t launch_moe_experts(const MoeArgs& a, hipStream_t st);
 bool moe_shape_supported(int H, int I);  // the expert GEMMs' K splits exist for H and I
