@@ -178,15 +178,22 @@ def main():
         r = StepRunner(wk, dev)
         r.chain_bufs = [torch.empty(wk["workload"].b, H, dtype=torch.float32, device=dev)
                         for _ in r.layers]
+        r.pool = r.pooled_buf()
         return r
 
     dense = wk["workload"].dense_inter > 0
 
-    def run_step(r, sb, stream=None):
+    # The timed layer step is sd_layer_step (unpooler included, input given as the unpooled
+    # branch).  pooled_step_us times sd_layer_step_pooled on the same copies, as in a stack:
+    # its input boundary gathers the previous layer's expert outputs (here its own previous
+    # output) and it leaves its own unpooled.
+    def run_step(r, sb, stream=None, pool=False):
         if chain:
             r.chain(sb, r.act["branch_in"], r.chain_bufs, with_tau=False, stream=stream)
         elif dense:
             r.dense_step(0, sb, stream=stream)
+        elif pool:
+            r.layer_step_pooled(0, sb, r.pool, r.pool, stream=stream)
         else:
             r.layer_step(0, sb, r.act["branch_in"], stream=stream)
 
@@ -211,16 +218,53 @@ def main():
     print(f"[bench] {R} rotation copies, {step_bytes / 1e6:.1f} MB algorithmic per step",
           file=sys.stderr, flush=True)
 
-    # Graphs on a side stream: one graph holds the R copies' layer steps back to back (as a
-    # serving graph holds a model's consecutive layers), so replays rotate through the copies
-    # and no graph launch separates two steps inside it; K % R leftover steps replay
-    # single-step graphs.  Every replay step is a whole layer step.
+    # Every timed step sees the same inputs: a step updates its stream (and, pooled, its
+    # pooled branch) in place, and an ever-growing stream would drift the routing and the
+    # bytes a step moves, so each copy's inputs are restored from a snapshot between graph
+    # replays, outside the timed intervals (events around each replay only).  Graphs run on
+    # a side stream; one graph holds the R copies' steps back to back (as a serving graph
+    # holds a model's consecutive layers); K % R leftover steps replay single-step graphs.
     st = torch.cuda.Stream()
     streams = [r.act["stream"].clone() for r in runners]
+    pooled = not chain and not dense
     with torch.cuda.stream(st):
         for r, sb in zip(runners, streams):
             run_step(r, sb, stream=st)      # warm (lazy module load)
+            sb.copy_(r.act["stream"])
+            if pooled:                      # its output becomes the copy's pooled input
+                run_step(r, sb, stream=st, pool=True)
+                sb.copy_(r.act["stream"])
     torch.cuda.synchronize()
+    snaps = []
+    for r, sb in zip(runners, streams):
+        sn = dict(s=sb.clone())
+        if pooled:
+            sn["y"] = r.pool["y"].clone()
+            sn["rt"] = {k: v.clone() for k, v in r.pool["route_t"].items()}
+        snaps.append(sn)
+
+    def restore():
+        for r, sb, sn in zip(runners, streams, snaps):
+            sb.copy_(sn["s"])
+            if pooled:
+                r.pool["y"].copy_(sn["y"])
+                for k, v in r.pool["route_t"].items():
+                    v.copy_(sn["rt"][k])
+
+    # bytes per step from each copy's own routing on exactly the timed inputs
+    touched = [int((c > 0).sum()) for c in counts_per_layer] if chain else int((counts > 0).sum())
+    if pooled:
+        with torch.cuda.stream(st):
+            for r, sb in zip(runners, streams):
+                run_step(r, sb, stream=st)
+        torch.cuda.synchronize()
+        copy_counts = [r.route_t["expert_counts"].cpu().numpy() for r in runners]
+        with torch.cuda.stream(st):
+            restore()
+        torch.cuda.synchronize()
+        step_bytes = float(np.mean([algorithmic_bytes(wk, [c])[0] for c in copy_counts]))
+        touched = [int((c > 0).sum()) for c in copy_counts]
+
     g_all = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g_all, stream=st):
         for r, sb in zip(runners, streams):
@@ -233,40 +277,45 @@ def main():
         singles.append(g)
     torch.cuda.synchronize()
 
-    with torch.cuda.stream(st):
-        for i in range(max(1, args.warmup // R)):
-            g_all.replay()
-    torch.cuda.synchronize()
+    def timed_replays(graph, n):
+        """Replays graph n times, inputs restored before each; us of each replay."""
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        with torch.cuda.stream(st):
+            for e0_, e1_ in evs:
+                restore()
+                e0_.record(st)
+                graph.replay()
+                e1_.record(st)
+        torch.cuda.synchronize()
+        return np.array([a_.elapsed_time(b_) for a_, b_ in evs]) * 1e3
+
+    timed_replays(g_all, max(1, args.warmup // R))
     K = args.steps
     n_all, n_rest = K // R, K % R
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_all + n_rest + 1)]
-    torch.cuda.synchronize()
-    with torch.cuda.stream(st):
-        ev[0].record(st)
-        for i in range(n_all):
-            g_all.replay()
-            ev[i + 1].record(st)
-        for i in range(n_rest):
-            singles[i].replay()
-            ev[n_all + i + 1].record(st)
-    torch.cuda.synchronize()
-    total_ms = ev[0].elapsed_time(ev[n_all + n_rest])
-    per = np.array([ev[i].elapsed_time(ev[i + 1]) / R for i in range(n_all)]) * 1e3  # us per step
-    us = total_ms * 1e3 / K
+    per_all = timed_replays(g_all, n_all) if n_all else np.zeros(0)
+    rest = [float(timed_replays(singles[i], 1)[0]) for i in range(n_rest)]
+    us = (float(per_all.sum()) + sum(rest)) / K
+    per = per_all / R if n_all else np.array(rest)  # us per step
     graphs = singles
 
-    # hot-cache number (same copy every step), labelled separately
-    with torch.cuda.stream(st):
-        h0 = torch.cuda.Event(enable_timing=True)
-        h1 = torch.cuda.Event(enable_timing=True)
-        for _ in range(10):
-            graphs[0].replay()
-        h0.record(st)
-        for _ in range(50):
-            graphs[0].replay()
-        h1.record(st)
-    torch.cuda.synchronize()
-    hot_us = h0.elapsed_time(h1) * 1e3 / 50
+    # the pooled layer step (sd_layer_step_pooled) on the same copies and inputs
+    pooled_us = None
+    if pooled:
+        # the maps the timed step left in each copy's route feed the roofline loop below
+        plain_expert_bytes = [algorithmic_bytes(wk, [c])[1] for c in copy_counts]
+        g_pool = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_pool, stream=st):
+            for r, sb in zip(runners, streams):
+                run_step(r, sb, stream=st, pool=True)
+        torch.cuda.synchronize()
+        timed_replays(g_pool, max(1, args.warmup // R))
+        pooled_us = float(timed_replays(g_pool, max(1, min(K, 200) // R)).mean()) / R
+
+    # hot-cache number (same copy every step, inputs restored between replays), labelled
+    # separately
+    timed_replays(graphs[0], 10)
+    hot_us = float(timed_replays(graphs[0], 50).mean())
 
     # dominant kernels: the routed-expert GEMMs (sd_moe_experts: k_moe_w13 then k_moe_w2),
     # timed live with HIP events on their launch stream, rotating over the copies like the
@@ -299,6 +348,8 @@ def main():
         e1.record(st)
     torch.cuda.synchronize()
     exp_us = e0.elapsed_time(e1) * 1e3 / n_it      # average per launch, back to back
+    if pooled:  # each copy's own touched experts, in the loop's rotation
+        expert_bytes = float(np.mean([plain_expert_bytes[i % R] for i in range(n_it)]))
     achieved = expert_bytes / (exp_us * 1e-6) / 1e9
 
     out = {
@@ -320,13 +371,14 @@ def main():
                    "n_q_heads": d["n_q_heads"], "n_kv_heads": d["n_kv_heads"],
                    "head_dim": d["head_dim"], "experts": d["n_experts"], "top_k": d["top_k"],
                    "inter": d["inter"], "context": int(wk["layers"][0]["seq_lens"].sum()),
-                   "touched_experts": [int((c > 0).sum()) for c in counts_per_layer] if chain
-                   else int((counts > 0).sum()),
-                   "layers": len(counts_per_layer), "rotation_copies": R},
+                   "touched_experts": touched,
+                   "layers": len(counts_per_layer), "rotation_copies": R,
+                   "layer_step": "chain" if chain else ("dense" if dense else "sd_layer_step")},
         "step_bytes": int(step_bytes),
         "step_GBps": round(step_bytes / (us * 1e-6) / 1e9, 1),
         "step_frac_hbm": round(step_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
         "tokens_per_s": round(b * 1e6 / us, 1),
+        "pooled_step_us": None if pooled_us is None else round(pooled_us, 3),
         "us_p10_p50_p90": [round(float(np.percentile(per, q)), 3) for q in (10, 50, 90)],
         "hot_cache_us": round(hot_us, 3),
         "roofline": {"bound": "hbm",

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define SD_ABI_VERSION 5
+#define SD_ABI_VERSION 6
 
 enum {
   SD_OK = 0,
@@ -237,6 +237,28 @@ int sd_layer_step(const sd_dims *dims, int32_t b, float *stream, const float *br
                   const void *front_embed, const sd_layer_weights *w, const sd_kv *kv,
                   const float *logit_bias, float *branch_out, const sd_route *route_out,
                   void *ws, size_t ws_bytes, void *stream_handle);
+
+/* A pooled MoE branch: the routed experts' per-slot outputs y_slots fp32 [b * k, H] and the
+ * routing that weighs them (route: topk_w and slot_of are read; every field is written by
+ * the step that produces it). */
+typedef struct sd_pooled {
+  float *y_slots;
+  const sd_route *route;
+} sd_pooled;
+
+/* The layer step of a stack, with the unpooler moved into the next layer's input boundary
+ * ([DEC] SpecializedDecode.run: the input boundary gathers the previous layer's MoE output
+ * before its dual norm).  branch_in: the previous layer's pooled output, gathered as
+ * u[t] = sum over j < k, in order, of topk_w[t, j] * y_slots[slot_of[t, j]], then the same
+ * boundary as sd_layer_step (NULL: the front, from front_embed).  branch_out: this layer's
+ * experts write y_slots and the routing writes route, and no unpooler runs; the final
+ * boundary of a stack gathers with sd_moe_unpool.  Every other argument and result is as
+ * for sd_layer_step.  branch_out may be branch_in (it is read before it is written). */
+int sd_layer_step_pooled(const sd_dims *dims, int32_t b, float *stream,
+                         const sd_pooled *branch_in, const void *front_embed,
+                         const sd_layer_weights *w, const sd_kv *kv, const float *logit_bias,
+                         const sd_pooled *branch_out, void *ws, size_t ws_bytes,
+                         void *stream_handle);
 
 /* Draft head on bf16 hidden rows h [b, hidden] ([DSP] compute_draft_logits,
  * apply_output_logit_transform, draft_id_to_target_id; [RT] unsupported: BF16 logits):

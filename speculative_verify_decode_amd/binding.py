@@ -61,6 +61,10 @@ class SdCtxLayer(ctypes.Structure):
                 ("v_cache", c_void_p), ("num_blocks", c_int), ("slot_mapping", c_void_p)]
 
 
+class SdPooled(ctypes.Structure):
+    _fields_ = [("y_slots", c_void_p), ("route", ctypes.POINTER(SdRoute))]
+
+
 SYMBOLS = {
     "sd_abi_version": (c_int, []),
     "sd_last_error": (ctypes.c_char_p, []),
@@ -84,6 +88,11 @@ SYMBOLS = {
     "sd_layer_step": (c_int, [ctypes.POINTER(SdDims), c_int, c_void_p, c_void_p, c_void_p,
                               ctypes.POINTER(SdLayerWeights), ctypes.POINTER(SdKv), c_void_p,
                               c_void_p, ctypes.POINTER(SdRoute), c_void_p, c_size_t, c_void_p]),
+    "sd_layer_step_pooled": (c_int, [ctypes.POINTER(SdDims), c_int, c_void_p,
+                                     ctypes.POINTER(SdPooled), c_void_p,
+                                     ctypes.POINTER(SdLayerWeights), ctypes.POINTER(SdKv),
+                                     c_void_p, ctypes.POINTER(SdPooled), c_void_p, c_size_t,
+                                     c_void_p]),
     "sd_draft_head": (c_int, [c_int, c_int, c_int, c_void_p, c_void_p, c_float, c_float,
                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                               c_void_p]),
@@ -255,6 +264,23 @@ def layer_step(dims, b, stream_buf, branch_in, front_embed, layer_w, kv, logit_b
                                ptr(logit_bias), ptr(branch_out),
                                ctypes.byref(route) if route is not None else None, ptr(ws),
                                ws.numel() * ws.element_size(), cur_stream(stream)))
+
+
+def make_pooled(y_slots, route):
+    """A pooled MoE branch: y_slots fp32 [b * k, H] and its SdRoute (kept alive by the
+    returned struct's _keep)."""
+    p = SdPooled(y_slots=ptr(y_slots), route=ctypes.pointer(route))
+    p._keep = (y_slots, route)
+    return p
+
+
+def layer_step_pooled(dims, b, stream_buf, pooled_in, front_embed, layer_w, kv, logit_bias,
+                      pooled_out, ws, stream=None):
+    _check(lib().sd_layer_step_pooled(ctypes.byref(dims), b, ptr(stream_buf),
+                                      ctypes.byref(pooled_in) if pooled_in is not None else None,
+                                      ptr(front_embed), ctypes.byref(layer_w), ctypes.byref(kv),
+                                      ptr(logit_bias), ctypes.byref(pooled_out), ptr(ws),
+                                      ws.numel() * ws.element_size(), cur_stream(stream)))
 
 
 def make_dense_layer_weights(lay):

@@ -469,24 +469,38 @@ int sd_moe_unpool(const sd_dims* dims, int32_t b, const float* y_slots, const sd
   return ok();
 }
 
-int sd_layer_step(const sd_dims* dims, int32_t b, float* stream, const float* branch_in,
-                  const void* front_embed, const sd_layer_weights* w, const sd_kv* kv,
-                  const float* logit_bias, float* branch_out, const sd_route* route_out,
-                  void* ws, size_t ws_bytes, void* stream_handle) {
+namespace {
+
+// The layer step.  Input: branch_in (fp32 [b, H]), or pool_in (the previous layer's pooled
+// MoE output, gathered by the input boundary), or neither (the front, from front_embed).
+// Output: branch_out (the unpooled branch), or pool_out (y_slots and the route, no unpool).
+int layer_step_impl(const sd_dims* dims, int32_t b, float* stream, const float* branch_in,
+                    const sd_pooled* pool_in, const void* front_embed, const sd_layer_weights* w,
+                    const sd_kv* kv, const float* logit_bias, float* branch_out,
+                    const sd_route* route_out, const sd_pooled* pool_out, void* ws,
+                    size_t ws_bytes, void* stream_handle) {
   SD_CHECK(check_dims(dims));
   SD_CHECK(check_rows(dims, b));
   if (w == nullptr) return fail(SD_EINVAL, "layer weights are null");
   if (!w->g_pre_attn || !w->g_post_attn || !w->g_pre_ffn)
     return fail(SD_EINVAL, "a layer gain is null");
-  if (branch_in != nullptr && !w->g_post_prev) return fail(SD_EINVAL, "g_post_prev is null");
-  if (branch_in == nullptr && front_embed == nullptr)
+  const bool has_in = branch_in != nullptr || pool_in != nullptr;
+  if (has_in && !w->g_post_prev) return fail(SD_EINVAL, "g_post_prev is null");
+  if (!has_in && front_embed == nullptr)
     return fail(SD_EINVAL, "the first layer's front needs front_embed");
   SD_CHECK(check_attn_weights(&w->attn));
   SD_CHECK(check_moe_weights(&w->moe, true, true));
   SD_CHECK(check_kv(dims, b, kv));
-  if (!stream || !branch_out || !aligned16(branch_out) ||
-      (branch_in != nullptr && !aligned16(branch_in)))
-    return fail(SD_EINVAL, "stream or branch_out null, or a branch misaligned");
+  if (!stream || (branch_in != nullptr && !aligned16(branch_in)))
+    return fail(SD_EINVAL, "stream null, or branch_in misaligned");
+  if (pool_out == nullptr && (!branch_out || !aligned16(branch_out)))
+    return fail(SD_EINVAL, "branch_out null or misaligned");
+  for (const sd_pooled* pp : {pool_in, pool_out}) {
+    if (pp == nullptr) continue;
+    if (!pp->y_slots || !aligned16(pp->y_slots) || !pp->route)
+      return fail(SD_EINVAL, "a pooled branch has a null or misaligned y_slots, or no route");
+    SD_CHECK(check_route(pp->route));
+  }
   if (route_out) SD_CHECK(check_route(route_out));
   SD_CHECK(check_ws(dims, b, kv->n_req, kv->max_seq_len, ws, ws_bytes));
   const Ws L = ws_layout(*dims, b, kv->n_req, kv->max_seq_len);
@@ -494,11 +508,19 @@ int sd_layer_step(const sd_dims* dims, int32_t b, float* stream, const float* br
   const int H = dims->hidden;
   uint16_t* x_a = at<uint16_t>(ws, L.x_a);
   uint16_t* x_a_lo = at<uint16_t>(ws, L.x_a_lo);
-  SD_LAUNCH(launch_dualnorm(b, H, stream, (const float*)branch_in, 1,
-                            (const uint16_t*)front_embed, w->g_post_prev, w->g_pre_attn,
-                            dims->eps, x_a, x_a_lo, nullptr, nullptr, at<int>(ws, L.counter),
-                            st),
-            "input boundary");
+  if (pool_in != nullptr) {
+    SD_LAUNCH(launch_dualnorm(b, H, stream, pool_in->y_slots, 1, nullptr, w->g_post_prev,
+                              w->g_pre_attn, dims->eps, x_a, x_a_lo, nullptr, nullptr,
+                              at<int>(ws, L.counter), st, pool_in->route->topk_w,
+                              pool_in->route->slot_of, dims->top_k),
+              "input boundary (gathering the pooled branch)");
+  } else {
+    SD_LAUNCH(launch_dualnorm(b, H, stream, (const float*)branch_in, 1,
+                              (const uint16_t*)front_embed, w->g_post_prev, w->g_pre_attn,
+                              dims->eps, x_a, x_a_lo, nullptr, nullptr, at<int>(ws, L.counter),
+                              st),
+              "input boundary");
+  }
   float* a = at<float>(ws, L.a);
   int a_parts = 1;
   SD_CHECK(run_attention(dims, b, x_a, x_a_lo, &w->attn, kv, a, kDenseSplit, ws, L, st,
@@ -507,7 +529,7 @@ int sd_layer_step(const sd_dims* dims, int32_t b, float* stream, const float* br
   uint16_t* x_m_lo = at<uint16_t>(ws, L.x_m_lo);
   _Float16* x16 = at<_Float16>(ws, L.x16);
   _Float16* x16_lo = at<_Float16>(ws, L.x16_lo);
-  const sd_route r = route_out ? *route_out : ws_route(ws, L);
+  const sd_route r = pool_out ? *pool_out->route : route_out ? *route_out : ws_route(ws, L);
   NormRouterArgs nr{};
   const RouterArgs* route_in_experts = nullptr;  // the expert kernel routes from the logits
   if (norm_router_parts(H, dims->n_experts, b, dims->top_k) > 0 && (a_parts == 1 || a_parts == 4)) {
@@ -527,12 +549,33 @@ int sd_layer_step(const sd_dims* dims, int32_t b, float* stream, const float* br
     SD_CHECK(run_route(dims, b, x_m, x_m_lo, w->moe.w_router, logit_bias, &r, nullptr, ws, L,
                        st));
   }
-  float* y = at<float>(ws, L.y);
+  float* y = pool_out ? pool_out->y_slots : at<float>(ws, L.y);
   SD_CHECK(run_experts(dims, b, x16, x16_lo, &w->moe, &r, y, nullptr, at<_Float16>(ws, L.h16),
                        at<_Float16>(ws, L.h16_lo), st, route_in_experts));
-  SD_LAUNCH(launch_unpool(b, H, dims->top_k, y, r.topk_w, r.slot_of, (float*)branch_out, st),
-            "unpooler");
+  if (pool_out == nullptr)
+    SD_LAUNCH(launch_unpool(b, H, dims->top_k, y, r.topk_w, r.slot_of, (float*)branch_out, st),
+              "unpooler");
   return ok();
+}
+
+}  // namespace
+
+int sd_layer_step(const sd_dims* dims, int32_t b, float* stream, const float* branch_in,
+                  const void* front_embed, const sd_layer_weights* w, const sd_kv* kv,
+                  const float* logit_bias, float* branch_out, const sd_route* route_out,
+                  void* ws, size_t ws_bytes, void* stream_handle) {
+  return layer_step_impl(dims, b, stream, branch_in, nullptr, front_embed, w, kv, logit_bias,
+                         branch_out, route_out, nullptr, ws, ws_bytes, stream_handle);
+}
+
+int sd_layer_step_pooled(const sd_dims* dims, int32_t b, float* stream,
+                         const sd_pooled* branch_in, const void* front_embed,
+                         const sd_layer_weights* w, const sd_kv* kv, const float* logit_bias,
+                         const sd_pooled* branch_out, void* ws, size_t ws_bytes,
+                         void* stream_handle) {
+  if (branch_out == nullptr) return fail(SD_EINVAL, "branch_out is null");
+  return layer_step_impl(dims, b, stream, nullptr, branch_in, front_embed, w, kv, logit_bias,
+                         nullptr, nullptr, branch_out, ws, ws_bytes, stream_handle);
 }
 
 // ------------------------------------------------------------------------ draft side

@@ -32,10 +32,15 @@ template <> struct VecT<4> { typedef f32x4_t T; };
 // element (v * 256 + tid) * VW, so every load is coalesced and as wide as H allows.  All
 // inputs (the NB branch partials, stream, both gains) are loaded before the first
 // reduction, so the row costs one round trip to memory; outputs leave as packed stores.
-template <int EPT, int NB>
+// POOL: the branch is the previous layer's pooled MoE output, gathered here (the weighted
+// unpooler): branch row t = sum over j < k, in order, of w[t, j] * y[slot_of[t, j]] (y fp32
+// [b * k, H]); the row's k slot ids and weights are read first, then every slot row at once.
+template <int EPT, int NB, bool POOL>
 __global__ __launch_bounds__(256) void k_dualnorm(int H, float* __restrict__ stream,
                                                   const float* __restrict__ branch,
                                                   size_t branch_stride,
+                                                  const float* __restrict__ pw,
+                                                  const int* __restrict__ pslot, int pk,
                                                   const uint16_t* __restrict__ front,
                                                   const float* __restrict__ g_post,
                                                   const float* __restrict__ g_pre, float eps,
@@ -62,12 +67,33 @@ __global__ __launch_bounds__(256) void k_dualnorm(int H, float* __restrict__ str
   }
   if (branch != nullptr) {
     float u[EPT], gp[EPT];
+    int sl[POOL ? 8 : 1];
+    float wj[POOL ? 8 : 1];
+    if constexpr (POOL) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        // clamped into the pooled rows, so a bad slot id reads a wrong row, never past y
+        sl[j] = min(max(pslot[row * pk + min(j, pk - 1)], 0), (int)gridDim.x * pk - 1);
+        wj[j] = j < pk ? pw[row * pk + j] : 0.f;
+      }
+    }
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
       const int i0 = (v * 256 + tid) * VW;
-      V bu = *(const V*)(branch + base + i0);
+      V bu;
+      if constexpr (POOL) {
+        // choices past k repeat the last slot with weight 0 (an exact +0 to the sum)
+        V yv[8];
 #pragma unroll
-      for (int p = 1; p < NB; ++p) bu += *(const V*)(branch + p * branch_stride + base + i0);
+        for (int j = 0; j < 8; ++j) yv[j] = *(const V*)(branch + (size_t)sl[j] * H + i0);
+        bu = V{};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) bu += wj[j] * yv[j];
+      } else {
+        bu = *(const V*)(branch + base + i0);
+#pragma unroll
+        for (int p = 1; p < NB; ++p) bu += *(const V*)(branch + p * branch_stride + base + i0);
+      }
       const V bs = *(const V*)(stream + base + i0);
       const V bg = *(const V*)(g_post + i0);
 #pragma unroll
@@ -128,21 +154,27 @@ __global__ __launch_bounds__(256) void k_dualnorm(int H, float* __restrict__ str
 hipError_t launch_dualnorm(int b, int H, float* stream, const float* branch, int nbranch,
                            const uint16_t* front, const float* g_post, const float* g_pre,
                            float eps, uint16_t* out, uint16_t* out_lo, _Float16* x16,
-                           _Float16* x16_lo, int* zero, hipStream_t st) {
+                           _Float16* x16_lo, int* zero, hipStream_t st, const float* pool_w,
+                           const int* pool_slot, int pool_k) {
   if ((x16 == nullptr) != (x16_lo == nullptr)) return hipErrorInvalidValue;
   if (branch != nullptr && nbranch < 1) return hipErrorInvalidValue;
+  const bool pool = pool_slot != nullptr;
+  if (pool && (branch == nullptr || pool_w == nullptr || pool_k < 1 || pool_k > 8))
+    return hipErrorInvalidValue;
   const dim3 grid(b), block(256);
   const size_t bs = (size_t)b * H;
   if (branch == nullptr) nbranch = 1;
   if (nbranch != 1 && nbranch != 2 && nbranch != 4) return hipErrorInvalidValue;
-#define SD_NORM_NB(E, NBV)                                                                 \
-  hipLaunchKernelGGL((k_dualnorm<E, NBV>), grid, block, 0, st, H, stream, branch, bs, front, \
-                     g_post, g_pre, eps, out, out_lo, x16, x16_lo, zero)
+#define SD_NORM_NB(E, NBV, P)                                                              \
+  hipLaunchKernelGGL((k_dualnorm<E, NBV, P>), grid, block, 0, st, H, stream, branch, bs,     \
+                     pool_w, pool_slot, pool_k, front, g_post, g_pre, eps, out, out_lo, x16,  \
+                     x16_lo, zero)
 #define SD_NORM_CASE(E)                                                                   \
   case E:                                                                                 \
-    if (nbranch == 1) SD_NORM_NB(E, 1);                                                   \
-    else if (nbranch == 2) SD_NORM_NB(E, 2);                                              \
-    else SD_NORM_NB(E, 4);                                                                \
+    if (pool) SD_NORM_NB(E, 1, true);                                                     \
+    else if (nbranch == 1) SD_NORM_NB(E, 1, false);                                       \
+    else if (nbranch == 2) SD_NORM_NB(E, 2, false);                                       \
+    else SD_NORM_NB(E, 4, false);                                                         \
     break;
   switch (H / 256) {
     SD_NORM_CASE(1)

@@ -127,10 +127,14 @@ __device__ __forceinline__ void dequant_unit(u32x4_t codes, uint32_t scales2, f1
 // out: bf16 pre-norm output (hi term); out_lo (optional): its bf16 lo term; x16 / x16_lo
 // (optional): fp16 hi / lo terms of the pre-norm output * 2^-8 (the expert input).
 // zero (optional): an int set to 0, for a later kernel's arrival counter.
+// pool_slot (optional): the branch is pooled, branch = y [b * pool_k, H], row t gathered
+// as sum over j of pool_w[t, j] * y[pool_slot[t, j]] (nbranch must be 1).
 hipError_t launch_dualnorm(int b, int H, float* stream, const float* branch, int nbranch,
                            const uint16_t* front, const float* g_post, const float* g_pre,
                            float eps, uint16_t* out, uint16_t* out_lo, _Float16* x16,
-                           _Float16* x16_lo, int* zero, hipStream_t st);
+                           _Float16* x16_lo, int* zero, hipStream_t st,
+                           const float* pool_w = nullptr, const int* pool_slot = nullptr,
+                           int pool_k = 0);
 
 enum GemmMode { GEMM_F32 = 0, GEMM_F32_BIAS = 2, GEMM_HEAD = 3 };
 

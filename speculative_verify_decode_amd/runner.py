@@ -117,6 +117,26 @@ class StepRunner:
                      stream)
         return out
 
+    def pooled_buf(self):
+        """A pooled MoE branch: y_slots fp32 [b * k, H] (zeros) and its own routing maps."""
+        k, H = self.d["top_k"], self.d["hidden"]
+        y = torch.zeros(self.b * k, H, dtype=torch.float32, device=self.device)
+        route_t, route = alloc_route(self.b, k, self.d["n_experts"], self.device)
+        for t in route_t.values():  # a valid (all-zero) branch until a step writes it
+            t.zero_()
+        return dict(y=y, route_t=route_t, route=route, p=B.make_pooled(y, route))
+
+    def layer_step_pooled(self, i, stream_buf, pooled_in, pooled_out, front_embed=None,
+                          stream=None):
+        """Layer i in pooled form: gathers pooled_in (None: the front) in its input boundary
+        and leaves its own experts' output in pooled_out (no unpooler)."""
+        L = self.layers[i]
+        B.layer_step_pooled(self.dims, self.b, stream_buf,
+                            None if pooled_in is None else pooled_in["p"], front_embed,
+                            L.weights, L.kv, self.act["logit_bias"], pooled_out["p"], self.ws,
+                            stream)
+        return pooled_out
+
     def dense_step(self, i, stream_buf, stream=None):
         """Layer i as a dense draft layer on stream_buf (in place)."""
         L = self.layers[i]

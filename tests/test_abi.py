@@ -55,7 +55,7 @@ def test_no_extra_exports_beyond_header(lib):
 
 
 def test_abi_version(lib):
-    assert B.abi_version() == 5
+    assert B.abi_version() == 6
 
 
 def test_workspace_bytes_host_only(lib):
