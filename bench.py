@@ -212,7 +212,9 @@ def main():
     counts = counts_per_layer[0]
     step_bytes, expert_bytes = algorithmic_bytes(wk, counts_per_layer)
     # (at most 16 copies: a step small enough to need more is launch-bound, not HBM-bound)
-    R = args.copies or min(16, max(2, math.ceil(1.0e9 / step_bytes)))
+    # at least 8 copies: every replay is timed on its own (inputs are restored between
+    # replays), so the fixed cost of starting a replay is shared by R steps
+    R = args.copies or min(16, max(8, math.ceil(1.0e9 / step_bytes)))
     R = max(1, min(R, args.steps))
     runners = [r0] + [make_runner() for _ in range(R - 1)]
     print(f"[bench] {R} rotation copies, {step_bytes / 1e6:.1f} MB algorithmic per step",
@@ -312,10 +314,15 @@ def main():
         timed_replays(g_pool, max(1, args.warmup // R))
         pooled_us = float(timed_replays(g_pool, max(1, min(K, 200) // R)).mean()) / R
 
-    # hot-cache number (same copy every step, inputs restored between replays), labelled
-    # separately
-    timed_replays(graphs[0], 10)
-    hot_us = float(timed_replays(graphs[0], 50).mean())
+    # hot-cache number (copy 0, R steps per replay, inputs restored between replays),
+    # labelled separately
+    g_hot = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_hot, stream=st):
+        for _ in range(R):
+            run_step(runners[0], streams[0], stream=st)
+    torch.cuda.synchronize()
+    timed_replays(g_hot, 2)
+    hot_us = float(timed_replays(g_hot, max(1, 50 // R)).mean()) / R
 
     # dominant kernels: the routed-expert GEMMs (sd_moe_experts: k_moe_w13 then k_moe_w2),
     # timed live with HIP events on their launch stream, rotating over the copies like the
