@@ -74,3 +74,47 @@ def test_pooled_step_rejects_missing_output():
             B.ctypes.byref(r.dims), r.b, B.ptr(s), None, B.ptr(r.act["front_embed"]),
             B.ctypes.byref(r.layers[0].weights), B.ctypes.byref(r.layers[0].kv), None, None,
             B.ptr(r.ws), r.ws.numel() * r.ws.element_size(), None))
+
+
+def test_pooled_step_graph_replays_match_eager():
+    """The pooled step reading and writing the same pooled buffer, captured once and replayed
+    from restored inputs with eager work in between, equals the eager step every time."""
+    wk = workload("tiny_b8_ctx128")
+    r = runner(wk)
+    pool = r.pooled_buf()
+    s = r.act["stream"].clone()
+    r.layer_step_pooled(0, s, None, pool, front_embed=r.act["front_embed"])  # a real pooled input
+    torch.cuda.synchronize()
+    s0 = r.act["stream"].clone()
+    k0, v0 = r.layers[0].t["k_cache"].clone(), r.layers[0].t["v_cache"].clone()
+    y0 = pool["y"].clone()
+    rt0 = {k: v.clone() for k, v in pool["route_t"].items()}
+
+    def restore():
+        s.copy_(s0)
+        r.layers[0].t["k_cache"].copy_(k0)
+        r.layers[0].t["v_cache"].copy_(v0)
+        pool["y"].copy_(y0)
+        for k, v in pool["route_t"].items():
+            v.copy_(rt0[k])
+
+    restore()
+    r.layer_step_pooled(0, s, pool, pool)
+    torch.cuda.synchronize()
+    eager_s, eager_y = s.clone(), pool["y"].clone()
+    eager_ids = pool["route_t"]["topk_ids"].clone()
+    st = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    restore()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=st):
+        r.layer_step_pooled(0, s, pool, pool, stream=st)
+    for rep in range(4):
+        restore()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _ = (torch.randn(1000, device=DEV) * 2).sum().item()     # eager work between replays
+        assert torch.equal(s.view(torch.int32), eager_s.view(torch.int32)), rep
+        assert torch.equal(pool["y"].view(torch.int32), eager_y.view(torch.int32)), rep
+        assert torch.equal(pool["route_t"]["topk_ids"], eager_ids), rep
