@@ -495,7 +495,7 @@ void k_attn_split(AttnArgs a, int cb, int n_chunks) {
 // chunk c's statistics into its weight exp2(m_c - M) (in LDS) and w_c * l_c (block-summed).
 // GEN as for the split: partial drafts map the column to its row through query_start, and
 // columns past a request's rows exit after issuing their loads.
-template <bool GEN>
+template <bool GEN, int NP>
 __global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a, int cb, int n_chunks, int qg) {
   constexpr int PASS = 32;
   __shared__ __align__(16) float s_w[1024];
@@ -517,20 +517,26 @@ __global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a, int cb, int n_
   const ReqRows rq = GEN ? req_rows(a, r) : ReqRows{r * a.q_rows, a.q_rows};
   const int t = rq.base + min(jr, max(rq.n - 1, 0));  // the step row of this column
   float gate = 0.f;  // the output gate, slices summed in order
+  {
+    float gp[NP];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const float gp = a.gate[(size_t)min(p, a.nparts - 1) * a.part_stride +
-                            (size_t)t * a.gate_stride + h * a.D + d];
-    gate += p < a.nparts ? gp : 0.f;
+    for (int p = 0; p < NP; ++p)
+      gp[p] = a.gate[(size_t)p * a.part_stride + (size_t)t * a.gate_stride + h * a.D + d];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) gate += gp[p];
   }
   const int L = min(a.seq_lens[r], a.max_blocks * 16);
   const int nc = max(min((((L + 15) >> 4) - (GEN ? first_block(a, r) : 0) + cb - 1) / cb,
                          n_chunks), 1);
   if (jr >= rq.n) return;  // uniform per workgroup, before any barrier
   // chunk statistics: thread c holds (m_c, l_c) of chunks c, c + D, ...
-  float mloc = -INFINITY;
-  for (int c = d; c < nc; c += blockDim.x) {
-    const float2 ml = c == d ? ml0 : *(const float2*)&a.part_ml[((p0 + c) * qg + qi) * 2];
+  // (the first chunk's pair is the one loaded above, kept out of the loop so it stays a
+  // register value)
+  s_w[d] = ml0.x;  // d < blockDim <= 1024; entries past nc are never used
+  s_lc[d] = ml0.y;
+  float mloc = d < nc ? ml0.x : -INFINITY;
+  for (int c = d + (int)blockDim.x; c < nc; c += blockDim.x) {
+    const float2 ml = *(const float2*)&a.part_ml[((p0 + c) * qg + qi) * 2];
     s_w[c] = ml.x;
     s_lc[c] = ml.y;
     mloc = fmaxf(mloc, ml.x);
@@ -628,11 +634,13 @@ hipError_t launch_attention(const AttnArgs& a, const AttnPlan& p, hipStream_t st
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 cgrid(a.n_req * a.q_rows * a.Hq), cblock(a.D);
-  if (gen)
-    hipLaunchKernelGGL(k_attn_combine<true>, cgrid, cblock, 0, st, a, p.chunk_blocks, p.n_chunks,
-                       p.qg);
-  else
-    hipLaunchKernelGGL(k_attn_combine<false>, cgrid, cblock, 0, st, a, p.chunk_blocks,
-                       p.n_chunks, p.qg);
+#define SD_COMB(GN, NPV)                                                                   \
+  hipLaunchKernelGGL((k_attn_combine<GN, NPV>), cgrid, cblock, 0, st, a, p.chunk_blocks,     \
+                     p.n_chunks, p.qg)
+  if (gen && a.nparts == 4) SD_COMB(true, 4);
+  else if (gen) SD_COMB(true, 1);
+  else if (a.nparts == 4) SD_COMB(false, 4);
+  else SD_COMB(false, 1);
+#undef SD_COMB
   return hipGetLastError();
 }
