@@ -76,11 +76,15 @@ __device__ void route_phase2(const RouterArgs& a, int KS, RL& R, bool out = true
   // z = sum over ks in order + bias, every (row, expert) at once: one round of loads.  The
   // LDS copy is an order key: larger key = earlier in (-z, index) order, NaN last.
   const size_t st = (size_t)b * E;
+  // the bias is read unconditionally (the partials stand in when there is none), so its load
+  // goes out with the partials' instead of after them
+  const float* bias = a.bias != nullptr ? a.bias : a.part;
   for (int idx = tid; idx < b * E; idx += NT) {
+    const float bv = bias[idx];
     float z = 0.f;
 #pragma unroll 16
     for (int j = 0; j < KS; ++j) z += a.part[j * st + idx];
-    if (a.bias != nullptr) z += a.bias[idx];
+    if (a.bias != nullptr) z += bv;
     if (out && a.logits != nullptr) a.logits[idx] = z;
     const uint32_t u = __float_as_uint(z == 0.f ? 0.f : z);  // -0 ties with +0
     R.key[idx] = z != z ? 0u : (u & 0x80000000u ? ~u : u | 0x80000000u);
@@ -564,11 +568,16 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w13(MoeArgs a) {
     // every workgroup routes from the router's logits (the same arithmetic, so the same
     // maps); workgroup 0 also writes the maps for the W2 kernel and the unpooler
     __shared__ RouteLdsT<64 * 32> R;  // b <= 64 rows, E <= 32 experts
-    for (int p = threadIdx.x; p < a.E; p += blockDim.x) {
-      meta.g13[p] = a.w13_gscale[p];
-      meta.g2[p] = a.w2_gscale[p];
-    }
+    // the global scales are read before the routing and staged after it, so their loads go
+    // out with the logits' (a barrier inside the routing keeps them there)
+    const int ge = min((int)threadIdx.x, a.E - 1);
+    const float g13v = a.w13_gscale[ge], g2v = a.w2_gscale[ge];
     route_phase2<32, 64 * KS>(a.r, 1, R, blockIdx.x == 0, &meta);
+    if ((int)threadIdx.x < a.E) {
+      meta.g13[threadIdx.x] = g13v;
+      meta.g2[threadIdx.x] = g2v;
+    }
+    __syncthreads();
   } else {
     stage_meta(a, meta);
   }
