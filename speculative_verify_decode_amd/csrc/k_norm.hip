@@ -103,6 +103,7 @@ __global__ __launch_bounds__(256) void k_dualnorm(int H, float* __restrict__ str
         gp[v * VW + j] = ((const float*)&bg)[j];
       }
     }
+    __builtin_amdgcn_sched_barrier(0);  // every load above is issued before the first use
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < EPT; ++e) ss += u[e] * u[e];
