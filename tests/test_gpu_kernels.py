@@ -288,3 +288,39 @@ def test_draft_head_ties_take_the_lower_index():
                  tgt, ws)
     torch.cuda.synchronize()
     assert ids.cpu().tolist() == [5] * b and tgt.cpu().tolist() == [38] * b
+
+
+def test_attn_negative_slots_store_nothing_and_read_the_cache():
+    """Rows with a negative slot: their new K/V are not stored, and attention reads whatever
+    the cache holds at their positions (here finite values planted there)."""
+    wk = workload("tiny_b8_ctx128")
+    lay, d = wk["layers"][0], wk["dims"]
+    rows = [2, 5]
+    sm = lay["slot_mapping"].clone()
+    kc0, vc0 = lay["k_cache"].clone(), lay["v_cache"].clone()
+    g = torch.Generator().manual_seed(7)
+    for j in rows:
+        blk, off = int(sm[j]) // 16, int(sm[j]) % 16
+        kc0[blk, :, off, :] = torch.randn(kc0.shape[1], kc0.shape[3], generator=g).to(kc0.dtype)
+        vc0[blk, :, :, off] = torch.randn(vc0.shape[1], vc0.shape[2], generator=g).to(vc0.dtype)
+        sm[j] = -1
+    lay2 = dict(lay, slot_mapping=sm, k_cache=kc0, v_cache=vc0)
+    wk2 = dict(wk, layers=[lay2])
+    r = runner(wk2)
+    b = r.b
+    x = wk["act"]["front_embed"]
+    out = torch.empty(b, d["hidden"], dtype=torch.float32, device=DEV)
+    L = r.layers[0]
+    B.attn_verify(r.dims, b, x.to(DEV), L.attn_w, L.kv, out, r.ws)
+    torch.cuda.synchronize()
+    q, k, v, gate = oracle.qkv_front(np64(x), np64(lay["w_qkv"]), np64(lay["positions"]),
+                                     d["n_q_heads"], d["n_kv_heads"], d["head_dim"], d["eps"],
+                                     d["rope_theta"], bool(d["qk_norm"]))
+    kc, vc = oracle.kv_write(np64(kc0), np64(vc0), k, v, np64(sm))
+    o = oracle.paged_attention(q, kc, vc, np64(lay["block_table"]), np64(lay["positions"]), d["q_rows"])
+    a = oracle.gate_oproj(o, gate, np64(lay["w_o"]))
+    assert_close(np64(out), a, "attention output with negative slots")
+    for j in rows:  # the planted values are still there
+        blk, off = int(lay["slot_mapping"][j]) // 16, int(lay["slot_mapping"][j]) % 16
+        assert torch.equal(L.t["k_cache"][blk, :, off, :].cpu(), kc0[blk, :, off, :])
+        assert torch.equal(L.t["v_cache"][blk, :, :, off].cpu(), vc0[blk, :, :, off])
