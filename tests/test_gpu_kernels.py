@@ -324,3 +324,36 @@ def test_attn_negative_slots_store_nothing_and_read_the_cache():
         blk, off = int(lay["slot_mapping"][j]) // 16, int(lay["slot_mapping"][j]) % 16
         assert torch.equal(L.t["k_cache"][blk, :, off, :].cpu(), kc0[blk, :, off, :])
         assert torch.equal(L.t["v_cache"][blk, :, :, off].cpu(), vc0[blk, :, :, off])
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("L", [7684, 7937])
+def test_attn_new_tokens_across_chunks_and_blocks(L):
+    """A request whose verify tokens straddle an attention chunk (256 tokens of 16 blocks at
+    this shape; L = 7684) or a 2-block window and a block (L = 7937): each chunk's workgroup
+    stores its own new tokens and reads the others from the cache."""
+    wk = workload("h4096_b8_ctx8k")
+    lay, d = wk["layers"][0], wk["dims"]
+    q = d["q_rows"]
+    pos = torch.arange(L - q, L, dtype=torch.int32)
+    bt = lay["block_table"][0].long()
+    sm = (bt[pos.long() // 16] * 16 + pos.long() % 16).to(torch.int64)
+    lay2 = dict(lay, seq_lens=torch.tensor([L], dtype=torch.int32), positions=pos, slot_mapping=sm)
+    r = runner(dict(wk, layers=[lay2]))
+    b = r.b
+    say(f"[gpu-test] attention with new tokens at {L - q}..{L - 1}")
+    x = wk["act"]["front_embed"]
+    out = torch.empty(b, d["hidden"], dtype=torch.float32, device=DEV)
+    Ld = r.layers[0]
+    B.attn_verify(r.dims, b, x.to(DEV), Ld.attn_w, Ld.kv, out, r.ws)
+    torch.cuda.synchronize()
+    qq, k, v, gate = oracle.qkv_front(np64(x), np64(lay["w_qkv"]), np64(pos),
+                                      d["n_q_heads"], d["n_kv_heads"], d["head_dim"], d["eps"],
+                                      d["rope_theta"], bool(d["qk_norm"]))
+    kc, vc = oracle.kv_write(np64(lay["k_cache"]), np64(lay["v_cache"]), k, v, np64(sm))
+    o = oracle.paged_attention(qq, kc, vc, np64(lay["block_table"]), np64(pos), q)
+    a = oracle.gate_oproj(o, gate, np64(lay["w_o"]))
+    assert_close(np64(out), a, "attention output")
+    slots = np64(sm)
+    got = np64(Ld.t["k_cache"][torch.from_numpy(slots // 16).to(DEV)])
+    assert_close(got[np.arange(b), :, slots % 16, :], kc[slots // 16, :, slots % 16, :], "written K")
