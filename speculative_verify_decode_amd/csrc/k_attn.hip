@@ -1,5 +1,7 @@
 // K-C: paged verify attention, split over KV blocks, then an LSE combine with the output
-// gate fused in.
+// gate fused in.  The split kernel's prologue is also the QKV projection's epilogue: it
+// sums the projection's K-slice partials, applies the per-head RMSNorm and RoPE to its
+// query group and stores the new tokens' K/V into the cache.
 //
 // Page "vllm.models.muse_spark.nvidia.specialized_decode.runtime.decode": the attention
 // block is QKV front -> attn2 -> o_proj (module docstring); attn2 reads block-table decode
@@ -60,7 +62,8 @@ __device__ __forceinline__ ReqRows req_rows(const AttnArgs& a, int r) {
 
 // Workgroup (chunk, kv head g, request r): blocks [chunk * cb, +cb) of the request, one
 // workgroup per CU at most.  The chunk's block ids (clamped to the pool) and the query
-// group (hi/lo) are staged in LDS first; each of the 4 waves then streams 2-block windows
+// group (hi/lo, computed from the projection partials) are staged in LDS first; NP is the
+// number of K-slice partials.  Each of the 4 waves then streams 2-block windows
 // w = 2 * wave + 8 j, loading window j + 1 while window j is in the matrix cores.  Loads
 // are unconditional: tokens past the request's end are masked after loading (scores by
 // selection to -inf, V by selection to 0).  K and V are read once: non-temporal loads.
