@@ -691,8 +691,8 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w13(MoeArgs a) {
   int u, end;
   unit_range(n_units, u, end);
   if (u >= end) return;
-  if constexpr (!PB) {  // several column tiles: their accumulators leave no room to prefetch
-    for (; u < end; ++u) {
+  if constexpr (!PB && NU > 2) {  // several column tiles: their accumulators leave no room
+    for (; u < end; ++u) {        // to prefetch four-tile slices
       const Unit U = unit_of(meta, u, NT);
       load_a(g0, u0, U, true);
       compute(g0, u0, bx, U, 0);
@@ -759,16 +759,17 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w2(MoeArgs a) {
 #pragma unroll
     for (int c = 0; c < NCT; ++c) {
       if (c >= nct) break;
+      // column tile 0 was loaded before the next unit's prefetch (bx0); later tiles here
       f16x8_t bl[NU][4];
-      if (!PB) load_bx<NU>(bl, rx, b_off(U, c));
-      f16x8_t (&bx)[NU][4] = PB ? bx0 : bl;
+      if (!PB && c > 0) load_bx<NU>(bl, rx, b_off(U, c));
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
         f16x8_t dw[4];
         sd::dequant_unit(sw.codes[u], sw.scales[u], dw);
 #pragma unroll
         for (int m = 0; m < 4; ++m)
-          acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dw[m], bx[u][m], acc[c], 0, 0, 0);
+          acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              dw[m], (PB || c == 0) ? bx0[u][m] : bl[u][m], acc[c], 0, 0, 0);
       }
     }
     if (KS > 1) {
@@ -801,29 +802,21 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w2(MoeArgs a) {
   };
 
   Slice<NU> w0, w1;
-  f16x8_t bx[NU][4];  // one column tile's activations (unused without PB)
+  f16x8_t bx[NU][4];  // column tile 0's activations of the unit being computed
   int u, end;
   unit_range(n_units, u, end);
   if (u >= end) return;
-  if constexpr (!PB) {
-    for (; u < end; ++u) {
-      const Unit U = unit_of(meta, u, NT);
-      load_a(w0, U, true);
-      compute(w0, bx, U, 0);
-    }
-    return;
-  }
   Unit U0 = unit_of(meta, u, NT), U1;
   int be = -1;
   load_a(w0, U0, true);
   while (true) {
-    if (PB && U0.e != be) { load_b0(bx, U0); be = U0.e; }
+    if (!PB || U0.e != be) { load_b0(bx, U0); be = U0.e; }
     const int n1 = u + 1;
     U1 = unit_of(meta, min(n1, end - 1), NT);
     load_a(w1, U1, n1 < end);
     compute(w0, bx, U0, 0);
     if (n1 >= end) break;
-    if (PB && U1.e != be) { load_b0(bx, U1); be = U1.e; }
+    if (!PB || U1.e != be) { load_b0(bx, U1); be = U1.e; }
     const int n2 = n1 + 1;
     U0 = unit_of(meta, min(n2, end - 1), NT);
     load_a(w0, U0, n2 < end);
