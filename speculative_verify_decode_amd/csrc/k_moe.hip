@@ -635,7 +635,8 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w13(MoeArgs a) {
     if (KS > 1) {
       if (wave > 0) {
 #pragma unroll
-        for (int c = 0; c < NCT; ++c) {
+        for (int c = 0; c < NCT; ++c) {  // only the unit's column tiles
+          if (c >= nct) break;
           red[buf][wave - 1][0][c][lane] = ag[c];
           red[buf][wave - 1][1][c][lane] = au[c];
         }
@@ -645,6 +646,7 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w13(MoeArgs a) {
     if (wave == 0) {
 #pragma unroll
       for (int c = 0; c < NCT; ++c) {
+        if (c >= nct) break;
 #pragma unroll
         for (int w = 0; w < KS - 1; ++w) {
           ag[c] += red[buf][w][0][c][lane];
@@ -775,13 +777,17 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w2(MoeArgs a) {
     if (KS > 1) {
       if (wave > 0) {
 #pragma unroll
-        for (int c = 0; c < NCT; ++c) red[buf][wave - 1][c][lane] = acc[c];
+        for (int c = 0; c < NCT; ++c) {  // only the unit's column tiles
+          if (c >= nct) break;
+          red[buf][wave - 1][c][lane] = acc[c];
+        }
       }
       __syncthreads();
     }
     if (wave == 0) {
 #pragma unroll
       for (int c = 0; c < NCT; ++c) {
+        if (c >= nct) break;
 #pragma unroll
         for (int w = 0; w < KS - 1; ++w) acc[c] += red[buf][w][c][lane];
 #pragma unroll
