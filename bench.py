@@ -78,6 +78,53 @@ def measured_traffic(workload):
     return int(fields["traffic_bytes_per_launch"])
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or "unknown"."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def rotation_copies(K, step_bytes, requested=0):
+    """Copies R of the weights and KV to rotate over: R divides the K timed steps, so every
+    timed replay is one whole R-step graph; at least enough copies that R * step_bytes >= 1 GB
+    (8 at the least, 16 at the most for that rule), at most 32.  Returns (R, remainder): a K
+    with no such divisor keeps R = the lower bound and replays its K % R remaining steps as
+    one graph of that many copies."""
+    if requested:
+        return requested, K % requested
+    lo = min(max(math.ceil(1.0e9 / step_bytes), 8), 16, K)
+    for R in range(lo, min(K, 32) + 1):
+        if K % R == 0:
+            return R, 0
+    return lo, K % lo
+
+
+def read_ceiling(dev, nbytes=1 << 30, reps=10):
+    """A plain streaming read of a 1 GiB buffer (sd_debug_read_probe): the practical HBM read
+    rate on this machine, timed with HIP events around reps back-to-back reads."""
+    from speculative_verify_decode_amd import binding as B
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    sink = B.read_probe_sink(dev)
+    for _ in range(2):
+        B.debug_read_probe(buf, sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        B.debug_read_probe(buf, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    del buf
+    gbps = nbytes / (us * 1e-6) / 1e9
+    return {"GBps": round(gbps, 1), "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+            "bytes": nbytes, "us": round(us, 3), "kernel": "sd_debug_read_probe"}
+
+
 def cpu_baseline(wk):
     """The oracle, as it stands, on full layer steps of the workload, repeated until about
     10 s of host time (at most 4 steps); the mean per step."""
@@ -94,12 +141,12 @@ def cpu_baseline(wk):
         oracle.layer_step(inp, d, branch_in=np64(act["branch_in"]))
         times.append(time.perf_counter() - t0)
     return {"value": float(np.mean(times)) * 1e6, "unit": "us per layer-step", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{len(times)} full layer steps of {wk['workload'].name} (fp64 NumPy oracle, "
                       f"{sum(times):.1f} s), {len(os.sched_getaffinity(0))} host cores visible"}
 
 
-def print_dense(args, wk, R, us, per, hot_us, step_bytes, runners, st):
+def print_dense(args, wk, R, us, per, hot_us, step_bytes, runners, st, timing):
     """The dense draft layer's line: the step (attention + dense SwiGLU, every weight byte
     once) and, beside it, the context-K/V store of the workload's context rows."""
     d, w = wk["dims"], wk["workload"]
@@ -132,6 +179,7 @@ def print_dense(args, wk, R, us, per, hot_us, step_bytes, runners, st):
         "step_GBps": round(step_bytes / (us * 1e-6) / 1e9, 1),
         "step_frac_hbm": round(step_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
         "us_p10_p50_p90": [round(float(np.percentile(per, q)), 3) for q in (10, 50, 90)],
+        **timing,
         "hot_cache_us": round(hot_us, 3),
         "roofline": {"bound": "hbm", "kernel": "whole dense layer step", "unit": "GB/s",
                      "achieved": round(step_bytes / (us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBPS,
@@ -149,7 +197,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="h4096_b8_ctx8k")
-    ap.add_argument("--copies", type=int, default=0, help="rotation copies (0: auto, >= 1 GB)")
+    ap.add_argument("--copies", type=int, default=0,
+                    help="rotation copies (0: auto: divides --steps, >= 1 GB)")
     ap.add_argument("--roofline-iters", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -211,11 +260,10 @@ def main():
         counts_per_layer.append(r0.route_t["expert_counts"].cpu().numpy())
     counts = counts_per_layer[0]
     step_bytes, expert_bytes = algorithmic_bytes(wk, counts_per_layer)
-    # (at most 16 copies: a step small enough to need more is launch-bound, not HBM-bound)
-    # at least 8 copies: every replay is timed on its own (inputs are restored between
-    # replays), so the fixed cost of starting a replay is shared by R steps
-    R = args.copies or min(16, max(8, math.ceil(1.0e9 / step_bytes)))
-    R = max(1, min(R, args.steps))
+    # every replay is timed on its own (inputs are restored between replays), so the fixed
+    # cost of starting a replay is shared by the R steps of one graph; R divides K, so every
+    # timed replay is a whole R-step graph
+    R, n_rest = rotation_copies(args.steps, step_bytes, args.copies)
     runners = [r0] + [make_runner() for _ in range(R - 1)]
     print(f"[bench] {R} rotation copies, {step_bytes / 1e6:.1f} MB algorithmic per step",
           file=sys.stderr, flush=True)
@@ -225,7 +273,7 @@ def main():
     # bytes a step moves, so each copy's inputs are restored from a snapshot between graph
     # replays, outside the timed intervals (events around each replay only).  Graphs run on
     # a side stream; one graph holds the R copies' steps back to back (as a serving graph
-    # holds a model's consecutive layers); K % R leftover steps replay single-step graphs.
+    # holds a model's consecutive layers).
     st = torch.cuda.Stream()
     streams = [r.act["stream"].clone() for r in runners]
     pooled = not chain and not dense
@@ -271,12 +319,12 @@ def main():
     with torch.cuda.graph(g_all, stream=st):
         for r, sb in zip(runners, streams):
             run_step(r, sb, stream=st)
-    singles = []
-    for r, sb in zip(runners, streams):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=st):
-            run_step(r, sb, stream=st)
-        singles.append(g)
+    g_rest = None
+    if n_rest:  # only when K has no divisor in the copies' range: its last K % R steps
+        g_rest = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_rest, stream=st):
+            for r, sb in zip(runners[:n_rest], streams[:n_rest]):
+                run_step(r, sb, stream=st)
     torch.cuda.synchronize()
 
     def timed_replays(graph, n):
@@ -292,14 +340,20 @@ def main():
         torch.cuda.synchronize()
         return np.array([a_.elapsed_time(b_) for a_, b_ in evs]) * 1e3
 
-    timed_replays(g_all, max(1, args.warmup // R))
+    timed_replays(g_all, max(1, math.ceil(args.warmup / R)))
     K = args.steps
-    n_all, n_rest = K // R, K % R
+    n_all = K // R
     per_all = timed_replays(g_all, n_all) if n_all else np.zeros(0)
-    rest = [float(timed_replays(singles[i], 1)[0]) for i in range(n_rest)]
-    us = (float(per_all.sum()) + sum(rest)) / K
-    per = per_all / R if n_all else np.array(rest)  # us per step
-    graphs = singles
+    rest = float(timed_replays(g_rest, 1)[0]) if g_rest is not None else 0.0
+    us = (float(per_all.sum()) + rest) / K
+    # percentiles of the per-step time over at least 10 whole replays (more replays than
+    # the K timed steps hold are taken for these figures only)
+    per = per_all / R
+    if len(per) < 10:
+        per = np.concatenate([per, timed_replays(g_all, 10 - len(per)) / R])
+    timing = {"percentile_replays": int(len(per)),
+              "timed_replays": {"steps_per_replay": R, "whole": n_all, "remainder_steps": n_rest},
+              "hbm_read_ceiling": read_ceiling(dev)}
 
     # the pooled layer step (sd_layer_step_pooled) on the same copies and inputs
     pooled_us = None
@@ -324,13 +378,14 @@ def main():
     timed_replays(g_hot, 2)
     hot_us = float(timed_replays(g_hot, max(1, 50 // R)).mean()) / R
 
-    # dominant kernels: the routed-expert GEMMs (sd_moe_experts: k_moe_w13 then k_moe_w2),
-    # timed live with HIP events on their launch stream, rotating over the copies like the
-    # step; their input is the attention boundary's expert-input form of the same rows
+    # dominant kernels: the routed-expert GEMMs (sd_moe_experts_x16: k_moe_w13 then k_moe_w2,
+    # the pair the layer step runs), timed live with HIP events on their launch stream,
+    # rotating over the copies like the step; their input is a boundary's expert-input form
+    # of the same rows
     d, b = wk["dims"], wk["workload"].b
     H = d["hidden"]
     if dense:
-        print_dense(args, wk, R, us, per, hot_us, step_bytes, runners, st)
+        print_dense(args, wk, R, us, per, hot_us, step_bytes, runners, st, timing)
         return
     y = torch.empty(b * d["top_k"], H, dtype=torch.float32, device=dev)
     x = []
@@ -347,11 +402,13 @@ def main():
     with torch.cuda.stream(st):
         for i in range(10):
             r = runners[i % R]
-            B.moe_experts(r.dims, b, x[i % R], r.layers[0].moe_w, r.route, y, None, r.ws, stream=st)
+            B.moe_experts_x16(r.dims, b, x[i % R], r.layers[0].moe_w, r.route, y, None, r.ws,
+                              stream=st)
         e0.record(st)
         for i in range(n_it):
             r = runners[i % R]
-            B.moe_experts(r.dims, b, x[i % R], r.layers[0].moe_w, r.route, y, None, r.ws, stream=st)
+            B.moe_experts_x16(r.dims, b, x[i % R], r.layers[0].moe_w, r.route, y, None, r.ws,
+                              stream=st)
         e1.record(st)
     torch.cuda.synchronize()
     exp_us = e0.elapsed_time(e1) * 1e3 / n_it      # average per launch, back to back
@@ -387,9 +444,10 @@ def main():
         "tokens_per_s": round(b * 1e6 / us, 1),
         "pooled_step_us": None if pooled_us is None else round(pooled_us, 3),
         "us_p10_p50_p90": [round(float(np.percentile(per, q)), 3) for q in (10, 50, 90)],
+        **timing,
         "hot_cache_us": round(hot_us, 3),
         "roofline": {"bound": "hbm",
-                     "kernel": "routed-expert GEMMs (sd_moe_experts: k_moe_w13 + k_moe_w2)",
+                     "kernel": "routed-expert GEMMs (sd_moe_experts_x16: k_moe_w13 + k_moe_w2)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic(args.workload),

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define SD_ABI_VERSION 6
+#define SD_ABI_VERSION 7
 
 enum {
   SD_OK = 0,
@@ -153,11 +153,14 @@ typedef struct sd_kv {
  * [E], expert_offsets int32 [E + 1] (exclusive prefix sum), slot_of int32 [b, k] (pooled
  * slot of each choice: a stable counting sort by (expert, row)), token_of_slot int32
  * [b * k] (its inverse), active_experts int32 [E + 1]: the ids of experts with a nonzero
- * count in ascending order, then at index E their number. */
+ * count in ascending order, then at index E their number.  logits (may be NULL) fp32
+ * [b, E] receives the router logits the routing ranked, bias included: the routing is
+ * exactly the top-k of these values by (-z, index). */
 typedef struct sd_route {
   int32_t *topk_ids;
   float *topk_w;
   int32_t *expert_counts, *expert_offsets, *slot_of, *token_of_slot, *active_experts;
+  float *logits;
 } sd_route;
 
 int sd_abi_version(void);
@@ -187,10 +190,14 @@ size_t sd_workspace_bytes(const sd_dims *dims, int32_t b, int32_t n_req, int32_t
  * branch fp32 [b, H] (the branches between blocks are fp32); front_embed bf16 [b, H];
  * gains fp32 [H]; out bf16 [b, H] = bf16(y) (e.g. the final hidden cast for the draft
  * head); out16 (may be NULL) fp16 [2, b, H] = the expert-input form of y: hi terms, then
- * lo terms, of y * 2^-8 (y * 2^-8 ~ hi + lo to about 2^-22 relative). */
+ * lo terms, of y * 2^-8 (y * 2^-8 ~ hi + lo to about 2^-22 relative).
+ * aux (may be NULL) fp32 [b, H]: the aux hidden-state tap, a copy of the stream this
+ * boundary hands on (after its residual add, before the norm), as the boundary of an aux
+ * layer and the final boundary write it for the drafter ([DEC] DecodeLayer.aux,
+ * SpecializedDecode.build / .run). */
 int sd_boundary_dualnorm(const sd_dims *dims, int32_t b, float *stream, const float *branch,
                          const void *front_embed, const float *g_post, const float *g_pre,
-                         void *out, void *out16, void *stream_handle);
+                         void *out, void *out16, float *aux, void *stream_handle);
 
 /* Attention of one layer ([DEC] module docstring: QKV front -> attn2 -> o_proj):
  * stacked QKV projection of x (bf16 [b, H]); weightless per-head RMSNorm of q and k when
@@ -204,21 +211,29 @@ int sd_attn_verify(const sd_dims *dims, int32_t b, const void *x, const sd_attn_
 
 /* Router -> routing -> pooler ([DEC] module docstring).  z = x (bf16 [b, H]) * w_router^T
  * + logit_bias (fp32 [b, E], may be NULL); top-k, weights and pooler maps into *route
- * (every field required).  logits_out fp32 [b, E] may be NULL. */
+ * (every field required except route->logits, which receives z when not NULL). */
 int sd_moe_route(const sd_dims *dims, int32_t b, const void *x, const void *w_router,
-                 const float *logit_bias, const sd_route *route, float *logits_out,
-                 void *ws, size_t ws_bytes, void *stream_handle);
+                 const float *logit_bias, const sd_route *route, void *ws, size_t ws_bytes,
+                 void *stream_handle);
 
 /* Routed experts over pooled slots ([DEC] module docstring: routed experts; [RT] module
  * list: NVFP4 routed experts): for slot s = (row t, expert e), y[s] = W2_e * h[s] with
  * h[s] = silu(g) * u and [g | u] = W13_e * x[t], weights dequantised exactly, fp32
- * accumulation, h kept at near-fp32 precision between the two GEMMs.  x16 fp16 [2, b, H]:
- * the expert input x as sd_boundary_dualnorm's out16 gives it (hi terms, then lo terms, of
- * x * 2^-8); route as produced by sd_moe_route; y_slots fp32 [b * k, H]; h_slots (may be
- * NULL) receives bf16(h) [b * k, I]. */
-int sd_moe_experts(const sd_dims *dims, int32_t b, const void *x16, const sd_moe_weights *w,
+ * accumulation, h kept at near-fp32 precision between the two GEMMs.  x bf16 [b, H] (the
+ * MoE input); route as produced by sd_moe_route; y_slots fp32 [b * k, H]; h_slots (may be
+ * NULL) receives bf16(h) [b * k, I].  The call first writes the expert GEMMs' input form
+ * of x into the workspace (see sd_moe_experts_x16), then runs the two GEMMs. */
+int sd_moe_experts(const sd_dims *dims, int32_t b, const void *x, const sd_moe_weights *w,
                    const sd_route *route, void *y_slots, void *h_slots, void *ws,
                    size_t ws_bytes, void *stream_handle);
+
+/* sd_moe_experts on the expert GEMMs' own input form, as the layer step feeds them: x16
+ * fp16 [2, b, H] holds the hi terms, then the lo terms, of x * 2^-8 (x * 2^-8 ~ hi + lo to
+ * about 2^-22 relative), which sd_boundary_dualnorm's out16 writes from the fp32 norm
+ * output.  Every other argument and result is as for sd_moe_experts. */
+int sd_moe_experts_x16(const sd_dims *dims, int32_t b, const void *x16,
+                       const sd_moe_weights *w, const sd_route *route, void *y_slots,
+                       void *h_slots, void *ws, size_t ws_bytes, void *stream_handle);
 
 /* Unpooler ([DEC] module docstring): out[t] = sum over j < k, in order, of
  * topk_w[t, j] * y_slots[slot_of[t, j]], in fp32.  y_slots fp32 [b * k, H];
@@ -232,11 +247,13 @@ int sd_moe_unpool(const sd_dims *dims, int32_t b, const float *y_slots, const sd
  * branch_in fp32 [b, H] (the previous layer's MoE output); front_embed bf16 [b, H];
  * branch_out fp32 [b, H] receives the unpooled MoE output (the next boundary's branch;
  * it may alias branch_in, which is read first).  route_out may be NULL (then routing lives
- * in the workspace); logit_bias may be NULL. */
+ * in the workspace; route_out->logits may be NULL); logit_bias may be NULL.  aux (may be
+ * NULL) fp32 [b, H]: the layer's aux hidden-state tap, written by its input boundary as
+ * sd_boundary_dualnorm's aux (the stream entering the layer's attention block). */
 int sd_layer_step(const sd_dims *dims, int32_t b, float *stream, const float *branch_in,
                   const void *front_embed, const sd_layer_weights *w, const sd_kv *kv,
                   const float *logit_bias, float *branch_out, const sd_route *route_out,
-                  void *ws, size_t ws_bytes, void *stream_handle);
+                  float *aux, void *ws, size_t ws_bytes, void *stream_handle);
 
 /* A pooled MoE branch: the routed experts' per-slot outputs y_slots fp32 [b * k, H] and the
  * routing that weighs them (route: topk_w and slot_of are read; every field is written by
@@ -251,13 +268,14 @@ typedef struct sd_pooled {
  * before its dual norm).  branch_in: the previous layer's pooled output, gathered as
  * u[t] = sum over j < k, in order, of topk_w[t, j] * y_slots[slot_of[t, j]], then the same
  * boundary as sd_layer_step (NULL: the front, from front_embed).  branch_out: this layer's
- * experts write y_slots and the routing writes route, and no unpooler runs; the final
- * boundary of a stack gathers with sd_moe_unpool.  Every other argument and result is as
- * for sd_layer_step.  branch_out may be branch_in (it is read before it is written). */
+ * experts write y_slots and the routing writes route (route->logits may be NULL), and no
+ * unpooler runs; the final boundary of a stack gathers with sd_moe_unpool.  Every other
+ * argument and result, aux included, is as for sd_layer_step.  branch_out may be
+ * branch_in (it is read before it is written). */
 int sd_layer_step_pooled(const sd_dims *dims, int32_t b, float *stream,
                          const sd_pooled *branch_in, const void *front_embed,
                          const sd_layer_weights *w, const sd_kv *kv, const float *logit_bias,
-                         const sd_pooled *branch_out, void *ws, size_t ws_bytes,
+                         const sd_pooled *branch_out, float *aux, void *ws, size_t ws_bytes,
                          void *stream_handle);
 
 /* Draft head on bf16 hidden rows h [b, hidden] ([DSP] compute_draft_logits,
@@ -331,6 +349,15 @@ int sd_context_kv(const sd_dims *dims, int32_t n_ctx, int32_t n_layers, const vo
  * k % 32 == 0. */
 int sd_debug_dequant(int32_t n, int32_t k, const uint8_t *codes, const uint8_t *scales,
                      float gscale, float *out, void *stream_handle);
+
+/* Measurement entry: one plain streaming read of bytes (> 0, a multiple of 16) at src
+ * (16-byte aligned), each 16-byte piece loaded once with the non-temporal policy of the
+ * step's weight and KV streams: the practical HBM read ceiling the step is measured
+ * against.  sink: uint32 [sd_read_probe_sink_words()] scratch the kernel may write. */
+int sd_debug_read_probe(const void *src, size_t bytes, uint32_t *sink, void *stream_handle);
+
+/* Words of sink that sd_debug_read_probe needs. */
+int32_t sd_read_probe_sink_words(void);
 
 #ifdef __cplusplus
 }

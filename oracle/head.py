@@ -11,7 +11,9 @@ from .layer import dual_norm, layer_step
 
 def final_boundary(stream, branch, g_post, g_final, eps):
     """The last gather + dual norm into the model's final norm ([DEC] module docstring,
-    ``final``).  Returns (new stream, h) with h in fp64 (not yet cast)."""
+    ``final``).  Returns (new stream, h) with h in fp64 (not yet cast).  The new stream is
+    also the final boundary's aux tap ([DEC] ``SpecializedDecode.run``: the final boundary
+    writes the last aux buffer), read like a layer's tap as the stream after the add."""
     return dual_norm(stream, branch, g_post, g_final, eps)
 
 
@@ -57,7 +59,8 @@ def chain_step(layers, dims, stream, branch_in, g_final, w_lm, multiplier, soft_
     ``layers`` is a list of per-layer input dicts (weights, caches, step metadata; the
     stream comes from ``stream``).  The first layer takes ``branch_in`` through its
     input boundary, each later layer the previous layer's unpooled branch.
-    Returns dict(layers=[per-layer outputs], stream, h, head=draft_head(...)).
+    Returns dict(layers=[per-layer outputs], stream, h, head=draft_head(...), aux=[each
+    layer's aux tap, then the final boundary's]).
     """
     outs = []
     s, u = np.asarray(stream, dtype=np.float64), branch_in
@@ -71,5 +74,5 @@ def chain_step(layers, dims, stream, branch_in, g_final, w_lm, multiplier, soft_
             on_layer(i)
         s, u = out["stream"], out["m"]
     s, h = final_boundary(s, u, layers[-1]["g_post_ffn"], g_final, dims["eps"])
-    return dict(layers=outs, stream=s, h=h,
+    return dict(layers=outs, stream=s, h=h, aux=[o["aux"] for o in outs] + [s],
                 head=draft_head(h, w_lm, multiplier, soft_cap, d2t))

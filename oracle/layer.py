@@ -334,7 +334,11 @@ def layer_step(inp, dims, branch_in=None, front_embed=None, route_override=None)
     replaces this step's own top-k, for teacher forcing at near ties; the weights are
     then the softmax over the replaced selection.
     Returns a dict with the new stream, the branch output m, the updated caches and
-    every intermediate.
+    every intermediate.  ``aux`` is the layer's aux hidden-state tap: the stream its
+    input boundary (or front) hands on, after the residual add and before the pre-norm.
+    [DEC] ``SpecializedDecode.run`` passes the layer's fp32 aux buffer to that boundary,
+    which writes it for the drafter (``DecodeLayer.aux``: the drafter's input); which
+    value is tapped is not printed, and this reads it as the stream entering the layer.
     """
     d = dims
     eps = d["eps"]
@@ -364,7 +368,7 @@ def layer_step(inp, dims, branch_in=None, front_embed=None, route_override=None)
                        inp["w13_codes"], inp["w13_scales"], inp["w13_gscale"],
                        inp["w2_codes"], inp["w2_scales"], inp["w2_gscale"], d["inter"])
     m = unpool(y, w, slot_of)
-    return dict(stream_in=s_after_in, x_a=x_a, q=q, k=k, v=v, gate=gate, k_cache=kc,
+    return dict(stream_in=s_after_in, aux=s_after_in, x_a=x_a, q=q, k=k, v=v, gate=gate, k_cache=kc,
                 v_cache=vc, o=o, a=a, stream=s, x_m=x_m, z=z, ids=ids, w=w, counts=counts,
                 offsets=offsets, slot_of=slot_of, token_of_slot=token_of_slot, h=h, y=y,
                 m=m)

@@ -45,9 +45,12 @@ class SdKv(ctypes.Structure):
                 ("max_seq_len", c_int), ("window", c_int), ("query_start", c_void_p)]
 
 
+ROUTE_FIELDS = ("topk_ids", "topk_w", "expert_counts", "expert_offsets", "slot_of",
+                "token_of_slot", "active_experts", "logits")
+
+
 class SdRoute(ctypes.Structure):
-    _fields_ = [(n, c_void_p) for n in ("topk_ids", "topk_w", "expert_counts", "expert_offsets",
-                                        "slot_of", "token_of_slot", "active_experts")]
+    _fields_ = [(n, c_void_p) for n in ROUTE_FIELDS]
 
 
 class SdDenseLayerWeights(ctypes.Structure):
@@ -74,30 +77,37 @@ SYMBOLS = {
                             c_void_p]),
     "sd_workspace_bytes": (c_size_t, [ctypes.POINTER(SdDims), c_int, c_int, c_int]),
     "sd_boundary_dualnorm": (c_int, [ctypes.POINTER(SdDims), c_int, c_void_p, c_void_p, c_void_p,
-                                     c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+                                     c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                     c_void_p]),
     "sd_attn_verify": (c_int, [ctypes.POINTER(SdDims), c_int, c_void_p,
                                ctypes.POINTER(SdAttnWeights), ctypes.POINTER(SdKv), c_void_p,
                                c_void_p, c_size_t, c_void_p]),
     "sd_moe_route": (c_int, [ctypes.POINTER(SdDims), c_int, c_void_p, c_void_p, c_void_p,
-                             ctypes.POINTER(SdRoute), c_void_p, c_void_p, c_size_t, c_void_p]),
+                             ctypes.POINTER(SdRoute), c_void_p, c_size_t, c_void_p]),
     "sd_moe_experts": (c_int, [ctypes.POINTER(SdDims), c_int, c_void_p,
                                ctypes.POINTER(SdMoeWeights), ctypes.POINTER(SdRoute), c_void_p,
                                c_void_p, c_void_p, c_size_t, c_void_p]),
+    "sd_moe_experts_x16": (c_int, [ctypes.POINTER(SdDims), c_int, c_void_p,
+                                   ctypes.POINTER(SdMoeWeights), ctypes.POINTER(SdRoute),
+                                   c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "sd_moe_unpool": (c_int, [ctypes.POINTER(SdDims), c_int, c_void_p, ctypes.POINTER(SdRoute),
                               c_void_p, c_void_p]),
     "sd_layer_step": (c_int, [ctypes.POINTER(SdDims), c_int, c_void_p, c_void_p, c_void_p,
                               ctypes.POINTER(SdLayerWeights), ctypes.POINTER(SdKv), c_void_p,
-                              c_void_p, ctypes.POINTER(SdRoute), c_void_p, c_size_t, c_void_p]),
+                              c_void_p, ctypes.POINTER(SdRoute), c_void_p, c_void_p, c_size_t,
+                              c_void_p]),
     "sd_layer_step_pooled": (c_int, [ctypes.POINTER(SdDims), c_int, c_void_p,
                                      ctypes.POINTER(SdPooled), c_void_p,
                                      ctypes.POINTER(SdLayerWeights), ctypes.POINTER(SdKv),
-                                     c_void_p, ctypes.POINTER(SdPooled), c_void_p, c_size_t,
-                                     c_void_p]),
+                                     c_void_p, ctypes.POINTER(SdPooled), c_void_p, c_void_p,
+                                     c_size_t, c_void_p]),
     "sd_draft_head": (c_int, [c_int, c_int, c_int, c_void_p, c_void_p, c_float, c_float,
                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                               c_void_p]),
     "sd_draft_head_workspace_bytes": (c_size_t, [c_int, c_int, c_int]),
     "sd_debug_dequant": (c_int, [c_int, c_int, c_void_p, c_void_p, c_float, c_void_p, c_void_p]),
+    "sd_debug_read_probe": (c_int, [c_void_p, c_size_t, c_void_p, c_void_p]),
+    "sd_read_probe_sink_words": (c_int, []),
     "sd_dense_workspace_bytes": (c_size_t, [ctypes.POINTER(SdDims), c_int, c_int, c_int, c_int]),
     "sd_dense_layer_step": (c_int, [ctypes.POINTER(SdDims), c_int, c_void_p,
                                     ctypes.POINTER(SdDenseLayerWeights), ctypes.POINTER(SdKv),
@@ -190,9 +200,8 @@ def make_layer_weights(lay):
 
 
 def make_route(r):
-    return SdRoute(**{k: ptr(r[k]) for k in ("topk_ids", "topk_w", "expert_counts",
-                                             "expert_offsets", "slot_of", "token_of_slot",
-                                             "active_experts")})
+    """SdRoute of a dict of device tensors (its "logits" entry is optional)."""
+    return SdRoute(**{k: ptr(r.get(k)) for k in ROUTE_FIELDS})
 
 
 # ------------------------------------------------------------------ entry points
@@ -228,10 +237,10 @@ def workspace_bytes(dims, b, n_req, max_seq_len):
 
 
 def boundary_dualnorm(dims, b, stream_buf, branch, front_embed, g_post, g_pre, out, stream=None,
-                      out16=None):
+                      out16=None, aux=None):
     _check(lib().sd_boundary_dualnorm(ctypes.byref(dims), b, ptr(stream_buf), ptr(branch),
                                       ptr(front_embed), ptr(g_post), ptr(g_pre), ptr(out),
-                                      ptr(out16), cur_stream(stream)))
+                                      ptr(out16), ptr(aux), cur_stream(stream)))
 
 
 def attn_verify(dims, b, x, attn_w, kv, out, ws, stream=None):
@@ -240,16 +249,22 @@ def attn_verify(dims, b, x, attn_w, kv, out, ws, stream=None):
                                 cur_stream(stream)))
 
 
-def moe_route(dims, b, x, w_router, logit_bias, route, logits_out, ws, stream=None):
+def moe_route(dims, b, x, w_router, logit_bias, route, ws, stream=None):
     _check(lib().sd_moe_route(ctypes.byref(dims), b, ptr(x), ptr(w_router), ptr(logit_bias),
-                              ctypes.byref(route), ptr(logits_out), ptr(ws),
-                              ws.numel() * ws.element_size(), cur_stream(stream)))
+                              ctypes.byref(route), ptr(ws), ws.numel() * ws.element_size(),
+                              cur_stream(stream)))
 
 
-def moe_experts(dims, b, x16, moe_w, route, y_slots, h_slots, ws, stream=None):
-    _check(lib().sd_moe_experts(ctypes.byref(dims), b, ptr(x16), ctypes.byref(moe_w),
+def moe_experts(dims, b, x, moe_w, route, y_slots, h_slots, ws, stream=None):
+    _check(lib().sd_moe_experts(ctypes.byref(dims), b, ptr(x), ctypes.byref(moe_w),
                                 ctypes.byref(route), ptr(y_slots), ptr(h_slots), ptr(ws),
                                 ws.numel() * ws.element_size(), cur_stream(stream)))
+
+
+def moe_experts_x16(dims, b, x16, moe_w, route, y_slots, h_slots, ws, stream=None):
+    _check(lib().sd_moe_experts_x16(ctypes.byref(dims), b, ptr(x16), ctypes.byref(moe_w),
+                                    ctypes.byref(route), ptr(y_slots), ptr(h_slots), ptr(ws),
+                                    ws.numel() * ws.element_size(), cur_stream(stream)))
 
 
 def moe_unpool(dims, b, y_slots, route, out, stream=None):
@@ -258,12 +273,12 @@ def moe_unpool(dims, b, y_slots, route, out, stream=None):
 
 
 def layer_step(dims, b, stream_buf, branch_in, front_embed, layer_w, kv, logit_bias, branch_out,
-               route, ws, stream=None):
+               route, ws, stream=None, aux=None):
     _check(lib().sd_layer_step(ctypes.byref(dims), b, ptr(stream_buf), ptr(branch_in),
                                ptr(front_embed), ctypes.byref(layer_w), ctypes.byref(kv),
                                ptr(logit_bias), ptr(branch_out),
-                               ctypes.byref(route) if route is not None else None, ptr(ws),
-                               ws.numel() * ws.element_size(), cur_stream(stream)))
+                               ctypes.byref(route) if route is not None else None, ptr(aux),
+                               ptr(ws), ws.numel() * ws.element_size(), cur_stream(stream)))
 
 
 def make_pooled(y_slots, route):
@@ -275,12 +290,13 @@ def make_pooled(y_slots, route):
 
 
 def layer_step_pooled(dims, b, stream_buf, pooled_in, front_embed, layer_w, kv, logit_bias,
-                      pooled_out, ws, stream=None):
+                      pooled_out, ws, stream=None, aux=None):
     _check(lib().sd_layer_step_pooled(ctypes.byref(dims), b, ptr(stream_buf),
                                       ctypes.byref(pooled_in) if pooled_in is not None else None,
                                       ptr(front_embed), ctypes.byref(layer_w), ctypes.byref(kv),
-                                      ptr(logit_bias), ctypes.byref(pooled_out), ptr(ws),
-                                      ws.numel() * ws.element_size(), cur_stream(stream)))
+                                      ptr(logit_bias), ctypes.byref(pooled_out), ptr(aux),
+                                      ptr(ws), ws.numel() * ws.element_size(),
+                                      cur_stream(stream)))
 
 
 def make_dense_layer_weights(lay):
@@ -337,3 +353,14 @@ def draft_head(hidden, draft_vocab, b, h, w_lm, multiplier, soft_cap, d2t, tau_o
 def debug_dequant(n, k, codes, scales, gscale, out, stream=None):
     _check(lib().sd_debug_dequant(n, k, ptr(codes), ptr(scales), gscale, ptr(out),
                                   cur_stream(stream)))
+
+
+def read_probe_sink(device):
+    """Scratch words sd_debug_read_probe may write."""
+    return torch.empty(lib().sd_read_probe_sink_words(), dtype=torch.int32, device=device)
+
+
+def debug_read_probe(src, sink, stream=None):
+    """One plain streaming read of the whole tensor src (the HBM read ceiling probe)."""
+    _check(lib().sd_debug_read_probe(ptr(src), src.numel() * src.element_size(), ptr(sink),
+                                     cur_stream(stream)))

@@ -250,12 +250,12 @@ int run_attention(const sd_dims* d, int b, const uint16_t* x, const uint16_t* x_
 // The router kernel's arrival counter must be 0 at launch: in a layer step the attention
 // boundary's norm kernel zeroes it; a standalone call zeroes it first.
 RouterArgs router_args(const sd_dims* d, int b, const uint16_t* x, const uint16_t* x_lo,
-                       const void* w_router, const float* bias, const sd_route* r, float* logits,
-                       void* ws, const Ws& L) {
+                       const void* w_router, const float* bias, const sd_route* r, void* ws,
+                       const Ws& L) {
   RouterArgs ra{};
   ra.b = b; ra.H = d->hidden; ra.E = d->n_experts; ra.k = d->top_k;
   ra.x = x; ra.x_lo = x_lo; ra.w = (const uint16_t*)w_router; ra.bias = bias;
-  ra.part = at<float>(ws, L.zpart); ra.counter = at<int>(ws, L.counter); ra.logits = logits;
+  ra.part = at<float>(ws, L.zpart); ra.counter = at<int>(ws, L.counter); ra.logits = r->logits;
   ra.ids = r->topk_ids; ra.w_out = r->topk_w; ra.counts = r->expert_counts;
   ra.offsets = r->expert_offsets; ra.slot_of = r->slot_of; ra.tos = r->token_of_slot;
   ra.active = r->active_experts;
@@ -263,9 +263,9 @@ RouterArgs router_args(const sd_dims* d, int b, const uint16_t* x, const uint16_
 }
 
 int run_route(const sd_dims* d, int b, const uint16_t* x, const uint16_t* x_lo,
-              const void* w_router, const float* bias, const sd_route* r, float* logits,
-              void* ws, const Ws& L, hipStream_t st) {
-  const RouterArgs ra = router_args(d, b, x, x_lo, w_router, bias, r, logits, ws, L);
+              const void* w_router, const float* bias, const sd_route* r, void* ws,
+              const Ws& L, hipStream_t st) {
+  const RouterArgs ra = router_args(d, b, x, x_lo, w_router, bias, r, ws, L);
   SD_LAUNCH(launch_router(ra, st), "router, routing and pooler");
   return SD_OK;
 }
@@ -318,7 +318,7 @@ int check_route(const sd_route* r) {
   if (r == nullptr || !r->topk_ids || !r->topk_w || !r->expert_counts || !r->expert_offsets ||
       !r->slot_of || !r->token_of_slot || !r->active_experts)
     return fail(SD_EINVAL, "a route pointer is null");
-  return SD_OK;
+  return SD_OK;  // r->logits is optional
 }
 
 sd_route ws_route(void* ws, const Ws& L) {
@@ -330,6 +330,7 @@ sd_route ws_route(void* ws, const Ws& L) {
   r.slot_of = at<int32_t>(ws, L.slot_of);
   r.token_of_slot = at<int32_t>(ws, L.tos);
   r.active_experts = at<int32_t>(ws, L.active);
+  r.logits = nullptr;
   return r;
 }
 
@@ -384,7 +385,7 @@ size_t sd_workspace_bytes(const sd_dims* dims, int32_t b, int32_t n_req, int32_t
 
 int sd_boundary_dualnorm(const sd_dims* dims, int32_t b, float* stream, const float* branch,
                          const void* front_embed, const float* g_post, const float* g_pre,
-                         void* out, void* out16, void* stream_handle) {
+                         void* out, void* out16, float* aux, void* stream_handle) {
   SD_CHECK(check_dims(dims));
   SD_CHECK(check_rows(dims, b));
   if (!stream || !out || !g_pre) return fail(SD_EINVAL, "stream, out or g_pre is null");
@@ -392,13 +393,14 @@ int sd_boundary_dualnorm(const sd_dims* dims, int32_t b, float* stream, const fl
     return fail(SD_EINVAL, "front mode needs front_embed");
   if (branch != nullptr && g_post == nullptr) return fail(SD_EINVAL, "g_post is null");
   if (!aligned16(stream) || !aligned16(out) || (branch != nullptr && !aligned16(branch)) || !aligned16(g_pre) ||
-      (g_post != nullptr && !aligned16(g_post)) || (out16 != nullptr && !aligned16(out16)))
-    return fail(SD_EINVAL, "stream, branch, gains and out16 must be 16-byte aligned");
+      (g_post != nullptr && !aligned16(g_post)) || (out16 != nullptr && !aligned16(out16)) ||
+      (aux != nullptr && !aligned16(aux)))
+    return fail(SD_EINVAL, "stream, branch, gains, out16 and aux must be 16-byte aligned");
   _Float16* x16 = (_Float16*)out16;
   SD_LAUNCH(launch_dualnorm(b, dims->hidden, stream, (const float*)branch, 1,
                             (const uint16_t*)front_embed, g_post, g_pre, dims->eps,
                             (uint16_t*)out, nullptr, x16,
-                            x16 ? x16 + (size_t)b * dims->hidden : nullptr, nullptr,
+                            x16 ? x16 + (size_t)b * dims->hidden : nullptr, nullptr, aux,
                             (hipStream_t)stream_handle),
             "dual norm");
   return ok();
@@ -420,34 +422,60 @@ int sd_attn_verify(const sd_dims* dims, int32_t b, const void* x, const sd_attn_
 }
 
 int sd_moe_route(const sd_dims* dims, int32_t b, const void* x, const void* w_router,
-                 const float* logit_bias, const sd_route* route, float* logits_out, void* ws,
-                 size_t ws_bytes, void* stream_handle) {
+                 const float* logit_bias, const sd_route* route, void* ws, size_t ws_bytes,
+                 void* stream_handle) {
   SD_CHECK(check_dims(dims));
   SD_CHECK(check_rows(dims, b));
   SD_CHECK(check_route(route));
   if (!x || !aligned16(x) || !w_router || !aligned16(w_router))
     return fail(SD_EINVAL, "x or w_router null or misaligned");
-  if (logits_out && !aligned16(logits_out)) return fail(SD_EINVAL, "logits_out misaligned");
+  if (route->logits && !aligned16(route->logits)) return fail(SD_EINVAL, "route logits misaligned");
   SD_CHECK(check_ws(dims, b, requests_of(dims, b), dims->q_rows, ws, ws_bytes));
   const Ws L = ws_layout(*dims, b, requests_of(dims, b), dims->q_rows);
   hipStream_t st = (hipStream_t)stream_handle;
   SD_LAUNCH(launch_zero_i32(at<int>(ws, L.counter), st), "router counter");
-  SD_CHECK(run_route(dims, b, (const uint16_t*)x, nullptr, w_router, logit_bias, route,
-                     logits_out, ws, L, st));
+  SD_CHECK(run_route(dims, b, (const uint16_t*)x, nullptr, w_router, logit_bias, route, ws, L,
+                     st));
   return ok();
 }
 
-int sd_moe_experts(const sd_dims* dims, int32_t b, const void* x16, const sd_moe_weights* w,
-                   const sd_route* route, void* y_slots, void* h_slots, void* ws,
-                   size_t ws_bytes, void* stream_handle) {
+namespace {
+
+// Shared checks of the two expert entry points; x names the input in messages.
+int check_experts(const sd_dims* dims, int32_t b, const void* x, const sd_moe_weights* w,
+                  const sd_route* route, void* y_slots, void* h_slots, void* ws,
+                  size_t ws_bytes, const char* xname) {
   SD_CHECK(check_dims(dims));
   SD_CHECK(check_rows(dims, b));
   SD_CHECK(check_moe_weights(w, false, true));
   SD_CHECK(check_route(route));
-  if (!x16 || !y_slots) return fail(SD_EINVAL, "x16 or y_slots is null");
-  if (!aligned16(x16) || !aligned16(y_slots) || (h_slots && !aligned16(h_slots)))
-    return fail(SD_EINVAL, "x16, y_slots and h_slots must be 16-byte aligned");
-  SD_CHECK(check_ws(dims, b, requests_of(dims, b), dims->q_rows, ws, ws_bytes));
+  if (!x || !y_slots) return fail(SD_EINVAL, "%s or y_slots is null", xname);
+  if (!aligned16(x) || !aligned16(y_slots) || (h_slots && !aligned16(h_slots)))
+    return fail(SD_EINVAL, "%s, y_slots and h_slots must be 16-byte aligned", xname);
+  return check_ws(dims, b, requests_of(dims, b), dims->q_rows, ws, ws_bytes);
+}
+
+}  // namespace
+
+int sd_moe_experts(const sd_dims* dims, int32_t b, const void* x, const sd_moe_weights* w,
+                   const sd_route* route, void* y_slots, void* h_slots, void* ws,
+                   size_t ws_bytes, void* stream_handle) {
+  SD_CHECK(check_experts(dims, b, x, w, route, y_slots, h_slots, ws, ws_bytes, "x"));
+  const Ws L = ws_layout(*dims, b, requests_of(dims, b), dims->q_rows);
+  hipStream_t st = (hipStream_t)stream_handle;
+  _Float16* x16 = at<_Float16>(ws, L.x16);
+  _Float16* x16_lo = at<_Float16>(ws, L.x16_lo);
+  SD_LAUNCH(launch_expert_input(b, dims->hidden, (const uint16_t*)x, x16, x16_lo, st),
+            "expert input");
+  SD_CHECK(run_experts(dims, b, x16, x16_lo, w, route, (float*)y_slots, (uint16_t*)h_slots,
+                       at<_Float16>(ws, L.h16), at<_Float16>(ws, L.h16_lo), st));
+  return ok();
+}
+
+int sd_moe_experts_x16(const sd_dims* dims, int32_t b, const void* x16,
+                       const sd_moe_weights* w, const sd_route* route, void* y_slots,
+                       void* h_slots, void* ws, size_t ws_bytes, void* stream_handle) {
+  SD_CHECK(check_experts(dims, b, x16, w, route, y_slots, h_slots, ws, ws_bytes, "x16"));
   const Ws L = ws_layout(*dims, b, requests_of(dims, b), dims->q_rows);
   const _Float16* hi = (const _Float16*)x16;
   SD_CHECK(run_experts(dims, b, hi, hi + (size_t)b * dims->hidden, w, route, (float*)y_slots,
@@ -477,7 +505,7 @@ namespace {
 int layer_step_impl(const sd_dims* dims, int32_t b, float* stream, const float* branch_in,
                     const sd_pooled* pool_in, const void* front_embed, const sd_layer_weights* w,
                     const sd_kv* kv, const float* logit_bias, float* branch_out,
-                    const sd_route* route_out, const sd_pooled* pool_out, void* ws,
+                    const sd_route* route_out, const sd_pooled* pool_out, float* aux, void* ws,
                     size_t ws_bytes, void* stream_handle) {
   SD_CHECK(check_dims(dims));
   SD_CHECK(check_rows(dims, b));
@@ -502,6 +530,10 @@ int layer_step_impl(const sd_dims* dims, int32_t b, float* stream, const float* 
     SD_CHECK(check_route(pp->route));
   }
   if (route_out) SD_CHECK(check_route(route_out));
+  if (aux != nullptr && !aligned16(aux)) return fail(SD_EINVAL, "aux misaligned");
+  const sd_route* rl = pool_out ? pool_out->route : route_out;
+  if (rl != nullptr && rl->logits != nullptr && !aligned16(rl->logits))
+    return fail(SD_EINVAL, "route logits misaligned");
   SD_CHECK(check_ws(dims, b, kv->n_req, kv->max_seq_len, ws, ws_bytes));
   const Ws L = ws_layout(*dims, b, kv->n_req, kv->max_seq_len);
   hipStream_t st = (hipStream_t)stream_handle;
@@ -511,14 +543,14 @@ int layer_step_impl(const sd_dims* dims, int32_t b, float* stream, const float* 
   if (pool_in != nullptr) {
     SD_LAUNCH(launch_dualnorm(b, H, stream, pool_in->y_slots, 1, nullptr, w->g_post_prev,
                               w->g_pre_attn, dims->eps, x_a, x_a_lo, nullptr, nullptr,
-                              at<int>(ws, L.counter), st, pool_in->route->topk_w,
+                              at<int>(ws, L.counter), aux, st, pool_in->route->topk_w,
                               pool_in->route->slot_of, dims->top_k),
               "input boundary (gathering the pooled branch)");
   } else {
     SD_LAUNCH(launch_dualnorm(b, H, stream, (const float*)branch_in, 1,
                               (const uint16_t*)front_embed, w->g_post_prev, w->g_pre_attn,
                               dims->eps, x_a, x_a_lo, nullptr, nullptr, at<int>(ws, L.counter),
-                              st),
+                              aux, st),
               "input boundary");
   }
   float* a = at<float>(ws, L.a);
@@ -538,16 +570,16 @@ int layer_step_impl(const sd_dims* dims, int32_t b, float* stream, const float* 
     nr.g_post = w->g_post_attn; nr.g_pre = w->g_pre_ffn; nr.eps = dims->eps;
     nr.out = nullptr; nr.out_lo = nullptr;  // the bf16 row feeds only the router
     nr.x16 = x16; nr.x16_lo = x16_lo;
-    nr.r = router_args(dims, b, nullptr, nullptr, w->moe.w_router, logit_bias, &r, nullptr, ws, L);
+    nr.r = router_args(dims, b, nullptr, nullptr, w->moe.w_router, logit_bias, &r, ws, L);
     nr.r.part = at<float>(ws, L.zpart);
     SD_LAUNCH(launch_norm_router(nr, a_parts, st), "attention boundary and router");
     route_in_experts = &nr.r;
   } else {
     SD_LAUNCH(launch_dualnorm(b, H, stream, a, a_parts, nullptr, w->g_post_attn, w->g_pre_ffn,
-                              dims->eps, x_m, x_m_lo, x16, x16_lo, at<int>(ws, L.counter), st),
+                              dims->eps, x_m, x_m_lo, x16, x16_lo, at<int>(ws, L.counter),
+                              nullptr, st),
               "attention boundary");
-    SD_CHECK(run_route(dims, b, x_m, x_m_lo, w->moe.w_router, logit_bias, &r, nullptr, ws, L,
-                       st));
+    SD_CHECK(run_route(dims, b, x_m, x_m_lo, w->moe.w_router, logit_bias, &r, ws, L, st));
   }
   float* y = pool_out ? pool_out->y_slots : at<float>(ws, L.y);
   SD_CHECK(run_experts(dims, b, x16, x16_lo, &w->moe, &r, y, nullptr, at<_Float16>(ws, L.h16),
@@ -563,19 +595,19 @@ int layer_step_impl(const sd_dims* dims, int32_t b, float* stream, const float* 
 int sd_layer_step(const sd_dims* dims, int32_t b, float* stream, const float* branch_in,
                   const void* front_embed, const sd_layer_weights* w, const sd_kv* kv,
                   const float* logit_bias, float* branch_out, const sd_route* route_out,
-                  void* ws, size_t ws_bytes, void* stream_handle) {
+                  float* aux, void* ws, size_t ws_bytes, void* stream_handle) {
   return layer_step_impl(dims, b, stream, branch_in, nullptr, front_embed, w, kv, logit_bias,
-                         branch_out, route_out, nullptr, ws, ws_bytes, stream_handle);
+                         branch_out, route_out, nullptr, aux, ws, ws_bytes, stream_handle);
 }
 
 int sd_layer_step_pooled(const sd_dims* dims, int32_t b, float* stream,
                          const sd_pooled* branch_in, const void* front_embed,
                          const sd_layer_weights* w, const sd_kv* kv, const float* logit_bias,
-                         const sd_pooled* branch_out, void* ws, size_t ws_bytes,
+                         const sd_pooled* branch_out, float* aux, void* ws, size_t ws_bytes,
                          void* stream_handle) {
   if (branch_out == nullptr) return fail(SD_EINVAL, "branch_out is null");
   return layer_step_impl(dims, b, stream, nullptr, branch_in, front_embed, w, kv, logit_bias,
-                         nullptr, nullptr, branch_out, ws, ws_bytes, stream_handle);
+                         nullptr, nullptr, branch_out, aux, ws, ws_bytes, stream_handle);
 }
 
 // ------------------------------------------------------------------------ draft side
@@ -771,6 +803,21 @@ int sd_debug_dequant(int32_t n, int32_t k, const uint8_t* codes, const uint8_t* 
     return fail(SD_EINVAL, "codes/scales/out null or misaligned");
   SD_LAUNCH(launch_debug_dequant(n, k, codes, scales, gscale, out, (hipStream_t)stream_handle),
             "debug dequant");
+  return ok();
+}
+
+namespace {
+constexpr int kProbeGrid = 2048;  // 8 workgroups per CU of a 256-CU device
+}  // namespace
+
+int32_t sd_read_probe_sink_words(void) { return kProbeGrid; }
+
+int sd_debug_read_probe(const void* src, size_t bytes, uint32_t* sink, void* stream_handle) {
+  if (!src || !sink || !aligned16(src) || bytes == 0 || bytes % 16)
+    return fail(SD_EINVAL, "read probe: src/sink null, src misaligned or bytes %zu not a "
+                "positive multiple of 16", bytes);
+  SD_LAUNCH(launch_read_probe(src, bytes, sink, kProbeGrid, (hipStream_t)stream_handle),
+            "read probe");
   return ok();
 }
 

@@ -48,7 +48,8 @@ __global__ __launch_bounds__(256) void k_dualnorm(int H, float* __restrict__ str
                                                   uint16_t* __restrict__ out_lo,
                                                   _Float16* __restrict__ x16,
                                                   _Float16* __restrict__ x16_lo,
-                                                  int* __restrict__ zero) {
+                                                  int* __restrict__ zero,
+                                                  float* __restrict__ aux) {
   constexpr int VW = EPT % 4 == 0 ? 4 : (EPT % 2 == 0 ? 2 : 1);
   constexpr int NV = EPT / VW;
   typedef typename VecT<VW>::T V;
@@ -127,6 +128,7 @@ __global__ __launch_bounds__(256) void k_dualnorm(int H, float* __restrict__ str
       ss += s[v * VW + j] * s[v * VW + j];
     }
     *(V*)(stream + base + (v * 256 + tid) * VW) = o;
+    if (aux != nullptr) *(V*)(aux + base + (v * 256 + tid) * VW) = o;
   }
   ss = sd::block_sum<4>(ss, red);
   const float r = rsqrtf(ss * inv_h + eps);
@@ -150,13 +152,37 @@ __global__ __launch_bounds__(256) void k_dualnorm(int H, float* __restrict__ str
   }
 }
 
+// bf16 x -> fp16 hi / lo terms of x * 2^-8, four elements per thread (H % 4 == 0).
+__global__ __launch_bounds__(256) void k_expert_input(int n4, const uint16_t* __restrict__ x,
+                                                      _Float16* __restrict__ x16,
+                                                      _Float16* __restrict__ x16_lo) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  const u32x2_t v = *(const u32x2_t*)(x + 4 * (size_t)i);
+  const float f[4] = {__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xffff0000u),
+                      __uint_as_float(v[1] << 16), __uint_as_float(v[1] & 0xffff0000u)};
+  _Float16 h[4], l[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sd::split_f16(f[j], h[j], l[j]);
+  store16<4>((uint16_t*)x16 + 4 * (size_t)i, (const uint16_t*)h);
+  store16<4>((uint16_t*)x16_lo + 4 * (size_t)i, (const uint16_t*)l);
+}
+
 }  // namespace
+
+hipError_t launch_expert_input(int b, int H, const uint16_t* x, _Float16* x16, _Float16* x16_lo,
+                               hipStream_t st) {
+  if (H % 4) return hipErrorInvalidValue;
+  const int n4 = b * H / 4;
+  hipLaunchKernelGGL(k_expert_input, dim3((n4 + 255) / 256), dim3(256), 0, st, n4, x, x16, x16_lo);
+  return hipGetLastError();
+}
 
 hipError_t launch_dualnorm(int b, int H, float* stream, const float* branch, int nbranch,
                            const uint16_t* front, const float* g_post, const float* g_pre,
                            float eps, uint16_t* out, uint16_t* out_lo, _Float16* x16,
-                           _Float16* x16_lo, int* zero, hipStream_t st, const float* pool_w,
-                           const int* pool_slot, int pool_k) {
+                           _Float16* x16_lo, int* zero, float* aux, hipStream_t st,
+                           const float* pool_w, const int* pool_slot, int pool_k) {
   if ((x16 == nullptr) != (x16_lo == nullptr)) return hipErrorInvalidValue;
   if (branch != nullptr && nbranch < 1) return hipErrorInvalidValue;
   const bool pool = pool_slot != nullptr;
@@ -169,7 +195,7 @@ hipError_t launch_dualnorm(int b, int H, float* stream, const float* branch, int
 #define SD_NORM_NB(E, NBV, P)                                                              \
   hipLaunchKernelGGL((k_dualnorm<E, NBV, P>), grid, block, 0, st, H, stream, branch, bs,     \
                      pool_w, pool_slot, pool_k, front, g_post, g_pre, eps, out, out_lo, x16,  \
-                     x16_lo, zero)
+                     x16_lo, zero, aux)
 #define SD_NORM_CASE(E)                                                                   \
   case E:                                                                                 \
     if (pool) SD_NORM_NB(E, 1, true);                                                     \

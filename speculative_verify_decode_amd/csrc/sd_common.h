@@ -127,14 +127,18 @@ __device__ __forceinline__ void dequant_unit(u32x4_t codes, uint32_t scales2, f1
 // out: bf16 pre-norm output (hi term); out_lo (optional): its bf16 lo term; x16 / x16_lo
 // (optional): fp16 hi / lo terms of the pre-norm output * 2^-8 (the expert input).
 // zero (optional): an int set to 0, for a later kernel's arrival counter.
+// aux (optional): fp32 [b, H] copy of the updated stream (the aux hidden-state tap).
 // pool_slot (optional): the branch is pooled, branch = y [b * pool_k, H], row t gathered
 // as sum over j of pool_w[t, j] * y[pool_slot[t, j]] (nbranch must be 1).
 hipError_t launch_dualnorm(int b, int H, float* stream, const float* branch, int nbranch,
                            const uint16_t* front, const float* g_post, const float* g_pre,
                            float eps, uint16_t* out, uint16_t* out_lo, _Float16* x16,
-                           _Float16* x16_lo, int* zero, hipStream_t st,
+                           _Float16* x16_lo, int* zero, float* aux, hipStream_t st,
                            const float* pool_w = nullptr, const int* pool_slot = nullptr,
                            int pool_k = 0);
+// x16 / x16_lo = fp16 hi / lo terms of x * 2^-8 for bf16 x [b, H] (the expert GEMMs' input)
+hipError_t launch_expert_input(int b, int H, const uint16_t* x, _Float16* x16, _Float16* x16_lo,
+                               hipStream_t st);
 
 enum GemmMode { GEMM_F32 = 0, GEMM_F32_BIAS = 2, GEMM_HEAD = 3 };
 
@@ -295,3 +299,7 @@ hipError_t launch_head_argmax(int b, int n_tiles, const float* val, const int* i
 
 hipError_t launch_debug_dequant(int n, int k, const uint8_t* codes, const uint8_t* scales,
                                 float gscale, float* out, hipStream_t st);
+
+// plain streaming read of bytes (a multiple of 16) at src; sink holds grid words
+hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int grid,
+                             hipStream_t st);

@@ -54,14 +54,29 @@ def alloc_route(b, k, E, device):
     r = dict(topk_ids=torch.empty(b, k, **i32), topk_w=torch.empty(b, k, dtype=torch.float32, device=device),
              expert_counts=torch.empty(E, **i32), expert_offsets=torch.empty(E + 1, **i32),
              slot_of=torch.empty(b, k, **i32), token_of_slot=torch.empty(b * k, **i32),
-             active_experts=torch.empty(E + 1, **i32))
+             active_experts=torch.empty(E + 1, **i32),
+             logits=torch.empty(b, E, dtype=torch.float32, device=device))
     return r, B.make_route(r)
+
+
+def head_multiplier(hidden, base_width, mode):
+    """The draft head's output multiplier from its config (page
+    "vllm.models.muse_spark.common.dspark", MuseSparkDSparkForCausalLM.__init__): the width
+    multiplier is hidden / base_width; the "mup" rule takes its reciprocal, "sp" its
+    reciprocal square root.  A config constant handed to sd_draft_head."""
+    width_mult = hidden / base_width
+    if mode == "mup":
+        return float(width_mult ** -1)
+    if mode == "sp":
+        return float(width_mult ** -0.5)
+    raise ValueError(f"unknown output multiplier rule {mode!r}")
 
 
 class StepRunner:
     """A whole workload (activations, layers, head) resident on one device."""
 
-    def __init__(self, wk, device="cuda:0"):
+    def __init__(self, wk, device="cuda:0", head_mult=None):
+        """head_mult: the draft head's output multiplier (None: from the head's config)."""
         self.device = torch.device(device)
         self.w = wk["workload"]
         self.d = wk["dims"]
@@ -97,8 +112,10 @@ class StepRunner:
         self.head = None
         if wk.get("head") is not None:
             h = wk["head"]
+            mult = (head_multiplier(self.d["hidden"], h["base_width"], h["mult_mode"])
+                    if head_mult is None else float(head_mult))
             self.head = dict(w_lm=B.pack_dense(to_dev(h["w_lm"], device)), g_final=to_dev(h["g_final"], device),
-                             d2t=to_dev(h["d2t"], device), multiplier=h["multiplier"],
+                             d2t=to_dev(h["d2t"], device), multiplier=mult,
                              soft_cap=h["soft_cap"])
             V = h["w_lm"].shape[0]
             self.head_ws = torch.empty(B.draft_head_workspace_bytes(H, V, self.b),
@@ -109,12 +126,12 @@ class StepRunner:
             self.tau = torch.empty(self.b, V, dtype=torch.float32, device=device)
 
     def layer_step(self, i, stream_buf, branch_in, front_embed=None, branch_out=None,
-                   with_route=True, stream=None):
+                   with_route=True, stream=None, aux=None):
         L = self.layers[i]
         out = self.branch_out if branch_out is None else branch_out
         B.layer_step(self.dims, self.b, stream_buf, branch_in, front_embed, L.weights, L.kv,
                      self.act["logit_bias"], out, self.route if with_route else None, self.ws,
-                     stream)
+                     stream, aux=aux)
         return out
 
     def pooled_buf(self):
@@ -148,15 +165,20 @@ class StepRunner:
         B.context_kv(self.dims, int(c["states"].shape[0]), c["states"], c["g_hidden"],
                      c["layers"], c["positions"], c["ws"], stream)
 
-    def chain(self, stream_buf, branch_in, branch_bufs, with_tau=True, stream=None):
+    def chain(self, stream_buf, branch_in, branch_bufs, with_tau=True, stream=None,
+              aux_bufs=None):
         """All layers through their input boundaries, the final boundary and the head.
-        branch_bufs: one fp32 [b, H] buffer per layer for the layer outputs."""
+        branch_bufs: one fp32 [b, H] buffer per layer for the layer outputs.  aux_bufs
+        (optional): one fp32 [b, H] buffer per layer for its aux tap, then one for the final
+        boundary's."""
         u = branch_in
         for i in range(len(self.layers)):
-            u = self.layer_step(i, stream_buf, u, branch_out=branch_bufs[i], stream=stream)
+            u = self.layer_step(i, stream_buf, u, branch_out=branch_bufs[i], stream=stream,
+                                aux=None if aux_bufs is None else aux_bufs[i])
         hd = self.head
         B.boundary_dualnorm(self.dims, self.b, stream_buf, u, None,
-                            self.layers[-1].t["g_post_ffn"], hd["g_final"], self.head_h, stream)
+                            self.layers[-1].t["g_post_ffn"], hd["g_final"], self.head_h, stream,
+                            aux=None if aux_bufs is None else aux_bufs[-1])
         V = hd["w_lm"].shape[0]
         B.draft_head(self.d["hidden"], V, self.b, self.head_h, hd["w_lm"], hd["multiplier"],
                      hd["soft_cap"], hd["d2t"], self.tau if with_tau else None, self.draft_ids,

@@ -43,7 +43,8 @@ class Workload:
     n_layers: int = 1
     draft_vocab: int = 0              # > 0: a draft head follows the last layer
     target_vocab: int = 0
-    base_width: int = 1024            # head multiplier = (hidden / base_width) ** -1
+    base_width: int = 1024            # the draft head's base width (width_mult = hidden / it)
+    mult_mode: str = "mup"            # the draft head's output-multiplier rule
     soft_cap: float = 30.0
     window: int = 0                   # sliding window of every layer (0: full causal)
     dense_inter: int = 0              # > 0: layers also carry a dense feed-forward (draft)
@@ -248,13 +249,14 @@ def make_activations(w: Workload, seed):
 
 def make_head(w: Workload, seed):
     """Draft head: lm_head bf16 [Vd, H] ~ N(0, 1/H), g_final ~ 1 + N(0, 0.1), and a d2t
-    map of Vd distinct target ids drawn from [0, target_vocab)."""
+    map of Vd distinct target ids drawn from [0, target_vocab).  The output multiplier is
+    not computed here: the head's config (base_width, mult_mode) is passed on."""
     H, V = w.hidden, w.draft_vocab
     d2t = rng_for(seed, "d2t").choice(w.target_vocab, V, replace=False).astype(np.int64)
     return dict(w_lm=_bf16(_normal(seed, "w_lm", (V, H), H ** -0.5)),
                 g_final=torch.from_numpy(1.0 + _normal(seed, "g_final", (H,), 0.1)),
                 d2t=torch.from_numpy(d2t),
-                multiplier=float((H / w.base_width) ** -1), soft_cap=float(w.soft_cap))
+                base_width=int(w.base_width), mult_mode=w.mult_mode, soft_cap=float(w.soft_cap))
 
 
 def make_workload(name_or_w, seed=None):

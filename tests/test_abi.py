@@ -55,7 +55,7 @@ def test_no_extra_exports_beyond_header(lib):
 
 
 def test_abi_version(lib):
-    assert B.abi_version() == 6
+    assert B.abi_version() == 7
 
 
 def test_workspace_bytes_host_only(lib):
@@ -68,10 +68,11 @@ def test_workspace_bytes_host_only(lib):
     assert B.workspace_bytes(d, 65, 9, 8192) == 0
 
 
-def _rc_dualnorm(d, b=8, stream=FAKE, branch=FAKE, front=None, g_post=FAKE, g_pre=FAKE, out=FAKE):
+def _rc_dualnorm(d, b=8, stream=FAKE, branch=FAKE, front=None, g_post=FAKE, g_pre=FAKE, out=FAKE,
+                 aux=None):
     L = B.lib()
     return L.sd_boundary_dualnorm(ctypes.byref(d) if d is not None else None, b, stream, branch,
-                                  front, g_post, g_pre, out, None, None)
+                                  front, g_post, g_pre, out, None, aux, None)
 
 
 @pytest.mark.parametrize("kw,code,text", [
@@ -96,6 +97,8 @@ def test_null_dims_and_pointers(lib):
     assert _rc_dualnorm(dims(), stream=None) == -1
     assert _rc_dualnorm(dims(), branch=None, front=None) == -1
     assert "front" in lib.sd_last_error().decode()
+    assert _rc_dualnorm(dims(), aux=FAKE + 4) == -1                # a misaligned aux tap
+    assert "aux" in lib.sd_last_error().decode()
 
 
 def test_row_count_limits(lib):
@@ -146,16 +149,38 @@ def test_layer_step_validation(lib):
                           moe=B.SdMoeWeights(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE))
     kv = _kv()
     L = B.lib()
-    rc = L.sd_layer_step(ctypes.byref(d), 8, FAKE, None, None, ctypes.byref(lw), ctypes.byref(kv),
-                         None, FAKE, None, None, 0, None)
-    assert rc == -1 and "front" in L.sd_last_error().decode()
-    rc = L.sd_layer_step(ctypes.byref(d), 8, FAKE, FAKE, None, ctypes.byref(lw), ctypes.byref(kv),
-                         None, FAKE, None, None, 0, None)
-    assert rc == -4
+    def rc(front=None, branch=FAKE, route=None, aux=None, ws=None, ws_bytes=0):
+        return L.sd_layer_step(ctypes.byref(d), 8, FAKE, branch, front, ctypes.byref(lw),
+                               ctypes.byref(kv), None, FAKE,
+                               ctypes.byref(route) if route is not None else None, aux, ws,
+                               ws_bytes, None)
+    assert rc(branch=None) == -1 and "front" in L.sd_last_error().decode()
+    assert rc() == -4
+    assert rc(aux=FAKE + 4) == -1 and "aux" in L.sd_last_error().decode()
+    route = B.SdRoute(*([FAKE] * 7), FAKE + 4)                     # misaligned logits
+    assert rc(route=route) == -1 and "logits" in L.sd_last_error().decode()
+    route = B.SdRoute(*([FAKE] * 7), None)                         # logits are optional
+    assert rc(route=route) == -4
     lw.moe.w13_codes = FAKE + 8
-    rc = L.sd_layer_step(ctypes.byref(d), 8, FAKE, FAKE, None, ctypes.byref(lw), ctypes.byref(kv),
-                         None, FAKE, None, FAKE, 1 << 40, None)
-    assert rc == -1 and "aligned" in L.sd_last_error().decode()
+    assert rc(ws=FAKE, ws_bytes=1 << 40) == -1 and "aligned" in L.sd_last_error().decode()
+
+
+def test_expert_entry_points_validation(lib):
+    d = dims()
+    mw = B.SdMoeWeights(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    route = B.SdRoute(*([FAKE] * 7), None)
+    for fn, name in ((lib.sd_moe_experts, "x"), (lib.sd_moe_experts_x16, "x16")):
+        def rc(x=FAKE, y=FAKE, ws=FAKE, ws_bytes=1 << 30, r=route):
+            return fn(ctypes.byref(d), 8, x, ctypes.byref(mw), ctypes.byref(r), y, None, ws,
+                      ws_bytes, None)
+        assert rc(x=None) == -1 and name in lib.sd_last_error().decode()
+        assert rc(x=FAKE + 2) == -1 and "aligned" in lib.sd_last_error().decode()
+        assert rc(ws=None) == -4
+        assert rc(r=B.SdRoute(None, *([FAKE] * 6), None)) == -1
+    assert lib.sd_moe_route(ctypes.byref(d), 8, FAKE, FAKE, None,
+                            ctypes.byref(B.SdRoute(*([FAKE] * 7), FAKE + 4)), FAKE, 1 << 30,
+                            None) == -1
+    assert "logits" in lib.sd_last_error().decode()
 
 
 def test_dense_layer_validation(lib):

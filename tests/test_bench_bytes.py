@@ -53,3 +53,18 @@ def test_untouched_experts_cost_nothing():
     a, _ = bench.algorithmic_bytes(_wk(H, Hq, Hkv, D, E, I, b, [128]), [zero])
     c, e = bench.algorithmic_bytes(_wk(H, Hq, Hkv, D, E, I, b, [128]), [one])
     assert c - a == e == 3 * H * I * (0.5 + 1.0 / 16) + 8
+
+
+def test_rotation_copies_divide_the_timed_steps():
+    from bench import rotation_copies
+    step = 353.1e6
+    assert rotation_copies(20, step) == (10, 0)      # the driver's --steps 20
+    assert rotation_copies(200, step) == (8, 0)
+    assert rotation_copies(5, step) == (5, 0)        # fewer steps than the usual copies
+    assert rotation_copies(1, step) == (1, 0)
+    assert rotation_copies(37, step) == (8, 5)       # no divisor in range: one remainder graph
+    assert rotation_copies(24, 0.9e6) == (24, 0)     # a tiny step: 16..32 copies
+    for K in range(1, 120):
+        R, rest = rotation_copies(K, step)
+        assert 1 <= R <= 32 and rest == K % R
+        assert rest == 0 or K > 32

@@ -13,8 +13,9 @@ from oracle.formats import dequant_nvfp4
 from speculative_verify_decode_amd import binding as B
 from speculative_verify_decode_amd import synth
 from speculative_verify_decode_amd.runner import alloc_route
-from tests.gpu_util import (DEV, check_route_stage_a, expert_input, head_flags, require_lib,
-                            runner, say, workload)
+from oracle.head import output_multiplier
+from tests.gpu_util import (DEV, check_route_stage_a, head_flags, require_lib, runner, say,
+                            workload)
 from tests.helpers import assert_close, np64
 
 pytestmark = pytest.mark.gpu
@@ -95,21 +96,25 @@ def test_boundary_dualnorm_modes(name):
     out = torch.empty(b, H, dtype=torch.bfloat16, device=DEV)
     out16 = torch.empty(2, b, H, dtype=torch.float16, device=DEV)
     gp, gq = lay["g_post_prev"].to(DEV), lay["g_pre_attn"].to(DEV)
+    aux = torch.full((b, H), float("nan"), dtype=torch.float32, device=DEV)
     B.boundary_dualnorm(dims, b, s, act["branch_in"].float().to(DEV), None, gp, gq, out,
-                        out16=out16)
+                        out16=out16, aux=aux)
     torch.cuda.synchronize()
     s_ref, x_ref = oracle.dual_norm(np64(act["stream"]), np64(act["branch_in"]), np64(lay["g_post_prev"]),
                                     np64(lay["g_pre_attn"]), d["eps"])
     assert_close(np64(s), s_ref, "stream")
+    assert torch.equal(aux, s)                       # the tap is the stream it hands on
+    assert_close(np64(aux), s_ref, "aux tap")
     assert_close(np64(out), x_ref, "pre-norm output")
     # the expert-input form: hi + lo = y * 2^-8 to fp32 accuracy
     terms = np64(out16)
     assert_close((terms[0] + terms[1]) * 256.0, x_ref, "expert-input terms", tol=1e-4)
     # front mode: the stream becomes the embedding
-    B.boundary_dualnorm(dims, b, s, None, act["front_embed"].to(DEV), None, gq, out)
+    B.boundary_dualnorm(dims, b, s, None, act["front_embed"].to(DEV), None, gq, out, aux=aux)
     torch.cuda.synchronize()
     s_ref, x_ref = oracle.front_norm(np64(act["front_embed"]), np64(lay["g_pre_attn"]), d["eps"])
     assert np.array_equal(np64(s), s_ref)
+    assert np.array_equal(np64(aux), s_ref)
     assert_close(np64(out), x_ref, "front pre-norm output")
 
 
@@ -188,14 +193,16 @@ def test_moe_route_matches_oracle(name):
     r = runner(wk)
     lay, d, b = wk["layers"][0], wk["dims"], r.b
     x = wk["act"]["front_embed"]
-    z = torch.empty(b, d["n_experts"], dtype=torch.float32, device=DEV)
-    B.moe_route(r.dims, b, x.to(DEV), r.layers[0].t["w_router"], r.act["logit_bias"], r.route, z, r.ws)
+    z = r.route_t["logits"]
+    B.moe_route(r.dims, b, x.to(DEV), r.layers[0].t["w_router"], r.act["logit_bias"], r.route, r.ws)
     torch.cuda.synchronize()
     z_ref = oracle.router_logits(np64(x), np64(lay["w_router"]), np64(wk["act"].get("logit_bias")))
     assert_close(np64(z), z_ref, "router logits", tol=1e-3)
     gid = np64(r.route_t["topk_ids"])
     flagged = check_route_stage_a(z_ref, gid, d["top_k"])
     say(f"[gpu-test] route {name}: {len(flagged)} near-tie rows")
+    # the ids are exactly the (-z, index) top-k of the logits the routing ranked, every row
+    assert np.array_equal(gid, oracle.topk_route(np64(z), d["top_k"])[0])
     # weights: softmax over the GPU's own selection of the exact logits
     sel = np.take_along_axis(z_ref, gid.astype(np.int64), 1)
     ex = np.exp(sel - sel.max(1, keepdims=True))
@@ -221,10 +228,10 @@ def test_moe_experts_and_unpool_match_oracle(name):
     lay, d, b = wk["layers"][0], wk["dims"], r.b
     k, I, H = d["top_k"], d["inter"], d["hidden"]
     x = wk["act"]["front_embed"]
-    B.moe_route(r.dims, b, x.to(DEV), r.layers[0].t["w_router"], r.act["logit_bias"], r.route, None, r.ws)
+    B.moe_route(r.dims, b, x.to(DEV), r.layers[0].t["w_router"], r.act["logit_bias"], r.route, r.ws)
     y = torch.empty(b * k, H, dtype=torch.float32, device=DEV)
     h = torch.empty(b * k, I, dtype=torch.bfloat16, device=DEV)
-    B.moe_experts(r.dims, b, expert_input(x).to(DEV), r.layers[0].moe_w, r.route, y, h, r.ws)
+    B.moe_experts(r.dims, b, x.to(DEV), r.layers[0].moe_w, r.route, y, h, r.ws)
     m = torch.empty(b, H, dtype=torch.float32, device=DEV)
     B.moe_unpool(r.dims, b, y, r.route, m)
     torch.cuda.synchronize()
@@ -244,6 +251,38 @@ def test_moe_experts_and_unpool_match_oracle(name):
     assert_close(np64(m), m_ref, "unpooled output")
 
 
+@pytest.mark.timeout(600)
+def test_moe_experts_x16_on_the_boundary_output():
+    """The split-form entry point on the expert input a boundary writes (front mode: the
+    pre-norm of the embedding), against the oracle's experts on the oracle's norm output."""
+    wk = workload("h4096_b8_ctx8k")
+    r = runner(wk)
+    lay, act, d, b = wk["layers"][0], wk["act"], wk["dims"], r.b
+    k, H = d["top_k"], d["hidden"]
+    x = act["front_embed"]
+    B.moe_route(r.dims, b, x.to(DEV), r.layers[0].t["w_router"], None, r.route, r.ws)
+    s = torch.empty(b, H, dtype=torch.float32, device=DEV)
+    hb = torch.empty(b, H, dtype=torch.bfloat16, device=DEV)
+    x16 = torch.empty(2, b, H, dtype=torch.float16, device=DEV)
+    B.boundary_dualnorm(r.dims, b, s, None, x.to(DEV), None, r.layers[0].t["g_pre_ffn"], hb,
+                        out16=x16)
+    y = torch.empty(b * k, H, dtype=torch.float32, device=DEV)
+    B.moe_experts_x16(r.dims, b, x16, r.layers[0].moe_w, r.route, y, None, r.ws)
+    torch.cuda.synchronize()
+    _, x_ref = oracle.front_norm(np64(x), np64(lay["g_pre_ffn"]), d["eps"])
+    rt = {kk: np64(v) for kk, v in r.route_t.items()}
+    touched = np.nonzero(rt["expert_counts"])[0][:6]
+    _, y_ref = oracle.moe_experts(x_ref, rt["expert_counts"], rt["expert_offsets"],
+                                  rt["token_of_slot"], np64(lay["w13_codes"]),
+                                  np64(lay["w13_scales"]), np64(lay["w13_gscale"]),
+                                  np64(lay["w2_codes"]), np64(lay["w2_scales"]),
+                                  np64(lay["w2_gscale"]), d["inter"], experts=set(touched.tolist()))
+    off = rt["expert_offsets"]
+    rows = np.concatenate([np.arange(off[e], off[e + 1]) for e in touched])
+    w = assert_close(np64(y)[rows], y_ref[rows], "expert output y (split form)")
+    say(f"[gpu-test] experts x16: worst scaled err {w:.2e}")
+
+
 # ------------------------------------------------------------------------ draft head
 @pytest.mark.timeout(600)
 def test_draft_head_full_size_matches_oracle():
@@ -253,13 +292,14 @@ def test_draft_head_full_size_matches_oracle():
     H, V, b = w.hidden, w.draft_vocab, w.b
     h = synth._bf16(synth._normal(0, "head_probe_h", (b, H)))
     w_lm, d2t = B.pack_dense(hd["w_lm"].to(DEV)), hd["d2t"].to(DEV)
+    mult = output_multiplier(H, hd["base_width"], hd["mult_mode"])
     ws = torch.empty(B.draft_head_workspace_bytes(H, V, b), dtype=torch.uint8, device=DEV)
     tau = torch.empty(b, V, dtype=torch.float32, device=DEV)
     ids = torch.empty(b, dtype=torch.int32, device=DEV)
     tgt = torch.empty(b, dtype=torch.int64, device=DEV)
-    B.draft_head(H, V, b, h.to(DEV), w_lm, hd["multiplier"], hd["soft_cap"], d2t, tau, ids, tgt, ws)
+    B.draft_head(H, V, b, h.to(DEV), w_lm, mult, hd["soft_cap"], d2t, tau, ids, tgt, ws)
     torch.cuda.synchronize()
-    ref = oracle.draft_head(np64(h), np64(hd["w_lm"]), hd["multiplier"], hd["soft_cap"], np64(hd["d2t"]))
+    ref = oracle.draft_head(np64(h), np64(hd["w_lm"]), mult, hd["soft_cap"], np64(hd["d2t"]))
     exact = np64(h) @ np64(hd["w_lm"]).T
     flagged = head_flags(exact)
     say(f"[gpu-test] head: {flagged.sum()} near-midpoint rows")

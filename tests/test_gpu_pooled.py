@@ -73,7 +73,7 @@ def test_pooled_step_rejects_missing_output():
         B._check(B.lib().sd_layer_step_pooled(
             B.ctypes.byref(r.dims), r.b, B.ptr(s), None, B.ptr(r.act["front_embed"]),
             B.ctypes.byref(r.layers[0].weights), B.ctypes.byref(r.layers[0].kv), None, None,
-            B.ptr(r.ws), r.ws.numel() * r.ws.element_size(), None))
+            None, B.ptr(r.ws), r.ws.numel() * r.ws.element_size(), None))
 
 
 def test_pooled_step_graph_replays_match_eager():

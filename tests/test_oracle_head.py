@@ -59,6 +59,14 @@ def test_head_rounds_hidden_to_bf16_first():
     assert out["logits"][0, 0] == 1.0
 
 
+def test_product_head_multiplier_follows_the_oracle():
+    """The runner computes the head's multiplier from its config; it must be the oracle's."""
+    from speculative_verify_decode_amd.runner import head_multiplier
+    for hidden, base in ((4096, 1024), (256, 64), (1024, 1024), (6144, 256)):
+        for mode in ("mup", "sp"):
+            assert head_multiplier(hidden, base, mode) == OH.output_multiplier(hidden, base, mode)
+
+
 def test_final_boundary_is_library_dual_norm():
     s, m = RNG.standard_normal((2, 48)), RNG.standard_normal((2, 48))
     gp, gf = 1 + 0.1 * RNG.standard_normal(48), 1 + 0.1 * RNG.standard_normal(48)
@@ -75,7 +83,8 @@ def test_two_layer_chain_matches_torch_composition():
     act, dims, head = wk["act"], wk["dims"], wk["head"]
     layers = [oracle_layer_inputs(l, act) for l in wk["layers"]]
     out = oracle.chain_step(layers, dims, np64(act["stream"]), np64(act["branch_in"]),
-                            np64(head["g_final"]), np64(head["w_lm"]), head["multiplier"],
+                            np64(head["g_final"]), np64(head["w_lm"]),
+                            OH.output_multiplier(w.hidden, head["base_width"], head["mult_mode"]),
                             head["soft_cap"], np64(head["d2t"]))
     # independent composition: torch layer twice, library rms_norm, torch argmax
     a = dict(act)
@@ -91,3 +100,8 @@ def test_two_layer_chain_matches_torch_composition():
     assert np.allclose(out["head"]["logits"], lg.numpy(), atol=0.02)   # bf16 ulp at most
     assert out["head"]["ids"].tolist() == torch.argmax(lg, 1).tolist()
     assert out["head"]["target_ids"].tolist() == head["d2t"][torch.argmax(lg, 1)].tolist()
+    # aux taps: each layer's input-boundary stream, then the final boundary's stream
+    assert len(out["aux"]) == 3
+    assert np.array_equal(out["aux"][-1], out["stream"])
+    for i in range(2):
+        assert np.array_equal(out["aux"][i], out["layers"][i]["stream_in"])

@@ -138,6 +138,27 @@ def test_kv_write_targets_slots_and_rounds_to_bf16():
     assert np.isnan(kc).all()                     # input untouched
 
 
+def test_kv_write_negative_slot_writes_nothing():
+    """A negative slot marks a row whose K/V is not stored (vLLM's padding convention):
+    the cache changes at the other rows' slots only, exactly as if the row were absent,
+    and in particular the last block (where a negative index would land) is untouched."""
+    nb, hkv, d = 5, 2, 8
+    kc = RNG.standard_normal((nb, hkv, 16, d))
+    vc = RNG.standard_normal((nb, hkv, d, 16))
+    k = RNG.standard_normal((4, hkv, d))
+    v = RNG.standard_normal((4, hkv, d))
+    slots = np.array([2 * 16 + 3, -1, 0 * 16 + 9, -16])
+    keep = slots >= 0
+    k2, v2 = oracle.kv_write(kc, vc, k, v, slots)
+    k3, v3 = oracle.kv_write(kc, vc, k[keep], v[keep], slots[keep])
+    assert np.array_equal(k2, k3) and np.array_equal(v2, v3)
+    assert np.array_equal(k2[nb - 1], kc[nb - 1]) and np.array_equal(v2[nb - 1], vc[nb - 1])
+    changed = np.argwhere((k2 != kc).any(axis=(1, 3)))           # (block, offset) pairs
+    assert sorted(map(tuple, changed.tolist())) == [(0, 9), (2, 3)]
+    k4, v4 = oracle.kv_write(kc, vc, k, v, np.full(4, -5))
+    assert np.array_equal(k4, kc) and np.array_equal(v4, vc)
+
+
 # ------------------------------------------------------------------- attention
 def _attn_case(n_req=2, q_rows=8, hq=4, hkv=2, d=16, lens=(45, 70), nb=16, seed=0):
     rng = np.random.default_rng(seed)
@@ -426,13 +447,28 @@ def test_tiny_layer_matches_independent_torch_composition():
     lay, act, dims = wk["layers"][0], wk["act"], wk["dims"]
     ref = torch_ref.layer(lay, act, dims, act["branch_in"])
     out = oracle.layer_step(oracle_layer_inputs(lay, act), dims, branch_in=np64(act["branch_in"]))
-    for key in ("x_a", "gate", "o", "a", "stream", "x_m", "z", "w", "m"):
+    for key in ("aux", "x_a", "gate", "o", "a", "stream", "x_m", "z", "w", "m"):
         r = ref[key].numpy().reshape(out[key].shape)
         assert np.allclose(out[key], r, rtol=1e-10, atol=1e-10), key
     for key in ("q", "k", "v"):
         assert np.allclose(out[key], ref[key].numpy(), atol=1e-10), key
     assert np.array_equal(out["ids"], ref["ids"].numpy())
     assert np.isfinite(out["m"]).all() and np.isfinite(out["stream"]).all()
+
+
+def test_aux_tap_is_the_stream_entering_the_attention_block():
+    """The aux tap is the stream the input boundary hands on: its pre-norm is the attention
+    input, and at the front it is the embedding itself (a copy, not a view)."""
+    wk = synth.make_workload("tiny_b8_ctx128")
+    lay, act, dims = wk["layers"][0], wk["act"], wk["dims"]
+    out = oracle.layer_step(oracle_layer_inputs(lay, act), dims, branch_in=np64(act["branch_in"]))
+    g = torch.from_numpy(np64(lay["g_pre_attn"]))
+    x_ref = F.rms_norm(torch.from_numpy(out["aux"]), (dims["hidden"],), g, dims["eps"]).numpy()
+    assert np.allclose(out["x_a"], x_ref, rtol=1e-12, atol=1e-12)
+    assert not np.allclose(out["aux"], out["stream"])       # the attention boundary moved on
+    front = oracle.layer_step(oracle_layer_inputs(lay, act), dims,
+                              front_embed=np64(act["front_embed"]))
+    assert np.array_equal(front["aux"], np64(act["front_embed"]))
 
 
 def test_tiny_partial_drafts_layer_matches_independent_torch_composition():

@@ -12,6 +12,7 @@ from tests import test_oracle_formats as TF
 from tests import test_oracle_layer as TL
 
 ORIG_ATTN, ORIG_E4M3, ORIG_POOLER = OL.paged_attention, OF.e4m3_decode, OL.pooler
+ORIG_KV_WRITE = OL.kv_write
 
 
 def _rope_wrong_sign(x, positions, theta):
@@ -67,7 +68,19 @@ def _pooler_reversed(ids, n_experts):
     return c, off, slot_of, tos
 
 
+def _kv_write_python_negative_index(k_cache, v_cache, k, v, slot_mapping):
+    # forgets the negative-slot rule: slot -1 lands at offset 15 of the last block
+    kc = np.array(k_cache, dtype=np.float64, copy=True)
+    vc = np.array(v_cache, dtype=np.float64, copy=True)
+    for t, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
+        blk, off = int(slot) // 16, int(slot) % 16
+        kc[blk, :, off, :] = OF.bf16_round(k[t])
+        vc[blk, :, :, off] = OF.bf16_round(v[t])
+    return kc, vc
+
+
 MUTANTS = [
+    ("kv_write", _kv_write_python_negative_index, [TL.test_kv_write_negative_slot_writes_nothing]),
     ("rope", _rope_wrong_sign, [TL.test_rope_matches_complex_rotation]),
     ("topk_route", _topk_high_index, [TL.test_topk_ties_go_to_lower_index]),
     ("dual_norm", _dual_norm_plain_add, [TL.test_dual_norm_post_norm_on_branch_then_pre_norm]),

@@ -88,6 +88,7 @@ def layer(lay, act, dims, branch_in):
     eps = dims["eps"]
     b = act["stream"].shape[0]
     s = t64(act["stream"]) + rms(branch_in, lay["g_post_prev"], eps)
+    aux = s
     x_a = rms(s, lay["g_pre_attn"], eps)
     at = attn_block(lay, x_a, dims)
     s = s + rms(at["a"], lay["g_post_attn"], eps)
@@ -106,8 +107,8 @@ def layer(lay, act, dims, branch_in):
         gu = x_m[rows] @ w13.T
         h = F.silu(gu[:, :inter]) * gu[:, inter:]
         m[rows] += w[rows, js][:, None] * (h @ w2.T)
-    return dict(x_a=x_a, q=at["q"], k=at["k"], v=at["v"], gate=at["gate"], o=at["o"], a=at["a"],
-                stream=s, x_m=x_m, z=z, ids=ids, w=w, m=m)
+    return dict(aux=aux, x_a=x_a, q=at["q"], k=at["k"], v=at["v"], gate=at["gate"], o=at["o"],
+                a=at["a"], stream=s, x_m=x_m, z=z, ids=ids, w=w, m=m)
 
 
 def dense_layer(lay, stream, dims):
