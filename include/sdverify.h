@@ -278,6 +278,23 @@ int sd_layer_step_pooled(const sd_dims *dims, int32_t b, float *stream,
                          const sd_pooled *branch_out, float *aux, void *ws, size_t ws_bytes,
                          void *stream_handle);
 
+/* sd_layer_step for callers that cannot allocate (code under HIP graph capture that may not
+ * call hipMalloc, tight serving loops, harnesses that forbid allocation): the same step, the
+ * same arguments and results, with no workspace argument.  Its scratch is a static device
+ * array the library owns, sd_noalloc_scratch_bytes() (32 MiB) on each GPU it runs on, held
+ * until the process ends; its address is looked up on the first call on each device (with
+ * that device current).  A step whose workspace (sd_workspace_bytes) exceeds that size
+ * returns SD_EWORKSPACE before anything is enqueued.  The call allocates and frees nothing.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU (different
+ * streams, or graphs replayed concurrently) race and must be serialised by the caller. */
+int sd_layer_step_noalloc(const sd_dims *dims, int32_t b, float *stream, const float *branch_in,
+                          const void *front_embed, const sd_layer_weights *w, const sd_kv *kv,
+                          const float *logit_bias, float *branch_out, const sd_route *route_out,
+                          float *aux, void *stream_handle);
+
+/* Bytes of the static scratch of sd_layer_step_noalloc (per GPU). */
+size_t sd_noalloc_scratch_bytes(void);
+
 /* Draft head on bf16 hidden rows h [b, hidden] ([DSP] compute_draft_logits,
  * apply_output_logit_transform, draft_id_to_target_id; [RT] unsupported: BF16 logits):
  * logits = bf16(h * w_lm^T) with w_lm packed bf16 [draft_vocab, hidden]; tau = soft_cap *

@@ -101,6 +101,11 @@ SYMBOLS = {
                                      ctypes.POINTER(SdLayerWeights), ctypes.POINTER(SdKv),
                                      c_void_p, ctypes.POINTER(SdPooled), c_void_p, c_void_p,
                                      c_size_t, c_void_p]),
+    "sd_layer_step_noalloc": (c_int, [ctypes.POINTER(SdDims), c_int, c_void_p, c_void_p,
+                                      c_void_p, ctypes.POINTER(SdLayerWeights),
+                                      ctypes.POINTER(SdKv), c_void_p, c_void_p,
+                                      ctypes.POINTER(SdRoute), c_void_p, c_void_p]),
+    "sd_noalloc_scratch_bytes": (c_size_t, []),
     "sd_draft_head": (c_int, [c_int, c_int, c_int, c_void_p, c_void_p, c_float, c_float,
                               c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                               c_void_p]),
@@ -279,6 +284,16 @@ def layer_step(dims, b, stream_buf, branch_in, front_embed, layer_w, kv, logit_b
                                ptr(logit_bias), ptr(branch_out),
                                ctypes.byref(route) if route is not None else None, ptr(aux),
                                ptr(ws), ws.numel() * ws.element_size(), cur_stream(stream)))
+
+
+def layer_step_noalloc(dims, b, stream_buf, branch_in, front_embed, layer_w, kv, logit_bias,
+                       branch_out, route, stream=None, aux=None):
+    """sd_layer_step on the library's static scratch (no workspace argument)."""
+    _check(lib().sd_layer_step_noalloc(ctypes.byref(dims), b, ptr(stream_buf), ptr(branch_in),
+                                       ptr(front_embed), ctypes.byref(layer_w), ctypes.byref(kv),
+                                       ptr(logit_bias), ptr(branch_out),
+                                       ctypes.byref(route) if route is not None else None,
+                                       ptr(aux), cur_stream(stream)))
 
 
 def make_pooled(y_slots, route):

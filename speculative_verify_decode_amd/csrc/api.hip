@@ -10,9 +10,16 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "sd_common.h"
+
+// Scratch of sd_layer_step_noalloc: device memory the library owns, one copy per GPU the
+// library runs on, held until the process ends.  In host code this name is a host-side
+// stand-in, not a device address: host code reaches the array only through the pointer
+// hipGetSymbolAddress gives for the current device (scratch_ptr below).
+static __device__ __align__(256) unsigned char scratch[SD_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -334,6 +341,30 @@ sd_route ws_route(void* ws, const Ws& L) {
   return r;
 }
 
+// The current device's address of `scratch`, looked up once per device (with that device
+// current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+int scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SD_EUNSUPPORTED, "device %d (the scratch table holds %d)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(SD_EHIP, "hipGetSymbolAddress(scratch) gave a null address");
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return SD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -608,6 +639,31 @@ int sd_layer_step_pooled(const sd_dims* dims, int32_t b, float* stream,
   if (branch_out == nullptr) return fail(SD_EINVAL, "branch_out is null");
   return layer_step_impl(dims, b, stream, nullptr, branch_in, front_embed, w, kv, logit_bias,
                          nullptr, nullptr, branch_out, aux, ws, ws_bytes, stream_handle);
+}
+
+size_t sd_noalloc_scratch_bytes(void) { return SD_NOALLOC_SCRATCH_BYTES; }
+
+int sd_layer_step_noalloc(const sd_dims* dims, int32_t b, float* stream, const float* branch_in,
+                          const void* front_embed, const sd_layer_weights* w, const sd_kv* kv,
+                          const float* logit_bias, float* branch_out, const sd_route* route_out,
+                          float* aux, void* stream_handle) {
+  // host-only checks first: nothing touches the device before the size is known to fit
+  SD_CHECK(check_dims(dims));
+  SD_CHECK(check_rows(dims, b));
+  SD_CHECK(check_kv(dims, b, kv));
+  const size_t need = ws_layout(*dims, b, kv->n_req, kv->max_seq_len).total;
+  if (need > (size_t)SD_NOALLOC_SCRATCH_BYTES)
+    return fail(SD_EWORKSPACE,
+                "this step needs %zu bytes of scratch; the library's static scratch holds %zu "
+                "(use sd_layer_step with a workspace)",
+                need, (size_t)SD_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  SD_CHECK(scratch_ptr(&ws));
+  // Every region the step reads is written earlier in the same call (the one counter a
+  // kernel needs is zeroed by a preceding kernel), so the previous call's contents never
+  // reach the result; nothing is cleared with a memset.
+  return layer_step_impl(dims, b, stream, branch_in, nullptr, front_embed, w, kv, logit_bias,
+                         branch_out, route_out, nullptr, aux, ws, need, stream_handle);
 }
 
 // ------------------------------------------------------------------------ draft side

@@ -6,6 +6,9 @@
 
 #include "sdverify.h"
 
+// Bytes of the static scratch array of sd_layer_step_noalloc (one per GPU).
+#define SD_NOALLOC_SCRATCH_BYTES (32u << 20)
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));

@@ -268,3 +268,23 @@ def test_product_path_never_imports_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle", text, flags=re.M), f
                 assert "oracle/" not in text, f
+
+
+def test_noalloc_step_validates_on_the_host(lib):
+    """sd_layer_step_noalloc checks sizes before it touches the device: a step whose
+    workspace exceeds the static scratch fails with SD_EWORKSPACE, and bad arguments fail as
+    for sd_layer_step (no device is needed for either)."""
+    d = dims()
+    lw = B.SdLayerWeights(g_post_prev=FAKE, g_pre_attn=FAKE, g_post_attn=FAKE, g_pre_ffn=FAKE,
+                          attn=B.SdAttnWeights(FAKE, FAKE),
+                          moe=B.SdMoeWeights(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE))
+    assert lib.sd_noalloc_scratch_bytes() == 32 << 20
+    def rc(b=8, **kw):
+        kv = _kv(**kw)
+        return lib.sd_layer_step_noalloc(ctypes.byref(d), b, FAKE, FAKE, None, ctypes.byref(lw),
+                                         ctypes.byref(kv), None, FAKE, None, None, None)
+    assert rc(max_seq_len=1 << 24, max_blocks=1 << 20) == -4
+    assert "scratch" in lib.sd_last_error().decode()
+    assert B.workspace_bytes(d, 8, 1, 1 << 24) > lib.sd_noalloc_scratch_bytes()
+    assert rc(n_req=2) == -2                                       # b != n_req * q_rows
+    assert rc(b=0) == -2
