@@ -78,16 +78,13 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return s;
 }
 
-// E4M3FN byte -> fp32 (gfx950 decodes the OCP E4M3FN encoding).
-__device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
-  return __builtin_amdgcn_cvt_f32_fp8(byte, 0);
-}
-
 // Eight E2M1 codes (one dword, low nibble first) -> eight fp16 weights w = e2m1 * scale.
 // The hardware convert applies only the exponent of its scale operand, so it runs at
 // scale 1 (exact E2M1 values) and the E4M3 block scale is a packed fp16 multiply.  The
 // product of an E2M1 value (<= 2 significant bits) and an E4M3 value (<= 4 significant
 // bits, 2^-9 .. 448) is exact in fp16, so each weight is the exact dequantised value.
+// `scale2` holds the block's scale in both halves; written as a broadcast of one half of
+// a pair, the multiply reads it through the packed op's half selectors, at no cost.
 __device__ __forceinline__ f16x8_t dequant8(uint32_t codes, f16x2_t scale2) {
   f16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0);
   f16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1);
@@ -103,17 +100,13 @@ __device__ __forceinline__ f16x8_t dequant8(uint32_t codes, f16x2_t scale2) {
   return r;
 }
 
-__device__ __forceinline__ f16x2_t scale_pair(uint32_t e4m3_byte) {
-  _Float16 s = (_Float16)e4m3_to_f32(e4m3_byte);
-  f16x2_t r = {s, s};
-  return r;
-}
-
 // A 32-weight unit: 16 bytes of codes + 2 scale bytes -> four MFMA A/B operands of 8 fp16
-// (operand m holds weights 8m .. 8m+7 of the unit).
+// (operand m holds weights 8m .. 8m+7 of the unit).  Both E4M3 scales decode in one
+// packed convert (exact: every finite E4M3 value is an fp16 value).
 __device__ __forceinline__ void dequant_unit(u32x4_t codes, uint32_t scales2, f16x8_t out[4]) {
-  const f16x2_t s0 = scale_pair(scales2 & 0xFF);
-  const f16x2_t s1 = scale_pair((scales2 >> 8) & 0xFF);
+  const f16x2_t s = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(scales2, 1.0f, false);
+  const f16x2_t s0 = __builtin_shufflevector(s, s, 0, 0);
+  const f16x2_t s1 = __builtin_shufflevector(s, s, 1, 1);
   out[0] = dequant8(codes[0], s0);
   out[1] = dequant8(codes[1], s0);
   out[2] = dequant8(codes[2], s1);
