@@ -6,11 +6,12 @@
 // columns 8(l/16) .. +7) at bytes 16l .. 16l+15.  Every weight load instruction of a wave
 // is therefore one contiguous 1 KB piece, which streams at close to the HBM rate.
 //
-// M <= 8 with hi/lo terms (or M <= 16 without): one column tile.  A persistent grid of one
-// workgroup per CU walks the 16-row tiles; its NW waves split K and keep their slice of
-// the activations in registers for the whole launch; the next tile's weights are loaded
-// while the current one is reduced, so the weight stream never drains.  Larger M: one
-// workgroup per tile, activations re-read per tile from L2.  Activation rows past M are
+// Persistent kernel (M <= 64): a grid of one workgroup per CU walks the 16-row tiles; its
+// NW waves split K (and the grid splits K ksplit ways) and keep their slice of the
+// activations, NCT column tiles of 8 rows (16 without lo terms), in registers for the whole
+// launch; the next tile's weights are loaded while the current one is reduced, so the
+// weight stream never drains and the activations are read once per workgroup.  Shapes it
+// cannot hold: one workgroup per tile, activations re-read per tile from L2.  Activation rows past M are
 // read through buffer loads whose range check returns zero without a memory access.
 //
 // SPLIT: x carries bf16 hi/lo terms, 8 rows per column tile (columns 0-7 hi, 8-15 lo),
@@ -90,13 +91,14 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, int m, int tile, i
   }
 }
 
-// Persistent kernel, one column tile: wave w owns K steps [w S, (w+1) S) of every tile.
+// Persistent kernel, NCT column tiles: wave w owns K steps [w S, (w+1) S) of every tile.
 // Workgroup w owns K slice ks = w % ksplit (wave v: steps ks * KT / ksplit + v S ..) of the
 // tiles w / ksplit + j * (grid / ksplit); slice ks writes partial ks of the output, which
 // the consumer sums in slice order.
-template <int NW, int S, int MODE, bool SPLIT>
+template <int NCT, int NW, int S, int MODE, bool SPLIT>
 __global__ __launch_bounds__(64 * NW) void k_gemm_res(GemmArgs a, int ntiles) {
-  __shared__ f32x4_t red[2][NW - 1][64];
+  constexpr int RPC = SPLIT ? 8 : 16;  // activation rows per column tile
+  __shared__ f32x4_t red[2][NW - 1][NCT][64];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int i = lane & 15, g = lane >> 4;
@@ -107,13 +109,16 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_res(GemmArgs a, int ntiles) {
   // activations: hi terms at x, lo terms x_lo_off bytes further in the same buffer
   const uint32_t xbytes = (uint32_t)(a.M * a.K * 2);
   const auto rx = rsrc(a.x, (SPLIT ? a.x_lo_off : 0u) + xbytes);
-  const int m = SPLIT ? (i & 7) : i;
+  const int m = SPLIT ? (i & 7) : i;  // the lane's row within a column tile
   const bool lo = SPLIT && (i >> 3);
-  const uint32_t ob = x_off(m, a.M, a.K, kt0 * 32 + 8 * g);
-  const uint32_t ox = ob == kOob ? kOob : ob + (lo ? a.x_lo_off : 0u);
-  bf16x8_t bv[S];
+  bf16x8_t bv[NCT][S];
 #pragma unroll
-  for (int u = 0; u < S; ++u) bv[u] = buf_load8(rx, ox + 64 * u);
+  for (int c = 0; c < NCT; ++c) {
+    const uint32_t ob = x_off(RPC * c + m, a.M, a.K, kt0 * 32 + 8 * g);
+    const uint32_t ox = ob == kOob ? kOob : ob + (lo ? a.x_lo_off : 0u);
+#pragma unroll
+    for (int u = 0; u < S; ++u) bv[c][u] = buf_load8(rx, ox + 64 * u);
+  }
   GemmArgs ap = a;
   if (MODE != GEMM_HEAD) ap.y = (float*)a.y + (size_t)ks * a.M * a.N;
 
@@ -128,19 +133,30 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_res(GemmArgs a, int ntiles) {
     for (int u = 0; u < S; ++u) A[u] = buf_load8_nt(rw, o0 + 1024 * u);
   };
   auto finish = [&](bf16x8_t (&A)[S], int tile, int buf) {
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t acc[NCT];
 #pragma unroll
-    for (int u = 0; u < S; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[u], bv[u], acc, 0, 0, 0);
-    if (wave > 0) red[buf][wave - 1][lane] = acc;
+    for (int c = 0; c < NCT; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < S; ++u)
+#pragma unroll
+      for (int c = 0; c < NCT; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[u], bv[c][u], acc[c], 0, 0, 0);
+    if (wave > 0) {
+#pragma unroll
+      for (int c = 0; c < NCT; ++c) red[buf][wave - 1][c][lane] = acc[c];
+    }
     __syncthreads();
     if (wave == 0) {
 #pragma unroll
-      for (int w = 0; w < NW - 1; ++w) acc += red[buf][w][lane];
-      if (SPLIT) {
+      for (int c = 0; c < NCT; ++c) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] += __shfl_xor(acc[r], 8, 64);
+        for (int w = 0; w < NW - 1; ++w) acc[c] += red[buf][w][c][lane];
+        if (SPLIT) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[c][r] += __shfl_xor(acc[c][r], 8, 64);
+        }
+        if (!SPLIT || i < 8) store_tile<MODE>(ap, RPC * c + m, tile, ntiles, g, acc[c]);
       }
-      if (!SPLIT || i < 8) store_tile<MODE>(ap, m, tile, ntiles, g, acc);
     }
   };
   int t = grp;
@@ -238,28 +254,48 @@ int cu_count() {
   return n[dev];
 }
 
-template <int NW, int MODE, bool SPLIT>
+// Whether k_gemm_res<NCT, NW, S> fits one workgroup per CU: the resident activations
+// (NCT x S operands a lane) within the registers, the cross-wave reduction within LDS.
+// Registers a lane: activations 4 NCT S, two weight buffers 8 S, accumulators 4 NCT, and
+// about 40 more; 512 threads allow 256, 1024 allow 128.
+constexpr bool res_fits(int NCT, int NW, int S) {
+  return (NCT == 1 ? (S <= 16 && !(NW > 8 && S == 16))
+                   : 4 * NCT * S + 8 * S + 4 * NCT + 40 <= (NW > 8 ? 128 : 256)) &&
+         2 * (NW - 1) * NCT <= 120;  // KB of reduction buffers
+}
+
+template <int NCT, int NW, int S, int MODE, bool SPLIT>
+bool launch_res_s(const GemmArgs& a, int ntiles, int grid, hipStream_t st) {
+  if constexpr (!res_fits(NCT, NW, S)) {
+    return false;
+  } else {
+    hipLaunchKernelGGL((k_gemm_res<NCT, NW, S, MODE, SPLIT>), dim3(grid), dim3(64 * NW), 0, st,
+                       a, ntiles);
+    return true;
+  }
+}
+
+template <int NCT, int NW, int MODE, bool SPLIT>
 bool try_res(const GemmArgs& a, int ntiles, hipStream_t st) {
   const int KT = a.K / 32;
   if (KT % (NW * a.ksplit)) return false;
   if ((size_t)ntiles * KT * 1024 >= 0x80000000u) return false;  // buffer offsets are 32-bit
   const int grid = (min(ntiles * a.ksplit, cu_count()) / a.ksplit) * a.ksplit;
   if (grid < a.ksplit) return false;
-  const dim3 block(64 * NW);
   switch (KT / (NW * a.ksplit)) {
-    case 16:
-      if constexpr (NW > 8) {
-        return false;  // 16 waves x 16 resident steps do not fit the registers
-      } else {
-        hipLaunchKernelGGL((k_gemm_res<NW, 16, MODE, SPLIT>), dim3(grid), block, 0, st, a, ntiles);
-        return true;
-      }
-    case 8: hipLaunchKernelGGL((k_gemm_res<NW, 8, MODE, SPLIT>), dim3(grid), block, 0, st, a, ntiles); return true;
-    case 4: hipLaunchKernelGGL((k_gemm_res<NW, 4, MODE, SPLIT>), dim3(grid), block, 0, st, a, ntiles); return true;
-    case 2: hipLaunchKernelGGL((k_gemm_res<NW, 2, MODE, SPLIT>), dim3(grid), block, 0, st, a, ntiles); return true;
-    case 1: hipLaunchKernelGGL((k_gemm_res<NW, 1, MODE, SPLIT>), dim3(grid), block, 0, st, a, ntiles); return true;
+    case 16: return launch_res_s<NCT, NW, 16, MODE, SPLIT>(a, ntiles, grid, st);
+    case 8: return launch_res_s<NCT, NW, 8, MODE, SPLIT>(a, ntiles, grid, st);
+    case 4: return launch_res_s<NCT, NW, 4, MODE, SPLIT>(a, ntiles, grid, st);
+    case 2: return launch_res_s<NCT, NW, 2, MODE, SPLIT>(a, ntiles, grid, st);
+    case 1: return launch_res_s<NCT, NW, 1, MODE, SPLIT>(a, ntiles, grid, st);
     default: return false;
   }
+}
+
+template <int NCT, int MODE, bool SPLIT>
+bool try_res_nw(const GemmArgs& a, int ntiles, hipStream_t st) {
+  return try_res<NCT, 8, MODE, SPLIT>(a, ntiles, st) || try_res<NCT, 16, MODE, SPLIT>(a, ntiles, st) ||
+         try_res<NCT, 4, MODE, SPLIT>(a, ntiles, st);
 }
 
 template <int NCT, int NW, int MODE, bool SPLIT>
@@ -303,22 +339,21 @@ hipError_t launch_m(const GemmArgs& in, hipStream_t st) {
   }
   // the persistent kernel takes any K slicing; the per-tile kernel only whole K
   if (a.x_lo != nullptr) {
-    if (a.M <= 8) {
-      if (try_res<8, MODE, true>(a, ntiles, st) || try_res<16, MODE, true>(a, ntiles, st) ||
-          try_res<4, MODE, true>(a, ntiles, st))
-        return hipGetLastError();
-    }
+    const bool res = a.M <= 8    ? try_res_nw<1, MODE, true>(a, ntiles, st)
+                     : a.M <= 16 ? try_res_nw<2, MODE, true>(a, ntiles, st)
+                     : a.M <= 32 ? try_res_nw<4, MODE, true>(a, ntiles, st)
+                                 : try_res_nw<8, MODE, true>(a, ntiles, st);
+    if (res) return hipGetLastError();
     if (a.ksplit != 1) return hipErrorInvalidValue;
     if (a.M <= 8) return launch_tile<1, MODE, true>(a, ntiles, st);
     if (a.M <= 16) return launch_tile<2, MODE, true>(a, ntiles, st);
     if (a.M <= 32) return launch_tile<4, MODE, true>(a, ntiles, st);
     return launch_tile<8, MODE, true>(a, ntiles, st);
   }
-  if (a.M <= 16) {
-    if (try_res<8, MODE, false>(a, ntiles, st) || try_res<16, MODE, false>(a, ntiles, st) ||
-        try_res<4, MODE, false>(a, ntiles, st))
-      return hipGetLastError();
-  }
+  const bool res = a.M <= 16   ? try_res_nw<1, MODE, false>(a, ntiles, st)
+                   : a.M <= 32 ? try_res_nw<2, MODE, false>(a, ntiles, st)
+                               : try_res_nw<4, MODE, false>(a, ntiles, st);
+  if (res) return hipGetLastError();
   if (a.ksplit != 1) return hipErrorInvalidValue;
   if (a.M <= 16) return launch_tile<1, MODE, false>(a, ntiles, st);
   if (a.M <= 32) return launch_tile<2, MODE, false>(a, ntiles, st);
@@ -427,13 +462,15 @@ hipError_t launch_pack_fp4(int E, int N, int K, const uint8_t* codes, const uint
 
 bool gemm_split_ok(int M, int N, int K, bool lo, int ksplit) {
   if (ksplit == 1) return true;
-  if (M > (lo ? 8 : 16) || K % 32) return false;
+  const int rpc = lo ? 8 : 16;  // the persistent kernel's column tiles, as launch_m picks them
+  const int nct = M <= rpc ? 1 : M <= 2 * rpc ? 2 : M <= 4 * rpc ? 4 : (lo && M <= 8 * rpc) ? 8 : 0;
+  if (nct == 0 || M > 64 || K % 32) return false;
   const int KT = K / 32, ntiles = (N + 15) / 16;
   if ((size_t)ntiles * KT * 1024 >= 0x80000000u || ntiles * ksplit < ksplit) return false;
   for (int nw : {8, 16, 4}) {
     if (KT % (nw * ksplit)) continue;
     const int S = KT / (nw * ksplit);
-    if (S == 1 || S == 2 || S == 4 || S == 8 || (S == 16 && nw <= 8)) return true;
+    if ((S == 1 || S == 2 || S == 4 || S == 8 || S == 16) && res_fits(nct, nw, S)) return true;
   }
   return false;
 }

@@ -49,7 +49,51 @@ struct MoeMeta {
   int tos[512];
   float g13[256], g2[256];  // per-expert global scales: an LDS read in the epilogue, not a
                             // global load queued behind the next unit's weights
+  // expert groups: expert e with c pooled rows is ceil(c / 8) groups of at most 8 rows
+  // (one MFMA column tile each), in active-list order; at most E + b k / 8 groups
+  int ng;
+  int gexp[320], goff[320], gcnt[320];
+  int wsum[16];
 };
+
+// The expert groups of m's active list (block-wide: block scans over the active list, one
+// pass per blockDim.x experts).
+__device__ void build_groups(MoeMeta& m, int E) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  const int n_act = m.active[E];
+  int carry = 0;  // groups of the earlier passes
+  for (int a0 = 0; a0 < n_act; a0 += blockDim.x) {  // uniform
+    const int t = a0 + tid;
+    int e = 0, ng = 0;
+    if (t < n_act) {
+      e = m.active[t];
+      ng = (m.cnt[e] + 7) >> 3;
+    }
+    int inc = ng;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(inc, d, 64);
+      if (lane >= d) inc += v;
+    }
+    if (lane == 63) m.wsum[wave] = inc;
+    __syncthreads();
+    int base = 0, tot = 0;
+    for (int w = 0; w < nw; ++w) {
+      if (w < wave) base += m.wsum[w];
+      tot += m.wsum[w];
+    }
+    const int start = carry + base + inc - ng;
+    for (int j = 0; j < ng; ++j) {
+      m.gexp[start + j] = e;
+      m.goff[start + j] = m.off[e] + 8 * j;
+      m.gcnt[start + j] = min(8, m.cnt[e] - 8 * j);
+    }
+    carry += tot;
+    __syncthreads();  // wsum is reused by the next pass
+  }
+  if (tid == 0) m.ng = carry;
+  __syncthreads();
+}
 
 template <int KEYS>
 struct RouteLdsT {
@@ -488,6 +532,7 @@ __device__ __forceinline__ void stage_meta(const MoeArgs& a, MoeMeta& m) {
   }
   for (int p = threadIdx.x; p < nk; p += blockDim.x) m.tos[p] = a.tos[p];
   __syncthreads();
+  if (a.b > 8) build_groups(m, a.E);  // uniform; with b <= 8 every expert is one group
 }
 
 template <int NU>
@@ -536,22 +581,34 @@ __device__ __forceinline__ void load_bx(f16x8_t (&bx)[NU][4], __amdgpu_buffer_rs
           f16x8_t, __builtin_amdgcn_raw_buffer_load_b128(r, off + (uint32_t)(128 * u + 8 * m) * 2, 0, 0));
 }
 
+// A unit: row tile nt of expert group gi (expert e, pooled rows off .. off + Te - 1).
+// grouped: the group list is built (b > 8); otherwise group gi is active expert gi.
 struct Unit {
-  int e, nt, Te, off;
+  int gi, e, nt, Te, off;
 };
 
-__device__ __forceinline__ Unit unit_of(const MoeMeta& m, int u, int NT) {
+__device__ __forceinline__ Unit unit_of(const MoeMeta& m, int u, int NT, bool grouped) {
   Unit r;
-  const int ai = u / NT;
-  r.nt = u - ai * NT;
-  r.e = __builtin_amdgcn_readfirstlane(m.active[ai]);
-  r.Te = __builtin_amdgcn_readfirstlane(m.cnt[r.e]);
-  r.off = __builtin_amdgcn_readfirstlane(m.off[r.e]);
+  r.gi = u / NT;
+  r.nt = u - r.gi * NT;
+  if (grouped) {
+    r.e = __builtin_amdgcn_readfirstlane(m.gexp[r.gi]);
+    r.Te = __builtin_amdgcn_readfirstlane(m.gcnt[r.gi]);
+    r.off = __builtin_amdgcn_readfirstlane(m.goff[r.gi]);
+  } else {
+    r.e = __builtin_amdgcn_readfirstlane(m.active[r.gi]);
+    r.Te = __builtin_amdgcn_readfirstlane(m.cnt[r.e]);
+    r.off = __builtin_amdgcn_readfirstlane(m.off[r.e]);
+  }
   return r;
 }
 
+__device__ __forceinline__ int groups_of(const MoeMeta& m, int E, bool grouped) {
+  return grouped ? m.ng : m.active[E];
+}
+
 // Workgroup w walks the contiguous unit range [begin, end): consecutive units mostly share
-// an expert, so the activation operand is reloaded only when the expert changes.
+// an expert group, so the activation operand is reloaded only when the group changes.
 __device__ __forceinline__ void unit_range(int n_units, int& begin, int& end) {
   begin = (int)(((long)blockIdx.x * n_units) / gridDim.x);
   end = (int)(((long)(blockIdx.x + 1) * n_units) / gridDim.x);
@@ -577,12 +634,17 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w13(MoeArgs a) {
       meta.g13[threadIdx.x] = g13v;
       meta.g2[threadIdx.x] = g2v;
     }
-    __syncthreads();
+    if (a.b > 8) {
+      build_groups(meta, a.E);  // its barriers also cover the scales
+    } else {
+      __syncthreads();
+    }
   } else {
     stage_meta(a, meta);
   }
   const int NT = a.I >> 4;
-  const int n_units = meta.active[a.E] * NT;
+  const bool grouped = a.b > 8;
+  const int n_units = groups_of(meta, a.E, grouped) * NT;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int i = lane & 15, G = lane >> 4;
@@ -695,7 +757,7 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w13(MoeArgs a) {
   if (u >= end) return;
   if constexpr (!PB && NU > 2) {  // several column tiles: their accumulators leave no room
     for (; u < end; ++u) {        // to prefetch four-tile slices
-      const Unit U = unit_of(meta, u, NT);
+      const Unit U = unit_of(meta, u, NT, grouped);
       load_a(g0, u0, U, true);
       compute(g0, u0, bx, U, 0);
     }
@@ -703,19 +765,19 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w13(MoeArgs a) {
   }
   // two-deep pipeline: every load is unconditional (a missing next unit loads zeros from
   // no memory), so the wait before each compute covers exactly the unit it uses
-  Unit U0 = unit_of(meta, u, NT), U1;
-  int be = -1;  // expert whose activations are in bx
+  Unit U0 = unit_of(meta, u, NT, grouped), U1;
+  int bg = -1;  // expert group whose activations are in bx
   load_a(g0, u0, U0, true);
   while (true) {
-    if (PB && U0.e != be) { load_b0(bx, U0); be = U0.e; }
+    if (PB && U0.gi != bg) { load_b0(bx, U0); bg = U0.gi; }
     const int n1 = u + 1;
-    U1 = unit_of(meta, min(n1, end - 1), NT);
+    U1 = unit_of(meta, min(n1, end - 1), NT, grouped);
     load_a(g1, u1, U1, n1 < end);
     compute(g0, u0, bx, U0, 0);
     if (n1 >= end) break;
-    if (PB && U1.e != be) { load_b0(bx, U1); be = U1.e; }
+    if (PB && U1.gi != bg) { load_b0(bx, U1); bg = U1.gi; }
     const int n2 = n1 + 1;
-    U0 = unit_of(meta, min(n2, end - 1), NT);
+    U0 = unit_of(meta, min(n2, end - 1), NT, grouped);
     load_a(g0, u0, U0, n2 < end);
     compute(g1, u1, bx, U1, PB ? 1 : 0);
     if (n2 >= end) break;
@@ -732,7 +794,8 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w2(MoeArgs a) {
   __shared__ f32x4_t red[PB ? 2 : 1][NR][NCT][64];
   stage_meta(a, meta);
   const int NT = a.H >> 4;
-  const int n_units = meta.active[a.E] * NT;
+  const bool grouped = a.b > 8;
+  const int n_units = groups_of(meta, a.E, grouped) * NT;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int i = lane & 15, G = lane >> 4;
@@ -812,19 +875,19 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w2(MoeArgs a) {
   int u, end;
   unit_range(n_units, u, end);
   if (u >= end) return;
-  Unit U0 = unit_of(meta, u, NT), U1;
-  int be = -1;
+  Unit U0 = unit_of(meta, u, NT, grouped), U1;
+  int bg = -1;
   load_a(w0, U0, true);
   while (true) {
-    if (!PB || U0.e != be) { load_b0(bx, U0); be = U0.e; }
+    if (!PB || U0.gi != bg) { load_b0(bx, U0); bg = U0.gi; }
     const int n1 = u + 1;
-    U1 = unit_of(meta, min(n1, end - 1), NT);
+    U1 = unit_of(meta, min(n1, end - 1), NT, grouped);
     load_a(w1, U1, n1 < end);
     compute(w0, bx, U0, 0);
     if (n1 >= end) break;
-    if (!PB || U1.e != be) { load_b0(bx, U1); be = U1.e; }
+    if (!PB || U1.gi != bg) { load_b0(bx, U1); bg = U1.gi; }
     const int n2 = n1 + 1;
-    U0 = unit_of(meta, min(n2, end - 1), NT);
+    U0 = unit_of(meta, min(n2, end - 1), NT, grouped);
     load_a(w0, U0, n2 < end);
     compute(w1, bx, U1, PB ? 1 : 0);
     if (n2 >= end) break;
@@ -996,10 +1059,9 @@ hipError_t launch_moe_experts(const MoeArgs& in, hipStream_t st) {
   if (a.h16_lo < a.h16 + (size_t)a.b * a.k * a.I || (size_t)((const char*)a.h16_lo - (const char*)a.h16) + hb >= 0x80000000u)
     return hipErrorInvalidValue;
   a.h16_lo_off = (uint32_t)((const char*)a.h16_lo - (const char*)a.h16);
-  // a token chooses an expert at most once, so an expert holds at most b pooled tokens;
-  // b <= 8 fits one column tile, larger batches take up to 8 tiles (64 tokens)
-  if (a.b <= 8) return launch_experts_nct<1>(a, st);
-  return launch_experts_nct<8>(a, st);
+  // every unit is one expert group of at most 8 pooled rows (one MFMA column tile), so
+  // one kernel pair serves every batch: an expert with more rows is read once per group
+  return launch_experts_nct<1>(a, st);
 }
 
 hipError_t launch_unpool(int b, int H, int k, const float* y, const float* w, const int* slot_of,

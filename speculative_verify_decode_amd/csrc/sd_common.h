@@ -151,8 +151,9 @@ struct GemmArgs {
   int* head_idx;       // GEMM_HEAD: per (m, tile) its index
   float multiplier, soft_cap;
 };
-// ksplit > 1 is taken only by the persistent kernel (M <= 8 with lo terms, M <= 16
-// without); otherwise the launch fails with hipErrorInvalidValue.
+// ksplit > 1 is taken only by the persistent kernel (M <= 64, shapes whose resident
+// activations fit: gemm_split_ok says which); otherwise the launch fails with
+// hipErrorInvalidValue.
 hipError_t launch_gemm(GemmMode mode, const GemmArgs& a, hipStream_t st);
 bool gemm_split_ok(int M, int N, int K, bool lo, int ksplit);
 
