@@ -340,7 +340,8 @@ def main():
         torch.cuda.synchronize()
         return np.array([a_.elapsed_time(b_) for a_, b_ in evs]) * 1e3
 
-    timed_replays(g_all, max(1, math.ceil(args.warmup / R)))
+    # warm-up: W steps' worth of replays, and at least 3 (the first replays run slower)
+    timed_replays(g_all, max(3, math.ceil(args.warmup / R)))
     K = args.steps
     n_all = K // R
     per_all = timed_replays(g_all, n_all) if n_all else np.zeros(0)
@@ -365,7 +366,7 @@ def main():
             for r, sb in zip(runners, streams):
                 run_step(r, sb, stream=st, pool=True)
         torch.cuda.synchronize()
-        timed_replays(g_pool, max(1, args.warmup // R))
+        timed_replays(g_pool, max(3, math.ceil(args.warmup / R)))
         pooled_us = float(timed_replays(g_pool, max(1, min(K, 200) // R)).mean()) / R
 
     # hot-cache number (copy 0, R steps per replay, inputs restored between replays),

@@ -369,8 +369,9 @@ int sd_debug_dequant(int32_t n, int32_t k, const uint8_t *codes, const uint8_t *
 
 /* Measurement entry: one plain streaming read of bytes (> 0, a multiple of 16) at src
  * (16-byte aligned), each 16-byte piece loaded once with the non-temporal policy of the
- * step's weight and KV streams: the practical HBM read ceiling the step is measured
- * against.  sink: uint32 [sd_read_probe_sink_words()] scratch the kernel may write. */
+ * step's weight and KV streams, each workgroup reading one contiguous part: the practical
+ * HBM read ceiling the step is measured against.  sink: uint32
+ * [sd_read_probe_sink_words()] scratch the kernel may write. */
 int sd_debug_read_probe(const void *src, size_t bytes, uint32_t *sink, void *stream_handle);
 
 /* Words of sink that sd_debug_read_probe needs. */

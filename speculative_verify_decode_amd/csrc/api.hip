@@ -863,7 +863,7 @@ int sd_debug_dequant(int32_t n, int32_t k, const uint8_t* codes, const uint8_t* 
 }
 
 namespace {
-constexpr int kProbeGrid = 2048;  // 8 workgroups per CU of a 256-CU device
+constexpr int kProbeGrid = 8192;  // 32 workgroups per CU of a 256-CU device
 }  // namespace
 
 int32_t sd_read_probe_sink_words(void) { return kProbeGrid; }

@@ -9,19 +9,23 @@ namespace {
 
 constexpr int kUnroll = 8;  // independent 16-byte loads in flight per thread
 
+// Workgroup w reads the contiguous w-th part of the buffer, 1 KB per wave instruction and
+// kUnroll instructions in flight per wave.
 __global__ __launch_bounds__(256) void k_read_probe(const u32x4_t* __restrict__ src, size_t n16,
                                                      uint32_t* __restrict__ sink) {
-  const size_t stride = (size_t)gridDim.x * 256;
-  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const size_t beg = (size_t)blockIdx.x * per;
+  const size_t end = beg + per < n16 ? beg + per : n16;
+  size_t i = beg + threadIdx.x;
   uint32_t acc = 0;
-  for (; i + (kUnroll - 1) * stride < n16; i += kUnroll * stride) {
+  for (; i + (kUnroll - 1) * 256 < end; i += kUnroll * 256) {
     u32x4_t v[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+    for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(src + i + u * 256);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
   }
-  for (; i < n16; i += stride) {
+  for (; i < end; i += 256) {
     const u32x4_t v = __builtin_nontemporal_load(src + i);
     acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
   }
