@@ -10,6 +10,8 @@
 // exactly in registers from packed tiles, and the pooled tokens of the expert are the B
 // operand.  Only the experts the router picked are walked: the work list is the ascending
 // active-expert list the pooler writes.
+#include <type_traits>
+
 #include "sd_common.h"
 
 namespace {
@@ -49,16 +51,23 @@ struct MoeMeta {
   int tos[512];
   float g13[256], g2[256];  // per-expert global scales: an LDS read in the epilogue, not a
                             // global load queued behind the next unit's weights
-  // expert groups: expert e with c pooled rows is ceil(c / 8) groups of at most 8 rows
-  // (one MFMA column tile each), in active-list order; at most E + b k / 8 groups
+};
+
+// With expert groups (batches of more than 8 rows): expert e with c pooled rows is
+// ceil(c / 8) groups of at most 8 rows (one MFMA column tile each), in active-list order;
+// at most E + b k / 8 groups.  Kernels for b <= 8 use the plain MoeMeta (each expert is one
+// group), so they carry none of this.
+struct MoeMetaG : MoeMeta {
   int ng;
   int gexp[320], goff[320], gcnt[320];
   int wsum[16];
 };
+template <bool GRP>
+using MoeMetaT = typename std::conditional<GRP, MoeMetaG, MoeMeta>::type;
 
 // The expert groups of m's active list (block-wide: block scans over the active list, one
 // pass per blockDim.x experts).
-__device__ void build_groups(MoeMeta& m, int E) {
+__device__ void build_groups(MoeMetaG& m, int E) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
   const int n_act = m.active[E];
   int carry = 0;  // groups of the earlier passes
@@ -521,7 +530,8 @@ __global__ void k_zero_i32(int* p) { *p = 0; }
 // check returns zero without a memory access.
 
 
-__device__ __forceinline__ void stage_meta(const MoeArgs& a, MoeMeta& m) {
+template <class M>
+__device__ __forceinline__ void stage_meta(const MoeArgs& a, M& m) {
   const int nk = a.b * a.k;
   for (int p = threadIdx.x; p <= a.E; p += blockDim.x) m.active[p] = a.active[p];
   for (int p = threadIdx.x; p < a.E; p += blockDim.x) {
@@ -532,7 +542,7 @@ __device__ __forceinline__ void stage_meta(const MoeArgs& a, MoeMeta& m) {
   }
   for (int p = threadIdx.x; p < nk; p += blockDim.x) m.tos[p] = a.tos[p];
   __syncthreads();
-  if (a.b > 8) build_groups(m, a.E);  // uniform; with b <= 8 every expert is one group
+  if constexpr (std::is_same<M, MoeMetaG>::value) build_groups(m, a.E);
 }
 
 template <int NU>
@@ -582,16 +592,17 @@ __device__ __forceinline__ void load_bx(f16x8_t (&bx)[NU][4], __amdgpu_buffer_rs
 }
 
 // A unit: row tile nt of expert group gi (expert e, pooled rows off .. off + Te - 1).
-// grouped: the group list is built (b > 8); otherwise group gi is active expert gi.
+// Without a group list (MoeMeta), group gi is active expert gi.
 struct Unit {
   int gi, e, nt, Te, off;
 };
 
-__device__ __forceinline__ Unit unit_of(const MoeMeta& m, int u, int NT, bool grouped) {
+template <class M>
+__device__ __forceinline__ Unit unit_of(const M& m, int u, int NT) {
   Unit r;
   r.gi = u / NT;
   r.nt = u - r.gi * NT;
-  if (grouped) {
+  if constexpr (std::is_same<M, MoeMetaG>::value) {
     r.e = __builtin_amdgcn_readfirstlane(m.gexp[r.gi]);
     r.Te = __builtin_amdgcn_readfirstlane(m.gcnt[r.gi]);
     r.off = __builtin_amdgcn_readfirstlane(m.goff[r.gi]);
@@ -603,8 +614,10 @@ __device__ __forceinline__ Unit unit_of(const MoeMeta& m, int u, int NT, bool gr
   return r;
 }
 
-__device__ __forceinline__ int groups_of(const MoeMeta& m, int E, bool grouped) {
-  return grouped ? m.ng : m.active[E];
+template <class M>
+__device__ __forceinline__ int groups_of(const M& m, int E) {
+  if constexpr (std::is_same<M, MoeMetaG>::value) return m.ng;
+  else return m.active[E];
 }
 
 // Workgroup w walks the contiguous unit range [begin, end): consecutive units mostly share
@@ -615,11 +628,11 @@ __device__ __forceinline__ void unit_range(int n_units, int& begin, int& end) {
 }
 
 // W13 (gate rows [0, I), up rows [I, 2I)) + SwiGLU.  K = H = 128 * NU * KS.
-template <int NCT, int NU, int KS, bool RT>
+template <int NCT, int NU, int KS, bool RT, bool GRP>
 __global__ __launch_bounds__(64 * KS) void k_moe_w13(MoeArgs a) {
   constexpr bool PB = NCT == 1;  // activations prefetched with the weights
   constexpr int NR = KS > 1 ? KS - 1 : 1;
-  __shared__ MoeMeta meta;
+  __shared__ MoeMetaT<GRP> meta;
   __shared__ f32x4_t red[PB ? 2 : 1][NR][2][NCT][64];
   if constexpr (RT) {
     // every workgroup routes from the router's logits (the same arithmetic, so the same
@@ -634,7 +647,7 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w13(MoeArgs a) {
       meta.g13[threadIdx.x] = g13v;
       meta.g2[threadIdx.x] = g2v;
     }
-    if (a.b > 8) {
+    if constexpr (GRP) {
       build_groups(meta, a.E);  // its barriers also cover the scales
     } else {
       __syncthreads();
@@ -643,8 +656,7 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w13(MoeArgs a) {
     stage_meta(a, meta);
   }
   const int NT = a.I >> 4;
-  const bool grouped = a.b > 8;
-  const int n_units = groups_of(meta, a.E, grouped) * NT;
+  const int n_units = groups_of(meta, a.E) * NT;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int i = lane & 15, G = lane >> 4;
@@ -757,7 +769,7 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w13(MoeArgs a) {
   if (u >= end) return;
   if constexpr (!PB && NU > 2) {  // several column tiles: their accumulators leave no room
     for (; u < end; ++u) {        // to prefetch four-tile slices
-      const Unit U = unit_of(meta, u, NT, grouped);
+      const Unit U = unit_of(meta, u, NT);
       load_a(g0, u0, U, true);
       compute(g0, u0, bx, U, 0);
     }
@@ -765,19 +777,19 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w13(MoeArgs a) {
   }
   // two-deep pipeline: every load is unconditional (a missing next unit loads zeros from
   // no memory), so the wait before each compute covers exactly the unit it uses
-  Unit U0 = unit_of(meta, u, NT, grouped), U1;
+  Unit U0 = unit_of(meta, u, NT), U1;
   int bg = -1;  // expert group whose activations are in bx
   load_a(g0, u0, U0, true);
   while (true) {
     if (PB && U0.gi != bg) { load_b0(bx, U0); bg = U0.gi; }
     const int n1 = u + 1;
-    U1 = unit_of(meta, min(n1, end - 1), NT, grouped);
+    U1 = unit_of(meta, min(n1, end - 1), NT);
     load_a(g1, u1, U1, n1 < end);
     compute(g0, u0, bx, U0, 0);
     if (n1 >= end) break;
     if (PB && U1.gi != bg) { load_b0(bx, U1); bg = U1.gi; }
     const int n2 = n1 + 1;
-    U0 = unit_of(meta, min(n2, end - 1), NT, grouped);
+    U0 = unit_of(meta, min(n2, end - 1), NT);
     load_a(g0, u0, U0, n2 < end);
     compute(g1, u1, bx, U1, PB ? 1 : 0);
     if (n2 >= end) break;
@@ -786,16 +798,15 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w13(MoeArgs a) {
 }
 
 // W2: y[slot, n] = h[slot] . W2_e[n], fp32.  K = I = 128 * NU * KS.
-template <int NCT, int NU, int KS>
+template <int NCT, int NU, int KS, bool GRP>
 __global__ __launch_bounds__(64 * KS) void k_moe_w2(MoeArgs a) {
   constexpr bool PB = NCT == 1;
   constexpr int NR = KS > 1 ? KS - 1 : 1;
-  __shared__ MoeMeta meta;
+  __shared__ MoeMetaT<GRP> meta;
   __shared__ f32x4_t red[PB ? 2 : 1][NR][NCT][64];
   stage_meta(a, meta);
   const int NT = a.H >> 4;
-  const bool grouped = a.b > 8;
-  const int n_units = groups_of(meta, a.E, grouped) * NT;
+  const int n_units = groups_of(meta, a.E) * NT;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int i = lane & 15, G = lane >> 4;
@@ -875,19 +886,19 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w2(MoeArgs a) {
   int u, end;
   unit_range(n_units, u, end);
   if (u >= end) return;
-  Unit U0 = unit_of(meta, u, NT, grouped), U1;
+  Unit U0 = unit_of(meta, u, NT), U1;
   int bg = -1;
   load_a(w0, U0, true);
   while (true) {
     if (!PB || U0.gi != bg) { load_b0(bx, U0); bg = U0.gi; }
     const int n1 = u + 1;
-    U1 = unit_of(meta, min(n1, end - 1), NT, grouped);
+    U1 = unit_of(meta, min(n1, end - 1), NT);
     load_a(w1, U1, n1 < end);
     compute(w0, bx, U0, 0);
     if (n1 >= end) break;
     if (!PB || U1.gi != bg) { load_b0(bx, U1); bg = U1.gi; }
     const int n2 = n1 + 1;
-    U0 = unit_of(meta, min(n2, end - 1), NT, grouped);
+    U0 = unit_of(meta, min(n2, end - 1), NT);
     load_a(w0, U0, n2 < end);
     compute(w1, bx, U1, PB ? 1 : 0);
     if (n2 >= end) break;
@@ -967,8 +978,8 @@ int cus() {
   return n[dev];
 }
 
-template <int NCT>
-hipError_t launch_experts_nct(const MoeArgs& a, hipStream_t st) {
+template <bool GRP>
+hipError_t launch_experts(const MoeArgs& a, hipStream_t st) {
   const Split s13 = split_for(a.H), s2 = split_for(a.I);
   // persistent grids: the live units are at most E * tiles
   const int g13 = min(cus(), a.E * (a.I / 16));
@@ -977,9 +988,9 @@ hipError_t launch_experts_nct(const MoeArgs& a, hipStream_t st) {
 #define SD_W13(NU, KS)                                                                     \
   if (!done && s13.nu == NU && s13.ks == KS) {                                             \
     if (a.route)                                                                           \
-      hipLaunchKernelGGL((k_moe_w13<NCT, NU, KS, true>), dim3(g13), dim3(64 * KS), 0, st, a); \
+      hipLaunchKernelGGL((k_moe_w13<1, NU, KS, true, GRP>), dim3(g13), dim3(64 * KS), 0, st, a); \
     else                                                                                   \
-      hipLaunchKernelGGL((k_moe_w13<NCT, NU, KS, false>), dim3(g13), dim3(64 * KS), 0, st, a); \
+      hipLaunchKernelGGL((k_moe_w13<1, NU, KS, false, GRP>), dim3(g13), dim3(64 * KS), 0, st, a); \
     done = true;                                                                          \
   }
   SD_SPLITS(SD_W13)
@@ -990,7 +1001,7 @@ hipError_t launch_experts_nct(const MoeArgs& a, hipStream_t st) {
   done = false;
 #define SD_W2(NU, KS)                                                                      \
   if (!done && s2.nu == NU && s2.ks == KS) {                                               \
-    hipLaunchKernelGGL((k_moe_w2<NCT, NU, KS>), dim3(g2), dim3(64 * KS), 0, st, a);        \
+    hipLaunchKernelGGL((k_moe_w2<1, NU, KS, GRP>), dim3(g2), dim3(64 * KS), 0, st, a);     \
     done = true;                                                                          \
   }
   SD_SPLITS(SD_W2)
@@ -1060,8 +1071,9 @@ hipError_t launch_moe_experts(const MoeArgs& in, hipStream_t st) {
     return hipErrorInvalidValue;
   a.h16_lo_off = (uint32_t)((const char*)a.h16_lo - (const char*)a.h16);
   // every unit is one expert group of at most 8 pooled rows (one MFMA column tile), so
-  // one kernel pair serves every batch: an expert with more rows is read once per group
-  return launch_experts_nct<1>(a, st);
+  // one kernel pair serves every batch: an expert with more rows is read once per group;
+  // with b <= 8 every expert is one group and the kernels build no group list
+  return a.b > 8 ? launch_experts<true>(a, st) : launch_experts<false>(a, st);
 }
 
 hipError_t launch_unpool(int b, int H, int k, const float* y, const float* w, const int* slot_of,
