@@ -87,7 +87,7 @@ def test_context_kv_store_matches_oracle(name):
     """Staged: (A) the GPU's normalised context rows against the oracle's, one bf16 step;
     (B) the oracle's projection, K norm, RoPE and store run on the GPU's own rows against the
     GPU's cache, one bf16 step (a row element on a rounding midpoint in (A) moves every
-    product it enters, so end to end only a loose bound holds, checked last)."""
+    product it enters, so end to end the project's bar 2e-2 (1 + |ref|) is checked last)."""
     wk = workload(name)
     r = runner(wk)
     d, ctx, lays = wk["dims"], wk["context"], wk["layers"]
@@ -124,11 +124,12 @@ def test_context_kv_store_matches_oracle(name):
             if blk not in touched:
                 assert np.array_equal(gk[blk], before[li][0][blk], equal_nan=True), (li, blk)
                 assert np.array_equal(gv[blk], before[li][1][blk], equal_nan=True), (li, blk)
-        # end to end against the oracle from the context states: K and V have unit scale
+        # end to end against the oracle from the context states, at the project's bar
+        # 2e-2 (1 + |ref|) (the staged checks above hold the tighter one-bf16-step bounds)
         for j, slot in enumerate(slots):
             got_k, got_v = gk[slot // 16, :, slot % 16, :], gv[slot // 16, :, :, slot % 16]
-            assert np.abs(got_k - ke[li, j]).max() <= 2.0 ** -4, (li, j, "K end to end")
-            assert np.abs(got_v - ve[li, j]).max() <= 2.0 ** -4, (li, j, "V end to end")
+            assert (np.abs(got_k - ke[li, j]) <= 2e-2 * (1 + np.abs(ke[li, j]))).all(), (li, j, "K end to end")
+            assert (np.abs(got_v - ve[li, j]) <= 2e-2 * (1 + np.abs(ve[li, j]))).all(), (li, j, "V end to end")
         exact = np.mean([np.array_equal(gk[s // 16, :, s % 16, :], nk[li][s // 16, :, s % 16, :])
                          for s in slots])
         say(f"[gpu-test] context {name} layer {li}: {exact:.0%} of K rows bit-exact")
