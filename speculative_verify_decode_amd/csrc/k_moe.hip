@@ -567,14 +567,16 @@ __device__ __forceinline__ ExpertRes expert_res(const uint8_t* codes, const uint
 // The wave's NU consecutive tiles from tile index `t0` of the expert; t0 < 0 loads zeros
 // without touching memory (a prefetch past the last unit), so the load count never
 // depends on a branch and every wait stays exact.
+// The offset is a per-lane part (the lane's bytes in a tile, or out of range) plus a
+// wave-uniform tile offset, so the loads need no per-lane address arithmetic.
 template <int NU>
 __device__ __forceinline__ void load_slice(Slice<NU>& s, const ExpertRes& r, int t0, int lane) {
+  const uint32_t lc = t0 < 0 ? kOob : 16u * lane, ls = t0 < 0 ? kOob : 2u * lane;
+  const uint32_t t = t0 < 0 ? 0u : (uint32_t)t0;
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
-    const uint32_t oc = t0 < 0 ? kOob : (uint32_t)(t0 + u) * 1024u + 16u * lane;
-    const uint32_t os = t0 < 0 ? kOob : (uint32_t)(t0 + u) * 128u + 2u * lane;
-    s.codes[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r.c, oc, 0, kStream));
-    s.scales[u] = __builtin_amdgcn_raw_buffer_load_b16(r.s, os, 0, kStream);
+    s.codes[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r.c, lc, (t + u) * 1024u, kStream));
+    s.scales[u] = __builtin_amdgcn_raw_buffer_load_b16(r.s, ls, (t + u) * 128u, kStream);
   }
 }
 
@@ -600,8 +602,8 @@ struct Unit {
 template <class M>
 __device__ __forceinline__ Unit unit_of(const M& m, int u, int NT) {
   Unit r;
-  r.gi = u / NT;
-  r.nt = u - r.gi * NT;
+  r.gi = __builtin_amdgcn_readfirstlane(u / NT);
+  r.nt = __builtin_amdgcn_readfirstlane(u - r.gi * NT);
   if constexpr (std::is_same<M, MoeMetaG>::value) {
     r.e = __builtin_amdgcn_readfirstlane(m.gexp[r.gi]);
     r.Te = __builtin_amdgcn_readfirstlane(m.gcnt[r.gi]);
@@ -614,10 +616,11 @@ __device__ __forceinline__ Unit unit_of(const M& m, int u, int NT) {
   return r;
 }
 
+// (wave-uniform: the walk's loop control then stays scalar)
 template <class M>
 __device__ __forceinline__ int groups_of(const M& m, int E) {
-  if constexpr (std::is_same<M, MoeMetaG>::value) return m.ng;
-  else return m.active[E];
+  if constexpr (std::is_same<M, MoeMetaG>::value) return __builtin_amdgcn_readfirstlane(m.ng);
+  else return __builtin_amdgcn_readfirstlane(m.active[E]);
 }
 
 // Workgroup w walks the contiguous unit range [begin, end): consecutive units mostly share
@@ -628,12 +631,19 @@ __device__ __forceinline__ void unit_range(int n_units, int& begin, int& end) {
 }
 
 // W13 (gate rows [0, I), up rows [I, 2I)) + SwiGLU.  K = H = 128 * NU * KS.
-template <int NCT, int NU, int KS, bool RT, bool GRP>
+//
+// Row block j (8 rows) of an expert group is one MFMA A tile: gate rows 8j .. 8j + 7 in tile
+// rows 0-7 and the up rows of the same index in tile rows 8-15, so one accumulator carries
+// both and each output lane finds its SwiGLU partner 32 lanes away.  A unit is the pair of
+// blocks 2p, 2p + 1, which together read packed gate tile p and up tile p.  Workgroups split
+// the walk in blocks, so a range may start or end half-way through a unit: the missing block
+// loads nothing and stores nothing.  With 19 experts of I = 1536 the longest range is then
+// 7.5 units against 7.125 on average, where whole units gave 8.
+template <int NU, int KS, bool RT, bool GRP>
 __global__ __launch_bounds__(64 * KS) void k_moe_w13(MoeArgs a) {
-  constexpr bool PB = NCT == 1;  // activations prefetched with the weights
   constexpr int NR = KS > 1 ? KS - 1 : 1;
   __shared__ MoeMetaT<GRP> meta;
-  __shared__ f32x4_t red[PB ? 2 : 1][NR][2][NCT][64];
+  __shared__ f32x4_t red[2][NR][2][64];
   if constexpr (RT) {
     // every workgroup routes from the router's logits (the same arithmetic, so the same
     // maps); workgroup 0 also writes the maps for the W2 kernel and the unpooler
@@ -655,8 +665,7 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w13(MoeArgs a) {
   } else {
     stage_meta(a, meta);
   }
-  const int NT = a.I >> 4;
-  const int n_units = groups_of(meta, a.E) * NT;
+  const int NT = a.I >> 4;  // units (16-row tile pairs) per expert group
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int i = lane & 15, G = lane >> 4;
@@ -666,85 +675,83 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w13(MoeArgs a) {
   // hi terms at x16, lo terms x16_lo_off bytes further in the same buffer (or none)
   const uint32_t xbytes = (uint32_t)(a.b * K * 2);
   const auto rx = rsrc(a.x16, a.x16_lo_off + xbytes);
+  // this lane's row of block 2p (+1) is row i % 8 (+8) of packed gate tile p (i < 8) or of
+  // up tile p (i >= 8); the up tiles follow the I / 16 gate tiles.  A load's offset is this
+  // per-lane constant (byte of the lane's row within tile 0 of its matrix half) plus a
+  // wave-uniform tile offset, so a unit's loads need no per-lane address arithmetic.
+  const int l_base = (lane & 48) + (i & 7);
+  const uint32_t lane_c = (i < 8 ? 0u : (uint32_t)(NT * KT) * 1024u) + 16u * l_base;
+  const uint32_t lane_s = (i < 8 ? 0u : (uint32_t)(NT * KT) * 128u) + 2u * l_base;
 
-  // lane's B byte offset for column tile c of unit U
-  auto b_off = [&](const Unit& U, int c) -> uint32_t {
-    const int slot = 8 * c + (i & 7);
+  // lane's B byte offset for unit U (column tile 0: at most 8 pooled rows per group)
+  auto b_off = [&](const Unit& U) -> uint32_t {
+    const int slot = i & 7;
     if (slot >= U.Te || (lo && a.x16_lo_off == 0)) return kOob;
     return (lo ? a.x16_lo_off : 0u) +
            (uint32_t)(((size_t)meta.tos[U.off + slot] * K + kw * 128 + 32 * G) * 2);
   };
-  // weights of unit U (valid == false: zeros, no memory traffic)
-  auto load_a = [&](Slice<NU>& sg, Slice<NU>& su, const Unit& U, bool valid) {
+  // weights of blocks 2 U.nt (+1) where valid (else zeros, no memory traffic: the
+  // out-of-range part of the offset is the per-lane one)
+  auto load_a = [&](Slice<NU>& sa, Slice<NU>& sb, const Unit& U, bool va, bool vb) {
     const ExpertRes r = expert_res(a.w13_codes, a.w13_scales, code_bytes, U.e);
-    const int t0 = U.nt * KT + kw;
-    load_slice<NU>(sg, r, valid ? t0 : -1, lane);
-    load_slice<NU>(su, r, valid ? t0 + NT * KT : -1, lane);
+    const uint32_t t0 = (uint32_t)(U.nt * KT + kw);
+    const uint32_t ca = va ? lane_c : kOob, cb = vb ? lane_c + 128u : kOob;
+    const uint32_t sa_o = va ? lane_s : kOob, sb_o = vb ? lane_s + 16u : kOob;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const uint32_t t = t0 + (uint32_t)u;
+      sa.codes[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r.c, ca, t * 1024u, kStream));
+      sb.codes[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r.c, cb, t * 1024u, kStream));
+      sa.scales[u] = __builtin_amdgcn_raw_buffer_load_b16(r.s, sa_o, t * 128u, kStream);
+      sb.scales[u] = __builtin_amdgcn_raw_buffer_load_b16(r.s, sb_o, t * 128u, kStream);
+    }
   };
-  auto load_b0 = [&](f16x8_t (&bx)[NU][4], const Unit& U) { load_bx<NU>(bx, rx, b_off(U, 0)); };
-  auto compute = [&](const Slice<NU>& sg, const Slice<NU>& su, f16x8_t (&bx0)[NU][4],
-                     const Unit& U, int buf) {
-    f32x4_t ag[NCT], au[NCT];
+  auto compute = [&](const Slice<NU>& sa, const Slice<NU>& sb, const f16x8_t (&bx)[NU][4],
+                     const Unit& U, bool va, bool vb, int buf) {
+    f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int c = 0; c < NCT; ++c) ag[c] = au[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const int nct = (U.Te + 7) >> 3;
+    for (int u = 0; u < NU; ++u) {
+      f16x8_t da[4], db[4];
+      sd::dequant_unit(sa.codes[u], sa.scales[u], da);
+      sd::dequant_unit(sb.codes[u], sb.scales[u], db);
 #pragma unroll
-    for (int c = 0; c < NCT; ++c) {
-      if (c >= nct) break;
-      f16x8_t bl[NU][4];
-      if (!PB) load_bx<NU>(bl, rx, b_off(U, c));
-      f16x8_t (&bx)[NU][4] = PB ? bx0 : bl;
-#pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        f16x8_t dg[4], du[4];
-        sd::dequant_unit(sg.codes[u], sg.scales[u], dg);
-        sd::dequant_unit(su.codes[u], su.scales[u], du);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          ag[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dg[m], bx[u][m], ag[c], 0, 0, 0);
-          au[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(du[m], bx[u][m], au[c], 0, 0, 0);
-        }
+      for (int m = 0; m < 4; ++m) {
+        acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(da[m], bx[u][m], acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(db[m], bx[u][m], acc[1], 0, 0, 0);
       }
     }
     if (KS > 1) {
       if (wave > 0) {
-#pragma unroll
-        for (int c = 0; c < NCT; ++c) {  // only the unit's column tiles
-          if (c >= nct) break;
-          red[buf][wave - 1][0][c][lane] = ag[c];
-          red[buf][wave - 1][1][c][lane] = au[c];
-        }
+        red[buf][wave - 1][0][lane] = acc[0];
+        red[buf][wave - 1][1][lane] = acc[1];
       }
       __syncthreads();
     }
     if (wave == 0) {
+      f32x4_t up[2];
 #pragma unroll
-      for (int c = 0; c < NCT; ++c) {
-        if (c >= nct) break;
+      for (int j = 0; j < 2; ++j) {
 #pragma unroll
-        for (int w = 0; w < KS - 1; ++w) {
-          ag[c] += red[buf][w][0][c][lane];
-          au[c] += red[buf][w][1][c][lane];
-        }
+        for (int w = 0; w < KS - 1; ++w) acc[j] += red[buf][w][j][lane];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {  // hi + lo columns
-          ag[c][r] += __shfl_xor(ag[c][r], 8, 64);
-          au[c][r] += __shfl_xor(au[c][r], 8, 64);
+        for (int r = 0; r < 4; ++r) {
+          acc[j][r] += __shfl_xor(acc[j][r], 8, 64);  // hi + lo columns
+          up[j][r] = __shfl_xor(acc[j][r], 32, 64);   // tile rows 8-15: the up rows
         }
       }
-      if (i < 8) {
+      const int slot = i;
+      if (i < 8 && G < 2 && slot < U.Te) {
         const float sc = SD_X16_UNSCALE * meta.g13[U.e];
-        const int n = U.nt * 16 + 4 * G;  // lane rows n .. n+3 of the gate (and up) block
 #pragma unroll
-        for (int c = 0; c < NCT; ++c) {
-          const int slot = 8 * c + i;
-          if (slot >= U.Te) continue;
+        for (int j = 0; j < 2; ++j) {
+          if (!(j == 0 ? va : vb)) continue;
+          const int n = (2 * U.nt + j) * 8 + 4 * G;  // lane rows n .. n+3 of the gate (and up) block
           const size_t o = (size_t)(U.off + slot) * a.I + n;
           _Float16 hh[4], hl[4];
           uint16_t hb[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float gv = ag[c][r] * sc, uv = au[c][r] * sc;
+            const float gv = acc[j][r] * sc, uv = up[j][r] * sc;
             const float h = gv / (1.0f + __expf(-gv)) * uv;
             sd::split_f16(h, hh[r], hl[r]);
             hb[r] = sd::f2bf(h);
@@ -759,39 +766,37 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w13(MoeArgs a) {
         }
       }
     }
-    if (!PB && KS > 1) __syncthreads();  // single-buffered reduction space
   };
 
-  Slice<NU> g0, u0, g1, u1;
-  f16x8_t bx[NU][4];  // one column tile's activations (unused without PB)
-  int u, end;
-  unit_range(n_units, u, end);
-  if (u >= end) return;
-  if constexpr (!PB && NU > 2) {  // several column tiles: their accumulators leave no room
-    for (; u < end; ++u) {        // to prefetch four-tile slices
-      const Unit U = unit_of(meta, u, NT);
-      load_a(g0, u0, U, true);
-      compute(g0, u0, bx, U, 0);
-    }
-    return;
-  }
+  // this workgroup's blocks [hb, he) in the walk, as units [u, end)
+  int hb, he;
+  unit_range(groups_of(meta, a.E) * 2 * NT, hb, he);
+  hb = __builtin_amdgcn_readfirstlane(hb);
+  he = __builtin_amdgcn_readfirstlane(he);
+  if (hb >= he) return;
+  int u = hb >> 1;
+  const int end = (he + 1) >> 1;
+  auto va_of = [&](int p) { return 2 * p >= hb && p < end; };
+  auto vb_of = [&](int p) { return 2 * p + 1 < he; };
+  Slice<NU> a0, b0, a1, b1;
+  f16x8_t bx[NU][4];  // the current group's activations
   // two-deep pipeline: every load is unconditional (a missing next unit loads zeros from
   // no memory), so the wait before each compute covers exactly the unit it uses
   Unit U0 = unit_of(meta, u, NT), U1;
   int bg = -1;  // expert group whose activations are in bx
-  load_a(g0, u0, U0, true);
+  load_a(a0, b0, U0, va_of(u), vb_of(u));
   while (true) {
-    if (PB && U0.gi != bg) { load_b0(bx, U0); bg = U0.gi; }
+    if (U0.gi != bg) { load_bx<NU>(bx, rx, b_off(U0)); bg = U0.gi; }
     const int n1 = u + 1;
     U1 = unit_of(meta, min(n1, end - 1), NT);
-    load_a(g1, u1, U1, n1 < end);
-    compute(g0, u0, bx, U0, 0);
+    load_a(a1, b1, U1, va_of(n1), vb_of(n1));
+    compute(a0, b0, bx, U0, va_of(u), vb_of(u), 0);
     if (n1 >= end) break;
-    if (PB && U1.gi != bg) { load_b0(bx, U1); bg = U1.gi; }
+    if (U1.gi != bg) { load_bx<NU>(bx, rx, b_off(U1)); bg = U1.gi; }
     const int n2 = n1 + 1;
     U0 = unit_of(meta, min(n2, end - 1), NT);
-    load_a(g0, u0, U0, n2 < end);
-    compute(g1, u1, bx, U1, PB ? 1 : 0);
+    load_a(a0, b0, U0, va_of(n2), vb_of(n2));
+    compute(a1, b1, bx, U1, va_of(n1), vb_of(n1), 1);
     if (n2 >= end) break;
     u = n2;
   }
@@ -885,6 +890,8 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w2(MoeArgs a) {
   f16x8_t bx[NU][4];  // column tile 0's activations of the unit being computed
   int u, end;
   unit_range(n_units, u, end);
+  u = __builtin_amdgcn_readfirstlane(u);
+  end = __builtin_amdgcn_readfirstlane(end);
   if (u >= end) return;
   Unit U0 = unit_of(meta, u, NT), U1;
   int bg = -1;
@@ -894,12 +901,14 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w2(MoeArgs a) {
     const int n1 = u + 1;
     U1 = unit_of(meta, min(n1, end - 1), NT);
     load_a(w1, U1, n1 < end);
+    __builtin_amdgcn_sched_barrier(0);  // the prefetch leaves before the compute starts
     compute(w0, bx, U0, 0);
     if (n1 >= end) break;
     if (!PB || U1.gi != bg) { load_b0(bx, U1); bg = U1.gi; }
     const int n2 = n1 + 1;
     U0 = unit_of(meta, min(n2, end - 1), NT);
     load_a(w0, U0, n2 < end);
+    __builtin_amdgcn_sched_barrier(0);
     compute(w1, bx, U1, PB ? 1 : 0);
     if (n2 >= end) break;
     u = n2;
@@ -988,9 +997,9 @@ hipError_t launch_experts(const MoeArgs& a, hipStream_t st) {
 #define SD_W13(NU, KS)                                                                     \
   if (!done && s13.nu == NU && s13.ks == KS) {                                             \
     if (a.route)                                                                           \
-      hipLaunchKernelGGL((k_moe_w13<1, NU, KS, true, GRP>), dim3(g13), dim3(64 * KS), 0, st, a); \
+      hipLaunchKernelGGL((k_moe_w13<NU, KS, true, GRP>), dim3(g13), dim3(64 * KS), 0, st, a); \
     else                                                                                   \
-      hipLaunchKernelGGL((k_moe_w13<1, NU, KS, false, GRP>), dim3(g13), dim3(64 * KS), 0, st, a); \
+      hipLaunchKernelGGL((k_moe_w13<NU, KS, false, GRP>), dim3(g13), dim3(64 * KS), 0, st, a); \
     done = true;                                                                          \
   }
   SD_SPLITS(SD_W13)
