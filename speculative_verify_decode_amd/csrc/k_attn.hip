@@ -8,8 +8,9 @@
 // metadata for one request verifying q tokens (plan, decode_metadata).  The verify rows
 // are causal: row j sees positions 0 .. p_j of its request.
 //
-// Work split: workgroup (chunk, kv head g, request r) covers `chunk_blocks` KV blocks; its
-// 4 waves take 32-token windows (two blocks) in turn.  In MFMA step c over the head dim,
+// Work split: workgroup (slot, kv head g) covers one chunk of KV blocks of one request (the
+// chunk map below assigns slots to requests); its 4 waves take 32-token windows (two
+// blocks) in turn.  In MFMA step c over the head dim,
 // lane group G holds dims 32c + 8G .. +7 of K and of Q (any dim order serves if both
 // operands share it), so each K load instruction reads 64 contiguous bytes of 16 rows.  Every window is read once and
 // shared by all QG = (Hq/Hkv) * q_rows queries of (r, g) through MFMA:
@@ -28,6 +29,7 @@ namespace {
 
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr int kMaxChunkBlocks = 2048;
+constexpr int kMaxReqChunks = 1024;  // chunks of one request (the combine's LDS statistics)
 constexpr int kQRows = 8;  // verify rows per request (the host accepts only 8)
 
 // cos and sin of the RoPE angle pos * freq: the angle is reduced modulo 2 pi in double (it
@@ -60,8 +62,71 @@ __device__ __forceinline__ ReqRows req_rows(const AttnArgs& a, int r) {
   return {s0, min(max(a.query_start[r + 1] - s0, 0), min(a.q_rows, a.b - s0))};
 }
 
-// Workgroup (chunk, kv head g, request r): blocks [chunk * cb, +cb) of the request, one
-// workgroup per CU at most.  The chunk's block ids (clamped to the pool) and the query
+// ceil(n / d) for n >= 0, d >= 1, with rd the fp32 reciprocal of d: the fp32 quotient is
+// close to floor(n / d) (within one below 2^20), and the remainder corrects it exactly.
+__device__ __forceinline__ int ceil_div_small(int n, int d, float rd) {
+  int q = (int)((float)n * rd);
+  int rem = n - q * d;
+  while (rem < 0) { q -= 1; rem += d; }
+  while (rem >= d) { q += 1; rem -= d; }
+  return q + (rem > 0 ? 1 : 0);
+}
+
+// How the KV blocks of several requests map onto the nslot chunk slots of a KV head.  Every
+// request's visible blocks (from its first visible block to its last) are cut into chunks of
+// one size cb: the smallest multiple of 8 blocks, at most cb_host, whose chunks fit the
+// slots, so the workgroups of long and short requests get near-equal work.  Request r owns
+// slots off .. off + nch - 1 (request order).  cb_host always fits: the host sizes it for
+// every request at max_seq_len.  Lane r of the calling wave holds request r's off and nch
+// (n_req <= 64); every wave that calls this derives the same map.
+struct ChunkMap {
+  int cb;
+  int off, nch;  // this lane's request (0, 0 for lanes past n_req)
+};
+__device__ ChunkMap chunk_map(const AttnArgs& a, int cb_host, int nslot) {
+  const int lane = threadIdx.x & 63;
+  int span = 0;
+  if (lane < a.n_req) {
+    const int L = min(a.seq_lens[lane], a.max_blocks * 16);
+    span = max(((L + 15) >> 4) - first_block(a, lane), 0);
+  }
+  int S = span, smax = span;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    S += __shfl_xor(S, o, 64);
+    smax = max(smax, __shfl_xor(smax, o, 64));
+  }
+  S = __builtin_amdgcn_readfirstlane(S);
+  smax = __builtin_amdgcn_readfirstlane(smax);
+  // candidate sizes cb0 + 8 lane, from the least that could fit (and gives no request more
+  // than kMaxReqChunks chunks)
+  const int cb0 = max(max(8, (((S + nslot - 1) / nslot) + 7) & ~7),
+                      (((smax + kMaxReqChunks - 1) / kMaxReqChunks) + 7) & ~7);
+  const int cand = cb0 + 8 * lane;
+  const float rc = 1.0f / (float)cand;
+  int need = 0;
+  for (int q = 0; q < a.n_req; ++q) need += ceil_div_small(__builtin_amdgcn_readlane(span, q), cand, rc);
+  const uint64_t fits = __builtin_amdgcn_ballot_w64(need <= nslot && cand <= cb_host);
+  ChunkMap m;
+  m.cb = fits != 0 ? cb0 + 8 * (int)__builtin_ctzll(fits) : cb_host;
+  m.nch = lane < a.n_req ? (span + m.cb - 1) / m.cb : 0;
+  int inc = m.nch;  // inclusive prefix sum over the lanes
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += v;
+  }
+  m.off = inc - m.nch;
+  // seq_lens beyond the host's max_seq_len could ask for more slots than there are: such
+  // chunks get none (the slot range of every request stays inside the nslot slots)
+  m.off = min(m.off, nslot);
+  m.nch = min(m.nch, nslot - m.off);
+  return m;
+}
+
+// Workgroup (slot, kv head g): chunk `chunk` of request r, blocks [chunk * cb, +cb) from the
+// request's first visible block (one request: r = 0, chunk = slot, cb = cb_host; several:
+// the chunk map's), one workgroup per CU at most.  The chunk's block ids (clamped to the pool) and the query
 // group (hi/lo, computed from the projection partials) are staged in LDS first; NP is the
 // number of K-slice partials.  Each of the 4 waves then streams 2-block windows
 // w = 2 * wave + 8 j, loading window j + 1 while window j is in the matrix cores.  Loads
@@ -70,12 +135,12 @@ __device__ __forceinline__ ReqRows req_rows(const AttnArgs& a, int r) {
 //
 // GEN selects the general form (a sliding window or partial drafts): the first visible
 // block and the request's rows then come from device metadata, one more scalar round trip
-// before the first window.  Without it the chunk's block range and rows follow from the
-// launch alone, and every scalar load the first two windows need (their four block ids,
-// seq_len) goes out in one batch right after the kernel arguments.
+// before the first window.  Without it, and with one request, the chunk's block range and
+// rows follow from the launch alone, and every scalar load the first two windows need
+// (their four block ids, seq_len) goes out in one batch right after the kernel arguments.
 template <int D, int NQT, bool GEN, int NP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void k_attn_split(AttnArgs a, int cb, int n_chunks) {
+void k_attn_split(AttnArgs a, int cb_host, int nslot) {
   constexpr int QG = 16 * NQT;
   constexpr int NC = D / 32;   // MFMA steps over the head dim
   constexpr int NDT = D / 16;  // output dim tiles
@@ -89,9 +154,21 @@ void k_attn_split(AttnArgs a, int cb, int n_chunks) {
   __shared__ __align__(16) uint16_t s_kn[kQRows][D], s_vn[kQRows][D];  // new tokens' K, V
   __shared__ int s_kok[kQRows];  // row j's new K/V is stored (its slot is not negative)
 
-  const int chunk = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
+  const int slot = blockIdx.x, g = blockIdx.y;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  // the slot's request and chunk: one request takes the slots as its chunks of cb_host
+  // blocks; several share them through the chunk map (an unused slot has no work)
+  int r = 0, chunk = slot, cb = cb_host;
+  if (a.n_req > 1) {  // uniform
+    const ChunkMap cm = chunk_map(a, cb_host, nslot);
+    const uint64_t own = __builtin_amdgcn_ballot_w64(lane < a.n_req && cm.off <= slot &&
+                                                     slot < cm.off + cm.nch);
+    if (own == 0) return;  // uniform per workgroup, before any barrier
+    r = (int)__builtin_ctzll(own);
+    chunk = slot - __builtin_amdgcn_readlane(cm.off, r);
+    cb = cm.cb;
+  }
   const int i = lane & 15, G = lane >> 4;
   const int group = a.Hq / a.Hkv;
   // chunks start at the request's first visible block (block 0 without a window)
@@ -472,7 +549,7 @@ void k_attn_split(AttnArgs a, int cb, int n_chunks) {
     for (int dt = 0; dt < NDT; ++dt) *(f32x4_t*)&s_acc[wave][qi][16 * dt + 4 * G] = acc[dt][qt] * f;
   }
   __syncthreads();
-  const size_t pidx = ((size_t)r * a.Hkv + g) * n_chunks + chunk;
+  const size_t pidx = (size_t)g * nslot + slot;
   float* pacc = a.part_acc + pidx * QG * D;
   float* pml = a.part_ml + pidx * QG * 2;
   for (int e = tid * 4; e < QG * D; e += 1024) {
@@ -491,15 +568,16 @@ void k_attn_split(AttnArgs a, int cb, int n_chunks) {
 
 // One workgroup of D threads per (query column, query head) of each request: LSE-combine
 // the chunks, normalise, apply the output gate o * sigmoid(o_gate), store bf16 hi/lo terms.
-// The first pass of chunk values (32 per thread), each thread's chunk statistics (one (m, l)
-// pair per load) and the gate are loaded before seq_len is known: they read the chunk slots
-// the launch allocates, and the slots past the request's chunk count are dropped by
-// selection afterwards, so whatever they hold never reaches the result.  Thread c turns
+// With one request, the first pass of chunk values (32 per thread), each thread's chunk
+// statistics (one (m, l) pair per load) and the gate are loaded before seq_len is known:
+// they read the chunk slots the launch allocates, and the slots past the request's chunk
+// count are dropped by selection afterwards, so whatever they hold never reaches the result
+// (with several, the chunk map comes first: its slots depend on every request's length).  Thread c turns
 // chunk c's statistics into its weight exp2(m_c - M) (in LDS) and w_c * l_c (block-summed).
 // GEN as for the split: partial drafts map the column to its row through query_start, and
 // columns past a request's rows exit after issuing their loads.
 template <bool GEN, int NP>
-__global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a, int cb, int n_chunks, int qg) {
+__global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a, int cb_host, int nslot, int qg) {
   constexpr int PASS = 32;
   __shared__ __align__(16) float s_w[1024];
   __shared__ float s_lc[1024];
@@ -510,13 +588,22 @@ __global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a, int cb, int n_
   const int group = a.Hq / a.Hkv;
   const int g = h / group, hh = h - g * group;
   const int qi = hh * a.q_rows + jr;
-  const size_t p0 = ((size_t)r * a.Hkv + g) * n_chunks;
+  // the request's chunk slots: with one request all nslot slots (the chunks past its end
+  // are dropped below); with several, the chunk map's
+  int off = 0, nmax = nslot, cbm = cb_host;
+  if (a.n_req > 1) {  // uniform
+    const ChunkMap cm = chunk_map(a, cb_host, nslot);
+    off = min(__builtin_amdgcn_readlane(cm.off, r), nslot - 1);
+    nmax = max(min(__builtin_amdgcn_readlane(cm.nch, r), nslot - off), 1);
+    cbm = cm.cb;
+  }
+  const size_t p0 = (size_t)g * nslot + off;
   const float* pa = a.part_acc + (p0 * qg + qi) * a.D + d;
   const size_t cs = (size_t)qg * a.D;  // chunk stride
   float vals[PASS];
 #pragma unroll
-  for (int u = 0; u < PASS; ++u) vals[u] = pa[min(u, n_chunks - 1) * cs];
-  const float2 ml0 = *(const float2*)&a.part_ml[((p0 + min(d, n_chunks - 1)) * qg + qi) * 2];
+  for (int u = 0; u < PASS; ++u) vals[u] = pa[min(u, nmax - 1) * cs];
+  const float2 ml0 = *(const float2*)&a.part_ml[((p0 + min(d, nmax - 1)) * qg + qi) * 2];
   const ReqRows rq = GEN ? req_rows(a, r) : ReqRows{r * a.q_rows, a.q_rows};
   const int t = rq.base + min(jr, max(rq.n - 1, 0));  // the step row of this column
   float gate = 0.f;  // the output gate, slices summed in order
@@ -529,8 +616,8 @@ __global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a, int cb, int n_
     for (int p = 0; p < NP; ++p) gate += gp[p];
   }
   const int L = min(a.seq_lens[r], a.max_blocks * 16);
-  const int nc = max(min((((L + 15) >> 4) - (GEN ? first_block(a, r) : 0) + cb - 1) / cb,
-                         n_chunks), 1);
+  const int nc = max(min((((L + 15) >> 4) - (GEN ? first_block(a, r) : 0) + cbm - 1) / cbm,
+                         nmax), 1);
   if (jr >= rq.n) return;  // uniform per workgroup, before any barrier
   // chunk statistics: thread c holds (m_c, l_c) of chunks c, c + D, ...
   // (the first chunk's pair is the one loaded above, kept out of the loop so it stays a
@@ -609,17 +696,20 @@ int attn_chunk_bound(const sd_dims& d, int n_req, int max_seq_len) {
 }
 
 hipError_t launch_attention(const AttnArgs& a, const AttnPlan& p, hipStream_t st) {
-  const dim3 grid(p.n_chunks, a.Hkv, a.n_req), block(256);
+  // nslot chunk slots per KV head: as many workgroups as n_req requests of n_chunks chunks
+  const int nslot = p.n_chunks * a.n_req;
+  if (p.n_chunks > kMaxReqChunks) return hipErrorInvalidValue;
+  const dim3 grid(nslot, a.Hkv), block(256);
   const bool gen = a.window > 0 || a.query_start != nullptr;
   if (a.nparts != 1 && a.nparts != 4) return hipErrorInvalidValue;
 #define SD_ATTN_NP(DD, NQ, GN)                                                             \
   do {                                                                                     \
     if (a.nparts == 4)                                                                     \
       hipLaunchKernelGGL((k_attn_split<DD, NQ, GN, 4>), grid, block, 0, st, a,             \
-                         p.chunk_blocks, p.n_chunks);                                      \
+                         p.chunk_blocks, nslot);                                           \
     else                                                                                   \
       hipLaunchKernelGGL((k_attn_split<DD, NQ, GN, 1>), grid, block, 0, st, a,             \
-                         p.chunk_blocks, p.n_chunks);                                      \
+                         p.chunk_blocks, nslot);                                           \
   } while (0)
 #define SD_ATTN(DD, NQ)                                                                    \
   do {                                                                                     \
@@ -639,7 +729,7 @@ hipError_t launch_attention(const AttnArgs& a, const AttnPlan& p, hipStream_t st
   const dim3 cgrid(a.n_req * a.q_rows * a.Hq), cblock(a.D);
 #define SD_COMB(GN, NPV)                                                                   \
   hipLaunchKernelGGL((k_attn_combine<GN, NPV>), cgrid, cblock, 0, st, a, p.chunk_blocks,     \
-                     p.n_chunks, p.qg)
+                     nslot, p.qg)
   if (gen && a.nparts == 4) SD_COMB(true, 4);
   else if (gen) SD_COMB(true, 1);
   else if (a.nparts == 4) SD_COMB(false, 4);

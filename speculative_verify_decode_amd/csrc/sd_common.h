@@ -219,8 +219,8 @@ struct AttnArgs {
   const int* query_start;     // null: q_rows rows per request; else [n_req + 1] row starts
   int b;                      // rows of the step (query_start indices are clamped below it)
   float scale;
-  float* part_acc;            // [n_req * Hkv * n_chunks, qg, D]
-  float* part_ml;             // [n_req * Hkv * n_chunks, qg, 2]
+  float* part_acc;            // [Hkv, nslot = n_req * n_chunks, qg, D] (slot-major per head)
+  float* part_ml;             // [Hkv, nslot, qg, 2]
   const float* gate;          // row t of partial p at gate + p * part_stride + t * gate_stride
   int gate_stride;
   uint16_t* out;              // bf16 hi terms of the gated output [b, Hq * D]

@@ -119,10 +119,7 @@ def test_boundary_dualnorm_modes(name):
 
 
 # ------------------------------------------------------------------------ attention
-@pytest.mark.timeout(900)
-@pytest.mark.parametrize("name", ALL)
-def test_attn_verify_matches_oracle(name):
-    wk = workload(name)
+def check_attn_verify(wk, name):
     r = runner(wk)
     lay, d, b = wk["layers"][0], wk["dims"], r.b
     say(f"[gpu-test] attn_verify {name}")
@@ -152,6 +149,27 @@ def test_attn_verify_matches_oracle(name):
         mask = ~np.isnan(want)
         assert np.array_equal(np.isnan(got), ~mask), key
         assert_close(got[mask], want[mask], key)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ALL)
+def test_attn_verify_matches_oracle(name):
+    check_attn_verify(workload(name), name)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("ctx", [
+    (30000, 8, 16, 17, 4096, 9, 1000, 12000),  # one long request among minimal ones
+    (8, 8, 8, 8, 8, 8, 8, 24576),              # nearly all blocks in the last request
+    (2048,) * 8,                               # equal lengths
+])
+def test_attn_verify_skewed_request_lengths(ctx):
+    """Several requests share each KV head's chunk slots in proportion to their lengths, so
+    the chunk size differs from the host's (sized for every request at max_seq_len) and
+    requests own different slot counts, down to a single chunk of one block."""
+    w = synth.with_overrides(synth.WORKLOADS["h4096_b64_ragged"], ctx=ctx,
+                             name=f"h4096_skew_{ctx[0]}_{ctx[-1]}")
+    check_attn_verify(synth.make_workload(w), w.name)
 
 
 @pytest.mark.timeout(900)
