@@ -154,7 +154,10 @@ void k_attn_split(AttnArgs a, int cb_host, int nslot) {
   __shared__ __align__(16) uint16_t s_kn[kQRows][D], s_vn[kQRows][D];  // new tokens' K, V
   __shared__ int s_kok[kQRows];  // row j's new K/V is stored (its slot is not negative)
 
-  const int slot = blockIdx.x, g = blockIdx.y;
+  // (slot, head) from the XCD rank: the nslot workgroups of a KV head share an XCD, so the
+  // head's projection partials (read by every slot of the head) fill one L2 once
+  const int rank = xcd_rank(blockIdx.y * nslot + blockIdx.x, nslot * gridDim.y);
+  const int slot = rank % nslot, g = rank / nslot;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   // the slot's request and chunk: one request takes the slots as its chunks of cb_host

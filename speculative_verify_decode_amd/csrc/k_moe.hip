@@ -625,9 +625,13 @@ __device__ __forceinline__ int groups_of(const M& m, int E) {
 
 // Workgroup w walks the contiguous unit range [begin, end): consecutive units mostly share
 // an expert group, so the activation operand is reloaded only when the group changes.
+// Ranges go out XCD by XCD: the workgroups of one XCD walk one contiguous part of the
+// units, so when an expert's weights are walked once per expert group, the groups' reads
+// of a tile come from workgroups of one XCD at about the same time and share its L2.
 __device__ __forceinline__ void unit_range(int n_units, int& begin, int& end) {
-  begin = (int)(((long)blockIdx.x * n_units) / gridDim.x);
-  end = (int)(((long)(blockIdx.x + 1) * n_units) / gridDim.x);
+  const int r = xcd_rank(blockIdx.x, gridDim.x);
+  begin = (int)(((long)r * n_units) / gridDim.x);
+  end = (int)(((long)(r + 1) * n_units) / gridDim.x);
 }
 
 // W13 (gate rows [0, I), up rows [I, 2I)) + SwiGLU.  K = H = 128 * NU * KS.
@@ -720,50 +724,47 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w13(MoeArgs a) {
         acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(db[m], bx[u][m], acc[1], 0, 0, 0);
       }
     }
+    // block j's sum is finished by wave j (one wave when KS == 1): every other wave leaves
+    // its partial of the block in LDS, in the block's slot order of the other waves
+    const int jw = KS > 1 ? (wave < 2 ? wave : -1) : 0;  // the block this wave finishes
     if (KS > 1) {
-      if (wave > 0) {
-        red[buf][wave - 1][0][lane] = acc[0];
-        red[buf][wave - 1][1][lane] = acc[1];
-      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        if (wave != j) red[buf][wave - (wave > j ? 1 : 0)][j][lane] = acc[j];
       __syncthreads();
     }
-    if (wave == 0) {
-      f32x4_t up[2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < 2; ++j) {
+      if (KS > 1 ? jw != j : false) continue;  // wave-uniform
+      f32x4_t v = acc[j], up;
 #pragma unroll
-        for (int w = 0; w < KS - 1; ++w) acc[j] += red[buf][w][j][lane];
+      for (int w = 0; w < KS - 1; ++w) v += red[buf][w][j][lane];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          acc[j][r] += __shfl_xor(acc[j][r], 8, 64);  // hi + lo columns
-          up[j][r] = __shfl_xor(acc[j][r], 32, 64);   // tile rows 8-15: the up rows
-        }
+      for (int r = 0; r < 4; ++r) {
+        v[r] += __shfl_xor(v[r], 8, 64);  // hi + lo columns
+        up[r] = __shfl_xor(v[r], 32, 64);  // tile rows 8-15: the up rows
       }
       const int slot = i;
-      if (i < 8 && G < 2 && slot < U.Te) {
+      if (i < 8 && G < 2 && slot < U.Te && (j == 0 ? va : vb)) {
         const float sc = SD_X16_UNSCALE * meta.g13[U.e];
+        const int n = (2 * U.nt + j) * 8 + 4 * G;  // lane rows n .. n+3 of the gate (and up) block
+        const size_t o = (size_t)(U.off + slot) * a.I + n;
+        _Float16 hh[4], hl[4];
+        uint16_t hb[4];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          if (!(j == 0 ? va : vb)) continue;
-          const int n = (2 * U.nt + j) * 8 + 4 * G;  // lane rows n .. n+3 of the gate (and up) block
-          const size_t o = (size_t)(U.off + slot) * a.I + n;
-          _Float16 hh[4], hl[4];
-          uint16_t hb[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float gv = acc[j][r] * sc, uv = up[j][r] * sc;
-            const float h = gv / (1.0f + __expf(-gv)) * uv;
-            sd::split_f16(h, hh[r], hl[r]);
-            hb[r] = sd::f2bf(h);
-          }
-          *(u32x2_t*)(a.h16 + o) = u32x2_t{__builtin_bit_cast(uint32_t, f16x2_t{hh[0], hh[1]}),
-                                           __builtin_bit_cast(uint32_t, f16x2_t{hh[2], hh[3]})};
-          *(u32x2_t*)(a.h16_lo + o) = u32x2_t{__builtin_bit_cast(uint32_t, f16x2_t{hl[0], hl[1]}),
-                                              __builtin_bit_cast(uint32_t, f16x2_t{hl[2], hl[3]})};
-          if (a.h_bf16 != nullptr)
-            *(u32x2_t*)(a.h_bf16 + o) = u32x2_t{hb[0] | ((uint32_t)hb[1] << 16),
-                                                hb[2] | ((uint32_t)hb[3] << 16)};
+        for (int r = 0; r < 4; ++r) {
+          const float gv = v[r] * sc, uv = up[r] * sc;
+          const float h = gv / (1.0f + __expf(-gv)) * uv;
+          sd::split_f16(h, hh[r], hl[r]);
+          hb[r] = sd::f2bf(h);
         }
+        *(u32x2_t*)(a.h16 + o) = u32x2_t{__builtin_bit_cast(uint32_t, f16x2_t{hh[0], hh[1]}),
+                                         __builtin_bit_cast(uint32_t, f16x2_t{hh[2], hh[3]})};
+        *(u32x2_t*)(a.h16_lo + o) = u32x2_t{__builtin_bit_cast(uint32_t, f16x2_t{hl[0], hl[1]}),
+                                            __builtin_bit_cast(uint32_t, f16x2_t{hl[2], hl[3]})};
+        if (a.h_bf16 != nullptr)
+          *(u32x2_t*)(a.h_bf16 + o) = u32x2_t{hb[0] | ((uint32_t)hb[1] << 16),
+                                              hb[2] | ((uint32_t)hb[3] << 16)};
       }
     }
   };

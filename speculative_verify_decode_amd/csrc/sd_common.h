@@ -115,6 +115,16 @@ __device__ __forceinline__ void dequant_unit(u32x4_t codes, uint32_t scales2, f1
 
 }  // namespace sd
 
+// Workgroups are dispatched round-robin over the chip's 8 XCDs (workgroup w on XCD w % 8),
+// and each XCD has its own L2.  xcd_rank(w, G) renumbers the G workgroups XCD by XCD (the
+// first XCD's workgroups first, in dispatch order), so that workgroups given neighbouring
+// ranks share an L2 and data they both read is fetched into it once.
+__device__ __forceinline__ int xcd_rank(int w, int G) {
+  const int x = w & 7, l = w >> 3;
+  // XCD x' holds (G - x' + 7) / 8 workgroups; those of XCDs below x come first
+  return x * (G >> 3) + min(x, G & 7) + l;
+}
+
 // ---------------------------------------------------------------------------- launches
 // Every launcher enqueues on `st` and returns the launch status (hipGetLastError).
 
