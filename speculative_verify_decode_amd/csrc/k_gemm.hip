@@ -141,22 +141,26 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_res(GemmArgs a, int ntiles) {
 #pragma unroll
       for (int c = 0; c < NCT; ++c)
         acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[u], bv[c][u], acc[c], 0, 0, 0);
-    if (wave > 0) {
+    // column tile c is finished by wave c % NW: the other waves leave their partials of it
+    // in LDS (in their wave order), so with several column tiles the sums and stores are
+    // spread over the waves instead of all falling on one
 #pragma unroll
-      for (int c = 0; c < NCT; ++c) red[buf][wave - 1][c][lane] = acc[c];
+    for (int c = 0; c < NCT; ++c) {
+      const int o = c % NW;
+      if (wave != o) red[buf][wave - (wave > o ? 1 : 0)][c][lane] = acc[c];
     }
     __syncthreads();
-    if (wave == 0) {
 #pragma unroll
-      for (int c = 0; c < NCT; ++c) {
+    for (int c = 0; c < NCT; ++c) {
+      if (wave != c % NW) continue;  // wave-uniform
+      f32x4_t v = acc[c];
 #pragma unroll
-        for (int w = 0; w < NW - 1; ++w) acc[c] += red[buf][w][c][lane];
-        if (SPLIT) {
+      for (int w = 0; w < NW - 1; ++w) v += red[buf][w][c][lane];
+      if (SPLIT) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[c][r] += __shfl_xor(acc[c][r], 8, 64);
-        }
-        if (!SPLIT || i < 8) store_tile<MODE>(ap, RPC * c + m, tile, ntiles, g, acc[c]);
+        for (int r = 0; r < 4; ++r) v[r] += __shfl_xor(v[r], 8, 64);
       }
+      if (!SPLIT || i < 8) store_tile<MODE>(ap, RPC * c + m, tile, ntiles, g, v);
     }
   };
   int t = grp;
