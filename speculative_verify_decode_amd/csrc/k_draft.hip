@@ -13,22 +13,9 @@
 
 namespace {
 
-template <int VW>
-struct VecF;
-template <> struct VecF<1> { typedef float T; };
-template <> struct VecF<2> { typedef f32x2_t T; };
-template <> struct VecF<4> { typedef f32x4_t T; };
+using sd::store16;
+using sd::VecF;
 
-template <int VW>
-__device__ __forceinline__ void store_bf16(uint16_t* p, const uint16_t* v) {
-  if constexpr (VW == 4) {
-    *(u32x2_t*)p = u32x2_t{v[0] | ((uint32_t)v[1] << 16), v[2] | ((uint32_t)v[3] << 16)};
-  } else if constexpr (VW == 2) {
-    *(uint32_t*)p = v[0] | ((uint32_t)v[1] << 16);
-  } else {
-    *p = v[0];
-  }
-}
 
 // bf16 value of an fp32 (round to nearest even), as fp32
 __device__ __forceinline__ float rbf(float x) { return sd::bf2f(sd::f2bf(x)); }
@@ -109,7 +96,7 @@ __global__ __launch_bounds__(256) void k_draft_norm(int H, float* __restrict__ s
       uint16_t o[VW];
 #pragma unroll
       for (int j = 0; j < VW; ++j) o[j] = sd::f2bf(s[v * VW + j] * r * gq[v * VW + j]);
-      store_bf16<VW>(out + base + (v * 256 + tid) * VW, o);
+      store16<VW>(out + base + (v * 256 + tid) * VW, o);
     }
   }
 }
@@ -136,8 +123,8 @@ __global__ __launch_bounds__(256) void k_swiglu_dense(int b, int I, const float*
   uint16_t hi[4], lo[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) sd::split_bf16(g[j] / (1.0f + __expf(-g[j])) * u[j], hi[j], lo[j]);
-  store_bf16<4>(h + e, hi);
-  store_bf16<4>(h_lo + e, lo);
+  store16<4>(h + e, hi);
+  store16<4>(h_lo + e, lo);
 }
 
 // Context rows: x[l, row] = bf16(RMSNorm(bf16(RMSNorm(states[row]; g_hidden)); g_pre[l])).

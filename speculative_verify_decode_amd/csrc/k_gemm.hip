@@ -23,22 +23,18 @@
 
 namespace {
 
-// Buffer resource over [p, p + bytes): loads past `bytes` return 0 and touch no memory.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
-}
+using sd::kOob;
+using sd::kStream;
+using sd::rsrc;
+
 
 __device__ __forceinline__ bf16x8_t buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
-// Weights are read once per step: non-temporal loads (cache policy bit 1) stream them
-// without displacing reusable lines, which measurably raises the achieved HBM rate.
-constexpr int kStream = 2;
 __device__ __forceinline__ bf16x8_t buf_load8_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kStream));
 }
 
-constexpr uint32_t kOob = 0x80000000u;  // a byte offset past every activation buffer
 
 // Byte offset of the lane's activation row `m` at column k (kOob when m >= M).
 __device__ __forceinline__ uint32_t x_off(int m, int M, int K, int k) {

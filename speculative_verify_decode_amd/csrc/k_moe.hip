@@ -16,19 +16,15 @@
 
 namespace {
 
+using sd::kOob;
+using sd::kStream;
+using sd::rsrc;
+using sd::store16;
+
 // ---------------------------------------------------------------- router + routing + pooler
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
-}
-
-constexpr uint32_t kOob = 0x80000000u;  // a byte offset past every activation buffer
-
 __device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
-// Weights are read once per step: non-temporal loads (cache policy bit 1) stream them
-// without displacing reusable lines, which measurably raises the achieved HBM rate.
-constexpr int kStream = 2;
 
 // Phase 1, every workgroup: partial logits of one 16-expert tile over 256 columns of H
 // (4 waves x 2 MFMA steps; rows as bf16 hi/lo terms in columns 0-7 / 8-15 of NCT tiles),
@@ -382,16 +378,6 @@ __device__ __forceinline__ void load_f32v(const float* p, float* out) {
   }
 }
 
-template <int VW>
-__device__ __forceinline__ void store16v(uint16_t* p, const uint16_t* v) {
-  if constexpr (VW == 4) {
-    *(u32x2_t*)p = u32x2_t{v[0] | ((uint32_t)v[1] << 16), v[2] | ((uint32_t)v[3] << 16)};
-  } else if constexpr (VW == 2) {
-    *(uint32_t*)p = v[0] | ((uint32_t)v[1] << 16);
-  } else {
-    *p = v[0];
-  }
-}
 
 template <int EPT, int NB, int RS>
 __global__ __launch_bounds__(256) void k_norm_router(NormRouterArgs A) {
@@ -482,11 +468,11 @@ __global__ __launch_bounds__(256) void k_norm_router(NormRouterArgs A) {
       sd::split_f16(x[v * VW + jj], h16[jj], l16[jj]);
     }
     if (A.out != nullptr) {
-      store16v<VW>(A.out + i0, hi);
-      store16v<VW>(A.out_lo + i0, lo);
+      store16<VW>(A.out + i0, hi);
+      store16<VW>(A.out_lo + i0, lo);
     }
-    store16v<VW>((uint16_t*)A.x16 + i0, (const uint16_t*)h16);
-    store16v<VW>((uint16_t*)A.x16_lo + i0, (const uint16_t*)l16);
+    store16<VW>((uint16_t*)A.x16 + i0, (const uint16_t*)h16);
+    store16<VW>((uint16_t*)A.x16_lo + i0, (const uint16_t*)l16);
   }
   __syncthreads();
   // logits of the part's experts from the normalised row: fp32 products, lane sums over
@@ -621,6 +607,18 @@ template <class M>
 __device__ __forceinline__ int groups_of(const M& m, int E) {
   if constexpr (std::is_same<M, MoeMetaG>::value) return __builtin_amdgcn_readfirstlane(m.ng);
   else return __builtin_amdgcn_readfirstlane(m.active[E]);
+}
+
+// The unit after U in the walk: the next tile of U's group, or the first tile of the next
+// group (only then are the maps in LDS read again).  U must not be the walk's last unit.
+template <class M>
+__device__ __forceinline__ Unit next_unit(const M& m, const Unit& U, int NT) {
+  if (U.nt + 1 < NT) {  // wave-uniform
+    Unit V = U;
+    V.nt = U.nt + 1;
+    return V;
+  }
+  return unit_of(m, (U.gi + 1) * NT, NT);
 }
 
 // Workgroup w walks the contiguous unit range [begin, end): consecutive units mostly share
@@ -789,13 +787,13 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w13(MoeArgs a) {
   while (true) {
     if (U0.gi != bg) { load_bx<NU>(bx, rx, b_off(U0)); bg = U0.gi; }
     const int n1 = u + 1;
-    U1 = unit_of(meta, min(n1, end - 1), NT);
+    U1 = n1 < end ? next_unit(meta, U0, NT) : U0;  // past the end: loads nothing
     load_a(a1, b1, U1, va_of(n1), vb_of(n1));
     compute(a0, b0, bx, U0, va_of(u), vb_of(u), 0);
     if (n1 >= end) break;
     if (U1.gi != bg) { load_bx<NU>(bx, rx, b_off(U1)); bg = U1.gi; }
     const int n2 = n1 + 1;
-    U0 = unit_of(meta, min(n2, end - 1), NT);
+    U0 = n2 < end ? next_unit(meta, U1, NT) : U1;
     load_a(a0, b0, U0, va_of(n2), vb_of(n2));
     compute(a1, b1, bx, U1, va_of(n1), vb_of(n1), 1);
     if (n2 >= end) break;
@@ -900,14 +898,14 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w2(MoeArgs a) {
   while (true) {
     if (!PB || U0.gi != bg) { load_b0(bx, U0); bg = U0.gi; }
     const int n1 = u + 1;
-    U1 = unit_of(meta, min(n1, end - 1), NT);
+    U1 = n1 < end ? next_unit(meta, U0, NT) : U0;  // past the end: loads nothing
     load_a(w1, U1, n1 < end);
     __builtin_amdgcn_sched_barrier(0);  // the prefetch leaves before the compute starts
     compute(w0, bx, U0, 0);
     if (n1 >= end) break;
     if (!PB || U1.gi != bg) { load_b0(bx, U1); bg = U1.gi; }
     const int n2 = n1 + 1;
-    U0 = unit_of(meta, min(n2, end - 1), NT);
+    U0 = n2 < end ? next_unit(meta, U1, NT) : U1;
     load_a(w0, U0, n2 < end);
     __builtin_amdgcn_sched_barrier(0);
     compute(w1, bx, U1, PB ? 1 : 0);

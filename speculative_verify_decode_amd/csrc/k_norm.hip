@@ -10,23 +10,9 @@
 
 namespace {
 
-// VW consecutive 16-bit values as one store (VW = 1, 2 or 4).
-template <int VW>
-__device__ __forceinline__ void store16(uint16_t* p, const uint16_t* v) {
-  if constexpr (VW == 4) {
-    *(u32x2_t*)p = u32x2_t{v[0] | ((uint32_t)v[1] << 16), v[2] | ((uint32_t)v[3] << 16)};
-  } else if constexpr (VW == 2) {
-    *(uint32_t*)p = v[0] | ((uint32_t)v[1] << 16);
-  } else {
-    *p = v[0];
-  }
-}
+using sd::store16;
+using sd::VecF;
 
-template <int VW>
-struct VecT;
-template <> struct VecT<1> { typedef float T; };
-template <> struct VecT<2> { typedef f32x2_t T; };
-template <> struct VecT<4> { typedef f32x4_t T; };
 
 // H = 256 * EPT.  Thread tid owns NV vectors of VW consecutive elements, vector v at
 // element (v * 256 + tid) * VW, so every load is coalesced and as wide as H allows.  All
@@ -52,7 +38,7 @@ __global__ __launch_bounds__(256) void k_dualnorm(int H, float* __restrict__ str
                                                   float* __restrict__ aux) {
   constexpr int VW = EPT % 4 == 0 ? 4 : (EPT % 2 == 0 ? 2 : 1);
   constexpr int NV = EPT / VW;
-  typedef typename VecT<VW>::T V;
+  typedef typename VecF<VW>::T V;
   __shared__ float red[4];
   const int row = blockIdx.x, tid = threadIdx.x;
   if (zero != nullptr && row == 0 && tid == 0) *zero = 0;

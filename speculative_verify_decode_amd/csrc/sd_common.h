@@ -31,6 +31,35 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 namespace sd {
 
+// Buffer resource over [p, p + bytes): loads at offsets past `bytes` return 0 and touch no
+// memory (the range check), so an out-of-range offset is a load with no traffic.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
+constexpr uint32_t kOob = 0x80000000u;  // a byte offset past every buffer the kernels read
+// Weights and K/V are read once per step: non-temporal loads (cache policy bit 1) stream
+// them without displacing reusable lines, which measurably raises the achieved HBM rate.
+constexpr int kStream = 2;
+
+// VW consecutive 16-bit values as one store (VW = 1, 2 or 4).
+template <int VW>
+__device__ __forceinline__ void store16(uint16_t* p, const uint16_t* v) {
+  if constexpr (VW == 4) {
+    *(u32x2_t*)p = u32x2_t{v[0] | ((uint32_t)v[1] << 16), v[2] | ((uint32_t)v[3] << 16)};
+  } else if constexpr (VW == 2) {
+    *(uint32_t*)p = v[0] | ((uint32_t)v[1] << 16);
+  } else {
+    *p = v[0];
+  }
+}
+
+// fp32 vector of VW lanes (VW = 1, 2 or 4).
+template <int VW>
+struct VecF;
+template <> struct VecF<1> { typedef float T; };
+template <> struct VecF<2> { typedef f32x2_t T; };
+template <> struct VecF<4> { typedef f32x4_t T; };
+
 __device__ __forceinline__ float bf2f(uint16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
 
 // fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
