@@ -114,7 +114,7 @@ int check_rows(const sd_dims* d, int b) {
 int requests_of(const sd_dims* d, int b) { return (b + d->q_rows - 1) / d->q_rows; }
 
 struct Ws {
-  size_t x_a, x_a_lo, qkv, part_acc, part_ml, o, o_lo, a, x_m, x_m_lo, x16,
+  size_t x_a, x_a_lo, s1, qkv, part_acc, part_ml, o, o_lo, a, x_m, x_m_lo, x16,
       x16_lo, zpart, counter, ids, w, counts, offsets, slot_of, tos, active, h16, h16_lo, y, total;
 };
 
@@ -132,6 +132,7 @@ Ws ws_layout(const sd_dims& d, int b, int n_req, int max_seq_len) {
   auto take = [&](size_t bytes) { size_t at = o; o += up(bytes); return at; };
   w.x_a = take(B * H * 2);
   w.x_a_lo = take(B * H * 2);
+  w.s1 = take(B * H * 4);
   w.qkv = take(kDenseSplit * B * N * 4);
   w.part_acc = take(parts * p.qg * D * 4);
   w.part_ml = take(parts * p.qg * 2 * 4);
@@ -428,7 +429,7 @@ int sd_boundary_dualnorm(const sd_dims* dims, int32_t b, float* stream, const fl
       (aux != nullptr && !aligned16(aux)))
     return fail(SD_EINVAL, "stream, branch, gains, out16 and aux must be 16-byte aligned");
   _Float16* x16 = (_Float16*)out16;
-  SD_LAUNCH(launch_dualnorm(b, dims->hidden, stream, (const float*)branch, 1,
+  SD_LAUNCH(launch_dualnorm(b, dims->hidden, stream, stream, (const float*)branch, 1,
                             (const uint16_t*)front_embed, g_post, g_pre, dims->eps,
                             (uint16_t*)out, nullptr, x16,
                             x16 ? x16 + (size_t)b * dims->hidden : nullptr, nullptr, aux,
@@ -571,14 +572,17 @@ int layer_step_impl(const sd_dims* dims, int32_t b, float* stream, const float* 
   const int H = dims->hidden;
   uint16_t* x_a = at<uint16_t>(ws, L.x_a);
   uint16_t* x_a_lo = at<uint16_t>(ws, L.x_a_lo);
+  // the stream after the input boundary: the attention boundary reads it here and writes the
+  // caller's stream, so no kernel of the step updates a row that another workgroup still reads
+  float* s1 = at<float>(ws, L.s1);
   if (pool_in != nullptr) {
-    SD_LAUNCH(launch_dualnorm(b, H, stream, pool_in->y_slots, 1, nullptr, w->g_post_prev,
+    SD_LAUNCH(launch_dualnorm(b, H, stream, s1, pool_in->y_slots, 1, nullptr, w->g_post_prev,
                               w->g_pre_attn, dims->eps, x_a, x_a_lo, nullptr, nullptr,
                               at<int>(ws, L.counter), aux, st, pool_in->route->topk_w,
                               pool_in->route->slot_of, dims->top_k),
               "input boundary (gathering the pooled branch)");
   } else {
-    SD_LAUNCH(launch_dualnorm(b, H, stream, (const float*)branch_in, 1,
+    SD_LAUNCH(launch_dualnorm(b, H, stream, s1, (const float*)branch_in, 1,
                               (const uint16_t*)front_embed, w->g_post_prev, w->g_pre_attn,
                               dims->eps, x_a, x_a_lo, nullptr, nullptr, at<int>(ws, L.counter),
                               aux, st),
@@ -597,7 +601,8 @@ int layer_step_impl(const sd_dims* dims, int32_t b, float* stream, const float* 
   const RouterArgs* route_in_experts = nullptr;  // the expert kernel routes from the logits
   if (norm_router_parts(H, dims->n_experts, b, dims->top_k) > 0 && (a_parts == 1 || a_parts == 4)) {
     // attention boundary and the router's product in one launch
-    nr.H = H; nr.branch = a; nr.branch_stride = (size_t)b * H; nr.stream = stream;
+    nr.H = H; nr.branch = a; nr.branch_stride = (size_t)b * H; nr.stream_in = s1;
+    nr.stream = stream;
     nr.g_post = w->g_post_attn; nr.g_pre = w->g_pre_ffn; nr.eps = dims->eps;
     nr.out = nullptr; nr.out_lo = nullptr;  // the bf16 row feeds only the router
     nr.x16 = x16; nr.x16_lo = x16_lo;
@@ -606,7 +611,7 @@ int layer_step_impl(const sd_dims* dims, int32_t b, float* stream, const float* 
     SD_LAUNCH(launch_norm_router(nr, a_parts, st), "attention boundary and router");
     route_in_experts = &nr.r;
   } else {
-    SD_LAUNCH(launch_dualnorm(b, H, stream, a, a_parts, nullptr, w->g_post_attn, w->g_pre_ffn,
+    SD_LAUNCH(launch_dualnorm(b, H, s1, stream, a, a_parts, nullptr, w->g_post_attn, w->g_pre_ffn,
                               dims->eps, x_m, x_m_lo, x16, x16_lo, at<int>(ws, L.counter),
                               nullptr, st),
               "attention boundary");

@@ -405,7 +405,7 @@ __global__ __launch_bounds__(256) void k_norm_router(NormRouterArgs A) {
     const int i0 = (v * 256 + tid) * VW;
 #pragma unroll
     for (int p = 0; p < NB; ++p) load_f32v<VW>(A.branch + p * A.branch_stride + base + i0, &pb[p][v * VW]);
-    load_f32v<VW>(A.stream + base + i0, &s[v * VW]);
+    load_f32v<VW>(A.stream_in + base + i0, &s[v * VW]);
     load_f32v<VW>(A.g_post + i0, &gp[v * VW]);
     load_f32v<VW>(A.g_pre + i0, &gq[v * VW]);
   }
@@ -1047,6 +1047,8 @@ hipError_t launch_norm_router(const NormRouterArgs& a, int nbranch, hipStream_t 
   const int rs = norm_router_parts(a.H, a.r.E, a.r.b, a.r.k);
   if (rs == 0 || (nbranch != 1 && nbranch != 4)) return hipErrorInvalidValue;
   if ((a.out == nullptr) != (a.out_lo == nullptr)) return hipErrorInvalidValue;
+  // the parts of a row each read the whole incoming row and write their share of the new one
+  if (a.stream_in == nullptr || (rs > 1 && a.stream_in == a.stream)) return hipErrorInvalidValue;
   const dim3 grid(a.r.b * rs), block(256);
 #define SD_NR(EPT, NB, RS)                                                             \
   if (a.H == 256 * EPT && nbranch == NB && rs == RS) {                                 \

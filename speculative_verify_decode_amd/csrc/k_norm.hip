@@ -21,8 +21,11 @@ using sd::VecF;
 // POOL: the branch is the previous layer's pooled MoE output, gathered here (the weighted
 // unpooler): branch row t = sum over j < k, in order, of w[t, j] * y[slot_of[t, j]] (y fp32
 // [b * k, H]); the row's k slot ids and weights are read first, then every slot row at once.
+// The updated stream goes to stream_out, which may be the stream itself (a workgroup reads
+// its whole row before it writes it).
 template <int EPT, int NB, bool POOL>
-__global__ __launch_bounds__(256) void k_dualnorm(int H, float* __restrict__ stream,
+__global__ __launch_bounds__(256) void k_dualnorm(int H, const float* stream,
+                                                  float* stream_out,
                                                   const float* __restrict__ branch,
                                                   size_t branch_stride,
                                                   const float* __restrict__ pw,
@@ -113,7 +116,7 @@ __global__ __launch_bounds__(256) void k_dualnorm(int H, float* __restrict__ str
       ((float*)&o)[j] = s[v * VW + j];
       ss += s[v * VW + j] * s[v * VW + j];
     }
-    *(V*)(stream + base + (v * 256 + tid) * VW) = o;
+    *(V*)(stream_out + base + (v * 256 + tid) * VW) = o;
     if (aux != nullptr) *(V*)(aux + base + (v * 256 + tid) * VW) = o;
   }
   ss = sd::block_sum<4>(ss, red);
@@ -164,7 +167,8 @@ hipError_t launch_expert_input(int b, int H, const uint16_t* x, _Float16* x16, _
   return hipGetLastError();
 }
 
-hipError_t launch_dualnorm(int b, int H, float* stream, const float* branch, int nbranch,
+hipError_t launch_dualnorm(int b, int H, const float* stream, float* stream_out,
+                           const float* branch, int nbranch,
                            const uint16_t* front, const float* g_post, const float* g_pre,
                            float eps, uint16_t* out, uint16_t* out_lo, _Float16* x16,
                            _Float16* x16_lo, int* zero, float* aux, hipStream_t st,
@@ -179,7 +183,8 @@ hipError_t launch_dualnorm(int b, int H, float* stream, const float* branch, int
   if (branch == nullptr) nbranch = 1;
   if (nbranch != 1 && nbranch != 2 && nbranch != 4) return hipErrorInvalidValue;
 #define SD_NORM_NB(E, NBV, P)                                                              \
-  hipLaunchKernelGGL((k_dualnorm<E, NBV, P>), grid, block, 0, st, H, stream, branch, bs,     \
+  hipLaunchKernelGGL((k_dualnorm<E, NBV, P>), grid, block, 0, st, H, stream, stream_out,     \
+                     branch, bs,                                                          \
                      pool_w, pool_slot, pool_k, front, g_post, g_pre, eps, out, out_lo, x16,  \
                      x16_lo, zero, aux)
 #define SD_NORM_CASE(E)                                                                   \

@@ -163,9 +163,11 @@ __device__ __forceinline__ int xcd_rank(int w, int G) {
 // (optional): fp16 hi / lo terms of the pre-norm output * 2^-8 (the expert input).
 // zero (optional): an int set to 0, for a later kernel's arrival counter.
 // aux (optional): fp32 [b, H] copy of the updated stream (the aux hidden-state tap).
+// stream_out: the updated stream (may be `stream` itself).
 // pool_slot (optional): the branch is pooled, branch = y [b * pool_k, H], row t gathered
 // as sum over j of pool_w[t, j] * y[pool_slot[t, j]] (nbranch must be 1).
-hipError_t launch_dualnorm(int b, int H, float* stream, const float* branch, int nbranch,
+hipError_t launch_dualnorm(int b, int H, const float* stream, float* stream_out,
+                           const float* branch, int nbranch,
                            const uint16_t* front, const float* g_post, const float* g_pre,
                            float eps, uint16_t* out, uint16_t* out_lo, _Float16* x16,
                            _Float16* x16_lo, int* zero, float* aux, hipStream_t st,
@@ -195,6 +197,7 @@ struct GemmArgs {
 // hipErrorInvalidValue.
 hipError_t launch_gemm(GemmMode mode, const GemmArgs& a, hipStream_t st);
 bool gemm_split_ok(int M, int N, int K, bool lo, int ksplit);
+
 
 // Weight packing (layouts in sdverify.h).
 hipError_t launch_pack_dense(int N, int K, const uint16_t* src, uint16_t* dst, hipStream_t st);
@@ -291,7 +294,8 @@ struct NormRouterArgs {
   int H;
   const float* branch;     // fp32 [nbranch, b, H]
   size_t branch_stride;    // floats between partials
-  float* stream;
+  const float* stream_in;  // the stream entering the boundary
+  float* stream;           // the updated stream (not stream_in: parts of a row write it)
   const float *g_post, *g_pre;
   float eps;
   uint16_t *out, *out_lo;  // bf16 hi / lo terms of the pre-FFN norm output

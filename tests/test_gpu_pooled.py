@@ -9,7 +9,7 @@ import torch
 
 from speculative_verify_decode_amd import binding as B
 from tests.gpu_util import DEV, runner, say, workload
-from tests.helpers import assert_close, np64
+from tests.helpers import assert_close, close, np64
 
 pytestmark = pytest.mark.gpu
 
@@ -60,7 +60,10 @@ def test_pooled_steps_match_plain_steps(name):
         assert np.array_equal(ids1[n], ids2[n]), n
     d_s = float((s1 - s2).abs().max())
     d_m = float((u - m2).abs().max())
-    say(f"[gpu-test] {name}: max |diff| stream {d_s:.3e} branch {d_m:.3e}")
+    _, w_s, _ = close(np64(s2), np64(s1), 0.0)
+    _, w_m, _ = close(np64(m2), np64(u), 0.0)
+    say(f"[gpu-test] {name}: max |diff| stream {d_s:.3e} branch {d_m:.3e}; "
+        f"scaled {w_s:.3e} {w_m:.3e}")
     assert_close(np64(s2), np64(s1).astype(np.float64), "stream", tol=1e-5)
     assert_close(np64(m2), np64(u).astype(np.float64), "branch", tol=1e-5)
 
