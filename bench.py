@@ -234,8 +234,20 @@ def main():
 
     # The timed layer step is sd_layer_step (unpooler included, input given as the unpooled
     # branch).  pooled_step_us times sd_layer_step_pooled on the same copies, as in a stack:
-    # its input boundary gathers the previous layer's expert outputs (here its own previous
-    # output) and it leaves its own unpooled.
+    # its input boundary gathers the previous layer's expert outputs and it leaves its own
+    # unpooled.  Its pooled input is the same branch in pooled form (pool_from_branch), so it
+    # routes to the same experts as the timed step.
+    def pool_from_branch(r):
+        """r's unpooled input branch as a pooled one: row t in slot t k with weight 1, the
+        row's other slots zero with weight 0, so the gather reproduces it exactly."""
+        k, b = wk["dims"]["top_k"], r.b
+        y, rt = r.pool["y"], r.pool["route_t"]
+        y.zero_()
+        y.view(b, k, H)[:, 0].copy_(r.act["branch_in"])
+        rt["topk_w"].zero_()
+        rt["topk_w"].view(b, k)[:, 0] = 1.0
+        rt["slot_of"].copy_(torch.arange(b * k, device=dev).view(rt["slot_of"].shape))
+
     def run_step(r, sb, stream=None, pool=False):
         if chain:
             r.chain(sb, r.act["branch_in"], r.chain_bufs, with_tau=False, stream=stream)
@@ -281,9 +293,10 @@ def main():
         for r, sb in zip(runners, streams):
             run_step(r, sb, stream=st)      # warm (lazy module load)
             sb.copy_(r.act["stream"])
-            if pooled:                      # its output becomes the copy's pooled input
+            if pooled:                      # warm the pooled form too
                 run_step(r, sb, stream=st, pool=True)
                 sb.copy_(r.act["stream"])
+                pool_from_branch(r)
     torch.cuda.synchronize()
     snaps = []
     for r, sb in zip(runners, streams):
