@@ -5,7 +5,6 @@ import functools
 import sys
 
 import numpy as np
-import torch
 
 from oracle.formats import bf16_round
 from speculative_verify_decode_amd import binding as B
@@ -92,11 +91,3 @@ def teacher_forcer(gpu_ids, rel, record):
         return out
     return f
 
-
-def expert_input(x):
-    """fp16 [2, b, H]: hi and lo terms of x * 2^-8, the form the expert entry point takes
-    (hi = fp16 rounding, lo = fp16 rounding of the remainder, computed in fp64)."""
-    xs = x.double() * 2.0 ** -8
-    hi = xs.half()
-    lo = (xs - hi.double()).half()
-    return torch.stack([hi, lo]).contiguous()
