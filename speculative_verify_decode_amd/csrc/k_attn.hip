@@ -271,15 +271,13 @@ void k_attn_split(AttnArgs a, int cb_host, int nslot) {
   const int64_t kslot = a.slot_mapping[krow];
   constexpr int NE = (kQRows * HALF + 255) / 256;  // RoPE table entries per thread
   int epos[NE];
-  double efreq[NE], kfreq[KPT];  // kernel-argument reads are memory loads too
+  double efreq[NE];  // kernel-argument reads are memory loads too
 #pragma unroll
   for (int e = 0; e < NE; ++e) {
     const int idx = min(tid + 256 * e, kQRows * HALF - 1);
     epos[e] = a.positions[row_of(idx / HALF)];
     efreq[e] = a.freq[idx % HALF];
   }
-#pragma unroll
-  for (int m = 0; m < KPT; ++m) kfreq[m] = a.freq[ln + 32 * m];
   load_win(W0, clamp_blk(id0), clamp_blk(id1));
 
   // query terms: slices summed in order from 0, per-head weightless RMSNorm over the
@@ -324,6 +322,8 @@ void k_attn_split(AttnArgs a, int cb_host, int nslot) {
   const int Ln0 = L - rq.n;
   const bool has_new = blk_begin < nblk && 16 * min(blk_begin + cb, nblk) > Ln0;
   if (has_new) {  // uniform
+    // the new tokens are the request's rows: their RoPE entries are the table's, row jn
+    __syncthreads();
     float k1[KPT], k2[KPT];
 #pragma unroll
     for (int m = 0; m < KPT; ++m) {
@@ -359,13 +359,13 @@ void k_attn_split(AttnArgs a, int cb_host, int nslot) {
 #pragma unroll
       for (int m = 0; m < KPT; ++m) {
         const int d = ln + 32 * m;
-        float c, sn, v1 = 0.f, v2 = 0.f;
+        const float c = s_cos[jn][d], sn = s_sin[jn][d];
+        float v1 = 0.f, v2 = 0.f;
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
           v1 += uv[p][0][m];
           v2 += uv[p][1][m];
         }
-        rope_cs(kpos, kfreq[m], c, sn);
         const uint16_t ka = sd::f2bf(k1[m] * c - k2[m] * sn), kb = sd::f2bf(k2[m] * c + k1[m] * sn);
         const uint16_t va = sd::f2bf(v1), vb = sd::f2bf(v2);
         s_kn[jn][d] = ka;
