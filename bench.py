@@ -106,7 +106,7 @@ def rotation_copies(K, step_bytes, requested=0):
 
 def read_ceiling(dev, nbytes=1 << 30, reps=10):
     """A plain streaming read of a 1 GiB buffer (sd_debug_read_probe): the practical HBM read
-    rate on this box, timed with HIP events around reps back-to-back reads."""
+    rate on this machine, timed with HIP events around reps back-to-back reads."""
     from speculative_verify_decode_amd import binding as B
     buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
     sink = B.read_probe_sink(dev)
@@ -203,9 +203,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported by this build "
-              "(the layer step is measured on one GPU's share; see the sharding notes)",
-              file=sys.stderr)
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (the layer step "
+              "is measured on one GPU's share of a sharded layer)", file=sys.stderr)
         sys.exit(2)
 
     from speculative_verify_decode_amd import binding as B

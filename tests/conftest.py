@@ -15,7 +15,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests never silently run on the CPU: without a GPU they are skipped here, and
-    # on a GPU machine the library must load or they fail loudly.
+    # on a machine with a GPU the library must load or they fail loudly.
     try:
         import torch
         has_gpu = torch.cuda.is_available()

@@ -20,7 +20,7 @@ def say(*a):
 
 
 def require_lib():
-    # On a GPU machine the HIP path must load: a missing library is a failure, not a skip.
+    # On a machine with a GPU the HIP path must load: a missing library is a failure, not a skip.
     return B.lib()
 
 

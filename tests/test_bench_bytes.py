@@ -58,7 +58,7 @@ def test_untouched_experts_cost_nothing():
 def test_rotation_copies_divide_the_timed_steps():
     from bench import rotation_copies
     step = 353.1e6
-    assert rotation_copies(20, step) == (10, 0)      # the driver's --steps 20
+    assert rotation_copies(20, step) == (10, 0)      # 20 steps: ten copies, whole replays only
     assert rotation_copies(200, step) == (8, 0)
     assert rotation_copies(5, step) == (5, 0)        # fewer steps than the usual copies
     assert rotation_copies(1, step) == (1, 0)
