@@ -741,14 +741,22 @@ int sd_dense_layer_step(const sd_dims* dims, int32_t b, float* stream,
   SD_LAUNCH(launch_draft_norm(1, b, H, stream, a, a_parts, w->g_post_attn, w->g_pre_ffn, eps,
                               x_f, st),
             "dense layer attention boundary");
-  GemmArgs g{};
-  g.M = b; g.N = 2 * I; g.K = H; g.x = x_f; g.x_lo = nullptr;
-  g.w = (const uint16_t*)w->w_gate_up; g.y = at<float>(ws, D.gu);
-  g.ksplit = gemm_split_ok(b, 2 * I, H, false, kDenseSplit) ? kDenseSplit : 1;
-  SD_LAUNCH(launch_gemm(GEMM_F32, g, st), "gate_up projection");
   uint16_t* h = at<uint16_t>(ws, D.h);
   uint16_t* h_lo = at<uint16_t>(ws, D.h_lo);
-  SD_LAUNCH(launch_swiglu_dense(b, I, at<float>(ws, D.gu), g.ksplit, h, h_lo, st), "SwiGLU");
+  GemmArgs g{};
+  g.M = b; g.N = 2 * I; g.K = H; g.x = x_f; g.x_lo = nullptr;
+  g.w = (const uint16_t*)w->w_gate_up;
+  if (gemm_swiglu_ok(b, 2 * I, H, false)) {
+    // one K slice: each workgroup finishes a gate tile and then its up tile, and the SwiGLU
+    // runs in the projection's epilogue
+    g.y = h; g.y_lo = h_lo; g.ksplit = 1;
+    SD_LAUNCH(launch_gemm(GEMM_SWIGLU, g, st), "gate_up projection with SwiGLU");
+  } else {
+    g.y = at<float>(ws, D.gu);
+    g.ksplit = gemm_split_ok(b, 2 * I, H, false, kDenseSplit) ? kDenseSplit : 1;
+    SD_LAUNCH(launch_gemm(GEMM_F32, g, st), "gate_up projection");
+    SD_LAUNCH(launch_swiglu_dense(b, I, at<float>(ws, D.gu), g.ksplit, h, h_lo, st), "SwiGLU");
+  }
   GemmArgs gd{};
   gd.M = b; gd.N = H; gd.K = I; gd.x = h; gd.x_lo = h_lo;
   gd.w = (const uint16_t*)w->w_down; gd.y = at<float>(ws, D.y);

@@ -116,7 +116,8 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_res(GemmArgs a, int ntiles) {
     for (int u = 0; u < S; ++u) bv[c][u] = buf_load8(rx, ox + 64 * u);
   }
   GemmArgs ap = a;
-  if (MODE != GEMM_HEAD) ap.y = (float*)a.y + (size_t)ks * a.M * a.N;
+  if (MODE != GEMM_HEAD && MODE != GEMM_SWIGLU) ap.y = (float*)a.y + (size_t)ks * a.M * a.N;
+  f32x4_t gsave = f32x4_t{0.f, 0.f, 0.f, 0.f};  // GEMM_SWIGLU: the finishing wave's gate sums
 
   // weights through a buffer resource: a tile index past the last loads zeros without a
   // memory access, so the prefetch of a missing next tile needs no branch and every wait
@@ -156,9 +157,41 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_res(GemmArgs a, int ntiles) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] += __shfl_xor(v[r], 8, 64);
       }
-      if (!SPLIT || i < 8) store_tile<MODE>(ap, RPC * c + m, tile, ntiles, g, v);
+      if constexpr (MODE == GEMM_SWIGLU) {
+        // buffer 0 finishes the gate tile, buffer 1 the up tile of the same columns
+        if (buf == 0) {
+          gsave = v;
+        } else if ((!SPLIT || i < 8) && RPC * c + m < a.M) {
+          uint16_t hh[4], hl[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            sd::split_bf16(gsave[r] / (1.0f + __expf(-gsave[r])) * v[r], hh[r], hl[r]);
+          const size_t o = (size_t)(RPC * c + m) * (a.N >> 1) + tile * 16 + 4 * g;
+          *(u32x2_t*)((uint16_t*)a.y + o) = u32x2_t{hh[0] | ((uint32_t)hh[1] << 16), hh[2] | ((uint32_t)hh[3] << 16)};
+          *(u32x2_t*)(a.y_lo + o) = u32x2_t{hl[0] | ((uint32_t)hl[1] << 16), hl[2] | ((uint32_t)hl[3] << 16)};
+        }
+      } else {
+        if (!SPLIT || i < 8) store_tile<MODE>(ap, RPC * c + m, tile, ntiles, g, v);
+      }
     }
   };
+  if constexpr (MODE == GEMM_SWIGLU) {
+    // column tile pairs p: gate tile p, then up tile p + NTG, into the two buffers in turn
+    const int NTG = ntiles >> 1;
+    int p = grp;
+    if (p >= NTG) return;  // uniform per workgroup
+    load(A0, p);
+    while (true) {
+      load(A1, p + NTG);
+      finish(A0, p, 0);
+      const int pn = p + ngrp;
+      load(A0, pn < NTG ? pn : ntiles);  // past the last pair: zeros, no memory access
+      finish(A1, p, 1);
+      if (pn >= NTG) break;
+      p = pn;
+    }
+    return;
+  }
   int t = grp;
   if (t >= ntiles) return;  // uniform per workgroup
   load(A0, t);
@@ -337,6 +370,15 @@ hipError_t launch_m(const GemmArgs& in, hipStream_t st) {
   } else {
     a.x_lo_off = 0;
   }
+  if constexpr (MODE == GEMM_SWIGLU) {
+    // one column tile of rows (the gate sums wait in the finishing wave's registers for the
+    // up tile), one K slice, the persistent kernel only
+    if (!gemm_swiglu_ok(a.M, a.N, a.K, a.x_lo != nullptr) || a.ksplit != 1 || a.y_lo == nullptr)
+      return hipErrorInvalidValue;
+    const bool res = a.x_lo != nullptr ? try_res_nw<1, MODE, true>(a, ntiles, st)
+                                       : try_res_nw<1, MODE, false>(a, ntiles, st);
+    return res ? hipGetLastError() : hipErrorInvalidValue;
+  } else {
   // the persistent kernel takes any K slicing; the per-tile kernel only whole K
   if (a.x_lo != nullptr) {
     const bool res = a.M <= 8    ? try_res_nw<1, MODE, true>(a, ntiles, st)
@@ -358,6 +400,7 @@ hipError_t launch_m(const GemmArgs& in, hipStream_t st) {
   if (a.M <= 16) return launch_tile<1, MODE, false>(a, ntiles, st);
   if (a.M <= 32) return launch_tile<2, MODE, false>(a, ntiles, st);
   return launch_tile<4, MODE, false>(a, ntiles, st);
+  }
 }
 
 // Row-major bf16 [N, K] -> packed tiles (rows past N are zero).  One thread per 16 bytes.
@@ -439,6 +482,7 @@ hipError_t launch_gemm(GemmMode mode, const GemmArgs& a, hipStream_t st) {
     case GEMM_F32: return launch_m<GEMM_F32>(a, st);
     case GEMM_F32_BIAS: return launch_m<GEMM_F32_BIAS>(a, st);
     case GEMM_HEAD: return launch_m<GEMM_HEAD>(a, st);
+    case GEMM_SWIGLU: return launch_m<GEMM_SWIGLU>(a, st);
   }
   return hipErrorInvalidValue;
 }
@@ -458,6 +502,18 @@ hipError_t launch_pack_fp4(int E, int N, int K, const uint8_t* codes, const uint
   hipLaunchKernelGGL(k_pack_fp4, dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256),
                      0, st, N, K, codes, scales, codes_out, scales_out, nlanes);
   return hipGetLastError();
+}
+
+bool gemm_swiglu_ok(int M, int N, int K, bool lo) {
+  if (M < 1 || M > (lo ? 8 : 16) || N % 32 != 0 || K % 32 != 0) return false;
+  const int KT = K / 32, ntiles = N / 16;
+  if ((size_t)ntiles * KT * 1024 >= 0x80000000u) return false;
+  for (int nw : {8, 16, 4}) {
+    if (KT % nw) continue;
+    const int S = KT / nw;
+    if ((S == 1 || S == 2 || S == 4 || S == 8 || S == 16) && res_fits(1, nw, S)) return true;
+  }
+  return false;
 }
 
 bool gemm_split_ok(int M, int N, int K, bool lo, int ksplit) {

@@ -177,7 +177,9 @@ hipError_t launch_dualnorm(int b, int H, const float* stream, float* stream_out,
 hipError_t launch_expert_input(int b, int H, const uint16_t* x, _Float16* x16, _Float16* x16_lo,
                                hipStream_t st);
 
-enum GemmMode { GEMM_F32 = 0, GEMM_F32_BIAS = 2, GEMM_HEAD = 3 };
+// GEMM_SWIGLU: W = [gate (N/2 rows); up (N/2 rows)], one K slice; y receives the bf16 hi
+// terms of silu(gate) * up [M, N/2] and y_lo their lo terms (N/2 a multiple of 16).
+enum GemmMode { GEMM_F32 = 0, GEMM_F32_BIAS = 2, GEMM_HEAD = 3, GEMM_SWIGLU = 4 };
 
 struct GemmArgs {
   int M, N, K;
@@ -191,12 +193,14 @@ struct GemmArgs {
   float* head_val;     // GEMM_HEAD: per (m, tile) best logit
   int* head_idx;       // GEMM_HEAD: per (m, tile) its index
   float multiplier, soft_cap;
+  uint16_t* y_lo;      // GEMM_SWIGLU: the lo terms
 };
 // ksplit > 1 is taken only by the persistent kernel (M <= 64, shapes whose resident
 // activations fit: gemm_split_ok says which); otherwise the launch fails with
 // hipErrorInvalidValue.
 hipError_t launch_gemm(GemmMode mode, const GemmArgs& a, hipStream_t st);
 bool gemm_split_ok(int M, int N, int K, bool lo, int ksplit);
+bool gemm_swiglu_ok(int M, int N, int K, bool lo);  // GEMM_SWIGLU serves the shape
 
 
 // Weight packing (layouts in sdverify.h).
