@@ -38,11 +38,23 @@ def _check_written(got_cache, ref_cache, slots, what, k_major, unit_scale=0.0):
         assert (err <= bound).all(), f"{what} slot {j}: at {i} got {g[i]} want {r[i]}"
 
 
+# More than 16 rows take the dense layer's other gate_up route: the split-K projection to
+# fp32 partials and a separate SwiGLU pass (16 rows or fewer fuse SwiGLU into the GEMM).
+_WIDE_DENSE = {
+    "tiny_dense_b32": synth.with_overrides(synth.WORKLOADS["tiny_dense"], n_req=4,
+                                           ctx=(128, 60, 17, 96), name="tiny_dense_b32"),
+    "h4096_b24_dense": synth.with_overrides(synth.WORKLOADS["h4096_b8_ctx8k_dense"], n_req=3,
+                                            ctx=(8192, 3001, 517), name="h4096_b24_dense"),
+}
+
+
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name,window", [("tiny_dense", 0), ("tiny_dense", 24),
-                                         ("h4096_b8_ctx8k_dense", 0)])
+                                         ("h4096_b8_ctx8k_dense", 0), ("tiny_dense_b32", 0),
+                                         ("tiny_dense_b32", 24), ("h4096_b24_dense", 0)])
 def test_dense_layer_step_matches_oracle(name, window):
-    wk = workload(name)                      # cached: not modified here
+    wk = workload(_WIDE_DENSE.get(name, name))   # cached: not modified here
+    assert (wk["workload"].b > 16) == (name in _WIDE_DENSE)
     r = runner(wk)
     r.layers[0].kv.window = window
     lay, d = wk["layers"][0], wk["dims"]
