@@ -111,11 +111,47 @@ struct RouteLdsT {
 };
 using RouteLds = RouteLdsT<64 * 256>;  // b <= 64 rows, E <= 256 experts
 
+// Inclusive prefix sum over the 64 lanes of a wave: shifts within each row of 16 lanes
+// (DPP row_shr 1, 2, 4, 8; a lane with no source adds 0), then each row adds the totals
+// of the rows before it, read from lanes 15, 31 and 47.
+__device__ __forceinline__ int wave_scan_incl(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);
+  const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31);
+  const int r2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return x + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
+
+// The softmax weight of choice p (row t = p / k) over its row's k selected logits, summed in
+// rank order; the ids and weights go to memory.  EMAX > 0: k <= 8, unrolled LDS reads.
+template <int EMAX, class RL>
+__device__ __forceinline__ void route_weight(const RouterArgs& a, const RL& R, int p) {
+  const int k = a.k, t = p / k;
+  const float m = R.sel[t * k];
+  float den = 0.f;
+  if constexpr (EMAX > 0) {
+    float sv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sv[j] = R.sel[t * k + j];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < k) den += expf(sv[j] - m);
+  } else {
+    for (int j = 0; j < k; ++j) den += expf(R.sel[t * k + j] - m);
+  }
+  a.ids[p] = R.ids[p];
+  a.w_out[p] = expf(R.sel[p] - m) / den;
+}
+
 // EMAX > 0: E <= EMAX and k <= 8, ranks and weights from fully unrolled LDS reads.  NT
 // threads (a multiple of 64, at least E).  out: write the maps (and the logits) to memory;
 // meta (may be null): the expert GEMMs' copy of the maps in LDS (active list, counts,
-// offsets, token of each slot).
-template <int EMAX, int NT, class RL>
+// offsets, token of each slot).  SOFT false: the ids and softmax weights are left to the
+// caller (route_weight over p < b k, after this returns; R keeps what it needs).
+template <int EMAX, int NT, bool SOFT = true, class RL>
 __device__ void route_phase2(const RouterArgs& a, int KS, RL& R, bool out = true,
                              MoeMeta* meta = nullptr) {
   const int tid = threadIdx.x, lane = tid & 63;
@@ -166,20 +202,8 @@ __device__ void route_phase2(const RouterArgs& a, int KS, RL& R, bool out = true
     }
     __syncthreads();
     for (int p = tid; p < nk; p += NT) {
-      const int t = p / k;
-      float sv[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) sv[j] = R.sel[t * k + j];
-      const float m = sv[0];
-      float den = 0.f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (j < k) den += expf(sv[j] - m);
-      const int ex = R.ids[p];
-      if (out) {
-        a.ids[p] = ex;
-        a.w_out[p] = expf(R.sel[p] - m) / den;
-      }
+      const int t = p / k, ex = R.ids[p];
+      if (SOFT && out) route_weight<EMAX>(a, R, p);
       atomicOr(t < 32 ? &R.mlo[ex] : &R.mhi[ex], 1u << (t & 31));
     }
   } else {
@@ -198,40 +222,43 @@ __device__ void route_phase2(const RouterArgs& a, int KS, RL& R, bool out = true
       }
     }
     __syncthreads();
-    for (int p = tid; p < nk; p += NT) {
-      const int t = p / k;
-      const float m = R.sel[t * k];
-      float den = 0.f;
-      for (int j = 0; j < k; ++j) den += expf(R.sel[t * k + j] - m);
-      if (out) {
-        a.ids[p] = R.ids[p];
-        a.w_out[p] = expf(R.sel[p] - m) / den;
-      }
-    }
+    if (SOFT && out)
+      for (int p = tid; p < nk; p += NT) route_weight<EMAX>(a, R, p);
     for (int p = tid; p < nk; p += NT) {
       const int t = p / k;
       atomicOr(t < 32 ? &R.mlo[R.ids[p]] : &R.mhi[R.ids[p]], 1u << (t & 31));
     }
   }
   __syncthreads();
-  // counts, exclusive offsets and the active list: block scans over experts (tid = e)
+  // counts, exclusive offsets and the active list: scans over experts (tid = e), within
+  // wave 0 when it holds every expert, else across the block's waves
   const int e = tid;  // NT >= E
   const int cnt = e < E ? __popc(R.mlo[e]) + __popc(R.mhi[e]) : 0;
   const int act = cnt > 0 ? 1 : 0;
-  int ic = cnt, ia = act;
+  int ic, ia, pc = 0, pa = 0, total, n_act;
+  if constexpr (EMAX > 0 && EMAX <= 64) {
+    ic = wave_scan_incl(cnt);
+    ia = wave_scan_incl(act);
+    total = __builtin_amdgcn_readlane(ic, 63);
+    n_act = __builtin_amdgcn_readlane(ia, 63);
+  } else {
+    ic = cnt;
+    ia = act;
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int uc = __shfl_up(ic, d, 64), ua = __shfl_up(ia, d, 64);
-    if (lane >= d) { ic += uc; ia += ua; }
-  }
-  if (lane == 63) { R.wc[wave] = ic; R.wa[wave] = ia; }
-  __syncthreads();
-  int pc = 0, pa = 0, total = 0, n_act = 0;
+    for (int d = 1; d < 64; d <<= 1) {
+      const int uc = __shfl_up(ic, d, 64), ua = __shfl_up(ia, d, 64);
+      if (lane >= d) { ic += uc; ia += ua; }
+    }
+    if (lane == 63) { R.wc[wave] = ic; R.wa[wave] = ia; }
+    __syncthreads();
+    total = 0;
+    n_act = 0;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    if (w < wave) { pc += R.wc[w]; pa += R.wa[w]; }
-    total += R.wc[w];
-    n_act += R.wa[w];
+    for (int w = 0; w < NW; ++w) {
+      if (w < wave) { pc += R.wc[w]; pa += R.wa[w]; }
+      total += R.wc[w];
+      n_act += R.wa[w];
+    }
   }
   const int off = pc + ic - cnt;
   if (e < E) {
@@ -646,15 +673,22 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w13(MoeArgs a) {
   constexpr int NR = KS > 1 ? KS - 1 : 1;
   __shared__ MoeMetaT<GRP> meta;
   __shared__ f32x4_t red[2][NR][2][64];
+  __shared__ RouteLdsT<64 * 32> R;  // routing (RT): b <= 64 rows, E <= 32 experts
+  // workgroup 0 writes the routing's ids and softmax weights after its last unit: only
+  // later kernels read them, and no workgroup's weight stream waits for them
+  auto route_weights = [&]() {
+    if constexpr (RT)
+      if (blockIdx.x == 0)
+        for (int p = threadIdx.x; p < a.r.b * a.r.k; p += blockDim.x) route_weight<32>(a.r, R, p);
+  };
   if constexpr (RT) {
     // every workgroup routes from the router's logits (the same arithmetic, so the same
     // maps); workgroup 0 also writes the maps for the W2 kernel and the unpooler
-    __shared__ RouteLdsT<64 * 32> R;  // b <= 64 rows, E <= 32 experts
     // the global scales are read before the routing and staged after it, so their loads go
     // out with the logits' (a barrier inside the routing keeps them there)
     const int ge = min((int)threadIdx.x, a.E - 1);
     const float g13v = a.w13_gscale[ge], g2v = a.w2_gscale[ge];
-    route_phase2<32, 64 * KS>(a.r, 1, R, blockIdx.x == 0, &meta);
+    route_phase2<32, 64 * KS, false>(a.r, 1, R, blockIdx.x == 0, &meta);
     if ((int)threadIdx.x < a.E) {
       meta.g13[threadIdx.x] = g13v;
       meta.g2[threadIdx.x] = g2v;
@@ -772,7 +806,10 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w13(MoeArgs a) {
   unit_range(groups_of(meta, a.E) * 2 * NT, hb, he);
   hb = __builtin_amdgcn_readfirstlane(hb);
   he = __builtin_amdgcn_readfirstlane(he);
-  if (hb >= he) return;
+  if (hb >= he) {
+    route_weights();
+    return;
+  }
   int u = hb >> 1;
   const int end = (he + 1) >> 1;
   auto va_of = [&](int p) { return 2 * p >= hb && p < end; };
@@ -799,6 +836,7 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w13(MoeArgs a) {
     if (n2 >= end) break;
     u = n2;
   }
+  route_weights();
 }
 
 // W2: y[slot, n] = h[slot] . W2_e[n], fp32.  K = I = 128 * NU * KS.
