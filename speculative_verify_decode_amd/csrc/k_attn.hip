@@ -91,11 +91,16 @@ __device__ ChunkMap chunk_map(const AttnArgs& a, int cb_host, int nslot) {
     span = max(((L + 15) >> 4) - first_block(a, lane), 0);
   }
   int S = span, smax = span;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    S += __shfl_xor(S, o, 64);
-    smax = max(smax, __shfl_xor(smax, o, 64));
-  }
+  auto step = [&](int oS, int om) {
+    S += oS;
+    smax = max(smax, om);
+  };
+  step(sd::lane_xor<32>(S), sd::lane_xor<32>(smax));
+  step(sd::lane_xor<16>(S), sd::lane_xor<16>(smax));
+  step(sd::lane_xor<8>(S), sd::lane_xor<8>(smax));
+  step(sd::lane_xor<4>(S), sd::lane_xor<4>(smax));
+  step(sd::lane_xor<2>(S), sd::lane_xor<2>(smax));
+  step(sd::lane_xor<1>(S), sd::lane_xor<1>(smax));
   S = __builtin_amdgcn_readfirstlane(S);
   smax = __builtin_amdgcn_readfirstlane(smax);
   // candidate sizes cb0 + 8 lane, from the least that could fit (and gives no request more
@@ -110,12 +115,7 @@ __device__ ChunkMap chunk_map(const AttnArgs& a, int cb_host, int nslot) {
   ChunkMap m;
   m.cb = fits != 0 ? cb0 + 8 * (int)__builtin_ctzll(fits) : cb_host;
   m.nch = lane < a.n_req ? (span + m.cb - 1) / m.cb : 0;
-  int inc = m.nch;  // inclusive prefix sum over the lanes
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int v = __shfl_up(inc, o, 64);
-    if (lane >= o) inc += v;
-  }
+  const int inc = sd::wave_scan_incl(m.nch);  // inclusive prefix sum over the lanes
   m.off = inc - m.nch;
   // seq_lens beyond the host's max_seq_len could ask for more slots than there are: such
   // chunks get none (the slot range of every request stays inside the nslot slots)
@@ -297,8 +297,7 @@ void k_attn_split(AttnArgs a, int cb_host, int nslot) {
     float ss = 0.f;
 #pragma unroll
     for (int m = 0; m < DPT; ++m) ss += x1[m] * x1[m] + x2[m] * x2[m];
-#pragma unroll
-    for (int o = 1; o < TPQ; o <<= 1) ss += __shfl_xor(ss, o, 64);
+    ss = sd::group_sum<TPQ>(ss);
     const float rn = rsqrtf(ss / (float)D + a.eps);
 #pragma unroll
     for (int m = 0; m < DPT; ++m) {
@@ -339,8 +338,7 @@ void k_attn_split(AttnArgs a, int cb_host, int nslot) {
       float sk = 0.f;
 #pragma unroll
       for (int m = 0; m < KPT; ++m) sk += k1[m] * k1[m] + k2[m] * k2[m];
-#pragma unroll
-      for (int o = 1; o < 32; o <<= 1) sk += __shfl_xor(sk, o, 64);
+      sk = sd::group_sum<32>(sk);
       const float rk = rsqrtf(sk / (float)D + a.eps);
 #pragma unroll
       for (int m = 0; m < KPT; ++m) {
@@ -473,8 +471,8 @@ void k_attn_split(AttnArgs a, int cb_host, int nslot) {
           sc[t][rr] = v;
           mx = fmaxf(mx, v);
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = fmaxf(mx, sd::lane_xor<16>(mx));
+      mx = fmaxf(mx, sd::lane_xor<32>(mx));
       // lazy rescaling: a column's reference maximum moves only when a score exceeds it by
       // more than 2^8 (in exp2 units), so p <= 256 and the accumulators are rescaled rarely;
       // exp2(s - m) with any fixed m gives the same normalised result
@@ -536,8 +534,8 @@ void k_attn_split(AttnArgs a, int cb_host, int nslot) {
 #pragma unroll
   for (int qt = 0; qt < NQT; ++qt) {
     float l = lsum[qt];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
+    l += sd::lane_xor<16>(l);
+    l += sd::lane_xor<32>(l);
     lsum[qt] = l;
     if (G == 0) s_m[wave][16 * qt + i] = mrun[qt];
   }

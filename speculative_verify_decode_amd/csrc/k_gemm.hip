@@ -74,12 +74,11 @@ __device__ __forceinline__ void store_tile(const GemmArgs& a, int m, int tile, i
       tau[r] = a.soft_cap > 0.f ? a.soft_cap * tanhf(x / a.soft_cap) : x;
     }
     if (mv && a.y != nullptr) *(f32x4_t*)((float*)a.y + (size_t)m * a.N + nb) = tau;
-#pragma unroll
-    for (int o = 16; o <= 32; o <<= 1) {
-      const float ov = __shfl_xor(best, o, 64);
-      const int oi = __shfl_xor(bidx, o, 64);
+    auto take = [&](float ov, int oi) {
       if (ov > best || (ov == best && oi < bidx)) { best = ov; bidx = oi; }
-    }
+    };
+    take(sd::lane_xor<16>(best), sd::lane_xor<16>(bidx));
+    take(sd::lane_xor<32>(best), sd::lane_xor<32>(bidx));
     if (mv && g == 0) {
       a.head_val[(size_t)m * ntiles + tile] = best;
       a.head_idx[(size_t)m * ntiles + tile] = bidx;
@@ -155,7 +154,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_res(GemmArgs a, int ntiles) {
       for (int w = 0; w < NW - 1; ++w) v += red[buf][w][c][lane];
       if (SPLIT) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] += __shfl_xor(v[r], 8, 64);
+        for (int r = 0; r < 4; ++r) v[r] += sd::lane_xor<8>(v[r]);
       }
       if constexpr (MODE == GEMM_SWIGLU) {
         // buffer 0 finishes the gate tile, buffer 1 the up tile of the same columns
@@ -265,7 +264,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_tile(GemmArgs a) {
     for (int w = 0; w < NW - 1; ++w) acc[c] += red[w][c][lane];
     if (SPLIT) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[c][r] += __shfl_xor(acc[c][r], 8, 64);
+      for (int r = 0; r < 4; ++r) acc[c][r] += sd::lane_xor<8>(acc[c][r]);
     }
   }
   if (SPLIT && i >= 8) return;
@@ -458,12 +457,15 @@ __global__ __launch_bounds__(256) void k_head_argmax(int n_tiles, int n_vocab,
     const int ii = idx[(size_t)m * n_tiles + t];
     if (v > best || (v == best && ii < bi)) { best = v; bi = ii; }
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const float ov = __shfl_xor(best, o, 64);
-    const int oi = __shfl_xor(bi, o, 64);
+  auto take = [&](float ov, int oi) {
     if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
-  }
+  };
+  take(sd::lane_xor<32>(best), sd::lane_xor<32>(bi));
+  take(sd::lane_xor<16>(best), sd::lane_xor<16>(bi));
+  take(sd::lane_xor<8>(best), sd::lane_xor<8>(bi));
+  take(sd::lane_xor<4>(best), sd::lane_xor<4>(bi));
+  take(sd::lane_xor<2>(best), sd::lane_xor<2>(bi));
+  take(sd::lane_xor<1>(best), sd::lane_xor<1>(bi));
   if ((threadIdx.x & 63) == 0) { sv[threadIdx.x >> 6] = best; si[threadIdx.x >> 6] = bi; }
   __syncthreads();
   if (threadIdx.x == 0) {

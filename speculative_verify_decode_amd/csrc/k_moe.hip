@@ -74,12 +74,7 @@ __device__ void build_groups(MoeMetaG& m, int E) {
       e = m.active[t];
       ng = (m.cnt[e] + 7) >> 3;
     }
-    int inc = ng;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int v = __shfl_up(inc, d, 64);
-      if (lane >= d) inc += v;
-    }
+    const int inc = sd::wave_scan_incl(ng);
     if (lane == 63) m.wsum[wave] = inc;
     __syncthreads();
     int base = 0, tot = 0;
@@ -110,20 +105,6 @@ struct RouteLdsT {
   int wc[16], wa[16];
 };
 using RouteLds = RouteLdsT<64 * 256>;  // b <= 64 rows, E <= 256 experts
-
-// Inclusive prefix sum over the 64 lanes of a wave: shifts within each row of 16 lanes
-// (DPP row_shr 1, 2, 4, 8; a lane with no source adds 0), then each row adds the totals
-// of the rows before it, read from lanes 15, 31 and 47.
-__device__ __forceinline__ int wave_scan_incl(int x) {
-  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);
-  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);
-  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);
-  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);
-  const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31);
-  const int r2 = __builtin_amdgcn_readlane(x, 47);
-  const int row = (threadIdx.x & 63) >> 4;
-  return x + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
-}
 
 // The softmax weight of choice p (row t = p / k) over its row's k selected logits, summed in
 // rank order; the ids and weights go to memory.  EMAX > 0: k <= 8, unrolled LDS reads.
@@ -237,18 +218,13 @@ __device__ void route_phase2(const RouterArgs& a, int KS, RL& R, bool out = true
   const int act = cnt > 0 ? 1 : 0;
   int ic, ia, pc = 0, pa = 0, total, n_act;
   if constexpr (EMAX > 0 && EMAX <= 64) {
-    ic = wave_scan_incl(cnt);
-    ia = wave_scan_incl(act);
+    ic = sd::wave_scan_incl(cnt);
+    ia = sd::wave_scan_incl(act);
     total = __builtin_amdgcn_readlane(ic, 63);
     n_act = __builtin_amdgcn_readlane(ia, 63);
   } else {
-    ic = cnt;
-    ia = act;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int uc = __shfl_up(ic, d, 64), ua = __shfl_up(ia, d, 64);
-      if (lane >= d) { ic += uc; ia += ua; }
-    }
+    ic = sd::wave_scan_incl(cnt);
+    ia = sd::wave_scan_incl(act);
     if (lane == 63) { R.wc[wave] = ic; R.wa[wave] = ia; }
     __syncthreads();
     total = 0;
@@ -347,7 +323,7 @@ __global__ __launch_bounds__(256) void k_router(RouterArgs a) {
         acc[c] += red[1][c][lane];
         acc[c] += red[2][c][lane];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[c][r] += __shfl_xor(acc[c][r], 8, 64);
+        for (int r = 0; r < 4; ++r) acc[c][r] += sd::lane_xor<8>(acc[c][r]);
         const int row = 8 * c + i;
         if (i < 8 && row < a.b) {
 #pragma unroll
@@ -518,9 +494,9 @@ __global__ __launch_bounds__(256) void k_norm_router(NormRouterArgs A) {
       acc += wh * xh;
     }
   }
-  acc += __shfl_xor(acc, 8, 64);
-  acc += __shfl_xor(acc, 16, 64);
-  acc += __shfl_xor(acc, 32, 64);
+  acc += sd::lane_xor<8>(acc);
+  acc += sd::lane_xor<16>(acc);
+  acc += sd::lane_xor<32>(acc);
   if (lane < 8) s_z[wave][lane] = acc;
   __syncthreads();
   if (tid < 8 && 8 * q + tid < a.E)
@@ -773,8 +749,8 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w13(MoeArgs a) {
       for (int w = 0; w < KS - 1; ++w) v += red[buf][w][j][lane];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        v[r] += __shfl_xor(v[r], 8, 64);  // hi + lo columns
-        up[r] = __shfl_xor(v[r], 32, 64);  // tile rows 8-15: the up rows
+        v[r] += sd::lane_xor<8>(v[r]);  // hi + lo columns
+        up[r] = sd::lane_xor<32>(v[r]);  // tile rows 8-15: the up rows
       }
       const int slot = i;
       if (i < 8 && G < 2 && slot < U.Te && (j == 0 ? va : vb)) {
@@ -907,7 +883,7 @@ __global__ __launch_bounds__(64 * KS) void k_moe_w2(MoeArgs a) {
 #pragma unroll
         for (int w = 0; w < KS - 1; ++w) acc[c] += red[buf][w][c][lane];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[c][r] += __shfl_xor(acc[c][r], 8, 64);
+        for (int r = 0; r < 4; ++r) acc[c][r] += sd::lane_xor<8>(acc[c][r]);
       }
       if (i < 8) {
         const float sc = SD_X16_UNSCALE * meta.g2[U.e];

@@ -81,16 +81,82 @@ __device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) 
   lo = f2bf(x - bf2f(hi));
 }
 
+// The 32-bit value of lane (lane ^ O) of the wave, O a power of two below 64, without a
+// round trip through the LDS crossbar: DPP within rows of 16 lanes (quad permutes for 1
+// and 2; for 4, row shifts by 4 into the banks of lanes 0-3 and 8-11 and out of the others;
+// for 8, a row rotate by 8) and the gfx950 permlane swaps across rows (each returns the
+// lower and the upper row of the pair).  Every lane of the wave must be active.
+template <int O, class T>
+__device__ __forceinline__ T lane_xor(T v) {
+  static_assert(sizeof(T) == 4, "32-bit values");
+  const int x = __builtin_bit_cast(int, v);
+  int r;
+  if constexpr (O == 1) {
+    r = __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xf, 0xf, false);  // quad_perm [1,0,3,2]
+  } else if constexpr (O == 2) {
+    r = __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xf, 0xf, false);  // quad_perm [2,3,0,1]
+  } else if constexpr (O == 4) {
+    r = __builtin_amdgcn_update_dpp(x, x, 0x104, 0xf, 0x5, false);  // row_shl:4, banks 0, 2
+    r = __builtin_amdgcn_update_dpp(r, x, 0x114, 0xf, 0xa, false);  // row_shr:4, banks 1, 3
+  } else if constexpr (O == 8) {
+    r = __builtin_amdgcn_update_dpp(0, x, 0x128, 0xf, 0xf, false);  // row_ror:8
+  } else if constexpr (O == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    r = (threadIdx.x & 16) ? p[0] : p[1];
+  } else {
+    static_assert(O == 32, "lane offsets 1 .. 32");
+    const auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    r = (threadIdx.x & 32) ? p[0] : p[1];
+  }
+  return __builtin_bit_cast(T, r);
+}
+
+// Butterfly over the wave, partners 32, 16, .., 1 in that order: every lane gets the same
+// bits.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  v += lane_xor<32>(v);
+  v += lane_xor<16>(v);
+  v += lane_xor<8>(v);
+  v += lane_xor<4>(v);
+  v += lane_xor<2>(v);
+  v += lane_xor<1>(v);
   return v;
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  v = fmaxf(v, lane_xor<32>(v));
+  v = fmaxf(v, lane_xor<16>(v));
+  v = fmaxf(v, lane_xor<8>(v));
+  v = fmaxf(v, lane_xor<4>(v));
+  v = fmaxf(v, lane_xor<2>(v));
+  v = fmaxf(v, lane_xor<1>(v));
   return v;
+}
+
+// Sum over aligned groups of N lanes (N = 2 .. 64), partners 1, 2, .., N / 2 in that order.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (N > 1) v += lane_xor<1>(v);
+  if constexpr (N > 2) v += lane_xor<2>(v);
+  if constexpr (N > 4) v += lane_xor<4>(v);
+  if constexpr (N > 8) v += lane_xor<8>(v);
+  if constexpr (N > 16) v += lane_xor<16>(v);
+  if constexpr (N > 32) v += lane_xor<32>(v);
+  return v;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts within each row of 16 lanes
+// (DPP row_shr 1, 2, 4, 8; a lane with no source adds 0), then each row adds the totals
+// of the rows before it, read from lanes 15, 31 and 47.
+__device__ __forceinline__ int wave_scan_incl(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);
+  const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31);
+  const int r2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return x + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
 }
 
 // Sum over a block of NW waves; `red` holds NW floats of LDS.  All threads get the sum.
