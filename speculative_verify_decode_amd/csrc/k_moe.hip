@@ -145,7 +145,7 @@ __device__ void route_phase2(const RouterArgs& a, int KS, RL& R, bool out = true
   // the bias is read unconditionally (the partials stand in when there is none), so its load
   // goes out with the partials' instead of after them
   const float* bias = a.bias != nullptr ? a.bias : a.part;
-  for (int idx = tid; idx < b * E; idx += NT) {
+  auto key_of = [&](int idx) {
     const float bv = bias[idx];
     float z = 0.f;
 #pragma unroll 16
@@ -153,7 +153,17 @@ __device__ void route_phase2(const RouterArgs& a, int KS, RL& R, bool out = true
     if (a.bias != nullptr) z += bv;
     if (out && a.logits != nullptr) a.logits[idx] = z;
     const uint32_t u = __float_as_uint(z == 0.f ? 0.f : z);  // -0 ties with +0
-    R.key[idx] = z != z ? 0u : (u & 0x80000000u ? ~u : u | 0x80000000u);
+    return z != z ? 0u : (u & 0x80000000u ? ~u : u | 0x80000000u);
+  };
+  if constexpr (EMAX > 0) {
+    // rows of EMAX keys, experts E .. EMAX - 1 padded with key 0
+    static_assert((EMAX & (EMAX - 1)) == 0 && EMAX % 8 == 0, "EMAX: a power of two, at least 8");
+    for (int p = tid; p < b * EMAX; p += NT) {
+      const int t = p / EMAX, e = p & (EMAX - 1);
+      R.key[p] = e < E ? key_of(t * E + e) : 0u;
+    }
+  } else {
+    for (int idx = tid; idx < b * E; idx += NT) R.key[idx] = key_of(idx);
   }
   if (tid < E) R.mlo[tid] = R.mhi[tid] = 0u;
   __syncthreads();
@@ -166,16 +176,22 @@ __device__ void route_phase2(const RouterArgs& a, int KS, RL& R, bool out = true
   };
   const int nk = b * k;
   if constexpr (EMAX > 0) {
-    for (int p = tid; p < b * E; p += NT) {
-      const int t = p / E, e = p - t * E;
-      const uint32_t* kr = R.key + t * E;  // reads past the row stay in the array, masked
+    for (int p = tid; p < b * EMAX; p += NT) {
+      const int t = p / EMAX, e = p & (EMAX - 1);
+      if (e >= E) continue;
+      const uint32_t* kr = R.key + t * EMAX;
       const uint32_t ke = kr[e];
-      uint32_t kk[EMAX];
-#pragma unroll
-      for (int j = 0; j < EMAX; ++j) kk[j] = kr[j];
+      // (key, EMAX - 1 - index) as one 64-bit value orders the row as (-z, index) does; a
+      // padding key (0, below any expert's index) never counts
+      const uint64_t ce = ((uint64_t)ke << 32) | (uint32_t)(EMAX - 1 - e);
       int rank = 0;
 #pragma unroll
-      for (int j = 0; j < EMAX; ++j) rank += (j < E && (kk[j] > ke || (kk[j] == ke && j < e))) ? 1 : 0;
+      for (int j0 = 0; j0 < EMAX; j0 += 8) {
+        if (j0 >= E) break;  // uniform; a row's padding past E in this group counts nothing
+#pragma unroll
+        for (int j = j0; j < j0 + 8; ++j)
+          rank += ((((uint64_t)kr[j]) << 32) | (uint32_t)(EMAX - 1 - j)) > ce ? 1 : 0;
+      }
       if (rank < k) {
         R.ids[t * k + rank] = e;
         R.sel[t * k + rank] = key_value(ke);
