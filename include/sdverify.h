@@ -367,6 +367,16 @@ int sd_context_kv(const sd_dims *dims, int32_t n_ctx, int32_t n_layers, const vo
 int sd_debug_dequant(int32_t n, int32_t k, const uint8_t *codes, const uint8_t *scales,
                      float gscale, float *out, void *stream_handle);
 
+/* Test entry: one wave (64 lanes) of the kernels' cross-lane exchanges on device arrays
+ * x fp32 [64] and xi int32 [64] (lane l holds x[l], xi[l]).  out fp32 [10, 64]: rows 0-5
+ * the value of lane l ^ 1, 2, 4, 8, 16, 32; row 6 the wave sum (butterfly over partners
+ * 32, 16, .., 1, each step adding the partner's value); row 7 the wave maximum (the same
+ * butterfly); rows 8 and 9 the sums over aligned groups of 8 and 32 lanes (partners 1, 2,
+ * .. in that order).  out_i int32 [2, 64]: row 0 the inclusive prefix sum of xi, row 1
+ * xi of lane l ^ 4.  Asynchronous on the stream. */
+int sd_debug_lanes(const float *x, const int32_t *xi, float *out, int32_t *out_i,
+                   void *stream_handle);
+
 /* Measurement entry: one plain streaming read of bytes (> 0, a multiple of 16) at src
  * (16-byte aligned), each 16-byte piece loaded once with the non-temporal policy of the
  * step's weight and KV streams, each workgroup reading one contiguous part: the practical

@@ -112,6 +112,7 @@ SYMBOLS = {
     "sd_draft_head_workspace_bytes": (c_size_t, [c_int, c_int, c_int]),
     "sd_debug_dequant": (c_int, [c_int, c_int, c_void_p, c_void_p, c_float, c_void_p, c_void_p]),
     "sd_debug_read_probe": (c_int, [c_void_p, c_size_t, c_void_p, c_void_p]),
+    "sd_debug_lanes": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "sd_read_probe_sink_words": (c_int, []),
     "sd_dense_workspace_bytes": (c_size_t, [ctypes.POINTER(SdDims), c_int, c_int, c_int, c_int]),
     "sd_dense_layer_step": (c_int, [ctypes.POINTER(SdDims), c_int, c_void_p,
@@ -368,6 +369,11 @@ def draft_head(hidden, draft_vocab, b, h, w_lm, multiplier, soft_cap, d2t, tau_o
 def debug_dequant(n, k, codes, scales, gscale, out, stream=None):
     _check(lib().sd_debug_dequant(n, k, ptr(codes), ptr(scales), gscale, ptr(out),
                                   cur_stream(stream)))
+
+
+def debug_lanes(x, xi, out, out_i, stream=None):
+    """One wave of the kernels' cross-lane exchanges (see sd_debug_lanes)."""
+    _check(lib().sd_debug_lanes(ptr(x), ptr(xi), ptr(out), ptr(out_i), cur_stream(stream)))
 
 
 def read_probe_sink(device):

@@ -875,6 +875,13 @@ int sd_debug_dequant(int32_t n, int32_t k, const uint8_t* codes, const uint8_t* 
   return ok();
 }
 
+int sd_debug_lanes(const float* x, const int32_t* xi, float* out, int32_t* out_i,
+                   void* stream_handle) {
+  if (!x || !xi || !out || !out_i) return fail(SD_EINVAL, "debug lanes: null pointer");
+  SD_LAUNCH(launch_debug_lanes(x, xi, out, out_i, (hipStream_t)stream_handle), "debug lanes");
+  return ok();
+}
+
 namespace {
 constexpr int kProbeGrid = 8192;  // 32 workgroups per CU of a 256-CU device
 }  // namespace

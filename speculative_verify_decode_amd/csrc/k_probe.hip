@@ -32,7 +32,37 @@ __global__ __launch_bounds__(256) void k_read_probe(const u32x4_t* __restrict__ 
   if (acc == 0x9e3779b9u) sink[blockIdx.x] = acc;
 }
 
+// One wave of the cross-lane helpers on lane values x (float) and xi (int): out rows 0-5
+// lane_xor<1 .. 32>(x), 6 wave_sum, 7 wave_max, 8 group_sum<8>, 9 group_sum<32>; out_i row 0
+// wave_scan_incl(xi), row 1 lane_xor<4>(xi).
+__global__ __launch_bounds__(64) void k_debug_lanes(const float* __restrict__ x,
+                                                    const int* __restrict__ xi,
+                                                    float* __restrict__ out,
+                                                    int* __restrict__ out_i) {
+  const int l = threadIdx.x;  // blockDim.x == 64
+  const float v = x[l];
+  const int iv = xi[l];
+  out[0 * 64 + l] = sd::lane_xor<1>(v);
+  out[1 * 64 + l] = sd::lane_xor<2>(v);
+  out[2 * 64 + l] = sd::lane_xor<4>(v);
+  out[3 * 64 + l] = sd::lane_xor<8>(v);
+  out[4 * 64 + l] = sd::lane_xor<16>(v);
+  out[5 * 64 + l] = sd::lane_xor<32>(v);
+  out[6 * 64 + l] = sd::wave_sum(v);
+  out[7 * 64 + l] = sd::wave_max(v);
+  out[8 * 64 + l] = sd::group_sum<8>(v);
+  out[9 * 64 + l] = sd::group_sum<32>(v);
+  out_i[0 * 64 + l] = sd::wave_scan_incl(iv);
+  out_i[1 * 64 + l] = sd::lane_xor<4>(iv);
+}
+
 }  // namespace
+
+hipError_t launch_debug_lanes(const float* x, const int* xi, float* out, int* out_i,
+                              hipStream_t st) {
+  hipLaunchKernelGGL(k_debug_lanes, dim3(1), dim3(64), 0, st, x, xi, out, out_i);
+  return hipGetLastError();
+}
 
 hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int grid,
                              hipStream_t st) {

@@ -411,5 +411,7 @@ hipError_t launch_debug_dequant(int n, int k, const uint8_t* codes, const uint8_
                                 float gscale, float* out, hipStream_t st);
 
 // plain streaming read of bytes (a multiple of 16) at src; sink holds grid words
+hipError_t launch_debug_lanes(const float* x, const int* xi, float* out, int* out_i,
+                              hipStream_t st);
 hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int grid,
                              hipStream_t st);

@@ -23,6 +23,42 @@ pytestmark = pytest.mark.gpu
 ALL = ["tiny_b8_ctx128", "h4096_b8_ctx8k", "h4096_b64_ragged", "h4096_b8_ctx131k"]
 
 
+# ------------------------------------------------------------------------ cross-lane helpers
+def test_cross_lane_exchanges_are_exact():
+    """The kernels' lane exchanges (DPP and permlane swaps) against their definition on the
+    lane index, bit for bit: partner values, the butterflies' float32 sums and maxima in
+    their stated partner order, and the integer prefix sum."""
+    require_lib()
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal(64) * 10.0).astype(np.float32)
+    x[5] = x[9]  # a repeated value
+    xi = rng.integers(-50, 50, 64).astype(np.int32)
+    xd = torch.from_numpy(x).to(DEV)
+    xid = torch.from_numpy(xi).to(DEV)
+    out = torch.empty(10, 64, dtype=torch.float32, device=DEV)
+    out_i = torch.empty(2, 64, dtype=torch.int32, device=DEV)
+    B.debug_lanes(xd, xid, out, out_i)
+    torch.cuda.synchronize()
+    got, got_i = out.cpu().numpy(), out_i.cpu().numpy()
+    lane = np.arange(64)
+    for row, o in enumerate([1, 2, 4, 8, 16, 32]):
+        assert np.array_equal(got[row], x[lane ^ o]), f"lane ^ {o}"
+
+    def butterfly(v, offsets, op):
+        v = v.copy()
+        for o in offsets:
+            v = op(v, v[lane ^ o]).astype(np.float32)
+        return v
+
+    add = lambda a, b: np.float32(a) + np.float32(b)
+    assert np.array_equal(got[6], butterfly(x, [32, 16, 8, 4, 2, 1], add)), "wave sum"
+    assert np.array_equal(got[7], np.full(64, x.max(), dtype=np.float32)), "wave max"
+    assert np.array_equal(got[8], butterfly(x, [1, 2, 4], add)), "sum over groups of 8"
+    assert np.array_equal(got[9], butterfly(x, [1, 2, 4, 8, 16], add)), "sum over groups of 32"
+    assert np.array_equal(got_i[0], np.cumsum(xi).astype(np.int32)), "inclusive prefix sum"
+    assert np.array_equal(got_i[1], xi[lane ^ 4]), "int lane ^ 4"
+
+
 # ------------------------------------------------------------------------ dequant
 def test_debug_dequant_is_bit_exact():
     require_lib()
