@@ -182,7 +182,7 @@ __device__ void route_phase2(const RouterArgs& a, int KS, RL& R, bool out = true
       const uint32_t* kr = R.key + t * EMAX;
       const uint32_t ke = kr[e];
       // (key, EMAX - 1 - index) as one 64-bit value orders the row as (-z, index) does; a
-      // padding key (0, below any expert's index) never counts
+      // padding entry (key 0 at an index past every expert) orders after every expert
       const uint64_t ce = ((uint64_t)ke << 32) | (uint32_t)(EMAX - 1 - e);
       int rank = 0;
 #pragma unroll

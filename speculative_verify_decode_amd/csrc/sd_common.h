@@ -147,7 +147,8 @@ __device__ __forceinline__ float group_sum(float v) {
 
 // Inclusive prefix sum over the 64 lanes of a wave: shifts within each row of 16 lanes
 // (DPP row_shr 1, 2, 4, 8; a lane with no source adds 0), then each row adds the totals
-// of the rows before it, read from lanes 15, 31 and 47.
+// of the rows before it, read from lanes 15, 31 and 47.  Every lane of the wave must be
+// active.
 __device__ __forceinline__ int wave_scan_incl(int x) {
   x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);
   x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);
