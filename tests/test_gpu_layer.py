@@ -92,6 +92,17 @@ def test_layer_step_end_to_end(name):
     run_and_compare(workload(name))
 
 
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("n_experts", [12, 20])
+def test_layer_step_expert_counts_off_the_grid(n_experts):
+    # expert counts that leave part of the router's 8-expert groups, and of the routing's
+    # 32-key rows, as padding
+    w = synth.with_overrides(synth.WORKLOADS["h4096_b8_ctx8k"], n_experts=n_experts,
+                             ctx=(1000,), pool_blocks=128, name=f"h4096_e{n_experts}")
+    say(f"[gpu-test] layer step {w.name}")
+    run_and_compare(synth.make_workload(w))
+
+
 def test_layer_step_front_mode_tiny():
     run_and_compare(workload("tiny_b8_ctx128"), front=True)
 
