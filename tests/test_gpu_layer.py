@@ -103,6 +103,19 @@ def test_layer_step_expert_counts_off_the_grid(n_experts):
     run_and_compare(synth.make_workload(w))
 
 
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("base,top_k", [("tiny_b8_ctx128", 1), ("tiny_b8_ctx128", 8),
+                                        ("h4096_b8_ctx8k", 1)])
+def test_layer_step_top_k_extremes(base, top_k):
+    # one choice per row (weight 1), and every expert of the tiny shape chosen by every row
+    over = dict(top_k=top_k, name=f"{base}_k{top_k}")
+    if base.startswith("h4096"):
+        over.update(ctx=(1000,), pool_blocks=128)
+    w = synth.with_overrides(synth.WORKLOADS[base], **over)
+    say(f"[gpu-test] layer step {w.name}")
+    run_and_compare(synth.make_workload(w))
+
+
 def test_layer_step_front_mode_tiny():
     run_and_compare(workload("tiny_b8_ctx128"), front=True)
 
